@@ -1,0 +1,321 @@
+// C ABI of the StreamKL library: argument validation, launch planning
+// (key-split count, fused or separate backward) and kernel launches on the
+// caller's stream.  Declared in include/streamkl.h.
+#include <mutex>
+#include <string.h>
+
+#include "../../include/streamkl.h"
+#include "kernels.hpp"
+#include "launch.hpp"
+
+namespace streamkl {
+
+// Merge of the split partial states, then the epilogue (one thread per row).
+__global__ __launch_bounds__(256) void splitk_merge_kernel(const float* __restrict__ ws, float* kl, float* lse1,
+                                                           float* lse2, int64_t BH, int n_q, int nsplit) {
+  const int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x;
+  if (i >= BH * n_q) return;
+  const int64_t bh = i / n_q;
+  const int q = (int)(i % n_q);
+  const int64_t fs = BH * (int64_t)nsplit * n_q;
+  RowState st = empty_state();
+  for (int z = 0; z < nsplit; ++z) {
+    const int64_t o = (bh * nsplit + z) * (int64_t)n_q + q;
+    RowState p = {ws[o], ws[o + fs], ws[o + 2 * fs], ws[o + 3 * fs], ws[o + 4 * fs]};
+    st = merge_state(st, p);
+  }
+  finish_state(st, kl + i, lse1 + i, lse2 + i);
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, int64_t n4) {
+  for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct DeviceInfo {
+  int checked = 0;
+  int gfx950 = 0;
+  int cus = 256;
+};
+std::mutex g_dev_mutex;
+DeviceInfo g_dev[64];
+
+// Device properties are read once per device; every later call reuses them.
+streamkl_status device_info(DeviceInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { g_last_hip_error = (int)e; return STREAMKL_ERR_HIP; }
+  if (dev < 0 || dev >= 64) return STREAMKL_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_dev_mutex);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) { g_last_hip_error = (int)e; return STREAMKL_ERR_HIP; }
+    d.gfx950 = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    d.cus = p.multiProcessorCount > 0 ? p.multiProcessorCount : 256;
+    d.checked = 1;
+  }
+  *out = d;
+  return d.gfx950 ? STREAMKL_OK : STREAMKL_ERR_UNSUPPORTED;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape checks that need no device.  Sizes are bounded so every in-head
+// offset fits in 32 bits and every grid fits in one dimension.
+streamkl_status check_shape(const streamkl_shape* s, int causal) {
+  if (!s) return STREAMKL_ERR_INVALID;
+  if (s->B < 1 || s->H < 1 || s->n_q < 1 || s->n_k < 1) return STREAMKL_ERR_INVALID;
+  if (s->dtype != STREAMKL_F32 && s->dtype != STREAMKL_BF16) return STREAMKL_ERR_INVALID;
+  if ((s->d1 != 64 && s->d1 != 128) || (s->d2 != 64 && s->d2 != 128)) return STREAMKL_ERR_UNSUPPORTED;
+  if (s->n_q > (1 << 24) || s->n_k > (1 << 24)) return STREAMKL_ERR_UNSUPPORTED;
+  if (s->B > (int64_t(1) << 20) || s->H > (int64_t(1) << 20) || s->B * s->H > (int64_t(1) << 20))
+    return STREAMKL_ERR_UNSUPPORTED;
+  if (causal && s->n_q > s->n_k) return STREAMKL_ERR_INVALID;
+  return STREAMKL_OK;
+}
+
+float log2e_scale(float scale, int d) { return (scale > 0.f ? scale : 1.0f / sqrtf((float)d)) * kLog2e; }
+float plain_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
+
+FwdLaunch pick_fwd(int dtype, int d1, int d2) {
+#define SKL_PICK(tn, a, b) if (d1 == a && d2 == b) return launch_fwd_##tn##_##a##_##b;
+  if (dtype == STREAMKL_F32) { SKL_PICK(f32, 64, 64) SKL_PICK(f32, 64, 128) SKL_PICK(f32, 128, 64) SKL_PICK(f32, 128, 128) }
+  else { SKL_PICK(bf16, 64, 64) SKL_PICK(bf16, 64, 128) SKL_PICK(bf16, 128, 64) SKL_PICK(bf16, 128, 128) }
+#undef SKL_PICK
+  return nullptr;
+}
+DqLaunch pick_dq(int dtype, int d1, int d2) {
+#define SKL_PICK(tn, a, b) if (d1 == a && d2 == b) return launch_bwd_dq_##tn##_##a##_##b;
+  if (dtype == STREAMKL_F32) { SKL_PICK(f32, 64, 64) SKL_PICK(f32, 64, 128) SKL_PICK(f32, 128, 64) SKL_PICK(f32, 128, 128) }
+  else { SKL_PICK(bf16, 64, 64) SKL_PICK(bf16, 64, 128) SKL_PICK(bf16, 128, 64) SKL_PICK(bf16, 128, 128) }
+#undef SKL_PICK
+  return nullptr;
+}
+DkLaunch pick_dk(int dtype, int d1, int d2) {
+#define SKL_PICK(tn, a, b) if (d1 == a && d2 == b) return launch_bwd_dk_##tn##_##a##_##b;
+  if (dtype == STREAMKL_F32) { SKL_PICK(f32, 64, 64) SKL_PICK(f32, 64, 128) SKL_PICK(f32, 128, 64) SKL_PICK(f32, 128, 128) }
+  else { SKL_PICK(bf16, 64, 64) SKL_PICK(bf16, 64, 128) SKL_PICK(bf16, 128, 64) SKL_PICK(bf16, 128, 128) }
+#undef SKL_PICK
+  return nullptr;
+}
+
+// Key-split plan.  Split-K (Method 3 of the technical summary) is for shapes
+// whose query blocks alone cannot fill the chip: aim for >= 4 workgroups per
+// CU, keep >= 4 key tiles per split.
+int plan_splits(const streamkl_shape* s, int causal, const streamkl_launch* l, int cus) {
+  (void)causal;
+  const int64_t tiles = cdiv(s->n_k, kFwdTile);
+  if (l && l->num_splits > 0) return (int)(l->num_splits < tiles ? l->num_splits : tiles);
+  const int64_t base = s->B * s->H * cdiv(s->n_q, kFwdRows);
+  const int64_t want = 4 * (int64_t)cus;
+  if (base >= want / 2) return 1;
+  int64_t sp = cdiv(want, base);
+  const int64_t maxsp = tiles / 4 > 1 ? tiles / 4 : 1;
+  if (sp > maxsp) sp = maxsp;
+  if (sp > 4096) sp = 4096;
+  return (int)(sp < 1 ? 1 : sp);
+}
+
+size_t ws_bytes(const streamkl_shape* s, int splits) {
+  return splits > 1 ? (size_t)20 * (size_t)(s->B * s->H) * (size_t)s->n_q * (size_t)splits : 0;
+}
+
+// Backward mode plan.  The fused kernel (Method 2: each query-key tile pair
+// visited once, dQ by atomics) moves 4*d_s bytes of fp32 atomics per query
+// row and 128-key block; on gfx950 device-scope fp32 atomics sustain about
+// 1.2 TB/s, so it only pays when the query-outer dQ kernel of the separate
+// mode cannot fill the chip (few query rows, long key ranges).
+int plan_bwd(const streamkl_shape* s, int causal, int setting, const streamkl_launch* l, int cus) {
+  if (l && l->bwd_mode != STREAMKL_BWD_AUTO) return l->bwd_mode;
+  const double ds = setting == 1 ? s->d2 : s->d1;
+  const double pairs = causal ? (double)s->n_q * (s->n_q + 1) / 2 + (double)s->n_q * (s->n_k - s->n_q)
+                              : (double)s->n_q * s->n_k;
+  const double heads = (double)(s->B * s->H);
+  const double rate = 1.0e15;  // sustained MFMA FLOP/s assumed for these kernels
+  const double f_qk = 2.0 * (s->d1 + s->d2), f_grad = 2.0 * ds;
+  const double wg_dk = heads * cdiv(s->n_k, kBwdKRows), wg_dq = heads * cdiv(s->n_q, kBwdQRows);
+  const double full = 2.0 * cus;
+  const double u_dk = wg_dk < full ? wg_dk / full : 1.0, u_dq = wg_dq < full ? wg_dq / full : 1.0;
+  const double t_sep = heads * pairs * (f_qk + f_grad) / (rate * u_dk) + heads * pairs * (f_qk + f_grad) / (rate * u_dq);
+  const double atomic_bytes = heads * pairs * 4.0 * ds / kBwdKRows;
+  double t_fused = heads * pairs * (f_qk + 2 * f_grad) / (rate * u_dk);
+  const double t_atomic = atomic_bytes / 1.2e12;
+  if (t_atomic > t_fused) t_fused = t_atomic;
+  return t_fused < t_sep ? STREAMKL_BWD_FUSED : STREAMKL_BWD_SEPARATE;
+}
+
+streamkl_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return STREAMKL_OK;
+  g_last_hip_error = (int)e;
+  return STREAMKL_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace streamkl
+
+using namespace streamkl;
+
+extern "C" {
+
+int streamkl_version(void) { return 1; }
+
+const char* streamkl_status_string(int status) {
+  switch (status) {
+    case STREAMKL_OK: return "ok";
+    case STREAMKL_ERR_INVALID: return "invalid argument";
+    case STREAMKL_ERR_UNSUPPORTED: return "unsupported shape or device";
+    case STREAMKL_ERR_WORKSPACE: return "workspace missing or too small";
+    case STREAMKL_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int streamkl_last_hip_error(void) { return g_last_hip_error; }
+
+int streamkl_fwd_plan(const streamkl_shape* shape, int causal, const streamkl_launch* launch) {
+  if (check_shape(shape, causal) != STREAMKL_OK) return 0;
+  if (launch && launch->num_splits < 0) return 0;
+  DeviceInfo d;
+  const int cus = device_info(&d) == STREAMKL_OK ? d.cus : 256;
+  int sp = plan_splits(shape, causal, launch, cus);
+  if (sp > 1 && (!launch || launch->num_splits == 0) &&
+      (!launch || !launch->workspace || launch->workspace_bytes < ws_bytes(shape, sp)))
+    sp = 1;
+  return sp;
+}
+
+size_t streamkl_fwd_workspace_bytes(const streamkl_shape* shape, int causal, const streamkl_launch* launch) {
+  if (check_shape(shape, causal) != STREAMKL_OK) return 0;
+  if (launch && launch->num_splits < 0) return 0;
+  DeviceInfo d;
+  const int cus = device_info(&d) == STREAMKL_OK ? d.cus : 256;
+  return ws_bytes(shape, plan_splits(shape, causal, launch, cus));
+}
+
+streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                             float scale1, float scale2, float* out_kl, float* out_lse1, float* out_lse2,
+                             const streamkl_shape* shape, const streamkl_launch* launch, void* stream) {
+  streamkl_status st = check_shape(shape, causal);
+  if (st != STREAMKL_OK) return st;
+  if (!Q1 || !K1 || !Q2 || !K2 || !out_kl || !out_lse1 || !out_lse2) return STREAMKL_ERR_INVALID;
+  if (!aligned(Q1, 16) || !aligned(K1, 16) || !aligned(Q2, 16) || !aligned(K2, 16)) return STREAMKL_ERR_INVALID;
+  if (!aligned(out_kl, 4) || !aligned(out_lse1, 4) || !aligned(out_lse2, 4)) return STREAMKL_ERR_INVALID;
+  if (!(scale1 == scale1) || !(scale2 == scale2)) return STREAMKL_ERR_INVALID;
+  if (launch && (launch->num_splits < 0 || launch->bwd_mode < 0 || launch->bwd_mode > 4)) return STREAMKL_ERR_INVALID;
+  DeviceInfo dev;
+  st = device_info(&dev);
+  if (st != STREAMKL_OK) return st;
+
+  int splits = plan_splits(shape, causal, launch, dev.cus);
+  const size_t need = ws_bytes(shape, splits);
+  if (splits > 1) {
+    const bool have = launch && launch->workspace && launch->workspace_bytes >= need &&
+                      aligned(launch->workspace, 4);
+    if (!have) {
+      if (launch && launch->num_splits > 1) return STREAMKL_ERR_WORKSPACE;
+      splits = 1;
+    }
+  }
+  FwdLaunch fn = pick_fwd(shape->dtype, shape->d1, shape->d2);
+  if (!fn) return STREAMKL_ERR_UNSUPPORTED;
+
+  FwdArgs a;
+  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
+  a.kl = out_kl; a.lse1 = out_lse1; a.lse2 = out_lse2;
+  a.ws = splits > 1 ? static_cast<float*>(launch->workspace) : nullptr;
+  a.BH = shape->B * shape->H;
+  a.n_q = (int)shape->n_q;
+  a.n_k = (int)shape->n_k;
+  a.nsplit = splits;
+  const int64_t tiles = cdiv(shape->n_k, kFwdTile);
+  a.keys_per_split = (int)(cdiv(tiles, splits) * kFwdTile);
+  a.nqb = (int)cdiv(shape->n_q, kFwdRows);
+  a.causal = causal ? 1 : 0;
+  a.c1 = log2e_scale(scale1, shape->d1);
+  a.c2 = log2e_scale(scale2, shape->d2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(fn(a, a.BH * a.nqb * splits, s));
+  if (st != STREAMKL_OK || splits == 1) return st;
+  const int64_t rows = a.BH * a.n_q;
+  hipLaunchKernelGGL(splitk_merge_kernel, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, s,
+                     (const float*)a.ws, out_kl, out_lse1, out_lse2, a.BH, a.n_q, splits);
+  return hip_status(hipGetLastError());
+}
+
+int streamkl_bwd_plan(const streamkl_shape* shape, int causal, int setting, const streamkl_launch* launch) {
+  if (check_shape(shape, causal) != STREAMKL_OK || (setting != 1 && setting != 2)) return 0;
+  if (launch && (launch->bwd_mode < 0 || launch->bwd_mode > 4)) return 0;
+  DeviceInfo d;
+  const int cus = device_info(&d) == STREAMKL_OK ? d.cus : 256;
+  return plan_bwd(shape, causal, setting, launch, cus);
+}
+
+streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                             float scale1, float scale2, const float* kl, const float* lse1, const float* lse2,
+                             const float* d_kl, float* dQ, float* dK, const streamkl_shape* shape,
+                             const streamkl_launch* launch, void* stream) {
+  if (setting != 1 && setting != 2) return STREAMKL_ERR_INVALID;
+  streamkl_status st = check_shape(shape, causal);
+  if (st != STREAMKL_OK) return st;
+  if (launch && (launch->num_splits < 0 || launch->bwd_mode < 0 || launch->bwd_mode > 4)) return STREAMKL_ERR_INVALID;
+  const int req = launch ? launch->bwd_mode : STREAMKL_BWD_AUTO;
+  const bool need_dq = req != STREAMKL_BWD_DK_ONLY, need_dk = req != STREAMKL_BWD_DQ_ONLY;
+  if (!Q1 || !K1 || !Q2 || !K2 || !lse1 || !lse2 || !d_kl) return STREAMKL_ERR_INVALID;
+  if ((need_dq && !dQ) || (need_dk && !dK)) return STREAMKL_ERR_INVALID;
+  if (setting == 2 && !kl) return STREAMKL_ERR_INVALID;
+  if (!aligned(Q1, 16) || !aligned(K1, 16) || !aligned(Q2, 16) || !aligned(K2, 16)) return STREAMKL_ERR_INVALID;
+  if (!aligned(lse1, 4) || !aligned(lse2, 4) || !aligned(d_kl, 4) || (kl && !aligned(kl, 4)))
+    return STREAMKL_ERR_INVALID;
+  if ((dQ && !aligned(dQ, 16)) || (dK && !aligned(dK, 4))) return STREAMKL_ERR_INVALID;
+  if (!(scale1 == scale1) || !(scale2 == scale2)) return STREAMKL_ERR_INVALID;
+  DeviceInfo dev;
+  st = device_info(&dev);
+  if (st != STREAMKL_OK) return st;
+  DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
+  DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
+  if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
+  const int mode = plan_bwd(shape, causal, setting, launch, dev.cus);
+
+  BwdArgs a;
+  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
+  a.kl = kl; a.lse1 = lse1; a.lse2 = lse2; a.g = d_kl;
+  a.dq = dQ; a.dk = dK;
+  a.BH = shape->B * shape->H;
+  a.n_q = (int)shape->n_q;
+  a.n_k = (int)shape->n_k;
+  a.causal = causal ? 1 : 0;
+  a.c1 = log2e_scale(scale1, shape->d1);
+  a.c2 = log2e_scale(scale2, shape->d2);
+  a.scale_s = setting == 1 ? plain_scale(scale2, shape->d2) : plain_scale(scale1, shape->d1);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
+  if (mode == STREAMKL_BWD_FUSED) {
+    const int ds = setting == 1 ? shape->d2 : shape->d1;
+    const int64_t n4 = a.BH * a.n_q * ds / 4;
+    int64_t fb = cdiv(n4, 256);
+    if (fb > 65536) fb = 65536;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)fb), dim3(256), 0, s, reinterpret_cast<float4*>(dQ), n4);
+    st = hip_status(hipGetLastError());
+    if (st != STREAMKL_OK) return st;
+    a.nblk = (int)nkb;
+    return hip_status(fk(a, setting, true, a.BH * nkb, s));
+  }
+  if (mode != STREAMKL_BWD_DQ_ONLY) {
+    a.nblk = (int)nkb;
+    st = hip_status(fk(a, setting, false, a.BH * nkb, s));
+    if (st != STREAMKL_OK) return st;
+  }
+  if (mode == STREAMKL_BWD_DK_ONLY) return STREAMKL_OK;
+  a.nblk = (int)nqb;
+  return hip_status(fq(a, setting, a.BH * nqb, s));
+}
+
+}  // extern "C"

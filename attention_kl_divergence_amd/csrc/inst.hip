@@ -1,0 +1,40 @@
+// One translation unit per (dtype, d1, d2): compiled several times with
+// -DSKL_T=<type> -DSKL_TN=<tag> -DSKL_D1=<d1> -DSKL_D2=<d2> so the kernel
+// instantiations build in parallel.  Each exports three launchers with
+// C++ linkage, named launch_<kind>_<tag>_<d1>_<d2>.
+#include "kernels.hpp"
+#include "launch.hpp"
+
+#define SKL_CAT_(a, b, c, d) a##_##b##_##c##_##d
+#define SKL_CAT(a, b, c, d) SKL_CAT_(a, b, c, d)
+
+namespace streamkl {
+
+hipError_t SKL_CAT(launch_fwd, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
+  hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, 4, kFwdTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t SKL_CAT(launch_bwd_dq, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, int64_t nblocks,
+                                                           hipStream_t st) {
+  if (setting == 1)
+    hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 1, kBwdKeyTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 2, kBwdKeyTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t SKL_CAT(launch_bwd_dk, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, bool fused, int64_t nblocks,
+                                                           hipStream_t st) {
+  const dim3 g((unsigned)nblocks), b(256);
+  if (setting == 1) {
+    if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, true>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, false>), g, b, 0, st, a);
+  } else {
+    if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, true>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, false>), g, b, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace streamkl

@@ -1,0 +1,37 @@
+// Tile sizes and the launcher table shared by the host layer and the
+// per-(dtype, d1, d2) instantiation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace streamkl {
+
+struct FwdArgs;
+struct BwdArgs;
+
+constexpr int kFwdRows = 128;     // query rows per forward workgroup (4 waves x 32)
+constexpr int kFwdTile = 64;      // key rows per forward LDS tile
+constexpr int kBwdQRows = 128;    // query rows per dQ workgroup
+constexpr int kBwdKeyTile = 64;   // key rows per dQ-kernel LDS tile
+constexpr int kBwdKRows = 128;    // key rows per dK workgroup (4 waves x 32)
+
+using FwdLaunch = hipError_t (*)(const FwdArgs&, int64_t, hipStream_t);
+using DqLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t);
+using DkLaunch = hipError_t (*)(const BwdArgs&, int, bool, int64_t, hipStream_t);
+
+#define SKL_DECL(tn, d1, d2)                                                                   \
+  hipError_t launch_fwd_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);              \
+  hipError_t launch_bwd_dq_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t);      \
+  hipError_t launch_bwd_dk_##tn##_##d1##_##d2(const BwdArgs&, int, bool, int64_t, hipStream_t);
+SKL_DECL(f32, 64, 64)
+SKL_DECL(f32, 64, 128)
+SKL_DECL(f32, 128, 64)
+SKL_DECL(f32, 128, 128)
+SKL_DECL(bf16, 64, 64)
+SKL_DECL(bf16, 64, 128)
+SKL_DECL(bf16, 128, 64)
+SKL_DECL(bf16, 128, 128)
+#undef SKL_DECL
+
+}  // namespace streamkl

@@ -1,0 +1,226 @@
+"""Thin Python binding of libstreamkl.so (the C ABI in include/streamkl.h).
+
+Argument marshalling only: torch supplies device memory (outputs and the
+split-K workspace) and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libstreamkl.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+F32, BF16 = 0, 1
+BWD_AUTO, BWD_FUSED, BWD_SEPARATE, BWD_DK_ONLY, BWD_DQ_ONLY = 0, 1, 2, 3, 4
+
+
+class StreamKLError(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{what}: {_lib().streamkl_status_string(status).decode()} (status {status})"
+        if status == ERR_HIP:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg)
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("n_q", ctypes.c_int64), ("n_k", ctypes.c_int64),
+                ("d1", ctypes.c_int32), ("d2", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Launch(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("bwd_mode", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_kl_divergence_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        sp, lp = ctypes.POINTER(Shape), ctypes.POINTER(Launch)
+        lib.streamkl_fwd.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, vp, sp, lp, vp]
+        lib.streamkl_fwd.restype = i32
+        lib.streamkl_bwd.argtypes = [i32, vp, vp, vp, vp, i32, f32, f32, vp, vp, vp, vp, vp, vp, sp, lp, vp]
+        lib.streamkl_bwd.restype = i32
+        lib.streamkl_fwd_workspace_bytes.argtypes = [sp, i32, lp]
+        lib.streamkl_fwd_workspace_bytes.restype = sz
+        lib.streamkl_fwd_plan.argtypes = [sp, i32, lp]
+        lib.streamkl_fwd_plan.restype = i32
+        lib.streamkl_bwd_plan.argtypes = [sp, i32, i32, lp]
+        lib.streamkl_bwd_plan.restype = i32
+        lib.streamkl_status_string.argtypes = [i32]
+        lib.streamkl_status_string.restype = ctypes.c_char_p
+        lib.streamkl_last_hip_error.argtypes = []
+        lib.streamkl_last_hip_error.restype = i32
+        lib.streamkl_version.argtypes = []
+        lib.streamkl_version.restype = i32
+        _LIB = lib
+    return _LIB
+
+
+def library():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _lib()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t}; expected float32 or bfloat16")
+
+
+def make_shape(B, H, n_q, n_k, d1, d2, dtype) -> Shape:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return Shape(B, H, n_q, n_k, d1, d2, code)
+
+
+def shape_of(q1, k1, q2, k2) -> Shape:
+    for t in (q1, k1, q2, k2):
+        if t.dim() != 4:
+            raise ValueError("Q and K tensors must be [B, H, N, d]")
+        if not t.is_contiguous():
+            raise ValueError("Q and K tensors must be contiguous")
+        if t.dtype != q1.dtype:
+            raise ValueError("Q1, K1, Q2, K2 must share one dtype")
+        if t.device != q1.device:
+            raise ValueError("Q1, K1, Q2, K2 must be on one device")
+    B, H, n_q, d1 = q1.shape
+    n_k = k1.shape[2]
+    d2 = q2.shape[3]
+    if tuple(k1.shape) != (B, H, n_k, d1) or tuple(q2.shape) != (B, H, n_q, d2) or tuple(k2.shape) != (B, H, n_k, d2):
+        raise ValueError("inconsistent Q/K shapes")
+    return make_shape(B, H, n_q, n_k, d1, d2, q1.dtype)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise StreamKLError(status, what, _lib().streamkl_last_hip_error())
+
+
+def fwd_plan(shape: Shape, causal: bool, num_splits: int = 0, with_workspace: bool = True) -> int:
+    """Key-split count the forward would use."""
+    lib = _lib()
+    ln = Launch(num_splits, 0, None, 0)
+    if with_workspace:
+        ln.workspace_bytes = lib.streamkl_fwd_workspace_bytes(ctypes.byref(shape), int(causal), ctypes.byref(ln))
+        ln.workspace = 16 if ln.workspace_bytes else None  # placeholder address, never dereferenced by the plan
+    return lib.streamkl_fwd_plan(ctypes.byref(shape), int(causal), ctypes.byref(ln))
+
+
+def fwd_workspace_bytes(shape: Shape, causal: bool, num_splits: int = 0) -> int:
+    ln = Launch(num_splits, 0, None, 0)
+    return _lib().streamkl_fwd_workspace_bytes(ctypes.byref(shape), int(causal), ctypes.byref(ln))
+
+
+def bwd_plan(shape: Shape, causal: bool, setting: int, bwd_mode: int = BWD_AUTO) -> int:
+    ln = Launch(0, bwd_mode, None, 0)
+    return _lib().streamkl_bwd_plan(ctypes.byref(shape), int(causal), int(setting), ctypes.byref(ln))
+
+
+def streamkl_fwd(q1, k1, q2, k2, causal: bool, scale1: float = 0.0, scale2: float = 0.0,
+                 num_splits: int = 0, out=None, workspace=None):
+    """Forward: returns (kl, lse1, lse2), fp32 [B, H, n_q].
+
+    num_splits: 0 = library's choice, 1 = no key split, k = k key splits.
+    out: optional preallocated (kl, lse1, lse2).  workspace: optional uint8
+    device tensor (allocated here when a split needs one and none is given).
+    """
+    shp = shape_of(q1, k1, q2, k2)
+    dev = q1.device
+    if out is None:
+        kw = dict(device=dev, dtype=torch.float32)
+        out = tuple(torch.empty((shp.B, shp.H, shp.n_q), **kw) for _ in range(3))
+    kl, lse1, lse2 = out
+    ln = Launch(num_splits, 0, None, 0)
+    need = _lib().streamkl_fwd_workspace_bytes(ctypes.byref(shp), int(causal), ctypes.byref(ln))
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ln.workspace = workspace.data_ptr()
+        ln.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = _lib().streamkl_fwd(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), int(causal),
+                             float(scale1), float(scale2), kl.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
+                             ctypes.byref(shp), ctypes.byref(ln), _stream(dev))
+    _check(st, "streamkl_fwd")
+    return kl, lse1, lse2
+
+
+def streamkl_bwd(setting: int, q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
+                 scale1: float = 0.0, scale2: float = 0.0, bwd_mode: int = BWD_AUTO, out=None):
+    """Backward: returns (dQ, dK) in fp32 for the trained model.
+
+    setting 1 -> (dQ2, dK2) with P1 fixed; setting 2 -> (dQ1, dK1) with P2 fixed.
+    """
+    shp = shape_of(q1, k1, q2, k2)
+    dev = q1.device
+    ds = shp.d2 if setting == 1 else shp.d1
+    if out is None:
+        kw = dict(device=dev, dtype=torch.float32)
+        out = (None if bwd_mode == BWD_DK_ONLY else torch.empty((shp.B, shp.H, shp.n_q, ds), **kw),
+               None if bwd_mode == BWD_DQ_ONLY else torch.empty((shp.B, shp.H, shp.n_k, ds), **kw))
+    dq, dk = out
+    for t in (lse1, lse2, d_kl) + ((kl,) if kl is not None else ()):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != shp.B * shp.H * shp.n_q:
+            raise ValueError("kl, lse1, lse2, d_kl must be contiguous fp32 [B, H, n_q]")
+    ln = Launch(0, bwd_mode, None, 0)
+    st = _lib().streamkl_bwd(int(setting), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), int(causal),
+                             float(scale1), float(scale2), kl.data_ptr() if kl is not None else None,
+                             lse1.data_ptr(), lse2.data_ptr(), d_kl.data_ptr(),
+                             dq.data_ptr() if dq is not None else None, dk.data_ptr() if dk is not None else None,
+                             ctypes.byref(shp), ctypes.byref(ln), _stream(dev))
+    _check(st, "streamkl_bwd")
+    return dq, dk
+
+
+class _KLFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q1, k1, q2, k2, causal, scale1, scale2, bwd_mode):
+        kl, lse1, lse2 = streamkl_fwd(q1, k1, q2, k2, causal, scale1, scale2)
+        ctx.save_for_backward(q1, k1, q2, k2, kl, lse1, lse2)
+        ctx.causal, ctx.scale1, ctx.scale2, ctx.bwd_mode = causal, scale1, scale2, bwd_mode
+        return kl
+
+    @staticmethod
+    def backward(ctx, g):
+        q1, k1, q2, k2, kl, lse1, lse2 = ctx.saved_tensors
+        g = g.contiguous().to(torch.float32)
+        grads = [None, None, None, None]
+        if ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
+            dq2, dk2 = streamkl_bwd(1, q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1, ctx.scale2,
+                                    ctx.bwd_mode)
+            grads[2], grads[3] = dq2.to(q2.dtype), dk2.to(k2.dtype)
+        if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
+            dq1, dk1 = streamkl_bwd(2, q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1, ctx.scale2,
+                                    ctx.bwd_mode)
+            grads[0], grads[1] = dq1.to(q1.dtype), dk1.to(k1.dtype)
+        return (*grads, None, None, None, None)
+
+
+def attention_kl(q1, k1, q2, k2, causal: bool = False, scale1: float = 0.0, scale2: float = 0.0,
+                 bwd_mode: int = BWD_AUTO):
+    """Per-row KL(P1 || P2) as an autograd function (gradients by streamkl_bwd).
+
+    Gradients flow to whichever of (Q1, K1) / (Q2, K2) require grad: the
+    student side uses setting 1 (teacher distribution held fixed), the
+    teacher side setting 2 (student distribution held fixed).
+    """
+    return _KLFunction.apply(q1, k1, q2, k2, causal, scale1, scale2, bwd_mode)

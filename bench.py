@@ -1,0 +1,191 @@
+"""Benchmark of the attention-KL hot path on one MI355X.
+
+One step = the StreamKL forward (KL, LSE1, LSE2) plus the setting-1
+backward (dQ2, dK2) over one batch of synthetic inputs already resident in
+HBM.  Default workload: B=1, H=32, N_Q=N_K=65536, d=128, bf16, causal.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  `value` is algorithmic TFLOP/s of the whole step:
+forward 2(d1+d2) and setting-1 backward 2(d1+d2)+4*d2 FLOPs per visible
+(query, key) pair; recomputation and masked-tile waste are not credited.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="h32-n64k-d128-bf16-causal")
+    ap.add_argument("--bwd-mode", default="auto", choices=["auto", "fused", "separate"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows of the oracle sample")
+    return ap.parse_args()
+
+
+def pairs_of(w):
+    n_q, n_k = w.n_q, w.n_k
+    if not w.causal:
+        return w.B * w.H * n_q * n_k
+    return w.B * w.H * (n_q * (n_q + 1) // 2 + n_q * (n_k - n_q))
+
+
+def cpu_baseline(w, rows_wanted):
+    """The fp64 oracle on the host: forward + setting-1 backward for a bounded
+    sample (the last rows of head 0, which see the full key range), reported
+    as algorithmic TFLOP/s like the GPU value."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    small = w.with_(H=1)
+    q1, k1, q2, k2 = workloads.generate(small, "cpu")
+    g = workloads.upstream_grad(small, "cpu", "mean")
+    hi = [t[0, 0].float().numpy().astype(np.float64) for t in (q1, k1, q2, k2)]
+    rows = np.arange(max(0, w.n_q - rows_wanted), w.n_q)
+    t0 = time.perf_counter()
+    oracle.head_forward(*hi, w.causal, rows=rows, block=64)
+    oracle.head_backward(1, *hi, w.causal, g[0, 0].numpy(), rows=rows, block=64)
+    dt = time.perf_counter() - t0
+    vis = oracle.valid_mask(rows, w.n_q, w.n_k, w.causal).sum()
+    flops = float(vis) * (2 * (w.d1 + w.d2) + 2 * (w.d1 + w.d2) + 4 * w.d2)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"numpy fp64 oracle, forward + setting-1 backward of the last {len(rows)} query rows of "
+                      f"one head over all {w.n_k} keys ({int(vis)} visible pairs)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the attention-KL path shards by heads "
+                                   "with no communication, so N GPUs run N independent copies; "
+                                   "run with --gpus 1"}))
+        return 2
+    import torch
+    import workloads
+    from attention_kl_divergence_amd import streamkl as sk
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q1, k1, q2, k2 = workloads.generate(w, dev)
+    g = workloads.upstream_grad(w, dev, "mean")
+    shp = sk.shape_of(q1, k1, q2, k2)
+    mode = {"auto": sk.BWD_AUTO, "fused": sk.BWD_FUSED, "separate": sk.BWD_SEPARATE}[args.bwd_mode]
+    plan = sk.bwd_plan(shp, w.causal, 1, mode)
+    splits = sk.fwd_plan(shp, w.causal)
+
+    f32 = dict(device=dev, dtype=torch.float32)
+    kl, l1, l2 = (torch.empty((w.B, w.H, w.n_q), **f32) for _ in range(3))
+    dq = torch.empty((w.B, w.H, w.n_q, w.d2), **f32)
+    dk = torch.empty((w.B, w.H, w.n_k, w.d2), **f32)
+    ws_bytes = sk.fwd_workspace_bytes(shp, w.causal)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    # Each kernel is launched by its own ABI call so HIP events on the launch
+    # stream bracket exactly one kernel (split-K adds its merge kernel).
+    if plan == sk.BWD_FUSED:
+        calls = [("fwd", lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, out=(kl, l1, l2), workspace=ws)),
+                 ("bwd_fused", lambda: sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g,
+                                                       bwd_mode=sk.BWD_FUSED, out=(dq, dk)))]
+    else:
+        calls = [("fwd", lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, out=(kl, l1, l2), workspace=ws)),
+                 ("bwd_dk", lambda: sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g,
+                                                    bwd_mode=sk.BWD_DK_ONLY, out=(None, dk))),
+                 ("bwd_dq", lambda: sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g,
+                                                    bwd_mode=sk.BWD_DQ_ONLY, out=(dq, None)))]
+
+    for _ in range(args.warmup):
+        for _, c in calls:
+            c()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for (name, c), (e0, e1) in zip(calls, ev[s]):
+            e0.record(stream)
+            c()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_call = {name: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
+                for i, (name, _) in enumerate(calls)}
+    ms_step = wall * 1e3 / args.steps
+    pairs = pairs_of(w)
+    f_fwd = 2 * (w.d1 + w.d2) * pairs
+    f_bwd = (2 * (w.d1 + w.d2) + 4 * w.d2) * pairs
+    flops_step = f_fwd + f_bwd
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    # algorithmic FLOPs each kernel is credited with (recompute in the dQ
+    # kernel of the separate mode is not credited)
+    credit = {"fwd": f_fwd, "bwd_fused": f_bwd,
+              "bwd_dk": (2 * (w.d1 + w.d2) + 2 * w.d2) * pairs, "bwd_dq": 2 * w.d2 * pairs}
+    dom = max(per_call, key=per_call.get)
+    ach = credit[dom] / (per_call[dom] * 1e-3) / 1e12
+    kernel_names = {"fwd": "fwd_kernel", "bwd_fused": "bwd_dk_kernel<FUSED>", "bwd_dk": "bwd_dk_kernel",
+                    "bwd_dq": "bwd_dq_kernel"}
+    roof = {"bound": "mfma", "kernel": kernel_names[dom], "achieved": round(ach, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+            "avg_ms": round(per_call[dom], 4)}
+
+    extra_hbm = 3 * 4 * w.B * w.H * w.n_q + ws_bytes
+    out = {
+        "metric": "attn-KL fwd/bwd TFLOP/s + % bf16 MFMA peak, H32 d128 causal 64K",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "n_q": w.n_q, "n_k": w.n_k, "d1": w.d1, "d2": w.d2,
+                   "causal": w.causal, "bwd_setting": 1,
+                   "bwd_mode": {sk.BWD_FUSED: "fused", sk.BWD_SEPARATE: "separate"}[plan],
+                   "fwd_splits": splits, "parallelism": "single GPU"},
+        "pct_of_mfma_peak": round(100 * value / peak, 2),
+        "per_kernel_ms": {k: round(v, 4) for k, v in per_call.items()},
+        "algorithmic_tflop_per_step": round(flops_step / 1e12, 3),
+        "extra_hbm_bytes": extra_hbm,
+        "materialised_bytes_avoided": 2 * w.B * w.H * w.n_q * w.n_k * 2,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

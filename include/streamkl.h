@@ -1,0 +1,158 @@
+/*
+ * streamkl.h — C ABI of the fused attention KL-divergence library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (StreamKL, arXiv 2606.20005; technical summary pages
+ * "StreamKL" on gist.science, ja/fr/ko):
+ *
+ *   S_t = scale_t * Q_t K_t^T            t = 1 (teacher), 2 (student)
+ *   P_t = row-wise softmax of S_t over the visible keys
+ *   KL[i] = sum_j P1[i,j] (log P1[i,j] - log P2[i,j])   = KL(P1 || P2)
+ *
+ * computed in one streaming pass over key tiles without materialising the
+ * N_Q x N_K distributions (Problem statement; Method 1, online formulation
+ * L = acc/l1 + LSE2 - LSE1 with LSE_t = m_t + log l_t).  Only KL, LSE1 and
+ * LSE2 are kept for the backward, which regenerates P_t = exp(S_t - LSE_t)
+ * tile by tile (Method 2, recomputation strategy).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers (HIP device memory of the current
+ *   device), 16-byte aligned.  Descriptor pointers (streamkl_shape,
+ *   streamkl_launch) are HOST pointers, read during the call only.
+ * - Q_t is [B, H, n_q, d_t] and K_t is [B, H, n_k, d_t], row-major and
+ *   contiguous, all four in the dtype of shape->dtype (fp32 or bf16).
+ *   Supported head dims: d_t in {64, 128}; d1 and d2 may differ.
+ * - Per-row vectors (kl, lse1, lse2, d_kl) are fp32 [B, H, n_q].
+ * - causal != 0 applies a bottom-right aligned mask: key j is visible to
+ *   query i iff j <= i + (n_k - n_q); this requires n_q <= n_k.  Key tiles
+ *   past the boundary are skipped (Method 1).
+ * - scale_t <= 0 selects 1/sqrt(d_t).
+ * - LSE values are natural logarithms.
+ * - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *   enqueues work: no host synchronisation, no device allocation, no
+ *   device memory freed.  The caller owns every buffer, including the
+ *   workspace.
+ * - Every argument is validated on the host before anything is enqueued;
+ *   a call that returns an error has enqueued nothing and written nothing.
+ *   Errors are reported only through the return value.  If a HIP launch
+ *   fails the call returns STREAMKL_ERR_HIP and streamkl_last_hip_error()
+ *   gives the hipError_t value (per calling thread).
+ */
+#ifndef STREAMKL_H_
+#define STREAMKL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STREAMKL_OK = 0,
+  STREAMKL_ERR_INVALID = 1,     /* null pointer, bad size, misaligned pointer, bad enum */
+  STREAMKL_ERR_UNSUPPORTED = 2, /* head dim outside {64,128}, device not gfx950 */
+  STREAMKL_ERR_WORKSPACE = 3,   /* split-K requested but workspace missing or too small */
+  STREAMKL_ERR_HIP = 4          /* a HIP runtime call failed */
+} streamkl_status;
+
+typedef enum { STREAMKL_F32 = 0, STREAMKL_BF16 = 1 } streamkl_dtype;
+
+typedef enum {
+  STREAMKL_BWD_AUTO = 0,     /* choose by the cost model of streamkl_bwd_plan */
+  STREAMKL_BWD_FUSED = 1,    /* one kernel per key block, dQ by fp32 atomics */
+  STREAMKL_BWD_SEPARATE = 2, /* a key-outer dK kernel, then a query-outer dQ kernel */
+  STREAMKL_BWD_DK_ONLY = 3,  /* only the key-outer dK kernel; dQ is not touched (may be NULL) */
+  STREAMKL_BWD_DQ_ONLY = 4   /* only the query-outer dQ kernel; dK is not touched (may be NULL) */
+} streamkl_bwd_mode;
+
+/* Problem shape (host struct). */
+typedef struct {
+  int64_t B, H, n_q, n_k;
+  int32_t d1, d2;   /* head dims of model 1 (teacher) and model 2 (student) */
+  int32_t dtype;    /* streamkl_dtype */
+} streamkl_shape;
+
+/* Launch options (host struct; a NULL pointer means all defaults). */
+typedef struct {
+  int32_t num_splits;      /* forward: 0 = auto, 1 = no key split, k = k key splits */
+  int32_t bwd_mode;        /* streamkl_bwd_mode */
+  void* workspace;         /* device memory for split-K partial states, may be NULL */
+  size_t workspace_bytes;
+} streamkl_launch;
+
+/*
+ * Bytes of workspace the forward needs for this shape and launch options
+ * (0 when no key split is used).  With num_splits = 0 (auto) this is the
+ * size for the split count the library would choose.  Returns 0 for
+ * invalid shapes.  Split-K: the technical summary, Method 3 (GPU kernel
+ * optimisations), partitions the key dimension across thread blocks for
+ * small N_Q; each split leaves five fp32 partial scalars per row, so the
+ * workspace is 20 * B * H * n_q * splits bytes.
+ */
+size_t streamkl_fwd_workspace_bytes(const streamkl_shape* shape, int causal,
+                                    const streamkl_launch* launch);
+
+/* The key-split count the forward will use (>= 1), or 0 for invalid input. */
+int streamkl_fwd_plan(const streamkl_shape* shape, int causal, const streamkl_launch* launch);
+
+/*
+ * Forward: KL[i], LSE1[i], LSE2[i] for every query row (Method 1).
+ * Inputs Q1, K1, Q2, K2 (device, read only).  Outputs out_kl, out_lse1,
+ * out_lse2 (device, fp32 [B,H,n_q], fully overwritten).  A split-K launch
+ * (launch->num_splits > 1, or auto with a workspace given) writes partial
+ * states to launch->workspace and merges them in a second kernel on the
+ * same stream; if the needed workspace is not given, auto mode falls back
+ * to one split and an explicit split count returns STREAMKL_ERR_WORKSPACE.
+ */
+streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, const void* K2,
+                             int causal, float scale1, float scale2,
+                             float* out_kl, float* out_lse1, float* out_lse2,
+                             const streamkl_shape* shape, const streamkl_launch* launch,
+                             void* stream);
+
+/* The backward mode streamkl_bwd will use (1 fused, 2 separate, or the
+ * requested 3/4), 0 if invalid. */
+int streamkl_bwd_plan(const streamkl_shape* shape, int causal, int setting,
+                      const streamkl_launch* launch);
+
+/*
+ * Backward (Method 2): gradients of sum_i d_kl[i] * KL[i].
+ *  setting 1: P1 held fixed, gradients to the student:  dQ = dQ2, dK = dK2
+ *             (dS2 = g (P2 - P1)), shapes [B,H,n_q,d2] and [B,H,n_k,d2];
+ *  setting 2: P2 held fixed, gradients to the teacher:  dQ = dQ1, dK = dK1
+ *             (dS1 = g P1 ((S1 - LSE1) - (S2 - LSE2) - KL), the log-ratio
+ *             formed from logits and the stored LSE, Method 3), shapes with d1.
+ * kl, lse1, lse2: the forward's outputs for the same inputs (device, fp32).
+ *   setting 1 does not read kl (it may be NULL).
+ * d_kl: upstream gradient per row (device, fp32 [B,H,n_q]).
+ * dQ, dK: device fp32 outputs, fully overwritten (the fused mode clears dQ
+ *   itself before accumulating into it with atomics, on the same stream).
+ *   With bwd_mode DK_ONLY (DQ_ONLY) only dK (dQ) is computed and the other
+ *   pointer may be NULL; these serve callers that train only keys or only
+ *   queries, and per-kernel timing.
+ * No workspace is needed.
+ */
+streamkl_status streamkl_bwd(int setting,
+                             const void* Q1, const void* K1, const void* Q2, const void* K2,
+                             int causal, float scale1, float scale2,
+                             const float* kl, const float* lse1, const float* lse2,
+                             const float* d_kl, float* dQ, float* dK,
+                             const streamkl_shape* shape, const streamkl_launch* launch,
+                             void* stream);
+
+/* Static text for a status code. */
+const char* streamkl_status_string(int status);
+
+/* hipError_t of the last STREAMKL_ERR_HIP returned on this thread (0 if none). */
+int streamkl_last_hip_error(void);
+
+/* Library version, for the Python binding's load check. */
+int streamkl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMKL_H_ */

@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library must load, export every function include/streamkl.h declares,
+and reject invalid arguments on the host before touching the device.  No
+call here passes validation with made-up device pointers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_kl_divergence_amd import streamkl as sk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "streamkl.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(streamkl_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("streamkl_fwd", "streamkl_bwd", "streamkl_fwd_workspace_bytes", "streamkl_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sk.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    lib = sk.library()
+    assert lib.streamkl_version() >= 1
+    assert lib.streamkl_status_string(0) == b"ok"
+    assert lib.streamkl_status_string(4) == b"HIP runtime error"
+    assert lib.streamkl_status_string(99) == b"unknown status"
+
+
+def _fwd(shape, ptr=0, causal=0, launch=None):
+    lib = sk.library()
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.streamkl_fwd(p, p, p, p, causal, 0.0, 0.0, p, p, p,
+                            ctypes.byref(shape) if shape is not None else None,
+                            ctypes.byref(launch) if launch is not None else None, None)
+
+
+def _bwd(setting, shape, ptr=0, causal=0):
+    lib = sk.library()
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.streamkl_bwd(setting, p, p, p, p, causal, 0.0, 0.0, p, p, p, p, p, p,
+                            ctypes.byref(shape) if shape is not None else None, None, None)
+
+
+GOOD = dict(B=1, H=2, n_q=64, n_k=64, d1=128, d2=128, dtype=sk.BF16)
+
+
+def shape(**kw):
+    d = dict(GOOD)
+    d.update(kw)
+    return sk.Shape(d["B"], d["H"], d["n_q"], d["n_k"], d["d1"], d["d2"], d["dtype"])
+
+
+def test_null_pointers_are_invalid():
+    assert _fwd(shape()) == sk.ERR_INVALID
+    assert _bwd(1, shape()) == sk.ERR_INVALID
+    assert _fwd(None) == sk.ERR_INVALID
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), sk.ERR_INVALID), (dict(H=0), sk.ERR_INVALID), (dict(n_q=0), sk.ERR_INVALID),
+    (dict(n_k=-1), sk.ERR_INVALID), (dict(dtype=7), sk.ERR_INVALID),
+    (dict(d1=96), sk.ERR_UNSUPPORTED), (dict(d2=256), sk.ERR_UNSUPPORTED),
+    (dict(n_q=1 << 25), sk.ERR_UNSUPPORTED),
+])
+def test_bad_shapes(kw, code):
+    # misaligned fake pointer: shape errors are reported first, the pointer is never used
+    assert _fwd(shape(**kw), ptr=8) == code
+    assert _bwd(2, shape(**kw), ptr=8) == code
+
+
+def test_causal_needs_nq_le_nk():
+    assert _fwd(shape(n_q=65, n_k=64), ptr=8, causal=1) == sk.ERR_INVALID
+
+
+def test_bad_setting_and_alignment():
+    assert _bwd(3, shape(), ptr=16) == sk.ERR_INVALID
+    assert _bwd(0, shape(), ptr=16) == sk.ERR_INVALID
+    # 8-byte aligned tensor pointers are rejected (16 is required) before any device call
+    assert _fwd(shape(), ptr=8) == sk.ERR_INVALID
+    assert _bwd(1, shape(), ptr=8) == sk.ERR_INVALID
+
+
+def test_bad_launch_options():
+    bad = sk.Launch(-1, 0, None, 0)
+    assert _fwd(shape(), ptr=8, launch=bad) == sk.ERR_INVALID
+    lib = sk.library()
+    assert lib.streamkl_fwd_workspace_bytes(ctypes.byref(shape()), 0, ctypes.byref(bad)) == 0
+    assert lib.streamkl_bwd_plan(ctypes.byref(shape()), 0, 5, None) == 0
+
+
+def test_workspace_sizing_and_plans():
+    lib = sk.library()
+    # decode-shaped: one query row, long key range -> the auto plan splits the keys
+    s = shape(H=32, n_q=1, n_k=131072)
+    ws = lib.streamkl_fwd_workspace_bytes(ctypes.byref(s), 0, None)
+    sp = sk.fwd_plan(s, False)
+    assert sp > 1 and ws == 20 * 32 * 1 * sp
+    # without a workspace the auto plan does not split
+    assert lib.streamkl_fwd_plan(ctypes.byref(s), 0, None) == 1
+    # explicit split counts are honoured (clamped to the number of key tiles)
+    assert sk.fwd_plan(s, False, num_splits=7) == 7
+    assert sk.fwd_plan(shape(n_k=128), False, num_splits=64) == 2
+    # long prefill: no split
+    assert sk.fwd_plan(shape(H=32, n_q=65536, n_k=65536), True) == 1
+    assert lib.streamkl_fwd_workspace_bytes(ctypes.byref(shape(H=32, n_q=65536, n_k=65536)), 1, None) == 0
+
+
+def test_bwd_mode_plan():
+    big = shape(H=32, n_q=65536, n_k=65536)
+    assert sk.bwd_plan(big, True, 1) == sk.BWD_SEPARATE
+    small_q = shape(H=32, n_q=16, n_k=131072)
+    assert sk.bwd_plan(small_q, False, 1) == sk.BWD_FUSED
+    assert sk.bwd_plan(big, True, 1, sk.BWD_FUSED) == sk.BWD_FUSED
+    assert sk.bwd_plan(small_q, False, 2, sk.BWD_SEPARATE) == sk.BWD_SEPARATE

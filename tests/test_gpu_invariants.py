@@ -1,0 +1,127 @@
+"""GPU invariants and robustness: exact zeros, symmetry, determinism, no stray writes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from attention_kl_divergence_amd import streamkl as sk
+from parity import check_forward_rows, check_grad, head_inputs, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def W(name, dt="bf16", d1=128, d2=128, causal=True, H=2, n_q=300, n_k=300, seed=11):
+    return workloads.Workload(name, 1, H, n_q, n_k, d1, d2, dt, causal, 0.5, d1 != d2, seed)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_models_exact_zero(dt, causal, cuda_device):
+    w = W("ident", dt=dt, causal=causal, n_q=190, n_k=260 if not causal else 190)
+    q1, k1, _, _ = workloads.generate(w, cuda_device)
+    for sp in (1, 3):
+        kl, l1, l2 = sk.streamkl_fwd(q1, k1, q1, k1, causal, num_splits=sp)
+        assert (kl == 0).all(), f"splits={sp}: max |KL| {kl.abs().max().item()}"
+        assert torch.equal(l1, l2)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    for s in (1, 2):
+        for m in (sk.BWD_FUSED, sk.BWD_SEPARATE):
+            dq, dk = sk.streamkl_bwd(s, q1, k1, q1, k1, causal, kl, l1, l2, g, bwd_mode=m)
+            assert (dq == 0).all() and (dk == 0).all()
+
+
+def test_causal_first_row(cuda_device):
+    w = W("row0", causal=True)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, True)
+    assert kl[0, :, 0].abs().max().item() < 1e-5
+    s1 = (q1[0, :, 0].float() * k1[0, :, 0].float()).sum(-1) / 128 ** 0.5
+    assert torch.allclose(l1[0, :, 0], s1, rtol=1e-5, atol=1e-5)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    for s in (1, 2):
+        dq, _ = sk.streamkl_bwd(s, q1, k1, q2, k2, True, kl, l1, l2, g)
+        assert dq[0, :, 0].abs().max().item() < 1e-6
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_key_shift_invariance_large_shift(dt, cuda_device):
+    """K_t + u leaves KL, dQ, dK unchanged; a large u stresses the max subtraction."""
+    w = W("shift", dt=dt, causal=True, d1=64, d2=64, n_q=160, n_k=160)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    u = 32.0  # exactly representable; bf16 keeps K + 32 to ~0.25 absolute
+    k1s, k2s = (k1.float() + u).to(k1.dtype), (k2.float() + u).to(k2.dtype)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1s, q2, k2s, True)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    dq, dk = sk.streamkl_bwd(1, q1, k1s, q2, k2s, True, kl, l1, l2, g)
+    for h in range(w.H):
+        hi = head_inputs(q1, k1s, q2, k2s, 0, h)
+        ref = oracle.head_forward(*hi, True)
+        check_forward_rows(f"shift h{h}", to_np(kl[0, h]), to_np(l1[0, h]), to_np(l2[0, h]), ref, w.torch_dtype)
+        rdq, rdk = oracle.head_backward(1, *hi, True, to_np(g[0, h]))
+        check_grad(f"shift h{h} dK", to_np(dk[0, h]), rdk)
+        if dt == "f32":
+            check_grad(f"shift h{h} dQ", to_np(dq[0, h]), rdq)
+        else:
+            # dQ = dS K with dS rounded to bf16 for the MFMA: a common key offset u
+            # turns that rounding (2^-9 relative) into an error ~ 2^-9 |u| / |K - u|
+            # that no longer cancels; only a loose bound holds here.
+            check_grad(f"shift h{h} dQ (bf16, loose)", to_np(dq[0, h]), rdq, tol=0.1)
+
+
+def test_fused_and_separate_agree_and_separate_is_deterministic(cuda_device):
+    w = W("modes", causal=True, H=4, n_q=700, n_k=700)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, True)
+    kl_b, _, _ = sk.streamkl_fwd(q1, k1, q2, k2, True)
+    assert torch.equal(kl, kl_b), "forward is not bitwise reproducible"
+    for s in (1, 2):
+        a = sk.streamkl_bwd(s, q1, k1, q2, k2, True, kl, l1, l2, g, bwd_mode=sk.BWD_SEPARATE)
+        b = sk.streamkl_bwd(s, q1, k1, q2, k2, True, kl, l1, l2, g, bwd_mode=sk.BWD_SEPARATE)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), "separate backward is not deterministic"
+        f = sk.streamkl_bwd(s, q1, k1, q2, k2, True, kl, l1, l2, g, bwd_mode=sk.BWD_FUSED)
+        assert torch.equal(f[1], a[1]), "dK of the fused and separate kernels should match bitwise"
+        check_grad(f"fused vs separate dQ s{s}", to_np(f[0]), to_np(a[0]), tol=1e-5)
+
+
+def test_no_writes_outside_outputs(cuda_device):
+    """Outputs are views into larger NaN-filled buffers: the guard bands must stay NaN."""
+    w = W("guard", causal=False, H=3, n_q=77, n_k=201)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    pad = 4096
+
+    def guarded(n):
+        buf = torch.full((n + 2 * pad,), float("nan"), device=cuda_device)
+        return buf, buf[pad:pad + n]
+
+    rows = w.B * w.H * w.n_q
+    bufs = [guarded(rows) for _ in range(3)]
+    out = tuple(v.view(w.B, w.H, w.n_q) for _, v in bufs)
+    for sp in (1, 4):
+        sk.streamkl_fwd(q1, k1, q2, k2, False, num_splits=sp, out=out)
+        torch.cuda.synchronize()
+        for buf, _ in bufs:
+            assert buf[:pad].isnan().all() and buf[-pad:].isnan().all()
+    kl, l1, l2 = out
+    for s, ds in ((1, w.d2), (2, w.d1)):
+        for m in (sk.BWD_FUSED, sk.BWD_SEPARATE):
+            bq, vq = guarded(rows * ds)
+            bk, vk = guarded(w.B * w.H * w.n_k * ds)
+            sk.streamkl_bwd(s, q1, k1, q2, k2, False, kl, l1, l2, g, bwd_mode=m,
+                            out=(vq.view(w.B, w.H, w.n_q, ds), vk.view(w.B, w.H, w.n_k, ds)))
+            torch.cuda.synchronize()
+            for buf in (bq, bk):
+                assert buf[:pad].isnan().all() and buf[-pad:].isnan().all()
+            assert not vq.isnan().any() and not vk.isnan().any()
+
+
+def test_failed_call_writes_nothing(cuda_device):
+    w = W("fail", causal=False, H=1, n_q=64, n_k=64)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    out = tuple(torch.full((1, 1, 64), 7.0, device=cuda_device) for _ in range(3))
+    with pytest.raises(sk.StreamKLError):
+        sk.streamkl_fwd(q1, k1, q2, k2, False, num_splits=-1, out=out)
+    torch.cuda.synchronize()
+    assert all((o == 7.0).all() for o in out)

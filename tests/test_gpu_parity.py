@@ -1,0 +1,180 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small shapes are compared element by element on every row; they span several
+tiles (64-key forward tiles, 128-row workgroups) and ragged tails.  The named
+workloads run at full size in the launch configuration the benchmark uses
+and are compared on sampled heads and rows (and, under causal masks, on the
+tail key rows whose dK the oracle can afford).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from attention_kl_divergence_amd import streamkl as sk
+from parity import check_forward_rows, check_grad, head_inputs, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_full(w, dev, g_kind="random", splits=(0,), modes=(sk.BWD_FUSED, sk.BWD_SEPARATE), settings=(1, 2)):
+    q1, k1, q2, k2 = workloads.generate(w, dev)
+    g = workloads.upstream_grad(w, dev, g_kind)
+    outs = {}
+    for sp in splits:
+        _say(f"  fwd {w.name} splits={sp}")
+        kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal, num_splits=sp)
+        torch.cuda.synchronize()
+        outs[sp] = (to_np(kl), to_np(l1), to_np(l2))
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal)
+    grads = {}
+    for s in settings:
+        for m in modes:
+            _say(f"  bwd {w.name} setting={s} mode={m}")
+            dq, dk = sk.streamkl_bwd(s, q1, k1, q2, k2, w.causal, kl, l1, l2, g, bwd_mode=m)
+            torch.cuda.synchronize()
+            grads[(s, m)] = (to_np(dq), to_np(dk))
+    gn = to_np(g)
+    for b in range(w.B):
+        for h in range(w.H):
+            hi = head_inputs(q1, k1, q2, k2, b, h)
+            ref = oracle.head_forward(*hi, w.causal)
+            for sp, (okl, ol1, ol2) in outs.items():
+                check_forward_rows(f"{w.name} b{b}h{h} sp{sp}", okl[b, h], ol1[b, h], ol2[b, h], ref, w.torch_dtype)
+            for s in settings:
+                rdq, rdk = oracle.head_backward(s, *hi, w.causal, gn[b, h])
+                for m in modes:
+                    dq, dk = grads[(s, m)]
+                    check_grad(f"{w.name} b{b}h{h} s{s} m{m} dQ", dq[b, h], rdq)
+                    check_grad(f"{w.name} b{b}h{h} s{s} m{m} dK", dk[b, h], rdk)
+    return outs, grads
+
+
+SMALL = [
+    # name, dtype, d1, d2, causal, B, H, n_q, n_k
+    ("f32-d64-nc", "f32", 64, 64, False, 1, 2, 200, 300),
+    ("f32-d64-c", "f32", 64, 64, True, 1, 2, 200, 300),
+    ("f32-d128-c", "f32", 128, 128, True, 2, 1, 129, 129),
+    ("f32-d64x128-nc", "f32", 64, 128, False, 1, 1, 33, 65),
+    ("bf16-d128-c", "bf16", 128, 128, True, 1, 2, 300, 300),
+    ("bf16-d128-nc", "bf16", 128, 128, False, 1, 2, 257, 517),
+    ("bf16-d128-c-rect", "bf16", 128, 128, True, 1, 2, 100, 333),
+    ("bf16-d64-c", "bf16", 64, 64, True, 2, 2, 190, 190),
+    ("bf16-d128x64-c", "bf16", 128, 64, True, 1, 2, 260, 260),
+    ("bf16-d64x128-nc", "bf16", 64, 128, False, 1, 2, 70, 129),
+    ("bf16-n1", "bf16", 128, 128, False, 1, 2, 1, 1),
+    ("bf16-n17-c", "bf16", 128, 128, True, 1, 2, 17, 17),
+    ("bf16-q1-k1000", "bf16", 128, 128, False, 1, 3, 1, 1000),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes_full_parity(case, cuda_device):
+    name, dt, d1, d2, causal, B, H, n_q, n_k = case
+    w = workloads.Workload(name, B, H, n_q, n_k, d1, d2, dt, causal, 0.5, d1 != d2, 7)
+    run_full(w, cuda_device, splits=(0, 1, 3))
+
+
+@pytest.mark.parametrize("kind", ["mean", "random"])
+def test_f32_512_workload_full(kind, cuda_device):
+    """The fp32 H=1 N=512 d=64 non-causal workload: forward and setting-1 backward, every row."""
+    w = workloads.WORKLOADS["h1-n512-d64-f32"]
+    run_full(w, cuda_device, g_kind=kind, splits=(0, 1, 4))
+
+
+# ----------------------------------------------------------------------------- full-size, sampled
+
+def sample_rows(n, k=96, seed=0):
+    r = np.random.default_rng(seed)
+    extra = r.choice(n, size=min(k, n), replace=False)
+    return np.unique(np.concatenate([[0, 1, n - 1], extra]).clip(0, n - 1))
+
+
+def run_sampled(w, dev, settings, heads=None, mode=sk.BWD_AUTO, dk_tail=2048, nrows=96):
+    _say(f"generate {w.name}")
+    q1, k1, q2, k2 = workloads.generate(w, dev)
+    g = workloads.upstream_grad(w, dev, "random")
+    _say(f"fwd {w.name}")
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal)
+    torch.cuda.synchronize()
+    heads = heads or [0, w.H - 1]
+    rows = sample_rows(w.n_q, nrows)
+    block = max(16, (1 << 24) // w.n_k)
+    grads = {}
+    for s in settings:
+        _say(f"bwd {w.name} setting {s} mode {mode} (plan {sk.bwd_plan(sk.shape_of(q1, k1, q2, k2), w.causal, s, mode)})")
+        dq, dk = sk.streamkl_bwd(s, q1, k1, q2, k2, w.causal, kl, l1, l2, g, bwd_mode=mode)
+        torch.cuda.synchronize()
+        grads[s] = (dq, dk)
+    for h in heads:
+        hi = head_inputs(q1, k1, q2, k2, 0, h)
+        gh = to_np(g[0, h])
+        _say(f"oracle {w.name} head {h}: {len(rows)} rows")
+        ref = oracle.head_forward(*hi, w.causal, rows=rows, block=block)
+        check_forward_rows(f"{w.name} h{h}", to_np(kl[0, h])[rows], to_np(l1[0, h])[rows], to_np(l2[0, h])[rows],
+                           ref, w.torch_dtype)
+        for s in settings:
+            dq, dk = grads[s]
+            rdq, _ = oracle.head_backward(s, *hi, w.causal, gh, rows=rows, block=block)
+            check_grad(f"{w.name} h{h} s{s} dQ rows", to_np(dq[0, h])[rows], rdq)
+            if w.causal and dk_tail:
+                keys = np.arange(w.n_k - dk_tail, w.n_k)
+                _say(f"oracle {w.name} head {h}: dK tail {dk_tail}")
+                rdk = oracle.head_backward_dk_rows(s, *hi, w.causal, gh, key_rows=keys, block=block)
+                check_grad(f"{w.name} h{h} s{s} dK tail", to_np(dk[0, h])[keys], rdk)
+            # every row of dS sums to zero, so the key-sum of dK vanishes up to
+            # the bf16 rounding of dS
+            dkh = dk[0, h].double()
+            colsum = dkh.sum(dim=0).norm().item()
+            _say(f"  |sum_j dK_j| / |dK| = {colsum / max(dkh.norm().item(), 1e-30):.3e}")
+            assert colsum <= 1e-2 * dkh.norm().item(), f"{w.name} h{h} s{s}: |sum_j dK_j| = {colsum:.3e}"
+    return kl, grads
+
+
+def test_workload_8k_causal_both_settings(cuda_device):
+    w = workloads.WORKLOADS["h32-n8k-d128-bf16-causal"]
+    run_sampled(w, cuda_device, settings=(1, 2), heads=[0, 13, 31], nrows=256)
+
+
+def test_workload_64k_causal_setting1(cuda_device):
+    w = workloads.WORKLOADS["h32-n64k-d128-bf16-causal"]
+    run_sampled(w, cuda_device, settings=(1,))
+
+
+def test_workload_64k_noncausal_setting1(cuda_device):
+    w = workloads.WORKLOADS["h32-n64k-d128-bf16"]
+    run_sampled(w, cuda_device, settings=(1,), dk_tail=0)
+
+
+@pytest.mark.parametrize("name", ["decode-h32-q1-k128k-d128-bf16", "decode-h32-q16-k128k-d128-bf16",
+                                  "decode-h32-q1-k512k-d128-bf16", "decode-h32-q16-k512k-d128-bf16"])
+def test_workload_decode_splitk(name, cuda_device):
+    w = workloads.WORKLOADS[name]
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    shp = sk.shape_of(q1, k1, q2, k2)
+    plan = sk.fwd_plan(shp, False)
+    _say(f"{name}: auto split plan {plan}")
+    assert plan > 1
+    res = {}
+    for sp in (0, 1, 2, 7, 64):
+        kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, False, num_splits=sp)
+        res[sp] = (to_np(kl), to_np(l1), to_np(l2))
+    torch.cuda.synchronize()
+    for h in (0, w.H - 1):
+        hi = head_inputs(q1, k1, q2, k2, 0, h)
+        ref = oracle.head_forward(*hi, False, block=16)
+        for sp, (kl, l1, l2) in res.items():
+            check_forward_rows(f"{name} h{h} sp{sp}", kl[0, h], l1[0, h], l2[0, h], ref, w.torch_dtype)
+    # the split count changes only fp32 rounding
+    for sp in (1, 2, 7, 64):
+        assert np.abs(res[sp][0] - res[0][0]).max() < 1e-4
+
+
+def test_workload_512k_two_head_dims_setting2(cuda_device):
+    w = workloads.WORKLOADS["h32-n512k-d128x64-bf16-causal"]
+    run_sampled(w, cuda_device, settings=(2,), heads=[0, 31], nrows=64, dk_tail=1024)
