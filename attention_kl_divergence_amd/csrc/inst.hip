@@ -11,7 +11,7 @@
 namespace streamkl {
 
 hipError_t SKL_CAT(launch_fwd, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, 4, kFwdTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -28,11 +28,11 @@ hipError_t SKL_CAT(launch_bwd_dk, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int 
                                                            hipStream_t st) {
   const dim3 g((unsigned)nblocks), b(256);
   if (setting == 1) {
-    if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, true>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, false>), g, b, 0, st, a);
+    if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, true, kBwdQTile<SKL_T>>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, false, kBwdQTile<SKL_T>>), g, b, 0, st, a);
   } else {
-    if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, true>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, false>), g, b, 0, st, a);
+    if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, true, kBwdQTile<SKL_T>>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, false, kBwdQTile<SKL_T>>), g, b, 0, st, a);
   }
   return hipGetLastError();
 }

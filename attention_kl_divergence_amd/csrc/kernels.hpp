@@ -1,6 +1,6 @@
 // StreamKL kernels for gfx950: one-pass forward (optionally split over keys),
-// split merge, key-outer backward (dK, optionally fused dQ by atomics) and
-// query-outer backward (dQ).
+// key-outer backward (dK, optionally fused dQ by atomics) and query-outer
+// backward (dQ).
 //
 // Pages: "StreamKL" technical summary (gist.science ja/fr/ko).
 //   Method 1 (online formulation): five running scalars per row and
@@ -18,6 +18,14 @@
 // Everything runs in base-2 units: y_t = S_t * log2(e) = s * c_t with
 // c_t = scale_t * log2(e) applied to the raw dot product s in fp32, so each
 // exponential is one v_exp_f32.
+//
+// Data movement: tiles of Q or K rows go HBM -> LDS with direct 16-byte
+// global->LDS loads (no VGPR staging), double-buffered so the next tile is in
+// flight while the current one is consumed, one barrier per tile.  Inside a
+// tile, 16-byte chunks of a row are XOR-swizzled by row so MFMA fragment reads
+// spread over all LDS banks.  Operands that need a column of a row-major tile
+// (k running down the rows) are read with the LDS transpose read
+// (ds_read_b64_tr_b16), so no tile is ever stored transposed.
 #pragma once
 
 #include "common.hpp"
@@ -61,43 +69,107 @@ struct BwdArgs {
   float scale_s;       // scale of the model that receives gradients
 };
 
-// Cooperative copy of `ROWS` rows of a [*, D] row-major global tensor (rows
-// r0.., rows >= rend read as zero) into LDS with leading dimension LD.
-template <typename T, int D, int LD, int ROWS, int NT>
-__device__ inline void load_rows(T* __restrict__ s, const T* __restrict__ g, int r0, int rend, int tid) {
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int CPR = D / EPC;
-  constexpr int TOTAL = ROWS * CPR;
+typedef __bf16 bf16x4_lds __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Swizzled LDS tile of row-major [rows][D] elements.  Chunk = 16 bytes.
+template <typename T, int D>
+struct Tile {
+  static constexpr int EPC = 16 / sizeof(T);               // elements per chunk
+  static constexpr int CPR = D / EPC;                      // chunks per row
+  static constexpr int RP = CPR >= 16 ? 1 : 16 / CPR;      // rows sharing a 256-byte bank window
+  static constexpr int SWM = (CPR >= 16 ? 16 : CPR) - 1;   // swizzle mask
+  __device__ static inline int swz(int r) { return (r / RP) & SWM; }
+  // element offset of (row r, column c)
+  __device__ static inline int off(int r, int c) { return r * D + (((c / EPC) ^ swz(r)) * EPC) + (c % EPC); }
+};
+
+// Issue the direct loads of rows [r0, r0+ROWS) of a [*, D] global tensor into
+// an LDS tile; rows past rmax re-read row rmax (callers mask them).  Each
+// wave-wide load fills 1 KB of LDS: lane L writes bytes [16L, 16L+16) of it,
+// so the lane picks the global chunk that belongs at that swizzled spot.
+template <typename T, int D, int ROWS, int NW>
+__device__ inline void tile_load_async(T* tile, const T* __restrict__ g, int r0, int rmax, int wave, int lane) {
+  using F = Tile<T, D>;
+  constexpr int NI = ROWS * F::CPR / 64;
+  static_assert(NI % NW == 0, "tile loads must split evenly over the waves");
 #pragma unroll
-  for (int c0 = 0; c0 < TOTAL; c0 += NT) {
-    const int c = c0 + tid;
-    if (TOTAL % NT == 0 || c < TOTAL) {
-      const int r = c / CPR, cc = c % CPR;
-      Chunk16 v = {{0u, 0u, 0u, 0u}};
-      if (r0 + r < rend) v = *reinterpret_cast<const Chunk16*>(g + (int64_t)(r0 + r) * D + cc * EPC);
-      *reinterpret_cast<Chunk16*>(s + r * LD + cc * EPC) = v;
-    }
+  for (int i = 0; i < NI / NW; ++i) {
+    const int J = wave * (NI / NW) + i;
+    const int P = J * 64 + lane;
+    const int r = P / F::CPR, pc = P % F::CPR;
+    const int lc = pc ^ F::swz(r);
+    const int gr = min(r0 + r, rmax);
+    const T* src = g + (int64_t)gr * D + lc * F::EPC;
+    __builtin_amdgcn_global_load_lds((const void*)src, (void __attribute__((address_space(3)))*)(tile + J * 64 * F::EPC),
+                                     16, 0, 0);
   }
 }
 
-// Same rows stored transposed: sT[d][r] (leading dimension LDT).
-template <typename T, int D, int LDT, int ROWS, int NT>
-__device__ inline void load_rows_T(T* __restrict__ sT, const T* __restrict__ g, int r0, int rend, int tid) {
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int CPR = D / EPC;
-  constexpr int TOTAL = ROWS * CPR;
-#pragma unroll
-  for (int c0 = 0; c0 < TOTAL; c0 += NT) {
-    const int c = c0 + tid;
-    if (TOTAL % NT == 0 || c < TOTAL) {
-      const int r = c % ROWS, cc = c / ROWS;
-      Chunk16 v = {{0u, 0u, 0u, 0u}};
-      if (r0 + r < rend) v = *reinterpret_cast<const Chunk16*>(g + (int64_t)(r0 + r) * D + cc * EPC);
-      const T* e = reinterpret_cast<const T*>(&v);
-#pragma unroll
-      for (int i = 0; i < EPC; ++i) sT[(cc * EPC + i) * LDT + r] = e[i];
-    }
-  }
+__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// MFMA operand with lane row = `row`, k from `k0`: natural layout read.
+template <typename T, int D>
+__device__ inline typename Mfma<T>::frag frag_tile(const T* tile, int row, int s, int grp) {
+  const int k = s * Mfma<T>::KSTEP + grp * Mfma<T>::KPL;
+  return *reinterpret_cast<const typename Mfma<T>::frag*>(tile + Tile<T, D>::off(row, k));
+}
+
+// MFMA operand whose lane column is n (0..31 within block n0) and whose k
+// values run down the rows of a row-major tile, in accumulator order
+// (k = acc_row(h*KPL + e', grp) + kb0).  bf16 uses two transpose reads.
+template <int D>
+__device__ inline bf16x8 fragcol_acc_bf16(const bf16* tile, int kb0, int n0, int h, int lane) {
+  using F = Tile<bf16, D>;
+  const int grp = lane >> 5, sub = (lane >> 4) & 1, r = lane & 15;
+  const int n = n0 + 16 * sub + 4 * (r & 3);
+  const int ka = kb0 + 16 * h + 4 * grp + (r >> 2);
+  const bf16x4_lds lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16x4_lds __attribute__((address_space(3)))*)(tile + F::off(ka, n)));
+  const bf16x4_lds hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16x4_lds __attribute__((address_space(3)))*)(tile + F::off(ka + 8, n)));
+  bf16x8 f;
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+  return f;
+}
+
+// Same, natural k order (k = kb0 + 16h + 8grp + e').
+template <int D>
+__device__ inline bf16x8 fragcol_nat_bf16(const bf16* tile, int kb0, int n0, int h, int lane) {
+  using F = Tile<bf16, D>;
+  const int grp = lane >> 5, sub = (lane >> 4) & 1, r = lane & 15;
+  const int n = n0 + 16 * sub + 4 * (r & 3);
+  const int ka = kb0 + 16 * h + 8 * grp + (r >> 2);
+  const bf16x4_lds lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16x4_lds __attribute__((address_space(3)))*)(tile + F::off(ka, n)));
+  const bf16x4_lds hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16x4_lds __attribute__((address_space(3)))*)(tile + F::off(ka + 4, n)));
+  bf16x8 f;
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+  return f;
+}
+
+// fp32 versions: one element per lane, k = acc_row(h, grp) (+kb0) or 2h + grp.
+template <int D>
+__device__ inline float fragcol_acc_f32(const float* tile, int kb0, int n0, int h, int lane) {
+  return tile[Tile<float, D>::off(kb0 + acc_row(h, lane >> 5), n0 + (lane & 31))];
+}
+template <int D>
+__device__ inline float fragcol_nat_f32(const float* tile, int kb0, int n0, int h, int lane) {
+  return tile[Tile<float, D>::off(kb0 + 2 * h + (lane >> 5), n0 + (lane & 31))];
+}
+
+template <typename T, int D>
+__device__ inline typename Mfma<T>::frag fragcol_acc(const T* tile, int kb0, int n0, int h, int lane) {
+  if constexpr (Mfma<T>::KPL == 1) return fragcol_acc_f32<D>(tile, kb0, n0, h, lane);
+  else return fragcol_acc_bf16<D>(tile, kb0, n0, h, lane);
+}
+template <typename T, int D>
+__device__ inline typename Mfma<T>::frag fragcol_nat(const T* tile, int kb0, int n0, int h, int lane) {
+  if constexpr (Mfma<T>::KPL == 1) return fragcol_nat_f32<D>(tile, kb0, n0, h, lane);
+  else return fragcol_nat_bf16<D>(tile, kb0, n0, h, lane);
 }
 
 template <typename T>
@@ -112,23 +184,86 @@ __device__ inline typename Mfma<T>::frag zero_frag() {
   return f;
 }
 
+// Fragment of a row of a global row-major [*, D] tensor (row clamped to a
+// valid one; `valid` false gives zeros).
+template <typename T, int D>
+__device__ inline typename Mfma<T>::frag frag_global(const T* g, int row, int rmax, bool valid, int s, int grp) {
+  const T* p = g + (int64_t)min(row, rmax) * D + s * Mfma<T>::KSTEP + grp * Mfma<T>::KPL;
+  typename Mfma<T>::frag f = *reinterpret_cast<const typename Mfma<T>::frag*>(p);
+  return valid ? f : zero_frag<T>();
+}
+
 // ---------------------------------------------------------------------------
-// Forward.  Workgroup = WQ waves, each owning 32 query rows; the workgroup
-// streams key tiles of BK rows of K1 and K2 through LDS.  Each wave computes
-// S^T = K Q^T so a lane's accumulator column is one query row: lane
-// (col, grp) keeps its own running state over the keys acc_row(., grp) of
-// every 32-key block, and the two lane groups merge once at the end.
-template <typename T, int D1, int D2, int WQ, int BK>
-__global__ __launch_bounds__(64 * WQ) void fwd_kernel(FwdArgs a) {
+// Forward online update of one lane's running state with NKB 32-key blocks of
+// raw dot products (s1, s2).  MASK: keys past `lim` are excluded.
+template <bool MASK, int NKB>
+__device__ inline void fwd_update(RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], float c1, float c2, int k0,
+                                  int lim, int grp) {
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const bool out = k0 + kb * 32 + acc_row(e, grp) > lim;
+        s1[kb][e] = out ? kNegInf : s1[kb][e];
+        s2[kb][e] = out ? kNegInf : s2[kb][e];
+      }
+  }
+  float mx1a = kNegInf, mx1b = kNegInf, mx2a = kNegInf, mx2b = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      mx1a = fmaxf(mx1a, fmaxf(s1[kb][e], s1[kb][e + 1]));
+      mx1b = fmaxf(mx1b, fmaxf(s1[kb][e + 2], s1[kb][e + 3]));
+      mx2a = fmaxf(mx2a, fmaxf(s2[kb][e], s2[kb][e + 1]));
+      mx2b = fmaxf(mx2b, fmaxf(s2[kb][e + 2], s2[kb][e + 3]));
+    }
+  const float M1n = fmaxf(st.M1, fmaxf(mx1a, mx1b) * c1);
+  const float M2n = fmaxf(st.M2, fmaxf(mx2a, mx2b) * c2);
+  const float m1 = MASK ? finite_or_zero(M1n) : M1n;
+  const float m2 = MASK ? finite_or_zero(M2n) : M2n;
+  const float al1 = exp2_fast(st.M1 - m1), al2 = exp2_fast(st.M2 - m2);
+  float tl1[4] = {0.f, 0.f, 0.f, 0.f}, tl2[4] = {0.f, 0.f, 0.f, 0.f}, tA[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float t1 = fmaf(s1[kb][e], c1, -m1);
+      const float t2 = fmaf(s2[kb][e], c2, -m2);
+      const float p1 = exp2_fast(t1);
+      const float p2 = exp2_fast(t2);
+      float d = t1 - t2;
+      if constexpr (MASK) d = (s1[kb][e] == kNegInf) ? 0.f : d;  // never form the ratio on masked keys
+      tl1[e & 3] += p1;
+      tl2[e & 3] += p2;
+      tA[e & 3] = fmaf(p1, d, tA[e & 3]);
+    }
+  const float sl1 = (tl1[0] + tl1[1]) + (tl1[2] + tl1[3]);
+  const float sl2 = (tl2[0] + tl2[1]) + (tl2[2] + tl2[3]);
+  const float sA = (tA[0] + tA[1]) + (tA[2] + tA[3]);
+  st.l1 = fmaf(al1, st.l1, sl1);
+  st.l2 = fmaf(al2, st.l2, sl2);
+  st.A = fmaf(al1, st.A, fmaf(m1 - m2, sl1, sA));
+  st.M1 = M1n;
+  st.M2 = M2n;
+}
+
+// ---------------------------------------------------------------------------
+// Forward.  Workgroup = 4 waves, each owning 32 query rows; key tiles of BK
+// rows of K1 and K2 stream through LDS.  Each wave computes S^T = K Q^T so a
+// lane's accumulator column is one query row: lane (col, grp) keeps its own
+// running state over the keys acc_row(., grp) of every 32-key block, and the
+// two lane groups merge once at the end.
+template <typename T, int D1, int D2, int BK>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
-  constexpr int PAD = 16 / sizeof(T);
-  constexpr int LD1 = D1 + PAD, LD2 = D2 + PAD;
-  constexpr int NT = 64 * WQ;
+  constexpr int NW = 4;
   constexpr int S1 = D1 / MF::KSTEP, S2 = D2 / MF::KSTEP;
   constexpr int NKB = BK / 32;
-  __shared__ __attribute__((aligned(16))) T sK1[BK * LD1];
-  __shared__ __attribute__((aligned(16))) T sK2[BK * LD2];
+  constexpr int TS = BK * (D1 + D2);  // elements of one stage
+  __shared__ __attribute__((aligned(1024))) T lds[2 * TS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
@@ -137,7 +272,7 @@ __global__ __launch_bounds__(64 * WQ) void fwd_kernel(FwdArgs a) {
   lin /= a.nsplit;
   const int64_t bh = lin % a.BH;
   const int qb = a.nqb - 1 - (int)(lin / a.BH);  // longest causal rows first
-  const int qwg0 = qb * 32 * WQ;
+  const int qwg0 = qb * 32 * NW;
   const int q0 = qwg0 + 32 * wave;
   const int qrow = q0 + col;
   const int off = a.n_k - a.n_q;
@@ -149,26 +284,39 @@ __global__ __launch_bounds__(64 * WQ) void fwd_kernel(FwdArgs a) {
 
   const int kbeg = z * a.keys_per_split;
   int kend = min(a.n_k, kbeg + a.keys_per_split);
-  if (a.causal) kend = min(kend, min(a.n_q, qwg0 + 32 * WQ) - 1 + off + 1);
+  if (a.causal) kend = min(kend, min(a.n_q, qwg0 + 32 * NW) - 1 + off + 1);
   const bool wave_rows = q0 < a.n_q;
   const int wave_kmax = a.causal ? (min(a.n_q, q0 + 32) - 1 + off) : 0x7fffffff;
+  const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int kmax = a.n_k - 1;
+
+  if (ntiles > 0) {
+    tile_load_async<T, D1, BK, NW>(lds, K1, kbeg, kmax, wave, lane);
+    tile_load_async<T, D2, BK, NW>(lds + BK * D1, K2, kbeg, kmax, wave, lane);
+  }
 
   frag qf1[S1], qf2[S2];
+  const bool qv = qrow < a.n_q;
 #pragma unroll
-  for (int s = 0; s < S1; ++s) qf1[s] = qrow < a.n_q ? frag_rowmajor(Q1 + (int64_t)q0 * D1, D1, s, col, grp) : zero_frag<T>();
+  for (int s = 0; s < S1; ++s) qf1[s] = frag_global<T, D1>(Q1, qrow, a.n_q - 1, qv, s, grp);
 #pragma unroll
-  for (int s = 0; s < S2; ++s) qf2[s] = qrow < a.n_q ? frag_rowmajor(Q2 + (int64_t)q0 * D2, D2, s, col, grp) : zero_frag<T>();
+  for (int s = 0; s < S2; ++s) qf2[s] = frag_global<T, D2>(Q2, qrow, a.n_q - 1, qv, s, grp);
 
   RowState st = empty_state();
   const float c1 = a.c1, c2 = a.c2;
 
-  for (int k0 = kbeg; k0 < kend; k0 += BK) {
+  for (int t = 0; t < ntiles; ++t) {
+    wait_loads();
     __syncthreads();
-    load_rows<T, D1, LD1, BK, NT>(sK1, K1, k0, kend, tid);
-    load_rows<T, D2, LD2, BK, NT>(sK2, K2, k0, kend, tid);
-    __syncthreads();
+    const int k0 = kbeg + t * BK;
+    if (t + 1 < ntiles) {
+      T* nb = lds + ((t + 1) & 1) * TS;
+      tile_load_async<T, D1, BK, NW>(nb, K1, k0 + BK, kmax, wave, lane);
+      tile_load_async<T, D2, BK, NW>(nb + BK * D1, K2, k0 + BK, kmax, wave, lane);
+    }
     if (!wave_rows || k0 > wave_kmax) continue;
-    const bool need_mask = (k0 + BK > kend) || (a.causal && k0 + BK - 1 > q0 + off);
+    const T* sK1 = lds + (t & 1) * TS;
+    const T* sK2 = sK1 + BK * D1;
 
     f32x16 s1[NKB], s2[NKB];
 #pragma unroll
@@ -176,59 +324,17 @@ __global__ __launch_bounds__(64 * WQ) void fwd_kernel(FwdArgs a) {
       s1[kb] = zero16();
       s2[kb] = zero16();
 #pragma unroll
-      for (int s = 0; s < S1; ++s) s1[kb] = MF::run(frag_rowmajor(sK1 + kb * 32 * LD1, LD1, s, col, grp), qf1[s], s1[kb]);
+      for (int s = 0; s < S1; ++s) s1[kb] = MF::run(frag_tile<T, D1>(sK1, kb * 32 + col, s, grp), qf1[s], s1[kb]);
 #pragma unroll
-      for (int s = 0; s < S2; ++s) s2[kb] = MF::run(frag_rowmajor(sK2 + kb * 32 * LD2, LD2, s, col, grp), qf2[s], s2[kb]);
+      for (int s = 0; s < S2; ++s) s2[kb] = MF::run(frag_tile<T, D2>(sK2, kb * 32 + col, s, grp), qf2[s], s2[kb]);
     }
-
+    const bool need_mask = (k0 + BK > kend) || (a.causal && k0 + BK - 1 > q0 + off);
     if (need_mask) {
       const int lim = a.causal ? min(kend - 1, qrow + off) : kend - 1;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kb * 32 + acc_row(e, grp);
-          if (key > lim) { s1[kb][e] = kNegInf; s2[kb][e] = kNegInf; }
-        }
+      fwd_update<true, NKB>(st, s1, s2, c1, c2, k0, lim, grp);
+    } else {
+      fwd_update<false, NKB>(st, s1, s2, c1, c2, k0, 0, grp);
     }
-
-    float mx1[4] = {kNegInf, kNegInf, kNegInf, kNegInf}, mx2[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        mx1[e & 3] = fmaxf(mx1[e & 3], s1[kb][e]);
-        mx2[e & 3] = fmaxf(mx2[e & 3], s2[kb][e]);
-      }
-    const float tmx1 = fmaxf(fmaxf(mx1[0], mx1[1]), fmaxf(mx1[2], mx1[3]));
-    const float tmx2 = fmaxf(fmaxf(mx2[0], mx2[1]), fmaxf(mx2[2], mx2[3]));
-    const float M1n = fmaxf(st.M1, tmx1 * c1), M2n = fmaxf(st.M2, tmx2 * c2);
-    const float m1 = finite_or_zero(M1n), m2 = finite_or_zero(M2n);
-    const float al1 = exp2_fast(st.M1 - m1), al2 = exp2_fast(st.M2 - m2);
-
-    float tl1[4] = {0.f, 0.f, 0.f, 0.f}, tl2[4] = {0.f, 0.f, 0.f, 0.f}, tA[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float t1 = fmaf(s1[kb][e], c1, -m1);
-        const float t2 = fmaf(s2[kb][e], c2, -m2);
-        const float p1 = exp2_fast(t1);
-        const float p2 = exp2_fast(t2);
-        float d = t1 - t2;
-        if (need_mask) d = (s1[kb][e] == kNegInf) ? 0.f : d;  // never form the ratio on masked keys
-        tl1[e & 3] += p1;
-        tl2[e & 3] += p2;
-        tA[e & 3] = fmaf(p1, d, tA[e & 3]);
-      }
-    const float sl1 = (tl1[0] + tl1[1]) + (tl1[2] + tl1[3]);
-    const float sl2 = (tl2[0] + tl2[1]) + (tl2[2] + tl2[3]);
-    const float sA = (tA[0] + tA[1]) + (tA[2] + tA[3]);
-    st.l1 = fmaf(al1, st.l1, sl1);
-    st.l2 = fmaf(al2, st.l2, sl2);
-    st.A = fmaf(al1, st.A, fmaf(m1 - m2, sl1, sA));
-    st.M1 = M1n;
-    st.M2 = M2n;
   }
 
   st = merge_state(st, shfl_xor_state(st, 32));
@@ -256,17 +362,15 @@ struct RowGrad {
 };
 
 template <int SETTING>
-__device__ inline RowGrad load_rowgrad(const BwdArgs& a, int64_t r) {
-  RowGrad o;
+__device__ inline RowGrad load_rowgrad(const BwdArgs& a, int64_t r, bool valid) {
+  RowGrad o = {0.f, 0.f, 0.f, 0.f, 0.f};
+  if (!valid) return o;
   o.L1 = a.lse1[r] * kLog2e;
   o.L2 = a.lse2[r] * kLog2e;
   o.gs = a.g[r] * a.scale_s;
   if constexpr (SETTING == 2) {
     o.a = o.gs * kLn2;
     o.b = o.gs * a.kl[r];
-  } else {
-    o.a = 0.f;
-    o.b = 0.f;
   }
   return o;
 }
@@ -291,27 +395,27 @@ __device__ inline T to_T(float x) { return (T)x; }
 
 // ---------------------------------------------------------------------------
 // Query-outer backward: dQ_s for 32 query rows per wave (4 waves), key tiles
-// of BK rows streamed through LDS (K1, K2 row-major for the logits, K_s
-// transposed for the dQ contraction).  Deterministic; no atomics.
+// of BK rows of K1 and K2 streamed through LDS.  S^T = K Q^T keeps a lane on
+// one query row, so dS from the accumulators is directly the A operand of
+// dQ = dS K_s; K_s's B operand is read down the key rows of its tile.
+// Deterministic; no atomics.
 template <typename T, int D1, int D2, int SETTING, int BK>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
+  constexpr int NW = 4;
   constexpr int DS = SETTING == 1 ? D2 : D1;
-  constexpr int PAD = 16 / sizeof(T);
-  constexpr int LD1 = D1 + PAD, LD2 = D2 + PAD, LDT = BK + PAD;
   constexpr int S1 = D1 / MF::KSTEP, S2 = D2 / MF::KSTEP;
   constexpr int NKB = BK / 32, NB = DS / 32, HS = 32 / MF::KSTEP;
-  __shared__ __attribute__((aligned(16))) T sK1[BK * LD1];
-  __shared__ __attribute__((aligned(16))) T sK2[BK * LD2];
-  __shared__ __attribute__((aligned(16))) T sKT[DS * LDT];
+  constexpr int TS = BK * (D1 + D2);
+  __shared__ __attribute__((aligned(1024))) T lds[2 * TS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
   const int64_t lin = blockIdx.x;
   const int64_t bh = lin % a.BH;
   const int qb = a.nblk - 1 - (int)(lin / a.BH);
-  const int q0 = qb * 128 + 32 * wave;
+  const int q0 = qb * 32 * NW + 32 * wave;
   const int qrow = q0 + col;
   const int off = a.n_k - a.n_q;
 
@@ -319,53 +423,67 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const T* K1 = reinterpret_cast<const T*>(a.k1) + bh * (int64_t)a.n_k * D1;
   const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
   const T* K2 = reinterpret_cast<const T*>(a.k2) + bh * (int64_t)a.n_k * D2;
-  const T* KS = SETTING == 1 ? K2 : K1;
 
   int kend = a.n_k;
-  if (a.causal) kend = min(kend, min(a.n_q, qb * 128 + 128) - 1 + off + 1);
+  if (a.causal) kend = min(kend, min(a.n_q, qb * 32 * NW + 32 * NW) - 1 + off + 1);
   const bool wave_rows = q0 < a.n_q;
   const int wave_kmax = a.causal ? (min(a.n_q, q0 + 32) - 1 + off) : 0x7fffffff;
+  const int ntiles = (kend + BK - 1) / BK;
+  const int kmax = a.n_k - 1;
+
+  tile_load_async<T, D1, BK, NW>(lds, K1, 0, kmax, wave, lane);
+  tile_load_async<T, D2, BK, NW>(lds + BK * D1, K2, 0, kmax, wave, lane);
 
   frag qf1[S1], qf2[S2];
+  const bool qv = qrow < a.n_q;
 #pragma unroll
-  for (int s = 0; s < S1; ++s) qf1[s] = qrow < a.n_q ? frag_rowmajor(Q1 + (int64_t)q0 * D1, D1, s, col, grp) : zero_frag<T>();
+  for (int s = 0; s < S1; ++s) qf1[s] = frag_global<T, D1>(Q1, qrow, a.n_q - 1, qv, s, grp);
 #pragma unroll
-  for (int s = 0; s < S2; ++s) qf2[s] = qrow < a.n_q ? frag_rowmajor(Q2 + (int64_t)q0 * D2, D2, s, col, grp) : zero_frag<T>();
-  RowGrad rg = {0.f, 0.f, 0.f, 0.f, 0.f};
-  if (qrow < a.n_q) rg = load_rowgrad<SETTING>(a, bh * a.n_q + qrow);
+  for (int s = 0; s < S2; ++s) qf2[s] = frag_global<T, D2>(Q2, qrow, a.n_q - 1, qv, s, grp);
+  const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.n_q + qrow, qv);
 
   f32x16 dqa[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dqa[nb] = zero16();
 
-  for (int k0 = 0; k0 < kend; k0 += BK) {
+  for (int t = 0; t < ntiles; ++t) {
+    wait_loads();
     __syncthreads();
-    load_rows<T, D1, LD1, BK, 256>(sK1, K1, k0, kend, tid);
-    load_rows<T, D2, LD2, BK, 256>(sK2, K2, k0, kend, tid);
-    load_rows_T<T, DS, LDT, BK, 256>(sKT, KS, k0, kend, tid);
-    __syncthreads();
+    const int k0 = t * BK;
+    if (t + 1 < ntiles) {
+      T* nbuf = lds + ((t + 1) & 1) * TS;
+      tile_load_async<T, D1, BK, NW>(nbuf, K1, k0 + BK, kmax, wave, lane);
+      tile_load_async<T, D2, BK, NW>(nbuf + BK * D1, K2, k0 + BK, kmax, wave, lane);
+    }
     if (!wave_rows || k0 > wave_kmax) continue;
+    const T* sK1 = lds + (t & 1) * TS;
+    const T* sK2 = sK1 + BK * D1;
+    const T* sKS = SETTING == 1 ? sK2 : sK1;
     const bool need_mask = (k0 + BK > kend) || (a.causal && k0 + BK - 1 > q0 + off);
     const int lim = a.causal ? min(kend - 1, qrow + off) : kend - 1;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 s1 = zero16(), s2 = zero16();
 #pragma unroll
-      for (int s = 0; s < S1; ++s) s1 = MF::run(frag_rowmajor(sK1 + kb * 32 * LD1, LD1, s, col, grp), qf1[s], s1);
+      for (int s = 0; s < S1; ++s) s1 = MF::run(frag_tile<T, D1>(sK1, kb * 32 + col, s, grp), qf1[s], s1);
 #pragma unroll
-      for (int s = 0; s < S2; ++s) s2 = MF::run(frag_rowmajor(sK2 + kb * 32 * LD2, LD2, s, col, grp), qf2[s], s2);
+      for (int s = 0; s < S2; ++s) s2 = MF::run(frag_tile<T, D2>(sK2, kb * 32 + col, s, grp), qf2[s], s2);
+      if (need_mask) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float ds = dS_elem<SETTING>(s1[e], s2[e], a.c1, a.c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
-        if (need_mask && k0 + kb * 32 + acc_row(e, grp) > lim) ds = 0.f;
-        s1[e] = ds;
+        for (int e = 0; e < 16; ++e) {
+          const float ds = dS_elem<SETTING>(s1[e], s2[e], a.c1, a.c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
+          s1[e] = (k0 + kb * 32 + acc_row(e, grp) > lim) ? 0.f : ds;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s1[e] = dS_elem<SETTING>(s1[e], s2[e], a.c1, a.c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
       }
 #pragma unroll
       for (int h = 0; h < HS; ++h) {
         const frag af = frag_from_acc(s1, h, T());
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          dqa[nb] = MF::run(af, fragT_accorder(sKT + nb * 32 * LDT, LDT, kb * 32, h, col, grp, T()), dqa[nb]);
+          dqa[nb] = MF::run(af, fragcol_acc<T, DS>(sKS, kb * 32, nb * 32, h, lane), dqa[nb]);
       }
     }
   }
@@ -382,25 +500,25 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Key-outer backward: each wave owns 32 key rows (workgroup: 4 waves, 128
 // keys), keeps K1, K2 in registers and accumulates dK_s in registers while
-// query tiles of 32 rows stream through LDS.  The logits are computed as
-// S = Q K^T so a lane's accumulator column is one key.  FUSED additionally
-// forms dQ_s for every query tile from the same dS (written to LDS) and adds
-// it to global dQ_s with fp32 atomics: each query-key pair is visited once.
-template <typename T, int D1, int D2, int SETTING, bool FUSED>
+// query tiles of BQ rows of Q1 and Q2 stream through LDS.  The logits are
+// computed as S = Q K^T so a lane's accumulator column is one key and dS from
+// the accumulators is directly the A operand of dK = dS^T Q_s; Q_s's B operand
+// is read down the query rows of its tile.  FUSED additionally forms dQ_s for
+// every query tile from the same dS (staged in LDS as [key][query]) and adds it
+// to global dQ_s with fp32 atomics, so each query-key pair is visited once.
+template <typename T, int D1, int D2, int SETTING, bool FUSED, int BQ>
 __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
-  constexpr int BQ = 32, WK = 4, BKW = 32 * WK;
+  constexpr int NW = 4, BKW = 32 * NW;
   constexpr int DS = SETTING == 1 ? D2 : D1;
-  constexpr int PAD = 16 / sizeof(T);
-  constexpr int LD1 = D1 + PAD, LD2 = D2 + PAD, LDT = BQ + PAD, LDD = BKW + PAD;
   constexpr int S1 = D1 / MF::KSTEP, S2 = D2 / MF::KSTEP;
-  constexpr int NB = DS / 32, HS = 32 / MF::KSTEP, HK = BKW / MF::KSTEP;
-  __shared__ __attribute__((aligned(16))) T sQ1[BQ * LD1];
-  __shared__ __attribute__((aligned(16))) T sQ2[BQ * LD2];
-  __shared__ __attribute__((aligned(16))) T sQT[DS * LDT];
-  __shared__ __attribute__((aligned(16))) float sL1[BQ], sL2[BQ], sGS[BQ], sRA[BQ], sRB[BQ];
-  __shared__ __attribute__((aligned(16))) T sdS[FUSED ? BQ * LDD : 1];
+  constexpr int NB = DS / 32, HS = 32 / MF::KSTEP, NQB = BQ / 32, HK = BKW / MF::KSTEP;
+  constexpr int TS = BQ * (D1 + D2);
+  constexpr int NSTAT = SETTING == 2 ? 5 : 3;
+  __shared__ __attribute__((aligned(1024))) T lds[2 * TS];
+  __shared__ __attribute__((aligned(16))) float sstat[2][NSTAT][BQ];
+  __shared__ __attribute__((aligned(1024))) T sdS[FUSED ? BKW * BQ : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
@@ -416,32 +534,62 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   const T* K1 = reinterpret_cast<const T*>(a.k1) + bh * (int64_t)a.n_k * D1;
   const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
   const T* K2 = reinterpret_cast<const T*>(a.k2) + bh * (int64_t)a.n_k * D2;
-  const T* QS = SETTING == 1 ? Q2 : Q1;
   const T* KS = SETTING == 1 ? K2 : K1;
 
-  frag kf1[S1], kf2[S2];
-#pragma unroll
-  for (int s = 0; s < S1; ++s) kf1[s] = krow < a.n_k ? frag_rowmajor(K1 + (int64_t)kwave * D1, D1, s, col, grp) : zero_frag<T>();
-#pragma unroll
-  for (int s = 0; s < S2; ++s) kf2[s] = krow < a.n_k ? frag_rowmajor(K2 + (int64_t)kwave * D2, D2, s, col, grp) : zero_frag<T>();
+  const int qbeg = a.causal ? max(0, kw0 - off) : 0;
+  const int qt0 = (qbeg / BQ) * BQ;
+  const int ntiles = qt0 < a.n_q ? (a.n_q - qt0 + BQ - 1) / BQ : 0;
+  const int qmax = a.n_q - 1;
 
-  // FUSED: this wave's dQ task is the 32-column block `wave` of dQ_s; it needs
-  // K_s[kw0 .. kw0+128)[32*wave + col] as the B operand, k = keys in order.
-  constexpr int NTASK = FUSED ? (NB < WK ? NB : WK) : 0;
+  // stats of one query tile: thread q < BQ loads row q (zeros past n_q)
+  auto load_stats = [&](int q0, RowGrad& rg) {
+    rg = load_rowgrad<SETTING>(a, bh * a.n_q + q0 + tid, tid < BQ && q0 + tid < a.n_q);
+  };
+  auto store_stats = [&](int buf, const RowGrad& rg) {
+    if (tid < BQ) {
+      sstat[buf][0][tid] = rg.L1;
+      sstat[buf][1][tid] = rg.L2;
+      sstat[buf][2][tid] = rg.gs;
+      if constexpr (SETTING == 2) {
+        sstat[buf][3][tid] = rg.a;
+        sstat[buf][4][tid] = rg.b;
+      }
+    }
+  };
+
+  RowGrad rgn;
+  if (ntiles > 0) {
+    tile_load_async<T, D1, BQ, NW>(lds, Q1, qt0, qmax, wave, lane);
+    tile_load_async<T, D2, BQ, NW>(lds + BQ * D1, Q2, qt0, qmax, wave, lane);
+    load_stats(qt0, rgn);
+    store_stats(0, rgn);
+  }
+
+  frag kf1[S1], kf2[S2];
+  const bool kv = krow < a.n_k;
+#pragma unroll
+  for (int s = 0; s < S1; ++s) kf1[s] = frag_global<T, D1>(K1, krow, a.n_k - 1, kv, s, grp);
+#pragma unroll
+  for (int s = 0; s < S2; ++s) kf2[s] = frag_global<T, D2>(K2, krow, a.n_k - 1, kv, s, grp);
+
+  // FUSED: wave w computes dQ_s columns [32*(w % NB), +32) for query blocks
+  // qb = w / NB, w / NB + NW / NB, ...; its B operand K_s[kw0 .. kw0+128)[cols]
+  // stays in registers, k = keys in natural order.
+  constexpr int NBF = NB < NW ? NB : NW;
   frag kcf[FUSED ? HK : 1];
   if constexpr (FUSED) {
-    if (wave < NTASK) {
+    const int dcol = 32 * (wave % NBF) + col;
 #pragma unroll
-      for (int h = 0; h < HK; ++h) {
-        if constexpr (MF::KPL == 1) {
-          const int key = kw0 + h * MF::KSTEP + grp;
-          kcf[h] = key < a.n_k ? (float)KS[(int64_t)key * DS + 32 * wave + col] : 0.f;
-        } else {
+    for (int h = 0; h < HK; ++h) {
+      if constexpr (MF::KPL == 1) {
+        const int key = kw0 + h * MF::KSTEP + grp;
+        kcf[h] = key < a.n_k ? (float)KS[(int64_t)key * DS + dcol] : 0.f;
+      } else {
 #pragma unroll
-          for (int e = 0; e < MF::KPL; ++e) {
-            const int key = kw0 + h * MF::KSTEP + grp * MF::KPL + e;
-            kcf[h][e] = key < a.n_k ? KS[(int64_t)key * DS + 32 * wave + col] : (T)0.f;
-          }
+        for (int e = 0; e < MF::KPL; ++e) {
+          const int key = kw0 + h * MF::KSTEP + grp * MF::KPL + e;
+          kcf[h][e] = KS[(int64_t)min(key, a.n_k - 1) * DS + dcol];
+          if (key >= a.n_k) kcf[h][e] = (T)0.f;
         }
       }
     }
@@ -450,68 +598,105 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   f32x16 dka[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dka[nb] = zero16();
+  const bool wave_has_keys = kwave < a.n_k;
 
-  const int qbeg = a.causal ? max(0, kw0 - off) : 0;
-  const int wave_has_keys = kwave < a.n_k;
-  for (int q0 = (qbeg / BQ) * BQ; q0 < a.n_q; q0 += BQ) {
+  for (int t = 0; t < ntiles; ++t) {
+    wait_loads();
     __syncthreads();
-    load_rows<T, D1, LD1, BQ, 256>(sQ1, Q1, q0, a.n_q, tid);
-    load_rows<T, D2, LD2, BQ, 256>(sQ2, Q2, q0, a.n_q, tid);
-    load_rows_T<T, DS, LDT, BQ, 256>(sQT, QS, q0, a.n_q, tid);
-    if (tid < BQ) {
-      RowGrad rg = {0.f, 0.f, 0.f, 0.f, 0.f};
-      if (q0 + tid < a.n_q) rg = load_rowgrad<SETTING>(a, bh * a.n_q + q0 + tid);
-      sL1[tid] = rg.L1;
-      sL2[tid] = rg.L2;
-      sGS[tid] = rg.gs;
-      sRA[tid] = rg.a;
-      sRB[tid] = rg.b;
+    const int q0 = qt0 + t * BQ;
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      T* nbuf = lds + ((t + 1) & 1) * TS;
+      tile_load_async<T, D1, BQ, NW>(nbuf, Q1, q0 + BQ, qmax, wave, lane);
+      tile_load_async<T, D2, BQ, NW>(nbuf + BQ * D1, Q2, q0 + BQ, qmax, wave, lane);
+      load_stats(q0 + BQ, rgn);
     }
-    __syncthreads();
-    const bool active = wave_has_keys && (!a.causal || kwave <= min(a.n_q, q0 + BQ) - 1 + off);
-    if (active) {
-      const bool need_mask = (q0 + BQ > a.n_q) || (kwave + 32 > a.n_k) || (a.causal && kwave + 31 > q0 + off);
-      f32x16 s1 = zero16(), s2 = zero16();
+    const T* sQ1 = lds + (t & 1) * TS;
+    const T* sQ2 = sQ1 + BQ * D1;
+    const T* sQS = SETTING == 1 ? sQ2 : sQ1;
+    const float* st = &sstat[t & 1][0][0];
+
 #pragma unroll
-      for (int s = 0; s < S1; ++s) s1 = MF::run(frag_rowmajor(sQ1, LD1, s, col, grp), kf1[s], s1);
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qb0 = q0 + 32 * qb;
+      const bool active = wave_has_keys && (!a.causal || kwave <= min(a.n_q, qb0 + 32) - 1 + off);
+      if (active) {
+        f32x16 s1 = zero16(), s2 = zero16();
 #pragma unroll
-      for (int s = 0; s < S2; ++s) s2 = MF::run(frag_rowmajor(sQ2, LD2, s, col, grp), kf2[s], s2);
+        for (int s = 0; s < S1; ++s) s1 = MF::run(frag_tile<T, D1>(sQ1, 32 * qb + col, s, grp), kf1[s], s1);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int ql = acc_row(e, grp);
-        float ds = dS_elem<SETTING>(s1[e], s2[e], a.c1, a.c2, sL1[ql], sL2[ql], sGS[ql], sRA[ql], sRB[ql]);
-        if (need_mask) {
-          const int q = q0 + ql;
-          const bool ok = q < a.n_q && krow < a.n_k && (!a.causal || krow <= q + off);
-          if (!ok) ds = 0.f;
+        for (int s = 0; s < S2; ++s) s2 = MF::run(frag_tile<T, D2>(sQ2, 32 * qb + col, s, grp), kf2[s], s2);
+        const bool need_mask = (qb0 + 32 > a.n_q) || (kwave + 32 > a.n_k) || (a.causal && kwave + 31 > qb0 + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ql = 32 * qb + 8 * i + 4 * grp;
+          const f32x4 L1 = *reinterpret_cast<const f32x4*>(st + 0 * BQ + ql);
+          const f32x4 L2 = *reinterpret_cast<const f32x4*>(st + 1 * BQ + ql);
+          const f32x4 GS = *reinterpret_cast<const f32x4*>(st + 2 * BQ + ql);
+          f32x4 RA = {0.f, 0.f, 0.f, 0.f}, RB = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (SETTING == 2) {
+            RA = *reinterpret_cast<const f32x4*>(st + 3 * BQ + ql);
+            RB = *reinterpret_cast<const f32x4*>(st + 4 * BQ + ql);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = 4 * i + j;
+            float ds = dS_elem<SETTING>(s1[e], s2[e], a.c1, a.c2, L1[j], L2[j], GS[j], RA[j], RB[j]);
+            if (need_mask) {
+              const int q = qb0 + 8 * i + 4 * grp + j;
+              const bool ok = q < a.n_q && krow < a.n_k && (!a.causal || krow <= q + off);
+              ds = ok ? ds : 0.f;
+            }
+            s1[e] = ds;
+          }
         }
-        s1[e] = ds;
+#pragma unroll
+        for (int h = 0; h < HS; ++h) {
+          const frag af = frag_from_acc(s1, h, T());
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            dka[nb] = MF::run(af, fragcol_acc<T, DS>(sQS, 32 * qb, nb * 32, h, lane), dka[nb]);
+        }
+        if constexpr (FUSED) {
+          // dS^T tile in LDS as [key][query]: 4 consecutive queries per store
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            T* p = sdS + Tile<T, BQ>::off(32 * wave + col, 32 * qb + 8 * i + 4 * grp);
+            if constexpr (MF::KPL == 1) {
+              *reinterpret_cast<f32x4*>(p) = f32x4{s1[4 * i], s1[4 * i + 1], s1[4 * i + 2], s1[4 * i + 3]};
+            } else {
+              bf16x4 v;
+              v[0] = (bf16)s1[4 * i]; v[1] = (bf16)s1[4 * i + 1]; v[2] = (bf16)s1[4 * i + 2]; v[3] = (bf16)s1[4 * i + 3];
+              *reinterpret_cast<bf16x4*>(p) = v;
+            }
+          }
+        }
+      } else if constexpr (FUSED) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          T* p = sdS + Tile<T, BQ>::off(32 * wave + col, 32 * qb + 8 * i + 4 * grp);
+          if constexpr (MF::KPL == 1) *reinterpret_cast<f32x4*>(p) = f32x4{0.f, 0.f, 0.f, 0.f};
+          else *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+        }
       }
-#pragma unroll
-      for (int h = 0; h < HS; ++h) {
-        const frag af = frag_from_acc(s1, h, T());
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          dka[nb] = MF::run(af, fragT_accorder(sQT + nb * 32 * LDT, LDT, 0, h, col, grp, T()), dka[nb]);
-      }
-      if constexpr (FUSED) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sdS[acc_row(e, grp) * LDD + 32 * wave + col] = to_T<T>(s1[e]);
-      }
-    } else if constexpr (FUSED) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sdS[acc_row(e, grp) * LDD + 32 * wave + col] = to_T<T>(0.f);
     }
+    if (more) store_stats((t + 1) & 1, rgn);
+
     if constexpr (FUSED) {
       __syncthreads();
-      if (wave < NTASK) {
+      constexpr int QSTEP = NW / NBF;
+#pragma unroll
+      for (int qb = wave / NBF; qb < NQB; qb += QSTEP) {
+        const int qb0 = q0 + 32 * qb;
+        if (qb0 >= a.n_q) continue;
         f32x16 dqa = zero16();
 #pragma unroll
-        for (int h = 0; h < HK; ++h) dqa = MF::run(frag_rowmajor(sdS, LDD, h, col, grp), kcf[h], dqa);
+        for (int h = 0; h < HK; ++h) dqa = MF::run(fragcol_nat<T, BQ>(sdS, 0, 32 * qb, h, lane), kcf[h], dqa);
+        const int dcol = 32 * (wave % NBF) + col;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int q = q0 + acc_row(e, grp);
-          if (q < a.n_q) atomicAdd(a.dq + (bh * a.n_q + q) * DS + 32 * wave + col, dqa[e]);
+          const int q = qb0 + acc_row(e, grp);
+          if (q < a.n_q) atomicAdd(a.dq + (bh * a.n_q + q) * DS + dcol, dqa[e]);
         }
       }
     }

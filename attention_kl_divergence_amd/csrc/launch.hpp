@@ -15,6 +15,8 @@ constexpr int kFwdTile = 64;      // key rows per forward LDS tile
 constexpr int kBwdQRows = 128;    // query rows per dQ workgroup
 constexpr int kBwdKeyTile = 64;   // key rows per dQ-kernel LDS tile
 constexpr int kBwdKRows = 128;    // key rows per dK workgroup (4 waves x 32)
+// query rows per LDS tile of the dK kernel (fp32 tiles are twice as large)
+template <typename T> constexpr int kBwdQTile = sizeof(T) == 2 ? 64 : 32;
 
 using FwdLaunch = hipError_t (*)(const FwdArgs&, int64_t, hipStream_t);
 using DqLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t);
