@@ -26,6 +26,8 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-munsafe-fp-atomics",
+    # keep MFMA accumulators in VGPRs (no accvgpr copies before the VALU softmax)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # packed fp32 VALU forms are disabled for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",

@@ -393,6 +393,38 @@ __device__ inline float dS_elem(float s1, float s2, float c1, float c2, float L1
 template <typename T>
 __device__ inline T to_T(float x) { return (T)x; }
 
+
+// dS for one 32x32 block of the key-outer kernel (lane = key, accumulator rows
+// = queries qb0 + acc_row(e, grp)); per-query stats come from LDS
+// (st[k*BQ + q]: L1, L2, gs, then a, b for setting 2).  MASK: queries outside
+// [qlo, n_q) get dS = 0.  Result overwrites s1.
+template <int SETTING, bool MASK, int BQ>
+__device__ inline void dS_rows_keyouter(f32x16& s1, const f32x16& s2, const float* st, int ql0, int qb0, int grp,
+                                        float c1, float c2, int qlo, int n_q) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ql = ql0 + 8 * i + 4 * grp;
+    const f32x4 L1 = *reinterpret_cast<const f32x4*>(st + 0 * BQ + ql);
+    const f32x4 L2 = *reinterpret_cast<const f32x4*>(st + 1 * BQ + ql);
+    const f32x4 GS = *reinterpret_cast<const f32x4*>(st + 2 * BQ + ql);
+    f32x4 RA = {0.f, 0.f, 0.f, 0.f}, RB = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (SETTING == 2) {
+      RA = *reinterpret_cast<const f32x4*>(st + 3 * BQ + ql);
+      RB = *reinterpret_cast<const f32x4*>(st + 4 * BQ + ql);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * i + j;
+      float ds = dS_elem<SETTING>(s1[e], s2[e], c1, c2, L1[j], L2[j], GS[j], RA[j], RB[j]);
+      if constexpr (MASK) {
+        const int q = qb0 + 8 * i + 4 * grp + j;
+        ds = ((q >= qlo) & (q < n_q)) ? ds : 0.f;
+      }
+      s1[e] = ds;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Query-outer backward: dQ_s for 32 query rows per wave (4 waves), key tiles
 // of BK rows of K1 and K2 streamed through LDS.  S^T = K Q^T keeps a lane on
@@ -599,6 +631,8 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dka[nb] = zero16();
   const bool wave_has_keys = kwave < a.n_k;
+  // queries that see this lane's key: [qlo, n_q)
+  const int qlo = kv ? (a.causal ? krow - off : 0) : 0x3fffffff;
 
   for (int t = 0; t < ntiles; ++t) {
     wait_loads();
@@ -627,29 +661,8 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
 #pragma unroll
         for (int s = 0; s < S2; ++s) s2 = MF::run(frag_tile<T, D2>(sQ2, 32 * qb + col, s, grp), kf2[s], s2);
         const bool need_mask = (qb0 + 32 > a.n_q) || (kwave + 32 > a.n_k) || (a.causal && kwave + 31 > qb0 + off);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ql = 32 * qb + 8 * i + 4 * grp;
-          const f32x4 L1 = *reinterpret_cast<const f32x4*>(st + 0 * BQ + ql);
-          const f32x4 L2 = *reinterpret_cast<const f32x4*>(st + 1 * BQ + ql);
-          const f32x4 GS = *reinterpret_cast<const f32x4*>(st + 2 * BQ + ql);
-          f32x4 RA = {0.f, 0.f, 0.f, 0.f}, RB = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (SETTING == 2) {
-            RA = *reinterpret_cast<const f32x4*>(st + 3 * BQ + ql);
-            RB = *reinterpret_cast<const f32x4*>(st + 4 * BQ + ql);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int e = 4 * i + j;
-            float ds = dS_elem<SETTING>(s1[e], s2[e], a.c1, a.c2, L1[j], L2[j], GS[j], RA[j], RB[j]);
-            if (need_mask) {
-              const int q = qb0 + 8 * i + 4 * grp + j;
-              const bool ok = q < a.n_q && krow < a.n_k && (!a.causal || krow <= q + off);
-              ds = ok ? ds : 0.f;
-            }
-            s1[e] = ds;
-          }
-        }
+        if (need_mask) dS_rows_keyouter<SETTING, true, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
+        else dS_rows_keyouter<SETTING, false, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
 #pragma unroll
         for (int h = 0; h < HS; ++h) {
           const frag af = frag_from_acc(s1, h, T());
