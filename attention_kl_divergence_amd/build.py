@@ -28,6 +28,9 @@ FLAGS = [
     "-munsafe-fp-atomics",
     # keep MFMA accumulators in VGPRs (no accvgpr copies before the VALU softmax)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # no value in these kernels is NaN by design (masked lanes are selected
+    # away), so max/min need no NaN-quieting and fold into v_max3_f32
+    "-fno-honor-nans",
     # packed fp32 VALU forms are disabled for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",

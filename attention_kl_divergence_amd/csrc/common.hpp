@@ -54,13 +54,6 @@ __device__ inline f32x16 zero16() {
 // Row (within a 32-row block) held by accumulator element e of lane group grp.
 __device__ inline int acc_row(int e, int grp) { return 8 * (e >> 2) + 4 * grp + (e & 3); }
 
-// Fragment of a row-major operand: row `col` of `base` (leading dim ld), k step s.
-template <typename T>
-__device__ inline typename Mfma<T>::frag frag_rowmajor(const T* base, int ld, int s, int col, int grp) {
-  const T* p = base + col * ld + s * Mfma<T>::KSTEP + grp * Mfma<T>::KPL;
-  return *reinterpret_cast<const typename Mfma<T>::frag*>(p);
-}
-
 // A-operand fragment built from a 32x32 accumulator whose lane column is the
 // operand's row; contraction runs over the accumulator's rows in the order
 // acc_row(h*KPL + e', grp).
@@ -72,23 +65,8 @@ __device__ inline bf16x8 frag_from_acc(const f32x16& c, int h, bf16) {
 }
 __device__ inline float frag_from_acc(const f32x16& c, int h, float) { return c[h]; }
 
-// B-operand fragment matching frag_from_acc's k order, read from a tile stored
-// transposed in LDS as tileT[n][k] (k contiguous, leading dim ldt): lane
-// column n = col, k = acc_row(h*KPL + e', grp) within the 32-k block k0.
-__device__ inline bf16x8 fragT_accorder(const bf16* tileT, int ldt, int k0, int h, int col, int grp, bf16) {
-  const bf16* p = tileT + col * ldt + k0 + 16 * h + 4 * grp;
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
-  bf16x8 f;
-  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-  return f;
-}
-__device__ inline float fragT_accorder(const float* tileT, int ldt, int k0, int h, int col, int grp, float) {
-  return tileT[col * ldt + k0 + acc_row(h, grp)];
-}
-
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 
 // The five running scalars of one (partial) row, in base-2 units:
 // M_t = running max of y_t = S_t * log2(e), l_t = sum 2^(y_t - M_t),
@@ -134,10 +112,5 @@ __device__ inline RowState shfl_xor_state(const RowState& s, int mask) {
   o.l2 = __shfl_xor(s.l2, mask);
   return o;
 }
-
-// 16-byte chunk copy helpers used by the cooperative tile loaders.
-struct alignas(16) Chunk16 {
-  uint32_t w[4];
-};
 
 }  // namespace streamkl

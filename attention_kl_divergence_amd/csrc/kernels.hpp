@@ -73,38 +73,70 @@ typedef __bf16 bf16x4_lds __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Swizzled LDS tile of row-major [rows][D] elements.  Chunk = 16 bytes.
+// The swizzle spreads (a) 16 consecutive rows read at one chunk (MFMA row
+// fragments) and (b) 4 consecutive rows read at two adjacent chunks (the
+// transpose reads) over distinct 16-byte bank groups of a 256-byte window.
 template <typename T, int D>
 struct Tile {
   static constexpr int EPC = 16 / sizeof(T);               // elements per chunk
   static constexpr int CPR = D / EPC;                      // chunks per row
   static constexpr int RP = CPR >= 16 ? 1 : 16 / CPR;      // rows sharing a 256-byte bank window
-  static constexpr int SWM = (CPR >= 16 ? 16 : CPR) - 1;   // swizzle mask
-  __device__ static inline int swz(int r) { return (r / RP) & SWM; }
+  static constexpr int CW = CPR >= 16 ? 16 : CPR;          // chunks of a row within one window
+  __device__ static inline int swz(int r) {
+    const int j = r / RP;
+    return ((j & (CW / 2 - 1)) << 1) | ((j / (CW / 2)) & 1);
+  }
   // element offset of (row r, column c)
   __device__ static inline int off(int r, int c) { return r * D + (((c / EPC) ^ swz(r)) * EPC) + (c % EPC); }
 };
 
-// Issue the direct loads of rows [r0, r0+ROWS) of a [*, D] global tensor into
-// an LDS tile; rows past rmax re-read row rmax (callers mask them).  Each
-// wave-wide load fills 1 KB of LDS: lane L writes bytes [16L, 16L+16) of it,
-// so the lane picks the global chunk that belongs at that swizzled spot.
+// Direct global->LDS loads of ROWS rows of a [*, D] global tensor into an LDS
+// tile.  Each wave-wide 16-byte buffer load fills 1 KB of LDS (lane L writes
+// bytes [16L, 16L+16) of it), so each lane fetches the global chunk that
+// belongs at that swizzled spot; those per-lane byte offsets are fixed for the
+// kernel.  Per tile only the buffer resource changes (scalar work): its base
+// is the tile's first row and its size the bytes left in the tensor, so rows
+// past the end read as zeros.
 template <typename T, int D, int ROWS, int NW>
-__device__ inline void tile_load_async(T* tile, const T* __restrict__ g, int r0, int rmax, int wave, int lane) {
+struct TileLoader {
   using F = Tile<T, D>;
-  constexpr int NI = ROWS * F::CPR / 64;
+  static constexpr int NI = ROWS * F::CPR / 64;
+  static constexpr int PER = NI / NW;
   static_assert(NI % NW == 0, "tile loads must split evenly over the waves");
+  int voff[PER];
+  int wave;
+  __device__ inline TileLoader(int wave_, int lane) : wave(wave_) {
 #pragma unroll
-  for (int i = 0; i < NI / NW; ++i) {
-    const int J = wave * (NI / NW) + i;
-    const int P = J * 64 + lane;
-    const int r = P / F::CPR, pc = P % F::CPR;
-    const int lc = pc ^ F::swz(r);
-    const int gr = min(r0 + r, rmax);
-    const T* src = g + (int64_t)gr * D + lc * F::EPC;
-    __builtin_amdgcn_global_load_lds((const void*)src, (void __attribute__((address_space(3)))*)(tile + J * 64 * F::EPC),
-                                     16, 0, 0);
+    for (int i = 0; i < PER; ++i) {
+      const int P = (wave * PER + i) * 64 + lane;
+      const int r = P / F::CPR, pc = P % F::CPR;
+      voff[i] = (r * D + (pc ^ F::swz(r)) * F::EPC) * (int)sizeof(T);
+    }
   }
-}
+  // rows [r0, r0 + ROWS) of g (a tensor with nrows rows) into `tile`
+  __device__ inline void issue(T* tile, const T* g, int r0, int nrows) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer-resource type exists only in the device pass
+    const int left = nrows - r0;
+    const uint32_t bytes = left > 0 ? (uint32_t)left * (uint32_t)(D * sizeof(T)) : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(g + (int64_t)r0 * D), (short)0, (int)bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(tile + (wave * PER + i) * 64 * F::EPC), 16, voff[i], 0, 0, 0);
+#endif
+  }
+};
+
+// Raise the wave's issue priority around bursts of matrix instructions, so a
+// co-resident wave in its VALU phase fills the issue slots in between.
+#ifdef SKL_PRIO
+#define SKL_PRIO_HI() __builtin_amdgcn_s_setprio(1)
+#define SKL_PRIO_LO() __builtin_amdgcn_s_setprio(0)
+#else
+#define SKL_PRIO_HI() ((void)0)
+#define SKL_PRIO_LO() ((void)0)
+#endif
 
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -249,6 +281,51 @@ __device__ inline void fwd_update(RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[
   st.M2 = M2n;
 }
 
+
+// One key tile of the forward for one wave: the logits of 32-key block kb+1
+// are computed on the matrix cores while the VALU runs the online update of
+// block kb (the scheduling groups interleave the two streams).
+template <typename T, int D1, int D2, int NKB, bool MASK>
+__device__ inline void fwd_tile(RowState& st, const T* sK1, const T* sK2, const typename Mfma<T>::frag* qf1,
+                                const typename Mfma<T>::frag* qf2, float c1, float c2, int k0, int lim, int col,
+                                int grp) {
+  using MF = Mfma<T>;
+  constexpr int S1 = D1 / MF::KSTEP, S2 = D2 / MF::KSTEP;
+  constexpr int SM = S1 > S2 ? S1 : S2;
+  f32x16 s1[NKB][1], s2[NKB][1];
+  auto logits = [&](int kb) {
+    s1[kb][0] = zero16();
+    s2[kb][0] = zero16();
+#pragma unroll
+    for (int s = 0; s < SM; ++s) {
+      if (s < S1) s1[kb][0] = MF::run(frag_tile<T, D1>(sK1, kb * 32 + col, s, grp), qf1[s < S1 ? s : 0], s1[kb][0]);
+      if (s < S2) s2[kb][0] = MF::run(frag_tile<T, D2>(sK2, kb * 32 + col, s, grp), qf2[s < S2 ? s : 0], s2[kb][0]);
+    }
+  };
+  SKL_PRIO_HI();
+  logits(0);
+  SKL_PRIO_LO();
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    if (kb + 1 < NKB) {
+      SKL_PRIO_HI();
+      logits(kb + 1);
+      SKL_PRIO_LO();
+    }
+    fwd_update<MASK, 1>(st, s1[kb], s2[kb], c1, c2, k0 + kb * 32, lim, grp);
+#ifdef SKL_SCHED_HINTS
+    if (kb + 1 < NKB) {
+#pragma unroll
+      for (int i = 0; i < S1 + S2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      }
+    }
+#endif
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Forward.  Workgroup = 4 waves, each owning 32 query rows; key tiles of BK
 // rows of K1 and K2 stream through LDS.  Each wave computes S^T = K Q^T so a
@@ -288,11 +365,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const bool wave_rows = q0 < a.n_q;
   const int wave_kmax = a.causal ? (min(a.n_q, q0 + 32) - 1 + off) : 0x7fffffff;
   const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-  const int kmax = a.n_k - 1;
 
+  const TileLoader<T, D1, BK, NW> ld1(wave, lane);
+  const TileLoader<T, D2, BK, NW> ld2(wave, lane);
   if (ntiles > 0) {
-    tile_load_async<T, D1, BK, NW>(lds, K1, kbeg, kmax, wave, lane);
-    tile_load_async<T, D2, BK, NW>(lds + BK * D1, K2, kbeg, kmax, wave, lane);
+    ld1.issue(lds, K1, kbeg, a.n_k);
+    ld2.issue(lds + BK * D1, K2, kbeg, a.n_k);
   }
 
   frag qf1[S1], qf2[S2];
@@ -311,29 +389,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const int k0 = kbeg + t * BK;
     if (t + 1 < ntiles) {
       T* nb = lds + ((t + 1) & 1) * TS;
-      tile_load_async<T, D1, BK, NW>(nb, K1, k0 + BK, kmax, wave, lane);
-      tile_load_async<T, D2, BK, NW>(nb + BK * D1, K2, k0 + BK, kmax, wave, lane);
+      ld1.issue(nb, K1, k0 + BK, a.n_k);
+      ld2.issue(nb + BK * D1, K2, k0 + BK, a.n_k);
     }
     if (!wave_rows || k0 > wave_kmax) continue;
     const T* sK1 = lds + (t & 1) * TS;
     const T* sK2 = sK1 + BK * D1;
 
-    f32x16 s1[NKB], s2[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s1[kb] = zero16();
-      s2[kb] = zero16();
-#pragma unroll
-      for (int s = 0; s < S1; ++s) s1[kb] = MF::run(frag_tile<T, D1>(sK1, kb * 32 + col, s, grp), qf1[s], s1[kb]);
-#pragma unroll
-      for (int s = 0; s < S2; ++s) s2[kb] = MF::run(frag_tile<T, D2>(sK2, kb * 32 + col, s, grp), qf2[s], s2[kb]);
-    }
     const bool need_mask = (k0 + BK > kend) || (a.causal && k0 + BK - 1 > q0 + off);
     if (need_mask) {
       const int lim = a.causal ? min(kend - 1, qrow + off) : kend - 1;
-      fwd_update<true, NKB>(st, s1, s2, c1, c2, k0, lim, grp);
+      fwd_tile<T, D1, D2, NKB, true>(st, sK1, sK2, qf1, qf2, c1, c2, k0, lim, col, grp);
     } else {
-      fwd_update<false, NKB>(st, s1, s2, c1, c2, k0, 0, grp);
+      fwd_tile<T, D1, D2, NKB, false>(st, sK1, sK2, qf1, qf2, c1, c2, k0, 0, col, grp);
     }
   }
 
@@ -461,10 +529,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const bool wave_rows = q0 < a.n_q;
   const int wave_kmax = a.causal ? (min(a.n_q, q0 + 32) - 1 + off) : 0x7fffffff;
   const int ntiles = (kend + BK - 1) / BK;
-  const int kmax = a.n_k - 1;
 
-  tile_load_async<T, D1, BK, NW>(lds, K1, 0, kmax, wave, lane);
-  tile_load_async<T, D2, BK, NW>(lds + BK * D1, K2, 0, kmax, wave, lane);
+  const TileLoader<T, D1, BK, NW> ld1(wave, lane);
+  const TileLoader<T, D2, BK, NW> ld2(wave, lane);
+  ld1.issue(lds, K1, 0, a.n_k);
+  ld2.issue(lds + BK * D1, K2, 0, a.n_k);
 
   frag qf1[S1], qf2[S2];
   const bool qv = qrow < a.n_q;
@@ -484,8 +553,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     const int k0 = t * BK;
     if (t + 1 < ntiles) {
       T* nbuf = lds + ((t + 1) & 1) * TS;
-      tile_load_async<T, D1, BK, NW>(nbuf, K1, k0 + BK, kmax, wave, lane);
-      tile_load_async<T, D2, BK, NW>(nbuf + BK * D1, K2, k0 + BK, kmax, wave, lane);
+      ld1.issue(nbuf, K1, k0 + BK, a.n_k);
+      ld2.issue(nbuf + BK * D1, K2, k0 + BK, a.n_k);
     }
     if (!wave_rows || k0 > wave_kmax) continue;
     const T* sK1 = lds + (t & 1) * TS;
@@ -496,10 +565,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 s1 = zero16(), s2 = zero16();
+      SKL_PRIO_HI();
 #pragma unroll
       for (int s = 0; s < S1; ++s) s1 = MF::run(frag_tile<T, D1>(sK1, kb * 32 + col, s, grp), qf1[s], s1);
 #pragma unroll
       for (int s = 0; s < S2; ++s) s2 = MF::run(frag_tile<T, D2>(sK2, kb * 32 + col, s, grp), qf2[s], s2);
+      SKL_PRIO_LO();
       if (need_mask) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -510,6 +581,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) s1[e] = dS_elem<SETTING>(s1[e], s2[e], a.c1, a.c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
       }
+      SKL_PRIO_HI();
 #pragma unroll
       for (int h = 0; h < HS; ++h) {
         const frag af = frag_from_acc(s1, h, T());
@@ -517,6 +589,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         for (int nb = 0; nb < NB; ++nb)
           dqa[nb] = MF::run(af, fragcol_acc<T, DS>(sKS, kb * 32, nb * 32, h, lane), dqa[nb]);
       }
+      SKL_PRIO_LO();
     }
   }
 
@@ -571,7 +644,6 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   const int qbeg = a.causal ? max(0, kw0 - off) : 0;
   const int qt0 = (qbeg / BQ) * BQ;
   const int ntiles = qt0 < a.n_q ? (a.n_q - qt0 + BQ - 1) / BQ : 0;
-  const int qmax = a.n_q - 1;
 
   // stats of one query tile: thread q < BQ loads row q (zeros past n_q)
   auto load_stats = [&](int q0, RowGrad& rg) {
@@ -590,9 +662,11 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   };
 
   RowGrad rgn;
+  const TileLoader<T, D1, BQ, NW> ld1(wave, lane);
+  const TileLoader<T, D2, BQ, NW> ld2(wave, lane);
   if (ntiles > 0) {
-    tile_load_async<T, D1, BQ, NW>(lds, Q1, qt0, qmax, wave, lane);
-    tile_load_async<T, D2, BQ, NW>(lds + BQ * D1, Q2, qt0, qmax, wave, lane);
+    ld1.issue(lds, Q1, qt0, a.n_q);
+    ld2.issue(lds + BQ * D1, Q2, qt0, a.n_q);
     load_stats(qt0, rgn);
     store_stats(0, rgn);
   }
@@ -641,8 +715,8 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
     const bool more = t + 1 < ntiles;
     if (more) {
       T* nbuf = lds + ((t + 1) & 1) * TS;
-      tile_load_async<T, D1, BQ, NW>(nbuf, Q1, q0 + BQ, qmax, wave, lane);
-      tile_load_async<T, D2, BQ, NW>(nbuf + BQ * D1, Q2, q0 + BQ, qmax, wave, lane);
+      ld1.issue(nbuf, Q1, q0 + BQ, a.n_q);
+      ld2.issue(nbuf + BQ * D1, Q2, q0 + BQ, a.n_q);
       load_stats(q0 + BQ, rgn);
     }
     const T* sQ1 = lds + (t & 1) * TS;
@@ -656,13 +730,16 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
       const bool active = wave_has_keys && (!a.causal || kwave <= min(a.n_q, qb0 + 32) - 1 + off);
       if (active) {
         f32x16 s1 = zero16(), s2 = zero16();
+        SKL_PRIO_HI();
 #pragma unroll
         for (int s = 0; s < S1; ++s) s1 = MF::run(frag_tile<T, D1>(sQ1, 32 * qb + col, s, grp), kf1[s], s1);
 #pragma unroll
         for (int s = 0; s < S2; ++s) s2 = MF::run(frag_tile<T, D2>(sQ2, 32 * qb + col, s, grp), kf2[s], s2);
+        SKL_PRIO_LO();
         const bool need_mask = (qb0 + 32 > a.n_q) || (kwave + 32 > a.n_k) || (a.causal && kwave + 31 > qb0 + off);
         if (need_mask) dS_rows_keyouter<SETTING, true, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
         else dS_rows_keyouter<SETTING, false, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
+        SKL_PRIO_HI();
 #pragma unroll
         for (int h = 0; h < HS; ++h) {
           const frag af = frag_from_acc(s1, h, T());
@@ -670,6 +747,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
           for (int nb = 0; nb < NB; ++nb)
             dka[nb] = MF::run(af, fragcol_acc<T, DS>(sQS, 32 * qb, nb * 32, h, lane), dka[nb]);
         }
+        SKL_PRIO_LO();
         if constexpr (FUSED) {
           // dS^T tile in LDS as [key][query]: 4 consecutive queries per store
 #pragma unroll
