@@ -92,6 +92,13 @@ FwdLaunch pick_fwd(int dtype, int d1, int d2) {
 #undef SKL_PICK
   return nullptr;
 }
+FwdLaunch pick_fwd_pp(int dtype, int d1, int d2) {
+#define SKL_PICK(tn, a, b) if (d1 == a && d2 == b) return launch_fwd_pp_##tn##_##a##_##b;
+  if (dtype == STREAMKL_F32) { SKL_PICK(f32, 64, 64) SKL_PICK(f32, 64, 128) SKL_PICK(f32, 128, 64) SKL_PICK(f32, 128, 128) }
+  else { SKL_PICK(bf16, 64, 64) SKL_PICK(bf16, 64, 128) SKL_PICK(bf16, 128, 64) SKL_PICK(bf16, 128, 128) }
+#undef SKL_PICK
+  return nullptr;
+}
 DqLaunch pick_dq(int dtype, int d1, int d2) {
 #define SKL_PICK(tn, a, b) if (d1 == a && d2 == b) return launch_bwd_dq_##tn##_##a##_##b;
   if (dtype == STREAMKL_F32) { SKL_PICK(f32, 64, 64) SKL_PICK(f32, 64, 128) SKL_PICK(f32, 128, 64) SKL_PICK(f32, 128, 128) }
@@ -224,7 +231,9 @@ streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, con
       splits = 1;
     }
   }
-  FwdLaunch fn = pick_fwd(shape->dtype, shape->d1, shape->d2);
+  // Without a key split, long query ranges use the 8-wave ping-pong kernel.
+  const bool pp = splits == 1 && shape->n_q > kFwdRows;
+  FwdLaunch fn = pp ? pick_fwd_pp(shape->dtype, shape->d1, shape->d2) : pick_fwd(shape->dtype, shape->d1, shape->d2);
   if (!fn) return STREAMKL_ERR_UNSUPPORTED;
 
   FwdArgs a;
@@ -237,7 +246,7 @@ streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, con
   a.nsplit = splits;
   const int64_t tiles = cdiv(shape->n_k, kFwdTile);
   a.keys_per_split = (int)(cdiv(tiles, splits) * kFwdTile);
-  a.nqb = (int)cdiv(shape->n_q, kFwdRows);
+  a.nqb = (int)cdiv(shape->n_q, pp ? kFwdPPRows : kFwdRows);
   a.causal = causal ? 1 : 0;
   a.c1 = log2e_scale(scale1, shape->d1);
   a.c2 = log2e_scale(scale2, shape->d2);

@@ -100,9 +100,9 @@ struct Tile {
 template <typename T, int D, int ROWS, int NW>
 struct TileLoader {
   using F = Tile<T, D>;
-  static constexpr int NI = ROWS * F::CPR / 64;
-  static constexpr int PER = NI / NW;
-  static_assert(NI % NW == 0, "tile loads must split evenly over the waves");
+  static constexpr int NI = ROWS * F::CPR / 64;       // wave-wide loads per tile
+  static constexpr int PER = (NI + NW - 1) / NW;       // loads per wave (the last waves may idle)
+  static_assert(NI * 64 == ROWS * F::CPR, "a tile must be whole 1 KB blocks");
   int voff[PER];
   int wave;
   __device__ inline TileLoader(int wave_, int lane) : wave(wave_) {
@@ -122,21 +122,12 @@ struct TileLoader {
         __builtin_amdgcn_make_buffer_rsrc((void*)(g + (int64_t)r0 * D), (short)0, (int)bytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(tile + (wave * PER + i) * 64 * F::EPC), 16, voff[i], 0, 0, 0);
+      if (NI % NW == 0 || wave * PER + i < NI)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(tile + (wave * PER + i) * 64 * F::EPC), 16, voff[i], 0, 0, 0);
 #endif
   }
 };
-
-// Raise the wave's issue priority around bursts of matrix instructions, so a
-// co-resident wave in its VALU phase fills the issue slots in between.
-#ifdef SKL_PRIO
-#define SKL_PRIO_HI() __builtin_amdgcn_s_setprio(1)
-#define SKL_PRIO_LO() __builtin_amdgcn_s_setprio(0)
-#else
-#define SKL_PRIO_HI() ((void)0)
-#define SKL_PRIO_LO() ((void)0)
-#endif
 
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -225,6 +216,22 @@ __device__ inline typename Mfma<T>::frag frag_global(const T* g, int row, int rm
   return valid ? f : zero_frag<T>();
 }
 
+
+// Scheduling pattern for a run of N matrix instructions that each consume R
+// LDS reads: issue the reads for the first AHEAD instructions, then alternate
+// one instruction with the reads of the instruction AHEAD places later, so
+// LDS latency hides behind the matrix pipeline.  Placed after the code it
+// orders, inside the same basic block.
+template <int N, int R, int AHEAD>
+__device__ inline void sched_mfma_lds() {
+  constexpr int PRE = AHEAD < N ? AHEAD : N;
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE * R, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + PRE < N) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+}
 // ---------------------------------------------------------------------------
 // Forward online update of one lane's running state with NKB 32-key blocks of
 // raw dot products (s1, s2).  MASK: keys past `lim` are excluded.
@@ -302,27 +309,11 @@ __device__ inline void fwd_tile(RowState& st, const T* sK1, const T* sK2, const 
       if (s < S2) s2[kb][0] = MF::run(frag_tile<T, D2>(sK2, kb * 32 + col, s, grp), qf2[s < S2 ? s : 0], s2[kb][0]);
     }
   };
-  SKL_PRIO_HI();
   logits(0);
-  SKL_PRIO_LO();
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    if (kb + 1 < NKB) {
-      SKL_PRIO_HI();
-      logits(kb + 1);
-      SKL_PRIO_LO();
-    }
+    if (kb + 1 < NKB) logits(kb + 1);
     fwd_update<MASK, 1>(st, s1[kb], s2[kb], c1, c2, k0 + kb * 32, lim, grp);
-#ifdef SKL_SCHED_HINTS
-    if (kb + 1 < NKB) {
-#pragma unroll
-      for (int i = 0; i < S1 + S2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
-      }
-    }
-#endif
   }
 }
 
@@ -419,6 +410,127 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       a.ws[o + 3 * fs] = st.M2;
       a.ws[o + 4 * fs] = st.l2;
     }
+  }
+}
+
+
+// Logits of one key tile for one wave: s_t[kb] = K_t[kb*32 .. +32) Q_t^T for
+// the wave's 32 query rows (raw dot products), 2*NKB independent chains.
+template <typename T, int D1, int D2, int NKB>
+__device__ inline void fwd_logits(f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], const T* sK1, const T* sK2,
+                                  const typename Mfma<T>::frag* qf1, const typename Mfma<T>::frag* qf2, int col,
+                                  int grp) {
+  using MF = Mfma<T>;
+  constexpr int S1 = D1 / MF::KSTEP, S2 = D2 / MF::KSTEP;
+  constexpr int SM = S1 > S2 ? S1 : S2;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    s1[kb] = zero16();
+    s2[kb] = zero16();
+  }
+#pragma unroll
+  for (int s = 0; s < SM; ++s)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (s < S1) s1[kb] = MF::run(frag_tile<T, D1>(sK1, kb * 32 + col, s, grp), qf1[s < S1 ? s : 0], s1[kb]);
+      if (s < S2) s2[kb] = MF::run(frag_tile<T, D2>(sK2, kb * 32 + col, s, grp), qf2[s < S2 ? s : 0], s2[kb]);
+    }
+  sched_mfma_lds<NKB * (S1 + S2), 1, 4>();
+}
+
+// ---------------------------------------------------------------------------
+// Forward, ping-pong form for long query ranges.  Workgroup = 8 waves (two per
+// SIMD), each owning 32 query rows; both wave groups read the same key tiles
+// from LDS.  Group A (waves 0-3) computes the logits of tile t while group B
+// (waves 4-7, the other wave on each SIMD) runs the online update of tile
+// t-1; after a barrier the roles swap.  Each SIMD thus keeps one wave on the
+// matrix cores and one on the VALU.
+template <typename T, int D1, int D2, int BK>
+__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
+  using MF = Mfma<T>;
+  using frag = typename MF::frag;
+  constexpr int NW = 8;
+  constexpr int S1 = D1 / MF::KSTEP, S2 = D2 / MF::KSTEP;
+  constexpr int NKB = BK / 32;
+  constexpr int TS = BK * (D1 + D2);
+  __shared__ __attribute__((aligned(1024))) T lds[2 * TS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, grp = lane >> 5;
+  const int group = wave >> 2;
+  const int64_t lin = blockIdx.x;
+  const int64_t bh = lin % a.BH;
+  const int qb = a.nqb - 1 - (int)(lin / a.BH);  // longest causal rows first
+  const int qwg0 = qb * 32 * NW;
+  const int q0 = qwg0 + 32 * wave;
+  const int qrow = q0 + col;
+  const int off = a.n_k - a.n_q;
+
+  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + bh * (int64_t)a.n_k * D1;
+  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + bh * (int64_t)a.n_k * D2;
+
+  int kend = a.n_k;
+  if (a.causal) kend = min(kend, min(a.n_q, qwg0 + 32 * NW) - 1 + off + 1);
+  const bool wave_rows = q0 < a.n_q;
+  const int wave_kmax = a.causal ? (min(a.n_q, q0 + 32) - 1 + off) : 0x7fffffff;
+  const int ntiles = (kend + BK - 1) / BK;
+
+  const TileLoader<T, D1, BK, NW> ld1(wave, lane);
+  const TileLoader<T, D2, BK, NW> ld2(wave, lane);
+  ld1.issue(lds, K1, 0, a.n_k);
+  ld2.issue(lds + BK * D1, K2, 0, a.n_k);
+
+  frag qf1[S1], qf2[S2];
+  const bool qv = qrow < a.n_q;
+#pragma unroll
+  for (int s = 0; s < S1; ++s) qf1[s] = frag_global<T, D1>(Q1, qrow, a.n_q - 1, qv, s, grp);
+#pragma unroll
+  for (int s = 0; s < S2; ++s) qf2[s] = frag_global<T, D2>(Q2, qrow, a.n_q - 1, qv, s, grp);
+
+  RowState st = empty_state();
+  const float c1 = a.c1, c2 = a.c2;
+  const int lim_row = a.causal ? min(kend - 1, qrow + off) : kend - 1;
+  f32x16 s1[NKB], s2[NKB];
+
+  auto update = [&](int k0) {
+    if (!wave_rows || k0 > wave_kmax) return;
+    const bool need_mask = (k0 + BK > kend) || (a.causal && k0 + BK - 1 > q0 + off);
+    if (need_mask) fwd_update<true, NKB>(st, s1, s2, c1, c2, k0, lim_row, grp);
+    else fwd_update<false, NKB>(st, s1, s2, c1, c2, k0, 0, grp);
+  };
+
+  for (int t = 0; t < ntiles; ++t) {
+    wait_loads();
+    __syncthreads();
+    const int k0 = t * BK;
+    if (t + 1 < ntiles) {
+      T* nb = lds + ((t + 1) & 1) * TS;
+      ld1.issue(nb, K1, k0 + BK, a.n_k);
+      ld2.issue(nb + BK * D1, K2, k0 + BK, a.n_k);
+    }
+    const T* sK1 = lds + (t & 1) * TS;
+    const T* sK2 = sK1 + BK * D1;
+    const bool active = wave_rows && k0 <= wave_kmax;
+    if (group == 0) {
+      if (active) fwd_logits<T, D1, D2, NKB>(s1, s2, sK1, sK2, qf1, qf2, col, grp);
+    } else if (t > 0) {
+      update(k0 - BK);
+    }
+    __syncthreads();
+    if (group == 0) {
+      update(k0);
+    } else if (active) {
+      fwd_logits<T, D1, D2, NKB>(s1, s2, sK1, sK2, qf1, qf2, col, grp);
+    }
+  }
+  if (group == 1 && ntiles > 0) update((ntiles - 1) * BK);
+
+  st = merge_state(st, shfl_xor_state(st, 32));
+  if (grp == 0 && qrow < a.n_q) {
+    const int64_t r = bh * a.n_q + qrow;
+    finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
   }
 }
 
@@ -565,12 +677,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 s1 = zero16(), s2 = zero16();
-      SKL_PRIO_HI();
+      constexpr int SM = S1 > S2 ? S1 : S2;
 #pragma unroll
-      for (int s = 0; s < S1; ++s) s1 = MF::run(frag_tile<T, D1>(sK1, kb * 32 + col, s, grp), qf1[s], s1);
-#pragma unroll
-      for (int s = 0; s < S2; ++s) s2 = MF::run(frag_tile<T, D2>(sK2, kb * 32 + col, s, grp), qf2[s], s2);
-      SKL_PRIO_LO();
+      for (int s = 0; s < SM; ++s) {
+        if (s < S1) s1 = MF::run(frag_tile<T, D1>(sK1, kb * 32 + col, s, grp), qf1[s < S1 ? s : 0], s1);
+        if (s < S2) s2 = MF::run(frag_tile<T, D2>(sK2, kb * 32 + col, s, grp), qf2[s < S2 ? s : 0], s2);
+      }
+      sched_mfma_lds<S1 + S2, 1, 4>();
       if (need_mask) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -581,7 +694,6 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) s1[e] = dS_elem<SETTING>(s1[e], s2[e], a.c1, a.c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
       }
-      SKL_PRIO_HI();
 #pragma unroll
       for (int h = 0; h < HS; ++h) {
         const frag af = frag_from_acc(s1, h, T());
@@ -589,7 +701,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         for (int nb = 0; nb < NB; ++nb)
           dqa[nb] = MF::run(af, fragcol_acc<T, DS>(sKS, kb * 32, nb * 32, h, lane), dqa[nb]);
       }
-      SKL_PRIO_LO();
+      sched_mfma_lds<HS * NB, MF::KPL == 1 ? 1 : 2, 2>();
     }
   }
 
@@ -730,16 +842,16 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
       const bool active = wave_has_keys && (!a.causal || kwave <= min(a.n_q, qb0 + 32) - 1 + off);
       if (active) {
         f32x16 s1 = zero16(), s2 = zero16();
-        SKL_PRIO_HI();
+        constexpr int SM = S1 > S2 ? S1 : S2;
 #pragma unroll
-        for (int s = 0; s < S1; ++s) s1 = MF::run(frag_tile<T, D1>(sQ1, 32 * qb + col, s, grp), kf1[s], s1);
-#pragma unroll
-        for (int s = 0; s < S2; ++s) s2 = MF::run(frag_tile<T, D2>(sQ2, 32 * qb + col, s, grp), kf2[s], s2);
-        SKL_PRIO_LO();
+        for (int s = 0; s < SM; ++s) {
+          if (s < S1) s1 = MF::run(frag_tile<T, D1>(sQ1, 32 * qb + col, s, grp), kf1[s < S1 ? s : 0], s1);
+          if (s < S2) s2 = MF::run(frag_tile<T, D2>(sQ2, 32 * qb + col, s, grp), kf2[s < S2 ? s : 0], s2);
+        }
+        sched_mfma_lds<S1 + S2, 1, 4>();
         const bool need_mask = (qb0 + 32 > a.n_q) || (kwave + 32 > a.n_k) || (a.causal && kwave + 31 > qb0 + off);
         if (need_mask) dS_rows_keyouter<SETTING, true, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
         else dS_rows_keyouter<SETTING, false, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
-        SKL_PRIO_HI();
 #pragma unroll
         for (int h = 0; h < HS; ++h) {
           const frag af = frag_from_acc(s1, h, T());
@@ -747,7 +859,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
           for (int nb = 0; nb < NB; ++nb)
             dka[nb] = MF::run(af, fragcol_acc<T, DS>(sQS, 32 * qb, nb * 32, h, lane), dka[nb]);
         }
-        SKL_PRIO_LO();
+        sched_mfma_lds<HS * NB, MF::KPL == 1 ? 1 : 2, 2>();
         if constexpr (FUSED) {
           // dS^T tile in LDS as [key][query]: 4 consecutive queries per store
 #pragma unroll
@@ -803,3 +915,4 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
 }
 
 }  // namespace streamkl
+

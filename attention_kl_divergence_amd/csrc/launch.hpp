@@ -11,6 +11,7 @@ struct FwdArgs;
 struct BwdArgs;
 
 constexpr int kFwdRows = 128;     // query rows per forward workgroup (4 waves x 32)
+constexpr int kFwdPPRows = 256;   // query rows per ping-pong forward workgroup (8 waves x 32)
 constexpr int kFwdTile = 64;      // key rows per forward LDS tile
 constexpr int kBwdQRows = 128;    // query rows per dQ workgroup
 constexpr int kBwdKeyTile = 64;   // key rows per dQ-kernel LDS tile
@@ -24,6 +25,7 @@ using DkLaunch = hipError_t (*)(const BwdArgs&, int, bool, int64_t, hipStream_t)
 
 #define SKL_DECL(tn, d1, d2)                                                                   \
   hipError_t launch_fwd_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);              \
+  hipError_t launch_fwd_pp_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);           \
   hipError_t launch_bwd_dq_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t);      \
   hipError_t launch_bwd_dk_##tn##_##d1##_##d2(const BwdArgs&, int, bool, int64_t, hipStream_t);
 SKL_DECL(f32, 64, 64)
