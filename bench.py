@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--workload", default="h32-n64k-d128-bf16-causal")
     ap.add_argument("--bwd-mode", default="auto", choices=["auto", "fused", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=6144, help="query rows of the oracle sample")
     return ap.parse_args()
 
 
