@@ -63,16 +63,20 @@ def cpu_baseline(w, rows_wanted):
     g = workloads.upstream_grad(small, "cpu", "mean")
     hi = [t[0, 0].float().numpy().astype(np.float64) for t in (q1, k1, q2, k2)]
     rows = np.arange(max(0, w.n_q - rows_wanted), w.n_q)
+    block = max(1, min(64, (1 << 22) // w.n_k))
     t0 = time.perf_counter()
-    oracle.head_forward(*hi, w.causal, rows=rows, block=64)
-    oracle.head_backward(1, *hi, w.causal, g[0, 0].numpy(), rows=rows, block=64)
+    oracle.head_forward(*hi, w.causal, rows=rows, block=block)
+    for setting in w.settings:
+        oracle.head_backward(setting, *hi, w.causal, g[0, 0].numpy(), rows=rows, block=block)
     dt = time.perf_counter() - t0
     vis = oracle.valid_mask(rows, w.n_q, w.n_k, w.causal).sum()
-    flops = float(vis) * (2 * (w.d1 + w.d2) + 2 * (w.d1 + w.d2) + 4 * w.d2)
+    qk = 2 * (w.d1 + w.d2)
+    flops = float(vis) * (qk + sum(qk + 4 * (w.d2 if st == 1 else w.d1) for st in w.settings))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": dt,
-            "sample": f"numpy fp64 oracle, forward + setting-1 backward of the last {len(rows)} query rows of "
-                      f"one head over all {w.n_k} keys ({int(vis)} visible pairs)"}
+            "sample": f"numpy fp64 oracle, forward" + "".join(f" + setting-{st} backward" for st in w.settings)
+                      + f" of the last {len(rows)} query rows of one head over all {w.n_k} keys"
+                      f" ({int(vis)} visible pairs)"}
 
 
 def main():
@@ -93,28 +97,31 @@ def main():
     g = workloads.upstream_grad(w, dev, "mean")
     shp = sk.shape_of(q1, k1, q2, k2)
     mode = {"auto": sk.BWD_AUTO, "fused": sk.BWD_FUSED, "separate": sk.BWD_SEPARATE}[args.bwd_mode]
-    plan = sk.bwd_plan(shp, w.causal, 1, mode)
     splits = sk.fwd_plan(shp, w.causal)
 
     f32 = dict(device=dev, dtype=torch.float32)
     kl, l1, l2 = (torch.empty((w.B, w.H, w.n_q), **f32) for _ in range(3))
-    dq = torch.empty((w.B, w.H, w.n_q, w.d2), **f32)
-    dk = torch.empty((w.B, w.H, w.n_k, w.d2), **f32)
     ws_bytes = sk.fwd_workspace_bytes(shp, w.causal)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     # Each kernel is launched by its own ABI call so HIP events on the launch
     # stream bracket exactly one kernel (split-K adds its merge kernel).
-    if plan == sk.BWD_FUSED:
-        calls = [("fwd", lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, out=(kl, l1, l2), workspace=ws)),
-                 ("bwd_fused", lambda: sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g,
-                                                       bwd_mode=sk.BWD_FUSED, out=(dq, dk)))]
-    else:
-        calls = [("fwd", lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, out=(kl, l1, l2), workspace=ws)),
-                 ("bwd_dk", lambda: sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g,
-                                                    bwd_mode=sk.BWD_DK_ONLY, out=(None, dk))),
-                 ("bwd_dq", lambda: sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g,
-                                                    bwd_mode=sk.BWD_DQ_ONLY, out=(dq, None)))]
+    calls = [("fwd", lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, out=(kl, l1, l2), workspace=ws))]
+    modes = {}
+    for setting in w.settings:
+        ds = w.d2 if setting == 1 else w.d1
+        dq = torch.empty((w.B, w.H, w.n_q, ds), **f32)
+        dk = torch.empty((w.B, w.H, w.n_k, ds), **f32)
+        plan = sk.bwd_plan(shp, w.causal, setting, mode)
+        modes[setting] = plan
+
+        def mk(m, o, st=setting):
+            return lambda: sk.streamkl_bwd(st, q1, k1, q2, k2, w.causal, kl, l1, l2, g, bwd_mode=m, out=o)
+        if plan == sk.BWD_FUSED:
+            calls.append((f"bwd{setting}_fused", mk(sk.BWD_FUSED, (dq, dk))))
+        else:
+            calls.append((f"bwd{setting}_dk", mk(sk.BWD_DK_ONLY, (None, dk))))
+            calls.append((f"bwd{setting}_dq", mk(sk.BWD_DQ_ONLY, (dq, None))))
 
     for _ in range(args.warmup):
         for _, c in calls:
@@ -138,29 +145,47 @@ def main():
                 for i, (name, _) in enumerate(calls)}
     ms_step = wall * 1e3 / args.steps
     pairs = pairs_of(w)
-    f_fwd = 2 * (w.d1 + w.d2) * pairs
-    f_bwd = (2 * (w.d1 + w.d2) + 4 * w.d2) * pairs
-    flops_step = f_fwd + f_bwd
+    qk = 2 * (w.d1 + w.d2)
+    # algorithmic FLOPs each call is credited with (the logit recompute of the
+    # separate mode's dQ kernel is not credited)
+    credit = {"fwd": qk * pairs}
+    for setting in w.settings:
+        ds = w.d2 if setting == 1 else w.d1
+        credit[f"bwd{setting}_fused"] = (qk + 4 * ds) * pairs
+        credit[f"bwd{setting}_dk"] = (qk + 2 * ds) * pairs
+        credit[f"bwd{setting}_dq"] = 2 * ds * pairs
+    flops_step = sum(credit[n] for n, _ in calls)
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     value = flops_step / (ms_step * 1e-3) / 1e12
+    esz = 2 if w.dtype == "bf16" else 4
+    fwd_bytes = w.B * w.H * ((w.n_q + w.n_k) * (w.d1 + w.d2) * esz + 12 * w.n_q)
 
-    # algorithmic FLOPs each kernel is credited with (recompute in the dQ
-    # kernel of the separate mode is not credited)
-    credit = {"fwd": f_fwd, "bwd_fused": f_bwd,
-              "bwd_dk": (2 * (w.d1 + w.d2) + 2 * w.d2) * pairs, "bwd_dq": 2 * w.d2 * pairs}
     dom = max(per_call, key=per_call.get)
-    ach = credit[dom] / (per_call[dom] * 1e-3) / 1e12
-    kernel_names = {"fwd": "fwd_kernel", "bwd_fused": "bwd_dk_kernel<FUSED>", "bwd_dk": "bwd_dk_kernel",
-                    "bwd_dq": "bwd_dq_kernel"}
-    roof = {"bound": "mfma", "kernel": kernel_names[dom], "achieved": round(ach, 2), "peak": peak,
-            "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
-            "avg_ms": round(per_call[dom], 4)}
+    kernel_names = {"fwd": "fwd_pp_kernel" if (splits == 1 and w.n_q > 128) else "fwd_kernel"}
+    for setting in w.settings:
+        kernel_names[f"bwd{setting}_fused"] = "bwd_dk_kernel<FUSED>"
+        kernel_names[f"bwd{setting}_dk"] = "bwd_dk_kernel"
+        kernel_names[f"bwd{setting}_dq"] = "bwd_dq_kernel"
+    decode = not w.settings and w.n_q <= 16
+    if decode:
+        ach = fwd_bytes / (per_call["fwd"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": kernel_names["fwd"] + (" + splitk_merge_kernel" if splits > 1 else ""),
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": None, "avg_ms": round(per_call["fwd"], 4)}
+    else:
+        ach = credit[dom] / (per_call[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": kernel_names[dom], "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                "avg_ms": round(per_call[dom], 4)}
 
     extra_hbm = 3 * 4 * w.B * w.H * w.n_q + ws_bytes
+    names = {sk.BWD_FUSED: "fused", sk.BWD_SEPARATE: "separate"}
+    headline = w.name == "h32-n64k-d128-bf16-causal"
     out = {
-        "metric": "attn-KL fwd/bwd TFLOP/s + % bf16 MFMA peak, H32 d128 causal 64K",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "metric": ("attn-KL fwd/bwd TFLOP/s + % bf16 MFMA peak, H32 d128 causal 64K" if headline
+                   else ("attn-KL split-K forward HBM GB/s" if decode else "attn-KL fwd/bwd TFLOP/s")),
+        "value": round(fwd_bytes / (ms_step * 1e-3) / 1e9, 1) if decode else round(value, 2),
+        "unit": "GB/s" if decode else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -171,18 +196,19 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "n_q": w.n_q, "n_k": w.n_k, "d1": w.d1, "d2": w.d2,
-                   "causal": w.causal, "bwd_setting": 1,
-                   "bwd_mode": {sk.BWD_FUSED: "fused", sk.BWD_SEPARATE: "separate"}[plan],
+                   "causal": w.causal, "bwd_settings": list(w.settings),
+                   "bwd_modes": {str(k): names[v] for k, v in modes.items()},
                    "fwd_splits": splits, "parallelism": "single GPU"},
         "pct_of_mfma_peak": round(100 * value / peak, 2),
         "per_kernel_ms": {k: round(v, 4) for k, v in per_call.items()},
-        "algorithmic_tflop_per_step": round(flops_step / 1e12, 3),
+        "algorithmic_tflop_per_step": round(flops_step / 1e12, 4),
         "extra_hbm_bytes": extra_hbm,
         "materialised_bytes_avoided": 2 * w.B * w.H * w.n_q * w.n_k * 2,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+        # about 4e8 visible pairs of oracle work (10-20 s on the host) at most
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, max(1, int(4e8 // w.n_k))))
     print(json.dumps(out))
     return 0
 

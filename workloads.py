@@ -33,6 +33,7 @@ class Workload:
     noise: float        # student = teacher + noise * N(0,1); ignored if independent
     independent: bool   # draw the student independently (different head dims)
     seed: int
+    settings: tuple = (1,)  # backward settings one step runs (empty: forward only)
 
     @property
     def torch_dtype(self):
@@ -47,14 +48,14 @@ class Workload:
 WORKLOADS = {
     w.name: w for w in [
         Workload("h1-n512-d64-f32", 1, 1, 512, 512, 64, 64, "f32", False, 0.3, False, 1),
-        Workload("h32-n8k-d128-bf16-causal", 1, 32, 8192, 8192, 128, 128, "bf16", True, 0.5, False, 2),
+        Workload("h32-n8k-d128-bf16-causal", 1, 32, 8192, 8192, 128, 128, "bf16", True, 0.5, False, 2, (1, 2)),
         Workload("h32-n64k-d128-bf16-causal", 1, 32, 65536, 65536, 128, 128, "bf16", True, 0.5, False, 3),
         Workload("h32-n64k-d128-bf16", 1, 32, 65536, 65536, 128, 128, "bf16", False, 0.5, False, 3),
-        Workload("decode-h32-q1-k128k-d128-bf16", 1, 32, 1, 131072, 128, 128, "bf16", False, 0.5, False, 4),
-        Workload("decode-h32-q16-k128k-d128-bf16", 1, 32, 16, 131072, 128, 128, "bf16", False, 0.5, False, 4),
-        Workload("decode-h32-q1-k512k-d128-bf16", 1, 32, 1, 524288, 128, 128, "bf16", False, 0.5, False, 4),
-        Workload("decode-h32-q16-k512k-d128-bf16", 1, 32, 16, 524288, 128, 128, "bf16", False, 0.5, False, 4),
-        Workload("h32-n512k-d128x64-bf16-causal", 1, 32, 524288, 524288, 128, 64, "bf16", True, 0.0, True, 5),
+        Workload("decode-h32-q1-k128k-d128-bf16", 1, 32, 1, 131072, 128, 128, "bf16", False, 0.5, False, 4, ()),
+        Workload("decode-h32-q16-k128k-d128-bf16", 1, 32, 16, 131072, 128, 128, "bf16", False, 0.5, False, 4, ()),
+        Workload("decode-h32-q1-k512k-d128-bf16", 1, 32, 1, 524288, 128, 128, "bf16", False, 0.5, False, 4, ()),
+        Workload("decode-h32-q16-k512k-d128-bf16", 1, 32, 16, 524288, 128, 128, "bf16", False, 0.5, False, 4, ()),
+        Workload("h32-n512k-d128x64-bf16-causal", 1, 32, 524288, 524288, 128, 64, "bf16", True, 0.0, True, 5, (2,)),
     ]
 }
 
