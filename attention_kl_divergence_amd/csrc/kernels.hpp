@@ -131,6 +131,23 @@ struct TileLoader {
 
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Barrier between the compute phases of a ping-pong loop.  It orders no
+// memory (each phase reads data a tile barrier already published), so unlike
+// __syncthreads it does not wait for the direct-to-LDS tile loads in flight.
+__device__ inline void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Barrier that publishes this wave's LDS stores to the workgroup, again
+// without waiting for the tile loads in flight.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // MFMA operand with lane row = `row`, k from `k0`: natural layout read.
 template <typename T, int D>
 __device__ inline typename Mfma<T>::frag frag_tile(const T* tile, int row, int s, int grp) {
@@ -142,7 +159,7 @@ __device__ inline typename Mfma<T>::frag frag_tile(const T* tile, int row, int s
 // values run down the rows of a row-major tile, in accumulator order
 // (k = acc_row(h*KPL + e', grp) + kb0).  bf16 uses two transpose reads.
 template <int D>
-__device__ inline bf16x8 fragcol_acc_bf16(const bf16* tile, int kb0, int n0, int h, int lane) {
+__device__ inline bf16x8 fragcol_acc_bf16(const bf16* __restrict__ tile, int kb0, int n0, int h, int lane) {
   using F = Tile<bf16, D>;
   const int grp = lane >> 5, sub = (lane >> 4) & 1, r = lane & 15;
   const int n = n0 + 16 * sub + 4 * (r & 3);
@@ -159,7 +176,7 @@ __device__ inline bf16x8 fragcol_acc_bf16(const bf16* tile, int kb0, int n0, int
 
 // Same, natural k order (k = kb0 + 16h + 8grp + e').
 template <int D>
-__device__ inline bf16x8 fragcol_nat_bf16(const bf16* tile, int kb0, int n0, int h, int lane) {
+__device__ inline bf16x8 fragcol_nat_bf16(const bf16* __restrict__ tile, int kb0, int n0, int h, int lane) {
   using F = Tile<bf16, D>;
   const int grp = lane >> 5, sub = (lane >> 4) & 1, r = lane & 15;
   const int n = n0 + 16 * sub + 4 * (r & 3);
@@ -518,7 +535,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     } else if (t > 0) {
       update(k0 - BK);
     }
-    __syncthreads();
+    phase_barrier();
     if (group == 0) {
       update(k0);
     } else if (active) {
@@ -534,25 +551,58 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   }
 }
 
-// Per-row quantities the backward needs, in base-2 units:
-// L_t = LSE_t * log2(e); gs = g * scale_s; setting 2 also a = gs * ln2 and
-// b = gs * KL, so that dS1 = P1 * (a * (t1 - t2) - b) with t_t = y_t - L_t.
+// Per-row quantities the backward needs, in base-2 units: exponent offsets
+// L_t and the gradient scale gs (g * scale_s; setting 1 keeps only its sign
+// and folds |g * scale_s| into L_t, see scale_rowgrad); setting 2 also
+// a = gs * ln2 and b = gs * KL, so that dS1 = P1 * (a * (t1 - t2) - b) with
+// t_t = y_t - L_t.
 struct RowGrad {
   float L1, L2, gs, a, b;
 };
 
+// The stored per-row values RowGrad is built from (zeros for invalid rows).
+struct RawRowGrad {
+  float lse1, lse2, g, kl;
+};
+
 template <int SETTING>
-__device__ inline RowGrad load_rowgrad(const BwdArgs& a, int64_t r, bool valid) {
-  RowGrad o = {0.f, 0.f, 0.f, 0.f, 0.f};
+__device__ inline RawRowGrad load_rowgrad_raw(const BwdArgs& a, int64_t r, bool valid) {
+  RawRowGrad o = {0.f, 0.f, 0.f, 0.f};
   if (!valid) return o;
-  o.L1 = a.lse1[r] * kLog2e;
-  o.L2 = a.lse2[r] * kLog2e;
-  o.gs = a.g[r] * a.scale_s;
-  if constexpr (SETTING == 2) {
-    o.a = o.gs * kLn2;
-    o.b = o.gs * a.kl[r];
+  o.lse1 = a.lse1[r];
+  o.lse2 = a.lse2[r];
+  o.g = a.g[r];
+  if constexpr (SETTING == 2) o.kl = a.kl[r];
+  return o;
+}
+
+// Setting 1 folds |gs| into the exponent offsets: L_t = LSE_t log2(e) -
+// log2|gs|, so exp2(y_t - L_t) is |gs| P_t and gs is replaced by its sign
+// (a zero gs gives +inf offsets and an exactly zero dS row).
+template <int SETTING>
+__device__ inline RowGrad scale_rowgrad(const BwdArgs& a, const RawRowGrad& w) {
+  RowGrad o;
+  const float gs = w.g * a.scale_s;
+  o.L1 = w.lse1 * kLog2e;
+  o.L2 = w.lse2 * kLog2e;
+  o.gs = gs;
+  o.a = 0.f;
+  o.b = 0.f;
+  if constexpr (SETTING == 1) {
+    const float lg = log2f(fabsf(gs));
+    o.L1 -= lg;
+    o.L2 -= lg;
+    o.gs = gs < 0.f ? -1.f : 1.f;
+  } else {
+    o.a = gs * kLn2;
+    o.b = gs * w.kl;
   }
   return o;
+}
+
+template <int SETTING>
+__device__ inline RowGrad load_rowgrad(const BwdArgs& a, int64_t r, bool valid) {
+  return scale_rowgrad<SETTING>(a, load_rowgrad_raw<SETTING>(a, r, valid));
 }
 
 // dS for one element from the raw dot products s1, s2 (see RowGrad).
@@ -570,8 +620,14 @@ __device__ inline float dS_elem(float s1, float s2, float c1, float c2, float L1
   }
 }
 
-template <typename T>
-__device__ inline T to_T(float x) { return (T)x; }
+// dS for one element of the query-outer kernel, where a lane holds one query
+// row: for setting 1 the row's sign (gs = +-1) is left out here and applied
+// to the row's dQ once at the end.
+template <int SETTING>
+__device__ inline float dS_elem_row(float s1, float s2, float c1, float c2, const RowGrad& rg) {
+  if constexpr (SETTING == 1) return exp2_fast(fmaf(s2, c2, -rg.L2)) - exp2_fast(fmaf(s1, c1, -rg.L1));
+  else return dS_elem<SETTING>(s1, s2, c1, c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
+}
 
 
 // dS for one 32x32 block of the key-outer kernel (lane = key, accumulator rows
@@ -654,6 +710,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int s = 0; s < S2; ++s) qf2[s] = frag_global<T, D2>(Q2, qrow, a.n_q - 1, qv, s, grp);
   const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.n_q + qrow, qv);
+  const float row_sign = SETTING == 1 ? rg.gs : 1.f;
 
   f32x16 dqa[NB];
 #pragma unroll
@@ -687,12 +744,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       if (need_mask) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float ds = dS_elem<SETTING>(s1[e], s2[e], a.c1, a.c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
+          const float ds = dS_elem_row<SETTING>(s1[e], s2[e], a.c1, a.c2, rg);
           s1[e] = (k0 + kb * 32 + acc_row(e, grp) > lim) ? 0.f : ds;
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s1[e] = dS_elem<SETTING>(s1[e], s2[e], a.c1, a.c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
+        for (int e = 0; e < 16; ++e) s1[e] = dS_elem_row<SETTING>(s1[e], s2[e], a.c1, a.c2, rg);
       }
 #pragma unroll
       for (int h = 0; h < HS; ++h) {
@@ -705,12 +762,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
+  // dQ accumulator rows are queries q0 + acc_row(e, grp); lane r < 32 holds
+  // query q0 + r's sign
+  const uint64_t neg = __ballot(row_sign < 0.f);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int q = q0 + acc_row(e, grp);
-      if (q < a.n_q) a.dq[(bh * a.n_q + q) * DS + nb * 32 + col] = dqa[nb][e];
+      const int r = acc_row(e, grp);
+      const int q = q0 + r;
+      const float v = ((neg >> r) & 1) ? -dqa[nb][e] : dqa[nb][e];
+      if (q < a.n_q) a.dq[(bh * a.n_q + q) * DS + nb * 32 + col] = v;
     }
 }
 
@@ -733,9 +795,16 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   constexpr int NB = DS / 32, HS = 32 / MF::KSTEP, NQB = BQ / 32, HK = BKW / MF::KSTEP;
   constexpr int TS = BQ * (D1 + D2);
   constexpr int NSTAT = SETTING == 2 ? 5 : 3;
-  __shared__ __attribute__((aligned(1024))) T lds[2 * TS];
-  __shared__ __attribute__((aligned(16))) float sstat[2][NSTAT][BQ];
-  __shared__ __attribute__((aligned(1024))) T sdS[FUSED ? BKW * BQ : 1];
+  // One LDS array holds the two tile buffers, the dS^T staging tile (FUSED)
+  // and the two per-query stats buffers: separate __shared__ objects would
+  // get distinct alias scopes, and then every tile read would be made to wait
+  // for the next tile's direct loads in flight.
+  constexpr int DSE = FUSED ? BKW * BQ : 0;                      // dS^T elements
+  constexpr int STAT_OFF = ((2 * TS + DSE) * (int)sizeof(T) + 15) / 16 * 16;  // bytes
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[STAT_OFF + 2 * NSTAT * BQ * 4];
+  T* lds = reinterpret_cast<T*>(smem);
+  T* sdS = lds + 2 * TS;
+  float(*sstat)[NSTAT][BQ] = reinterpret_cast<float(*)[NSTAT][BQ]>(smem + STAT_OFF);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
@@ -757,11 +826,14 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   const int qt0 = (qbeg / BQ) * BQ;
   const int ntiles = qt0 < a.n_q ? (a.n_q - qt0 + BQ - 1) / BQ : 0;
 
-  // stats of one query tile: thread q < BQ loads row q (zeros past n_q)
-  auto load_stats = [&](int q0, RowGrad& rg) {
-    rg = load_rowgrad<SETTING>(a, bh * a.n_q + q0 + tid, tid < BQ && q0 + tid < a.n_q);
+  // stats of one query tile: thread q < BQ loads row q raw (zeros past n_q);
+  // they are scaled and stored to LDS after the tile's compute, behind a
+  // scheduling barrier, so their load latency overlaps the whole tile
+  auto load_stats = [&](int q0, RawRowGrad& r) {
+    r = load_rowgrad_raw<SETTING>(a, bh * a.n_q + q0 + tid, tid < BQ && q0 + tid < a.n_q);
   };
-  auto store_stats = [&](int buf, const RowGrad& rg) {
+  auto store_stats = [&](int buf, const RawRowGrad& raw) {
+    const RowGrad rg = scale_rowgrad<SETTING>(a, raw);
     if (tid < BQ) {
       sstat[buf][0][tid] = rg.L1;
       sstat[buf][1][tid] = rg.L2;
@@ -773,7 +845,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
     }
   };
 
-  RowGrad rgn;
+  RawRowGrad rgn;
   const TileLoader<T, D1, BQ, NW> ld1(wave, lane);
   const TileLoader<T, D2, BQ, NW> ld2(wave, lane);
   if (ntiles > 0) {
@@ -826,10 +898,12 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
     const int q0 = qt0 + t * BQ;
     const bool more = t + 1 < ntiles;
     if (more) {
+      // stats first: vmcnt retires in order, so using them then waits only
+      // for these loads, not for the tile loads behind them
+      load_stats(q0 + BQ, rgn);
       T* nbuf = lds + ((t + 1) & 1) * TS;
       ld1.issue(nbuf, Q1, q0 + BQ, a.n_q);
       ld2.issue(nbuf + BQ * D1, Q2, q0 + BQ, a.n_q);
-      load_stats(q0 + BQ, rgn);
     }
     const T* sQ1 = lds + (t & 1) * TS;
     const T* sQ2 = sQ1 + BQ * D1;
@@ -883,10 +957,13 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
         }
       }
     }
-    if (more) store_stats((t + 1) & 1, rgn);
+    if (more) {
+      __builtin_amdgcn_sched_barrier(0);
+      store_stats((t + 1) & 1, rgn);
+    }
 
     if constexpr (FUSED) {
-      __syncthreads();
+      lds_barrier();
       constexpr int QSTEP = NW / NBF;
 #pragma unroll
       for (int qb = wave / NBF; qb < NQB; qb += QSTEP) {

@@ -82,7 +82,12 @@ def test_fused_and_separate_agree_and_separate_is_deterministic(cuda_device):
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), "separate backward is not deterministic"
         f = sk.streamkl_bwd(s, q1, k1, q2, k2, True, kl, l1, l2, g, bwd_mode=sk.BWD_FUSED)
         assert torch.equal(f[1], a[1]), "dK of the fused and separate kernels should match bitwise"
-        check_grad(f"fused vs separate dQ s{s}", to_np(f[0]), to_np(a[0]), tol=1e-5)
+        # Both dQ paths round the same dS to bf16, but from logits accumulated
+        # in different matrix-instruction orders, and setting 1 carries the row
+        # scale inside the exponent (|y - L| up to ~20-40, fp32 ulp ~2e-6..4e-6).
+        # A fraction ~1e-3 of dS elements then lands on the other bf16
+        # neighbour (2^-9 relative each): relative L2 ~ sqrt(1e-3) * 2e-3 = 6e-5.
+        check_grad(f"fused vs separate dQ s{s}", to_np(f[0]), to_np(a[0]), tol=1e-4)
 
 
 def test_no_writes_outside_outputs(cuda_device):
