@@ -131,6 +131,27 @@ struct TileLoader {
 
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Work item (head, block) of workgroup `lin` of a grid of BH * nblk.
+// Workgroups go to the 8 XCDs round-robin (workgroup i runs on XCD i % 8) and
+// each XCD has its own L2.  When the heads split evenly over the XCDs, XCD x
+// takes heads [x BH/8, (x+1) BH/8) one after the other, so the workgroups it
+// runs at a time share one head's tiles in its L2; otherwise the heads
+// interleave.  Within a head, blocks come in order 0, 1, ..., and the caller
+// maps that to its longest-first order.
+struct WorkItem {
+  int64_t bh;
+  int blk;
+};
+__device__ inline WorkItem work_item(int64_t lin, int64_t BH, int nblk) {
+  constexpr int X = 8;
+  if (BH % X == 0) {
+    const int64_t per = BH / X * nblk;
+    const int64_t v = (lin % X) * per + lin / X;
+    return {v / nblk, (int)(v % nblk)};
+  }
+  return {lin % BH, (int)(lin / BH)};
+}
+
 // Barrier between the compute phases of a ping-pong loop.  It orders no
 // memory (each phase reads data a tile barrier already published), so unlike
 // __syncthreads it does not wait for the direct-to-LDS tile loads in flight.
@@ -475,9 +496,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
   const int group = wave >> 2;
-  const int64_t lin = blockIdx.x;
-  const int64_t bh = lin % a.BH;
-  const int qb = a.nqb - 1 - (int)(lin / a.BH);  // longest causal rows first
+  const WorkItem wi = work_item(blockIdx.x, a.BH, a.nqb);
+  const int64_t bh = wi.bh;
+  const int qb = a.nqb - 1 - wi.blk;  // longest causal rows first
   const int qwg0 = qb * 32 * NW;
   const int q0 = qwg0 + 32 * wave;
   const int qrow = q0 + col;
@@ -680,9 +701,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
-  const int64_t lin = blockIdx.x;
-  const int64_t bh = lin % a.BH;
-  const int qb = a.nblk - 1 - (int)(lin / a.BH);
+  const WorkItem wi = work_item(blockIdx.x, a.BH, a.nblk);
+  const int64_t bh = wi.bh;
+  const int qb = a.nblk - 1 - wi.blk;  // longest causal rows first
   const int q0 = qb * 32 * NW + 32 * wave;
   const int qrow = q0 + col;
   const int off = a.n_k - a.n_q;
@@ -808,9 +829,9 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
-  const int64_t lin = blockIdx.x;
-  const int64_t bh = lin % a.BH;
-  const int kb = (int)(lin / a.BH);  // low key blocks see the most queries under causal masks: first
+  const WorkItem wi = work_item(blockIdx.x, a.BH, a.nblk);
+  const int64_t bh = wi.bh;
+  const int kb = wi.blk;  // low key blocks see the most queries under causal masks: first
   const int kw0 = kb * BKW;
   const int kwave = kw0 + 32 * wave;
   const int krow = kwave + col;
@@ -822,9 +843,14 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   const T* K2 = reinterpret_cast<const T*>(a.k2) + bh * (int64_t)a.n_k * D2;
   const T* KS = SETTING == 1 ? K2 : K1;
 
+  // Query tiles are visited from the last one down: under a causal mask every
+  // key block sees the high queries, so the workgroups running at a time all
+  // start on the same tile and move down together (L2 reuse), each stopping at
+  // its own first query tile.
   const int qbeg = a.causal ? max(0, kw0 - off) : 0;
   const int qt0 = (qbeg / BQ) * BQ;
   const int ntiles = qt0 < a.n_q ? (a.n_q - qt0 + BQ - 1) / BQ : 0;
+  const int qtl = qt0 + (ntiles - 1) * BQ;  // first tile visited
 
   // stats of one query tile: thread q < BQ loads row q raw (zeros past n_q);
   // they are scaled and stored to LDS after the tile's compute, behind a
@@ -849,9 +875,9 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   const TileLoader<T, D1, BQ, NW> ld1(wave, lane);
   const TileLoader<T, D2, BQ, NW> ld2(wave, lane);
   if (ntiles > 0) {
-    ld1.issue(lds, Q1, qt0, a.n_q);
-    ld2.issue(lds + BQ * D1, Q2, qt0, a.n_q);
-    load_stats(qt0, rgn);
+    ld1.issue(lds, Q1, qtl, a.n_q);
+    ld2.issue(lds + BQ * D1, Q2, qtl, a.n_q);
+    load_stats(qtl, rgn);
     store_stats(0, rgn);
   }
 
@@ -895,15 +921,15 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     wait_loads();
     __syncthreads();
-    const int q0 = qt0 + t * BQ;
+    const int q0 = qtl - t * BQ;
     const bool more = t + 1 < ntiles;
     if (more) {
       // stats first: vmcnt retires in order, so using them then waits only
       // for these loads, not for the tile loads behind them
-      load_stats(q0 + BQ, rgn);
+      load_stats(q0 - BQ, rgn);
       T* nbuf = lds + ((t + 1) & 1) * TS;
-      ld1.issue(nbuf, Q1, q0 + BQ, a.n_q);
-      ld2.issue(nbuf + BQ * D1, Q2, q0 + BQ, a.n_q);
+      ld1.issue(nbuf, Q1, q0 - BQ, a.n_q);
+      ld2.issue(nbuf + BQ * D1, Q2, q0 - BQ, a.n_q);
     }
     const T* sQ1 = lds + (t & 1) * TS;
     const T* sQ2 = sQ1 + BQ * D1;

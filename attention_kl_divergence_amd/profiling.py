@@ -1,0 +1,165 @@
+"""HBM traffic per kernel launch from rocprofv3 counter runs.
+
+The TCC counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are taken in
+two separate `rocprofv3 --pmc` runs of `bench.py --copy-ref-mib N`, which
+launches one plain device copy of known size (read N MiB, write N MiB)
+before the timed steps.  Each counter is scaled by known/measured for that
+copy dispatch, then averaged over the launches of each StreamKL kernel.
+
+    python -m attention_kl_divergence_amd.profiling traffic \\
+        --fetch <fetch run>/run_counter_collection.csv \\
+        --write <write run>/run_counter_collection.csv \\
+        --copy-mib N --workload NAME --command "..." --out profiles/<file>.md
+
+The summary carries a digest of the kernel sources and build flags; the
+benchmark reports the traffic figure only while that digest still matches.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+PROFILES = os.path.join(ROOT, "profiles")
+
+# kernels whose traffic is summarised: label -> pattern on the kernel name as
+# rocprofv3 reports it (mangled, e.g. ...bwd_dk_kernelIDF16bLi128ELi128ELi1ELb0E...,
+# or demangled, e.g. streamkl::bwd_dk_kernel<__bf16, 128, 128, 1, false, 64>)
+KERNELS = [
+    ("fwd_pp_kernel", r"fwd_pp_kernel"),
+    ("fwd_kernel", r"fwd_kernel"),
+    ("bwd_dk_kernel", r"bwd_dk_kernel(I.*Lb0E|<[^>]*false)"),
+    ("bwd_dk_kernel<FUSED>", r"bwd_dk_kernel(I.*Lb1E|<[^>]*true)"),
+    ("bwd_dq_kernel", r"bwd_dq_kernel"),
+    ("splitk_merge_kernel", r"splitk_merge_kernel"),
+]
+# the reference copy: torch.mul(src, 1.0, out=dst), the last such dispatch
+# before the first StreamKL kernel
+COPY_PATTERN = r"MulFunctor"
+STREAMKL_PATTERN = r"streamkl"
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the kernel sources and the device compile flags."""
+    from . import build
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hpp", ".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    h.update(" ".join(build.FLAGS).encode())
+    return h.hexdigest()
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(rows, counter):
+    """{dispatch id: (kernel name, value)} for one counter (summed over instances)."""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name = r["Kernel_Name"]
+        v = float(r["Counter_Value"])
+        if d in out:
+            out[d] = (name, out[d][1] + v)
+        else:
+            out[d] = (name, v)
+    return out
+
+
+def _label(name):
+    for label, pat in KERNELS:
+        if re.search(pat, name):
+            return label
+    return None
+
+
+def traffic(fetch_csv, write_csv, copy_mib):
+    """Calibrated HBM bytes per launch: {label: {"fetch_bytes", "write_bytes", "launches"}}."""
+    known = copy_mib * 1024 * 1024
+    res = {}
+    factors = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per = _per_dispatch(_rows(path), counter)
+        first = min((d for d, (n, _) in per.items() if re.search(STREAMKL_PATTERN, n)), default=None)
+        copies = [d for d, (n, _) in per.items() if re.search(COPY_PATTERN, n) and (first is None or d < first)]
+        if not copies:
+            raise SystemExit(f"no reference copy dispatch in {path}")
+        measured = per[max(copies)][1] * 1024.0
+        factors[counter] = known / measured
+        acc = collections.defaultdict(list)
+        for name, v in per.values():
+            lab = _label(name)
+            if lab:
+                acc[lab].append(v * 1024.0 * factors[counter])
+        key = "fetch_bytes" if counter == "FETCH_SIZE" else "write_bytes"
+        for lab, vals in acc.items():
+            res.setdefault(lab, {})[key] = sum(vals) / len(vals)
+            res[lab]["launches"] = len(vals)
+    return res, factors
+
+
+def load_summary(workload):
+    """The JSON block of profiles/traffic_<workload>.md, or None."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    return json.loads(m.group(1)) if m else None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--command", required=True, help="the commands that produced the two csv files")
+    t.add_argument("--out", required=True)
+    sub.add_parser("digest")
+    args = ap.parse_args(argv)
+    if args.cmd == "digest":
+        print(kernel_source_digest())
+        return 0
+    res, factors = traffic(args.fetch, args.write, args.copy_mib)
+    block = {"workload": args.workload, "source_digest": kernel_source_digest(),
+             "copy_reference_mib": args.copy_mib,
+             "scale": {k: round(v, 5) for k, v in factors.items()},
+             "kernels": {k: {kk: (round(vv) if kk != "launches" else vv) for kk, vv in v.items()}
+                         for k, v in res.items()}}
+    lines = [f"# HBM traffic per launch, workload {args.workload}", "",
+             "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two separate",
+             "rocprofv3 --pmc runs, each scaled by known/measured for a plain device",
+             f"copy of {args.copy_mib} MiB launched in the same run "
+             f"(FETCH scale {factors['FETCH_SIZE']:.4f}, WRITE scale {factors['WRITE_SIZE']:.4f}).", "",
+             "Commands:", "", "```", args.command, "```", "",
+             "| kernel | launches | HBM read (MB) | HBM write (MB) |", "|---|---|---|---|"]
+    for k, v in sorted(res.items()):
+        lines.append(f"| {k} | {v.get('launches', 0)} | {v.get('fetch_bytes', 0) / 1e6:.1f} | "
+                     f"{v.get('write_bytes', 0) / 1e6:.1f} |")
+    lines += ["", "```json", json.dumps(block, indent=1), "```", ""]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    print(args.out)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--bwd-mode", default="auto", choices=["auto", "fused", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="query rows of the oracle sample")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="launch one plain device copy of this size first (the counter reference "
+                         "for the HBM traffic summary)")
     return ap.parse_args()
 
 
@@ -123,6 +126,15 @@ def main():
             calls.append((f"bwd{setting}_dk", mk(sk.BWD_DK_ONLY, (None, dk))))
             calls.append((f"bwd{setting}_dq", mk(sk.BWD_DQ_ONLY, (dq, None))))
 
+    if args.copy_ref_mib > 0:
+        n = args.copy_ref_mib * (1 << 20) // 4
+        src = torch.ones(n, **f32)
+        dst = torch.empty(n, **f32)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)  # reads and writes copy_ref_mib MiB
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         for _, c in calls:
             c()
@@ -177,6 +189,16 @@ def main():
         roof = {"bound": "mfma", "kernel": kernel_names[dom], "achieved": round(ach, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
                 "avg_ms": round(per_call[dom], 4)}
+
+    # measured HBM bytes per launch of that kernel (calibrated TCC counters),
+    # valid only for the kernel sources they were taken with
+    from attention_kl_divergence_amd import profiling
+    summ = profiling.load_summary(w.name)
+    kname = roof["kernel"].split(" + ")[0]
+    if summ and summ.get("source_digest") == profiling.kernel_source_digest() and kname in summ["kernels"]:
+        t = summ["kernels"][kname]
+        roof["traffic"] = int(t.get("fetch_bytes", 0) + t.get("write_bytes", 0))
+        roof["traffic_unit"] = "bytes per launch (HBM read + write)"
 
     extra_hbm = 3 * 4 * w.B * w.H * w.n_q + ws_bytes
     names = {sk.BWD_FUSED: "fused", sk.BWD_SEPARATE: "separate"}
