@@ -123,9 +123,50 @@ def load_summary(workload):
     return json.loads(m.group(1)) if m else None
 
 
+def kernel_summary(stats_csv, bench_log, workload, command):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of bench.py
+    (library kernels only) next to the bench line the same run printed."""
+    rows = [r for r in _rows(stats_csv) if re.search(STREAMKL_PATTERN, r["Name"])]
+    total = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    bench = None
+    with open(bench_log) as f:
+        for line in f:
+            if line.startswith("{") and '"metric"' in line:
+                bench = json.loads(line)
+    lines = [f"# Kernel time summary, workload {workload}", "",
+             "Command (run from /tmp with TMPDIR=/tmp on one MI355X):", "", "```", command, "```", "",
+             "Source: `run_kernel_stats.csv`; library kernels only (the input generators' kernels are omitted).", "",
+             "| kernel | calls | average ms | min ms | max ms | share of library time |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = re.sub(r"^_ZN8streamkl", "", r["Name"])
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | {float(r['MinNs']) / 1e6:.3f} | "
+                     f"{float(r['MaxNs']) / 1e6:.3f} | {100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    if bench:
+        roof = bench.get("roofline", {})
+        lines += ["", "The same run's bench line (HIP events on the launch stream), per call in ms: " +
+                  ", ".join(f"{k} {v}" for k, v in bench.get("per_kernel_ms", {}).items()) + ".",
+                  f"Dominant kernel: {roof.get('kernel')} at {roof.get('avg_ms')} ms per launch, "
+                  f"{roof.get('achieved')} {roof.get('unit')} ({100 * roof.get('frac', 0):.1f}% of {roof.get('peak')})."]
+        dom = roof.get("kernel", "")
+        pat = dict(KERNELS).get(dom)
+        match = [r for r in rows if pat and re.search(pat, r["Name"])]
+        if match and roof.get("avg_ms"):
+            avg = float(match[0]["AverageNs"]) / 1e6
+            lines.append(f"rocprofv3 average for it: {avg:.3f} ms "
+                         f"({100 * (roof['avg_ms'] - avg) / avg:+.2f}% bench vs profiler).")
+    lines.append("")
+    return "\n".join(lines)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("--stats", required=True)
+    k.add_argument("--bench-log", required=True)
+    k.add_argument("--workload", required=True)
+    k.add_argument("--command", required=True)
+    k.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -137,6 +178,11 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "digest":
         print(kernel_source_digest())
+        return 0
+    if args.cmd == "kernels":
+        with open(args.out, "w") as f:
+            f.write(kernel_summary(args.stats, args.bench_log, args.workload, args.command))
+        print(args.out)
         return 0
     res, factors = traffic(args.fetch, args.write, args.copy_mib)
     block = {"workload": args.workload, "source_digest": kernel_source_digest(),
@@ -150,7 +196,9 @@ def main(argv=None):
              f"copy of {args.copy_mib} MiB launched in the same run "
              f"(FETCH scale {factors['FETCH_SIZE']:.4f}, WRITE scale {factors['WRITE_SIZE']:.4f}).", "",
              "Commands:", "", "```", args.command, "```", "",
-             "| kernel | launches | HBM read (MB) | HBM write (MB) |", "|---|---|---|---|"]
+             "FETCH_SIZE counts the L2 misses of each dispatch (served by the",
+             "memory-side cache or HBM), WRITE_SIZE the bytes written back.", "",
+             "| kernel | launches | read past L2 (MB) | written (MB) |", "|---|---|---|---|"]
     for k, v in sorted(res.items()):
         lines.append(f"| {k} | {v.get('launches', 0)} | {v.get('fetch_bytes', 0) / 1e6:.1f} | "
                      f"{v.get('write_bytes', 0) / 1e6:.1f} |")

@@ -198,7 +198,7 @@ def main():
     if summ and summ.get("source_digest") == profiling.kernel_source_digest() and kname in summ["kernels"]:
         t = summ["kernels"][kname]
         roof["traffic"] = int(t.get("fetch_bytes", 0) + t.get("write_bytes", 0))
-        roof["traffic_unit"] = "bytes per launch (HBM read + write)"
+        roof["traffic_unit"] = "bytes per launch: FETCH_SIZE + WRITE_SIZE, copy-calibrated"
 
     extra_hbm = 3 * 4 * w.B * w.H * w.n_q + ws_bytes
     names = {sk.BWD_FUSED: "fused", sk.BWD_SEPARATE: "separate"}
