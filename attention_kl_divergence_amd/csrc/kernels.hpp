@@ -653,9 +653,10 @@ __device__ inline float dS_elem_row(float s1, float s2, float c1, float c2, cons
 
 // dS for one 32x32 block of the key-outer kernel (lane = key, accumulator rows
 // = queries qb0 + acc_row(e, grp)); per-query stats come from LDS
-// (st[k*BQ + q]: L1, L2, gs, then a, b for setting 2).  MASK: queries outside
-// [qlo, n_q) get dS = 0.  Result overwrites s1.
-template <int SETTING, bool MASK, int BQ>
+// (st[k*BQ + q]: L1, L2, gs, then a, b for setting 2).  SIGNED = false
+// (setting 1, no negative gradient in the tile) skips gs, which is then +1.
+// MASK: queries outside [qlo, n_q) get dS = 0.  Result overwrites s1.
+template <int SETTING, bool MASK, int BQ, bool SIGNED = true>
 __device__ inline void dS_rows_keyouter(f32x16& s1, const f32x16& s2, const float* st, int ql0, int qb0, int grp,
                                         float c1, float c2, int qlo, int n_q) {
 #pragma unroll
@@ -663,7 +664,8 @@ __device__ inline void dS_rows_keyouter(f32x16& s1, const f32x16& s2, const floa
     const int ql = ql0 + 8 * i + 4 * grp;
     const f32x4 L1 = *reinterpret_cast<const f32x4*>(st + 0 * BQ + ql);
     const f32x4 L2 = *reinterpret_cast<const f32x4*>(st + 1 * BQ + ql);
-    const f32x4 GS = *reinterpret_cast<const f32x4*>(st + 2 * BQ + ql);
+    f32x4 GS = {1.f, 1.f, 1.f, 1.f};
+    if (SETTING != 1 || SIGNED) GS = *reinterpret_cast<const f32x4*>(st + 2 * BQ + ql);
     f32x4 RA = {0.f, 0.f, 0.f, 0.f}, RB = {0.f, 0.f, 0.f, 0.f};
     if constexpr (SETTING == 2) {
       RA = *reinterpret_cast<const f32x4*>(st + 3 * BQ + ql);
@@ -672,7 +674,11 @@ __device__ inline void dS_rows_keyouter(f32x16& s1, const f32x16& s2, const floa
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * i + j;
-      float ds = dS_elem<SETTING>(s1[e], s2[e], c1, c2, L1[j], L2[j], GS[j], RA[j], RB[j]);
+      float ds;
+      if constexpr (SETTING == 1 && !SIGNED)
+        ds = exp2_fast(fmaf(s2[e], c2, -L2[j])) - exp2_fast(fmaf(s1[e], c1, -L1[j]));
+      else
+        ds = dS_elem<SETTING>(s1[e], s2[e], c1, c2, L1[j], L2[j], GS[j], RA[j], RB[j]);
       if constexpr (MASK) {
         const int q = qb0 + 8 * i + 4 * grp + j;
         ds = ((q >= qlo) & (q < n_q)) ? ds : 0.f;
@@ -822,10 +828,12 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   // for the next tile's direct loads in flight.
   constexpr int DSE = FUSED ? BKW * BQ : 0;                      // dS^T elements
   constexpr int STAT_OFF = ((2 * TS + DSE) * (int)sizeof(T) + 15) / 16 * 16;  // bytes
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[STAT_OFF + 2 * NSTAT * BQ * 4];
+  constexpr int FLAG_OFF = STAT_OFF + 2 * NSTAT * BQ * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[FLAG_OFF + 2 * 4];
   T* lds = reinterpret_cast<T*>(smem);
   T* sdS = lds + 2 * TS;
   float(*sstat)[NSTAT][BQ] = reinterpret_cast<float(*)[NSTAT][BQ]>(smem + STAT_OFF);
+  int* sneg = reinterpret_cast<int*>(smem + FLAG_OFF);  // per stats buffer: a row has gs < 0
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
@@ -860,6 +868,8 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   };
   auto store_stats = [&](int buf, const RawRowGrad& raw) {
     const RowGrad rg = scale_rowgrad<SETTING>(a, raw);
+    const uint64_t neg = __ballot(tid < BQ && rg.gs < 0.f);  // wave 0 holds all BQ <= 64 rows
+    if (tid == 0) sneg[buf] = neg != 0;
     if (tid < BQ) {
       sstat[buf][0][tid] = rg.L1;
       sstat[buf][1][tid] = rg.L2;
@@ -935,6 +945,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
     const T* sQ2 = sQ1 + BQ * D1;
     const T* sQS = SETTING == 1 ? sQ2 : sQ1;
     const float* st = &sstat[t & 1][0][0];
+    const bool tile_signed = sneg[t & 1] != 0;
 
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -950,8 +961,15 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
         }
         sched_mfma_lds<S1 + S2, 1, 4>();
         const bool need_mask = (qb0 + 32 > a.n_q) || (kwave + 32 > a.n_k) || (a.causal && kwave + 31 > qb0 + off);
-        if (need_mask) dS_rows_keyouter<SETTING, true, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
-        else dS_rows_keyouter<SETTING, false, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
+        if (SETTING == 2 || tile_signed) {
+          if (need_mask) dS_rows_keyouter<SETTING, true, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
+          else dS_rows_keyouter<SETTING, false, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
+        } else {
+          if (need_mask)
+            dS_rows_keyouter<SETTING, true, BQ, false>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
+          else
+            dS_rows_keyouter<SETTING, false, BQ, false>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
+        }
 #pragma unroll
         for (int h = 0; h < HS; ++h) {
           const frag af = frag_from_acc(s1, h, T());
