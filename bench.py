@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--bwd-mode", default="auto", choices=["auto", "fused", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="query rows of the oracle sample")
+    ap.add_argument("--compare-modes", action="store_true",
+                    help="after the timed steps, time each backward setting once in the mode the plan "
+                         "did not pick (fused vs separate) and report it as alt_bwd_ms")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="launch one plain device copy of this size first (the counter reference "
                          "for the HBM traffic summary)")
@@ -228,6 +231,23 @@ def main():
         "materialised_bytes_avoided": 2 * w.B * w.H * w.n_q * w.n_k * 2,
         "roofline": roof,
     }
+    if args.compare_modes:
+        alt = {}
+        for setting in w.settings:
+            ds = w.d2 if setting == 1 else w.d1
+            other = sk.BWD_SEPARATE if modes[setting] == sk.BWD_FUSED else sk.BWD_FUSED
+            dq = torch.empty((w.B, w.H, w.n_q, ds), **f32)
+            dk = torch.empty((w.B, w.H, w.n_k, ds), **f32)
+            run = lambda: sk.streamkl_bwd(setting, q1, k1, q2, k2, w.causal, kl, l1, l2, g,  # noqa: E731
+                                          bwd_mode=other, out=(dq, dk))
+            run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            alt[f"bwd{setting}_{names[other]}"] = round(e0.elapsed_time(e1), 3)
+        out["alt_bwd_ms"] = alt
     if not args.no_cpu_baseline:
         # about 4e8 visible pairs of oracle work (10-20 s on the host) at most
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, max(1, int(4e8 // w.n_k))))
