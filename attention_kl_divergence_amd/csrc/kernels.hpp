@@ -28,6 +28,8 @@
 // (ds_read_b64_tr_b16), so no tile is ever stored transposed.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace streamkl {
@@ -232,6 +234,70 @@ __device__ inline typename Mfma<T>::frag fragcol_nat(const T* tile, int kb0, int
   if constexpr (Mfma<T>::KPL == 1) return fragcol_nat_f32<D>(tile, kb0, n0, h, lane);
   else return fragcol_nat_bf16<D>(tile, kb0, n0, h, lane);
 }
+
+// Per-lane byte offsets of the bf16 operand reads of a swizzled tile, for the
+// rows of its first 32-row block.  The swizzle repeats every 16 rows, so any
+// other block (and another tile buffer) is a constant away: with a constant
+// tile base every read is one LDS instruction with an immediate offset and no
+// address arithmetic.  The offsets are hidden from the optimiser so they stay
+// in registers instead of being recomputed per read.
+template <int D, int S>
+struct RowFragOffsets {  // operand rows: frag_tile(tile, 32 * blk + col, s, grp)
+  int o[S];
+  __device__ inline RowFragOffsets(int col, int grp) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      o[s] = Tile<bf16, D>::off(col, s * Mfma<bf16>::KSTEP + grp * Mfma<bf16>::KPL) * (int)sizeof(bf16);
+      asm volatile("" : "+v"(o[s]));
+    }
+  }
+  __device__ inline bf16x8 read(const bf16* tile, int blk, int s) const {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile + 32 * blk * D) + o[s]);
+  }
+  // called once per loop iteration: the offsets then look loop-variant, so
+  // the optimiser does not hoist tile base + offset sums into extra registers
+  __device__ inline void touch() {
+#pragma unroll
+    for (int s = 0; s < S; ++s) asm volatile("" : "+v"(o[s]));
+  }
+};
+
+template <int D, int NB>
+struct ColFragOffsets {  // column operands: fragcol_acc_bf16(tile, 32 * blk, 32 * nb, h, lane)
+  int lo[NB], hi[NB];
+  __device__ inline ColFragOffsets(int lane) {
+    const int grp = lane >> 5, sub = (lane >> 4) & 1, r = lane & 15;
+    const int ka = 4 * grp + (r >> 2);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = 32 * nb + 16 * sub + 4 * (r & 3);
+      lo[nb] = Tile<bf16, D>::off(ka, n) * (int)sizeof(bf16);
+      hi[nb] = Tile<bf16, D>::off(ka + 8, n) * (int)sizeof(bf16);
+      asm volatile("" : "+v"(lo[nb]), "+v"(hi[nb]));
+    }
+  }
+  __device__ inline bf16x8 read(const bf16* __restrict__ tile, int blk, int nb, int h) const {
+    const char* b = reinterpret_cast<const char*>(tile + (32 * blk + 16 * h) * D);
+    const bf16x4_lds l = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (bf16x4_lds __attribute__((address_space(3)))*)(b + lo[nb]));
+    const bf16x4_lds u = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (bf16x4_lds __attribute__((address_space(3)))*)(b + hi[nb]));
+    bf16x8 f;
+    f[0] = l[0]; f[1] = l[1]; f[2] = l[2]; f[3] = l[3];
+    f[4] = u[0]; f[5] = u[1]; f[6] = u[2]; f[7] = u[3];
+    return f;
+  }
+  __device__ inline void touch() {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(lo[nb]), "+v"(hi[nb]));
+  }
+};
+
+struct NoOffsets {  // stand-in for the offset tables where they are not used (fp32 tiles)
+  __device__ inline NoOffsets(int) {}
+  __device__ inline NoOffsets(int, int) {}
+  __device__ inline void touch() {}
+};
 
 template <typename T>
 __device__ inline typename Mfma<T>::frag zero_frag() {
@@ -743,29 +809,47 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dqa[nb] = zero16();
 
-  for (int t = 0; t < ntiles; ++t) {
-    wait_loads();
-    __syncthreads();
-    const int k0 = t * BK;
-    if (t + 1 < ntiles) {
-      T* nbuf = lds + ((t + 1) & 1) * TS;
-      ld1.issue(nbuf, K1, k0 + BK, a.n_k);
-      ld2.issue(nbuf + BK * D1, K2, k0 + BK, a.n_k);
-    }
-    if (!wave_rows || k0 > wave_kmax) continue;
-    const T* sK1 = lds + (t & 1) * TS;
-    const T* sK2 = sK1 + BK * D1;
-    const T* sKS = SETTING == 1 ? sK2 : sK1;
+  // bf16: per-lane LDS offsets computed once (K1/K2 rows share them when
+  // d1 == d2); fp32 computes addresses per read
+  constexpr bool BF = sizeof(T) == 2;
+  using RF1 = std::conditional_t<BF, RowFragOffsets<D1, S1>, NoOffsets>;
+  using RF2 = std::conditional_t<BF, RowFragOffsets<D2, S2>, NoOffsets>;
+  using CF = std::conditional_t<BF, ColFragOffsets<DS, NB>, NoOffsets>;
+  RF1 rf1(col, grp);
+  RF2 rf2 = [&]() -> RF2 {
+    if constexpr (std::is_same_v<RF1, RF2>) return rf1;
+    else return RF2(col, grp);
+  }();
+  CF cf(lane);
+  auto row1 = [&](const T* tile, int blk, int s) -> frag {
+    if constexpr (BF) return rf1.read(tile, blk, s);
+    else return frag_tile<T, D1>(tile, 32 * blk + col, s, grp);
+  };
+  auto row2 = [&](const T* tile, int blk, int s) -> frag {
+    if constexpr (BF) return rf2.read(tile, blk, s);
+    else return frag_tile<T, D2>(tile, 32 * blk + col, s, grp);
+  };
+  auto colop = [&](const T* tile, int blk, int nb, int h) -> frag {
+    if constexpr (BF) return cf.read(tile, blk, nb, h);
+    else return fragcol_acc<T, DS>(tile, 32 * blk, 32 * nb, h, lane);
+  };
+
+  // Tiles alternate between the two LDS buffers; stepping by two keeps each
+  // buffer's tile base a constant, so every LDS read is a per-lane offset plus
+  // an immediate (no address arithmetic per read).
+  auto tile = [&](const T* sK1, int k0) {
     const bool need_mask = (k0 + BK > kend) || (a.causal && k0 + BK - 1 > q0 + off);
     const int lim = a.causal ? min(kend - 1, qrow + off) : kend - 1;
+    const T* sK2 = sK1 + BK * D1;
+    const T* sKS = SETTING == 1 ? sK2 : sK1;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 s1 = zero16(), s2 = zero16();
       constexpr int SM = S1 > S2 ? S1 : S2;
 #pragma unroll
       for (int s = 0; s < SM; ++s) {
-        if (s < S1) s1 = MF::run(frag_tile<T, D1>(sK1, kb * 32 + col, s, grp), qf1[s < S1 ? s : 0], s1);
-        if (s < S2) s2 = MF::run(frag_tile<T, D2>(sK2, kb * 32 + col, s, grp), qf2[s < S2 ? s : 0], s2);
+        if (s < S1) s1 = MF::run(row1(sK1, kb, s), qf1[s < S1 ? s : 0], s1);
+        if (s < S2) s2 = MF::run(row2(sK2, kb, s), qf2[s < S2 ? s : 0], s2);
       }
       sched_mfma_lds<S1 + S2, 1, 4>();
       if (need_mask) {
@@ -782,11 +866,27 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       for (int h = 0; h < HS; ++h) {
         const frag af = frag_from_acc(s1, h, T());
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          dqa[nb] = MF::run(af, fragcol_acc<T, DS>(sKS, kb * 32, nb * 32, h, lane), dqa[nb]);
+        for (int nb = 0; nb < NB; ++nb) dqa[nb] = MF::run(af, colop(sKS, kb, nb, h), dqa[nb]);
       }
       sched_mfma_lds<HS * NB, MF::KPL == 1 ? 1 : 2, 2>();
     }
+  };
+  auto step = [&](int t, const T* sbuf, T* nbuf) {
+    wait_loads();
+    __syncthreads();
+    const int k0 = t * BK;
+    if (t + 1 < ntiles) {
+      ld1.issue(nbuf, K1, k0 + BK, a.n_k);
+      ld2.issue(nbuf + BK * D1, K2, k0 + BK, a.n_k);
+    }
+    if (wave_rows && k0 <= wave_kmax) tile(sbuf, k0);
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    rf1.touch();
+    if constexpr (!std::is_same_v<RF1, RF2>) rf2.touch();
+    cf.touch();
+    step(t, lds, lds + TS);
+    if (t + 1 < ntiles) step(t + 1, lds + TS, lds);
   }
 
   // dQ accumulator rows are queries q0 + acc_row(e, grp); lane r < 32 holds
