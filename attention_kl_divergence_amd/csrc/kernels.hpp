@@ -724,18 +724,21 @@ __device__ inline float dS_elem_row(float s1, float s2, float c1, float c2, cons
 // MASK: queries outside [qlo, n_q) get dS = 0.  Result overwrites s1.
 template <int SETTING, bool MASK, int BQ, bool SIGNED = true>
 __device__ inline void dS_rows_keyouter(f32x16& s1, const f32x16& s2, const float* st, int ql0, int qb0, int grp,
-                                        float c1, float c2, int qlo, int n_q) {
+                                        float c1, float c2, int qlo, int n_q, int lane_off) {
+  // st[k*BQ + q] for q = ql0 + 8i + 4grp + j; lane_off = 16 * grp bytes
+  auto at = [&](int k, int i) {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(st + k * BQ + ql0 + 8 * i) + lane_off);
+  };
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int ql = ql0 + 8 * i + 4 * grp;
-    const f32x4 L1 = *reinterpret_cast<const f32x4*>(st + 0 * BQ + ql);
-    const f32x4 L2 = *reinterpret_cast<const f32x4*>(st + 1 * BQ + ql);
+    const f32x4 L1 = at(0, i);
+    const f32x4 L2 = at(1, i);
     f32x4 GS = {1.f, 1.f, 1.f, 1.f};
-    if (SETTING != 1 || SIGNED) GS = *reinterpret_cast<const f32x4*>(st + 2 * BQ + ql);
+    if (SETTING != 1 || SIGNED) GS = at(2, i);
     f32x4 RA = {0.f, 0.f, 0.f, 0.f}, RB = {0.f, 0.f, 0.f, 0.f};
     if constexpr (SETTING == 2) {
-      RA = *reinterpret_cast<const f32x4*>(st + 3 * BQ + ql);
-      RB = *reinterpret_cast<const f32x4*>(st + 4 * BQ + ql);
+      RA = at(3, i);
+      RB = at(4, i);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1028,7 +1031,41 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   // queries that see this lane's key: [qlo, n_q)
   const int qlo = kv ? (a.causal ? krow - off : 0) : 0x3fffffff;
 
-  for (int t = 0; t < ntiles; ++t) {
+  // bf16: per-lane LDS offsets computed once (Q1/Q2 rows share them when
+  // d1 == d2); fp32 computes addresses per read
+  constexpr bool BF = sizeof(T) == 2;
+  using RF1 = std::conditional_t<BF, RowFragOffsets<D1, S1>, NoOffsets>;
+  using RF2 = std::conditional_t<BF, RowFragOffsets<D2, S2>, NoOffsets>;
+  using CF = std::conditional_t<BF, ColFragOffsets<DS, NB>, NoOffsets>;
+  RF1 rf1(col, grp);
+  // per-lane byte offset of the stats reads (16 * grp), kept opaque like
+  // the offset tables so each stats read is this register plus an immediate
+  int stat_off = 16 * grp;
+  asm volatile("" : "+v"(stat_off));
+  RF2 rf2 = [&]() -> RF2 {
+    if constexpr (std::is_same_v<RF1, RF2>) return rf1;
+    else return RF2(col, grp);
+  }();
+  auto row1 = [&](const T* tile, int blk, int s) -> frag {
+    if constexpr (BF) return rf1.read(tile, blk, s);
+    else return frag_tile<T, D1>(tile, 32 * blk + col, s, grp);
+  };
+  auto row2 = [&](const T* tile, int blk, int s) -> frag {
+    if constexpr (BF) return rf2.read(tile, blk, s);
+    else return frag_tile<T, D2>(tile, 32 * blk + col, s, grp);
+  };
+  CF cf(lane);
+  auto colop = [&](const T* tile, int blk, int nb, int h) -> frag {
+    if constexpr (BF) return cf.read(tile, blk, nb, h);
+    else return fragcol_acc<T, DS>(tile, 32 * blk, 32 * nb, h, lane);
+  };
+
+  // One query tile.  P is the tile's buffer (t & 1): tiles alternate between
+  // the two LDS buffers and the loop below steps by two, so each buffer's tile
+  // base is a constant and every LDS read is a per-lane offset plus an
+  // immediate.
+  auto step = [&](int t, auto P) {
+    constexpr int B = decltype(P)::value;
     wait_loads();
     __syncthreads();
     const int q0 = qtl - t * BQ;
@@ -1037,15 +1074,15 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
       // stats first: vmcnt retires in order, so using them then waits only
       // for these loads, not for the tile loads behind them
       load_stats(q0 - BQ, rgn);
-      T* nbuf = lds + ((t + 1) & 1) * TS;
+      T* nbuf = lds + (1 - B) * TS;
       ld1.issue(nbuf, Q1, q0 - BQ, a.n_q);
       ld2.issue(nbuf + BQ * D1, Q2, q0 - BQ, a.n_q);
     }
-    const T* sQ1 = lds + (t & 1) * TS;
+    const T* sQ1 = lds + B * TS;
     const T* sQ2 = sQ1 + BQ * D1;
     const T* sQS = SETTING == 1 ? sQ2 : sQ1;
-    const float* st = &sstat[t & 1][0][0];
-    const bool tile_signed = sneg[t & 1] != 0;
+    const float* st = &sstat[B][0][0];
+    const bool tile_signed = sneg[B] != 0;
 
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -1056,26 +1093,25 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
         constexpr int SM = S1 > S2 ? S1 : S2;
 #pragma unroll
         for (int s = 0; s < SM; ++s) {
-          if (s < S1) s1 = MF::run(frag_tile<T, D1>(sQ1, 32 * qb + col, s, grp), kf1[s < S1 ? s : 0], s1);
-          if (s < S2) s2 = MF::run(frag_tile<T, D2>(sQ2, 32 * qb + col, s, grp), kf2[s < S2 ? s : 0], s2);
+          if (s < S1) s1 = MF::run(row1(sQ1, qb, s), kf1[s < S1 ? s : 0], s1);
+          if (s < S2) s2 = MF::run(row2(sQ2, qb, s), kf2[s < S2 ? s : 0], s2);
         }
         sched_mfma_lds<S1 + S2, 1, 4>();
         const bool need_mask = (qb0 + 32 > a.n_q) || (kwave + 32 > a.n_k) || (a.causal && kwave + 31 > qb0 + off);
         if (SETTING == 2 || tile_signed) {
-          if (need_mask) dS_rows_keyouter<SETTING, true, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
-          else dS_rows_keyouter<SETTING, false, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
+          if (need_mask) dS_rows_keyouter<SETTING, true, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q, stat_off);
+          else dS_rows_keyouter<SETTING, false, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q, stat_off);
         } else {
           if (need_mask)
-            dS_rows_keyouter<SETTING, true, BQ, false>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
+            dS_rows_keyouter<SETTING, true, BQ, false>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q, stat_off);
           else
-            dS_rows_keyouter<SETTING, false, BQ, false>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q);
+            dS_rows_keyouter<SETTING, false, BQ, false>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q, stat_off);
         }
 #pragma unroll
         for (int h = 0; h < HS; ++h) {
           const frag af = frag_from_acc(s1, h, T());
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            dka[nb] = MF::run(af, fragcol_acc<T, DS>(sQS, 32 * qb, nb * 32, h, lane), dka[nb]);
+          for (int nb = 0; nb < NB; ++nb) dka[nb] = MF::run(af, colop(sQS, qb, nb, h), dka[nb]);
         }
         sched_mfma_lds<HS * NB, MF::KPL == 1 ? 1 : 2, 2>();
         if constexpr (FUSED) {
@@ -1103,7 +1139,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
     }
     if (more) {
       __builtin_amdgcn_sched_barrier(0);
-      store_stats((t + 1) & 1, rgn);
+      store_stats(1 - B, rgn);
     }
 
     if constexpr (FUSED) {
@@ -1124,6 +1160,15 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
         }
       }
     }
+  };
+
+  for (int t = 0; t < ntiles; t += 2) {
+    rf1.touch();
+    if constexpr (!std::is_same_v<RF1, RF2>) rf2.touch();
+    cf.touch();
+    asm volatile("" : "+v"(stat_off));
+    step(t, std::integral_constant<int, 0>());
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>());
   }
 
 #pragma unroll
