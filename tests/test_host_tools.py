@@ -1,0 +1,107 @@
+"""Host-side tools: the traffic calibration behind roofline.traffic, the
+summary format the benchmark reads back, and the benchmark's one-GPU guard."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from attention_kl_divergence_amd import build, profiling  # noqa: E402
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+          "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+          "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+MUL = "void at::native::vectorized_elementwise_kernel<4, at::native::BinaryFunctor<float, float, float, " \
+      "at::native::binary_internal::MulFunctor<float> >, std::array<char*, 3ul> >"
+DK = "_ZN8streamkl13bwd_dk_kernelIDF16bLi128ELi128ELi1ELb0ELi64EEEvNS_7BwdArgsE"
+DK_FUSED = "_ZN8streamkl13bwd_dk_kernelIDF16bLi128ELi128ELi1ELb1ELi64EEEvNS_7BwdArgsE"
+FWD_PP = "_ZN8streamkl13fwd_pp_kernelIDF16bLi128ELi128ELi64EEEvNS_7FwdArgsE"
+FWD = "_ZN8streamkl10fwd_kernelIDF16bLi128ELi128ELi64EEEvNS_7FwdArgsE"
+
+
+def write_csv(path, counter, rows):
+    """rows: (dispatch id, kernel name, [values per counter instance]) in KiB."""
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for d, name, vals in rows:
+            for v in vals:
+                w.writerow({k: 0 for k in FIELDS} | {"Dispatch_Id": d, "Kernel_Name": name,
+                                                     "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_traffic_calibration(tmp_path):
+    # 1024 MiB reference copy: FETCH reads half (scale 2), WRITE reads it exactly (scale 1);
+    # an earlier, smaller MulFunctor must not be taken as the reference, and a
+    # dispatch's instances are summed
+    fetch = tmp_path / "f.csv"
+    write = tmp_path / "w.csv"
+    write_csv(fetch, "FETCH_SIZE", [(1, MUL, [100.0]), (2, MUL, [262144.0, 262144.0]),
+                                    (3, DK, [1000.0]), (4, DK, [3000.0]), (5, FWD_PP, [50.0]),
+                                    (6, DK_FUSED, [7.0]), (7, FWD, [9.0])])
+    write_csv(write, "WRITE_SIZE", [(1, MUL, [10.0]), (2, MUL, [1048576.0]),
+                                    (3, DK, [64.0]), (4, DK, [64.0]), (5, FWD_PP, [2.0]),
+                                    (6, DK_FUSED, [1.0]), (7, FWD, [3.0])])
+    res, factors = profiling.traffic(str(fetch), str(write), 1024)
+    assert factors["FETCH_SIZE"] == pytest.approx(2.0)
+    assert factors["WRITE_SIZE"] == pytest.approx(1.0)
+    assert res["bwd_dk_kernel"]["launches"] == 2
+    assert res["bwd_dk_kernel"]["fetch_bytes"] == pytest.approx(2.0 * 2000.0 * 1024)
+    assert res["bwd_dk_kernel"]["write_bytes"] == pytest.approx(64.0 * 1024)
+    assert res["fwd_pp_kernel"]["fetch_bytes"] == pytest.approx(2.0 * 50.0 * 1024)
+    # the fused key-outer kernel and the plain forward get their own labels
+    assert res["bwd_dk_kernel<FUSED>"]["fetch_bytes"] == pytest.approx(2.0 * 7.0 * 1024)
+    assert res["fwd_kernel"]["write_bytes"] == pytest.approx(3.0 * 1024)
+
+
+def test_traffic_needs_a_reference_copy(tmp_path):
+    fetch = tmp_path / "f.csv"
+    write_csv(fetch, "FETCH_SIZE", [(1, DK, [1.0])])
+    with pytest.raises(SystemExit):
+        profiling.traffic(str(fetch), str(fetch), 1024)
+
+
+def test_summary_round_trip(tmp_path, monkeypatch):
+    fetch = tmp_path / "f.csv"
+    write = tmp_path / "w.csv"
+    write_csv(fetch, "FETCH_SIZE", [(1, MUL, [524288.0]), (2, DK, [10.0])])
+    write_csv(write, "WRITE_SIZE", [(1, MUL, [1048576.0]), (2, DK, [5.0])])
+    out = tmp_path / "traffic_wl.md"
+    assert profiling.main(["traffic", "--fetch", str(fetch), "--write", str(write), "--copy-mib", "1024",
+                           "--workload", "wl", "--command", "cmd", "--out", str(out)]) == 0
+    monkeypatch.setattr(profiling, "PROFILES", str(tmp_path))
+    summ = profiling.load_summary("wl")
+    assert summ["workload"] == "wl"
+    assert summ["source_digest"] == profiling.kernel_source_digest()
+    assert summ["kernels"]["bwd_dk_kernel"]["fetch_bytes"] == 20 * 1024
+    assert summ["kernels"]["bwd_dk_kernel"]["write_bytes"] == 5 * 1024
+    assert profiling.load_summary("missing") is None
+
+
+def test_source_digest_tracks_device_flags(monkeypatch):
+    d0 = profiling.kernel_source_digest()
+    assert d0 == profiling.kernel_source_digest()
+    monkeypatch.setattr(build, "FLAGS", build.FLAGS + ["-DSOMETHING_ELSE"])
+    assert profiling.kernel_source_digest() != d0
+
+
+def test_committed_summaries_parse():
+    for name in os.listdir(os.path.join(ROOT, "profiles")):
+        if name.startswith("traffic_") and name.endswith(".md"):
+            summ = profiling.load_summary(name[len("traffic_"):-len(".md")])
+            assert summ is not None and summ["kernels"], name
+            assert summ["scale"]["FETCH_SIZE"] > 0 and summ["scale"]["WRITE_SIZE"] > 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    msg = json.loads(p.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
