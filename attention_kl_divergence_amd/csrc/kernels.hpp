@@ -352,15 +352,16 @@ __device__ inline void fwd_update(RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[
         s2[kb][e] = out ? kNegInf : s2[kb][e];
       }
   }
+  // running maxima as chains of max(max(acc, a), b): one v_max3 per two values
   float mx1a = kNegInf, mx1b = kNegInf, mx2a = kNegInf, mx2b = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; e += 4) {
-      mx1a = fmaxf(mx1a, fmaxf(s1[kb][e], s1[kb][e + 1]));
-      mx1b = fmaxf(mx1b, fmaxf(s1[kb][e + 2], s1[kb][e + 3]));
-      mx2a = fmaxf(mx2a, fmaxf(s2[kb][e], s2[kb][e + 1]));
-      mx2b = fmaxf(mx2b, fmaxf(s2[kb][e + 2], s2[kb][e + 3]));
+      mx1a = fmaxf(fmaxf(mx1a, s1[kb][e]), s1[kb][e + 1]);
+      mx1b = fmaxf(fmaxf(mx1b, s1[kb][e + 2]), s1[kb][e + 3]);
+      mx2a = fmaxf(fmaxf(mx2a, s2[kb][e]), s2[kb][e + 1]);
+      mx2b = fmaxf(fmaxf(mx2b, s2[kb][e + 2]), s2[kb][e + 3]);
     }
   const float M1n = fmaxf(st.M1, fmaxf(mx1a, mx1b) * c1);
   const float M2n = fmaxf(st.M2, fmaxf(mx2a, mx2b) * c2);
