@@ -99,6 +99,12 @@ FwdLaunch pick_fwd_pp(int dtype, int d1, int d2) {
 #undef SKL_PICK
   return nullptr;
 }
+FwdLaunch pick_fwd_dec(int dtype, int d1, int d2) {
+#define SKL_PICK(tn, a, b) if (d1 == a && d2 == b) return launch_fwd_dec_##tn##_##a##_##b;
+  if (dtype == STREAMKL_BF16) { SKL_PICK(bf16, 64, 64) SKL_PICK(bf16, 64, 128) SKL_PICK(bf16, 128, 64) SKL_PICK(bf16, 128, 128) }
+#undef SKL_PICK
+  return nullptr;
+}
 DqLaunch pick_dq(int dtype, int d1, int d2) {
 #define SKL_PICK(tn, a, b) if (d1 == a && d2 == b) return launch_bwd_dq_##tn##_##a##_##b;
   if (dtype == STREAMKL_F32) { SKL_PICK(f32, 64, 64) SKL_PICK(f32, 64, 128) SKL_PICK(f32, 128, 64) SKL_PICK(f32, 128, 128) }
@@ -114,11 +120,27 @@ DkLaunch pick_dk(int dtype, int d1, int d2) {
   return nullptr;
 }
 
+// bf16 query ranges that fit one wave's 32 rows run the decode forward, in
+// which every wave is one key split.
+bool decode_shape(const streamkl_shape* s) { return s->dtype == STREAMKL_BF16 && s->n_q <= kDecRows; }
+
 // Key-split plan.  Split-K (Method 3 of the technical summary) is for shapes
-// whose query blocks alone cannot fill the chip: aim for >= 4 workgroups per
-// CU, keep >= 4 key tiles per split.
+// whose query blocks alone cannot fill the chip.  Decode shapes: about 4
+// waves (splits) per CU, all resident at once (one sweep through K1 and K2;
+// measured best at 32 heads, against 2-16 waves per CU), >= 8 key blocks per
+// split.  Otherwise: aim for >= 4 workgroups per CU, keep >= 4 key tiles per
+// split.
 int plan_splits(const streamkl_shape* s, int causal, const streamkl_launch* l, int cus) {
   (void)causal;
+  if (decode_shape(s)) {
+    const int64_t blocks = cdiv(s->n_k, kDecBlock);
+    if (l && l->num_splits > 0) return (int)(l->num_splits < blocks ? l->num_splits : blocks);
+    int64_t sp = cdiv(4 * (int64_t)cus, s->B * s->H);
+    const int64_t maxsp = blocks / 8 > 1 ? blocks / 8 : 1;
+    if (sp > maxsp) sp = maxsp;
+    if (sp > 4096) sp = 4096;
+    return (int)(sp < 1 ? 1 : sp);
+  }
   const int64_t tiles = cdiv(s->n_k, kFwdTile);
   if (l && l->num_splits > 0) return (int)(l->num_splits < tiles ? l->num_splits : tiles);
   const int64_t base = s->B * s->H * cdiv(s->n_q, kFwdRows);
@@ -231,9 +253,13 @@ streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, con
       splits = 1;
     }
   }
-  // Without a key split, long query ranges use the 8-wave ping-pong kernel.
+  // Without a key split, long query ranges use the 8-wave ping-pong kernel;
+  // split short bf16 query ranges use the decode kernel.
   const bool pp = splits == 1 && shape->n_q > kFwdRows;
-  FwdLaunch fn = pp ? pick_fwd_pp(shape->dtype, shape->d1, shape->d2) : pick_fwd(shape->dtype, shape->d1, shape->d2);
+  const bool dec = splits > 1 && decode_shape(shape);
+  FwdLaunch fn = dec  ? pick_fwd_dec(shape->dtype, shape->d1, shape->d2)
+                 : pp ? pick_fwd_pp(shape->dtype, shape->d1, shape->d2)
+                      : pick_fwd(shape->dtype, shape->d1, shape->d2);
   if (!fn) return STREAMKL_ERR_UNSUPPORTED;
 
   FwdArgs a;
@@ -244,14 +270,14 @@ streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, con
   a.n_q = (int)shape->n_q;
   a.n_k = (int)shape->n_k;
   a.nsplit = splits;
-  const int64_t tiles = cdiv(shape->n_k, kFwdTile);
-  a.keys_per_split = (int)(cdiv(tiles, splits) * kFwdTile);
+  const int unit = dec ? kDecBlock : kFwdTile;
+  a.keys_per_split = (int)(cdiv(cdiv(shape->n_k, unit), splits) * unit);
   a.nqb = (int)cdiv(shape->n_q, pp ? kFwdPPRows : kFwdRows);
   a.causal = causal ? 1 : 0;
   a.c1 = log2e_scale(scale1, shape->d1);
   a.c2 = log2e_scale(scale2, shape->d2);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(fn(a, a.BH * a.nqb * splits, s));
+  st = hip_status(fn(a, dec ? a.BH * cdiv(splits, 4) : a.BH * a.nqb * splits, s));
   if (st != STREAMKL_OK || splits == 1) return st;
   const int64_t rows = a.BH * a.n_q;
   hipLaunchKernelGGL(splitk_merge_kernel, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, s,

@@ -1,6 +1,6 @@
 // One translation unit per (dtype, d1, d2): compiled several times with
 // -DSKL_T=<type> -DSKL_TN=<tag> -DSKL_D1=<d1> -DSKL_D2=<d2> so the kernel
-// instantiations build in parallel.  Each exports three launchers with
+// instantiations build in parallel.  Each exports five launchers with
 // C++ linkage, named launch_<kind>_<tag>_<d1>_<d2>.
 #include "kernels.hpp"
 #include "launch.hpp"
@@ -18,6 +18,15 @@ hipError_t SKL_CAT(launch_fwd, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t
 hipError_t SKL_CAT(launch_fwd_pp, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
   hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile>), dim3((unsigned)nblocks), dim3(512), 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t SKL_CAT(launch_fwd_dec, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
+  if constexpr (sizeof(SKL_T) != 2) {
+    return hipErrorInvalidValue;  // bf16 only
+  } else {
+    hipLaunchKernelGGL((fwd_decode_kernel<SKL_D1, SKL_D2>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
 }
 
 hipError_t SKL_CAT(launch_bwd_dq, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, int64_t nblocks,

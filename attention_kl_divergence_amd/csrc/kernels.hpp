@@ -519,6 +519,138 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 }
 
 
+// ---------------------------------------------------------------------------
+// Forward for short query ranges (n_q <= 32, bf16), split along the keys.
+// Every wave is its own key split: it streams 32-key blocks of K1 and K2
+// from global memory straight into MFMA operand registers, two blocks in
+// flight, with no LDS tiles and no barriers in the loop, so each wave keeps
+// its own loads going while it runs the online update of the block before.
+// Split z takes blocks z, z + nsplit, z + 2 nsplit, ...: the splits running
+// at a time read neighbouring blocks, one front sweeping through K1 and K2
+// (contiguous ranges per split, many fronts, ran 3-7% slower).  Split z of
+// head bh is wave z % 4 of workgroup bh * ceil(nsplit / 4) + z / 4; the four
+// waves share the head's Q1 and Q2, held once in LDS.
+//
+// Operand order: lane group g feeds d-chunk 2s + g (8 elements) at MFMA step
+// s, the natural order, so each load instruction reads 32 bytes of each of
+// 32 key rows.
+template <int D>
+__device__ inline void dec_load_row(bf16x8 (&f)[D / 16], const bf16* base, int64_t row, int grp) {
+  constexpr int S = D / 16;
+  const bf16x8* p = reinterpret_cast<const bf16x8*>(base + row * D) + grp;
+#pragma unroll
+  for (int s = 0; s < S; ++s) f[s] = p[2 * s];
+}
+
+// rows [0, 32) of a [n_q, D] query tensor into a swizzled LDS tile (zeros
+// past n_q), 16-byte chunks spread over the workgroup's 256 threads
+template <int D>
+__device__ inline void dec_stage_q(bf16* tile, const bf16* q, int n_q, int tid) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = tid; i < 32 * CPR; i += 256) {
+    const int r = i / CPR, c = i % CPR;
+    bf16x8 v = zero_frag<bf16>();
+    if (r < n_q) v = *reinterpret_cast<const bf16x8*>(q + (int64_t)r * D + 8 * c);
+    *reinterpret_cast<bf16x8*>(tile + Tile<bf16, D>::off(r, 8 * c)) = v;
+  }
+}
+
+template <int D1, int D2>
+__global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
+  constexpr int NB = 2;  // blocks in flight per wave
+  using MF = Mfma<bf16>;
+  constexpr int S1 = D1 / 16, S2 = D2 / 16;
+  __shared__ __attribute__((aligned(1024))) bf16 sq[32 * (D1 + D2)];
+  bf16* sQ1 = sq;
+  bf16* sQ2 = sq + 32 * D1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, grp = lane >> 5;
+  const int64_t nwg = (a.nsplit + 3) / 4;
+  const int64_t bh = blockIdx.x / nwg;
+  const int z = (int)(blockIdx.x % nwg) * 4 + wave;
+  const int off = a.n_k - a.n_q;
+
+  const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.n_q * D1;
+  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + bh * (int64_t)a.n_k * D1;
+  const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.n_q * D2;
+  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + bh * (int64_t)a.n_k * D2;
+  dec_stage_q<D1>(sQ1, Q1, a.n_q, tid);
+  dec_stage_q<D2>(sQ2, Q2, a.n_q, tid);
+  __syncthreads();
+  if (z >= a.nsplit) return;
+
+  // block j of this split is the head's block j * nsplit + z
+  const int nball = (a.n_k + 31) / 32;
+  const int kb0 = 32 * z;
+  const int kstep = 32 * a.nsplit;
+  const int nblk = z < nball ? (nball - z + a.nsplit - 1) / a.nsplit : 0;
+  const int qrow = col;
+  // B operands: query row col, chunk 2s + grp, read from the LDS tile for
+  // every block (the per-block opaque offset keeps the compiler from hoisting
+  // them into 16 * S registers that the K blocks in flight need)
+  auto qfrag1 = [&](int s, int o) {
+    return *reinterpret_cast<const bf16x8*>(sQ1 + o + Tile<bf16, D1>::off(col, 8 * (2 * s + grp)));
+  };
+  auto qfrag2 = [&](int s, int o) {
+    return *reinterpret_cast<const bf16x8*>(sQ2 + o + Tile<bf16, D2>::off(col, 8 * (2 * s + grp)));
+  };
+
+  RowState st = empty_state();
+  const float c1 = a.c1, c2 = a.c2;
+  const int lim_row = a.causal ? min(a.n_k - 1, qrow + off) : a.n_k - 1;
+
+  // Blocks are loaded without conditions (past the last block the loads
+  // re-read the head's last key row, which is cached), so the same loads are
+  // in flight at every point of the loop and each block waits only for its own.
+  bf16x8 kf1[NB][S1], kf2[NB][S2];
+  auto load = [&](bf16x8(&f1)[S1], bf16x8(&f2)[S2], int j) {
+    const int64_t row = min(kb0 + kstep * j + col, a.n_k - 1);
+    dec_load_row<D1>(f1, K1, row, grp);
+    dec_load_row<D2>(f2, K2, row, grp);
+  };
+  // logits of block j from (f1, f2), then the load of block j + NB into the
+  // same registers, then the online update of block j (if it exists)
+  auto block = [&](bf16x8(&f1)[S1], bf16x8(&f2)[S2], int j) {
+    f32x16 s1[1] = {zero16()}, s2[1] = {zero16()};
+    int qo = 0;
+    asm volatile("" : "+v"(qo));
+#pragma unroll
+    for (int s = 0; s < (S1 > S2 ? S1 : S2); ++s) {
+      if (s < S1) s1[0] = MF::run(f1[s < S1 ? s : 0], qfrag1(s < S1 ? s : 0, qo), s1[0]);
+      if (s < S2) s2[0] = MF::run(f2[s < S2 ? s : 0], qfrag2(s < S2 ? s : 0, qo), s2[0]);
+    }
+    load(f1, f2, j + NB);
+    if (j >= nblk) return;
+    const int k0 = kb0 + kstep * j;
+    const bool need_mask = (k0 + 32 > a.n_k) || (a.causal && k0 + 31 > off);
+    if (need_mask) fwd_update<true, 1>(st, s1, s2, c1, c2, k0, lim_row, grp);
+    else fwd_update<false, 1>(st, s1, s2, c1, c2, k0, 0, grp);
+  };
+  if (nblk > 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      load(kf1[b], kf2[b], b);
+      __builtin_amdgcn_sched_barrier(0);  // keep the issue order of the blocks
+    }
+    for (int j = 0; j < nblk; j += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) block(kf1[b], kf2[b], j + b);
+    }
+  }
+
+  st = merge_state(st, shfl_xor_state(st, 32));
+  if (grp == 0 && qrow < a.n_q) {
+    const int64_t fs = a.BH * (int64_t)a.nsplit * a.n_q;
+    const int64_t o = (bh * a.nsplit + z) * (int64_t)a.n_q + qrow;
+    a.ws[o] = st.M1;
+    a.ws[o + fs] = st.l1;
+    a.ws[o + 2 * fs] = st.A;
+    a.ws[o + 3 * fs] = st.M2;
+    a.ws[o + 4 * fs] = st.l2;
+  }
+}
+
 // Logits of one key tile for one wave: s_t[kb] = K_t[kb*32 .. +32) Q_t^T for
 // the wave's 32 query rows (raw dot products), 2*NKB independent chains.
 template <typename T, int D1, int D2, int NKB>

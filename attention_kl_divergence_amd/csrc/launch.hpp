@@ -13,6 +13,8 @@ struct BwdArgs;
 constexpr int kFwdRows = 128;     // query rows per forward workgroup (4 waves x 32)
 constexpr int kFwdPPRows = 256;   // query rows per ping-pong forward workgroup (8 waves x 32)
 constexpr int kFwdTile = 64;      // key rows per forward LDS tile
+constexpr int kDecRows = 32;      // longest query range of the decode forward (one wave's rows)
+constexpr int kDecBlock = 32;     // key rows per decode-forward block
 constexpr int kBwdQRows = 128;    // query rows per dQ workgroup
 constexpr int kBwdKeyTile = 64;   // key rows per dQ-kernel LDS tile
 constexpr int kBwdKRows = 128;    // key rows per dK workgroup (4 waves x 32)
@@ -26,6 +28,7 @@ using DkLaunch = hipError_t (*)(const BwdArgs&, int, bool, int64_t, hipStream_t)
 #define SKL_DECL(tn, d1, d2)                                                                   \
   hipError_t launch_fwd_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);              \
   hipError_t launch_fwd_pp_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);           \
+  hipError_t launch_fwd_dec_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);          \
   hipError_t launch_bwd_dq_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t);      \
   hipError_t launch_bwd_dk_##tn##_##d1##_##d2(const BwdArgs&, int, bool, int64_t, hipStream_t);
 SKL_DECL(f32, 64, 64)

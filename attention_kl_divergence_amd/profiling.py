@@ -34,6 +34,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # rocprofv3 reports it (mangled, e.g. ...bwd_dk_kernelIDF16bLi128ELi128ELi1ELb0E...,
 # or demangled, e.g. streamkl::bwd_dk_kernel<__bf16, 128, 128, 1, false, 64>)
 KERNELS = [
+    ("fwd_decode_kernel", r"fwd_decode_kernel"),
     ("fwd_pp_kernel", r"fwd_pp_kernel"),
     ("fwd_kernel", r"fwd_kernel"),
     ("bwd_dk_kernel", r"bwd_dk_kernel(I.*Lb0E|<[^>]*false)"),

@@ -176,7 +176,15 @@ def main():
     fwd_bytes = w.B * w.H * ((w.n_q + w.n_k) * (w.d1 + w.d2) * esz + 12 * w.n_q)
 
     dom = max(per_call, key=per_call.get)
-    kernel_names = {"fwd": "fwd_pp_kernel" if (splits == 1 and w.n_q > 128) else "fwd_kernel"}
+    # the forward kernel the library picks: one wave per key split for short
+    # bf16 query ranges, the 8-wave ping-pong form for long unsplit ones
+    if splits > 1 and w.dtype == "bf16" and w.n_q <= 32:
+        fwd_kernel = "fwd_decode_kernel"
+    elif splits == 1 and w.n_q > 128:
+        fwd_kernel = "fwd_pp_kernel"
+    else:
+        fwd_kernel = "fwd_kernel"
+    kernel_names = {"fwd": fwd_kernel}
     for setting in w.settings:
         kernel_names[f"bwd{setting}_fused"] = "bwd_dk_kernel<FUSED>"
         kernel_names[f"bwd{setting}_dk"] = "bwd_dk_kernel"

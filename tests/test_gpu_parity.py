@@ -70,6 +70,11 @@ SMALL = [
     ("bf16-n1", "bf16", 128, 128, False, 1, 2, 1, 1),
     ("bf16-n17-c", "bf16", 128, 128, True, 1, 2, 17, 17),
     ("bf16-q1-k1000", "bf16", 128, 128, False, 1, 3, 1, 1000),
+    # query ranges of at most 32 rows: the one-wave-per-split decode kernel
+    ("bf16-dec-q16-k2000", "bf16", 128, 128, False, 1, 2, 16, 2000),
+    ("bf16-dec-q32-k1500-c", "bf16", 128, 128, True, 1, 2, 32, 1500),
+    ("bf16-dec-d128x64-q5-k777-c", "bf16", 128, 64, True, 1, 2, 5, 777),
+    ("bf16-dec-d64x128-q31-k300", "bf16", 64, 128, False, 2, 1, 31, 300),
 ]
 
 
