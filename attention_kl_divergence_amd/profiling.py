@@ -148,7 +148,7 @@ def kernel_summary(stats_csv, bench_log, workload, command):
                   ", ".join(f"{k} {v}" for k, v in bench.get("per_kernel_ms", {}).items()) + ".",
                   f"Dominant kernel: {roof.get('kernel')} at {roof.get('avg_ms')} ms per launch, "
                   f"{roof.get('achieved')} {roof.get('unit')} ({100 * roof.get('frac', 0):.1f}% of {roof.get('peak')})."]
-        dom = roof.get("kernel", "")
+        dom = roof.get("kernel", "").split(" + ")[0]
         pat = dict(KERNELS).get(dom)
         match = [r for r in rows if pat and re.search(pat, r["Name"])]
         if match and roof.get("avg_ms"):
