@@ -16,7 +16,8 @@ hipError_t SKL_CAT(launch_fwd, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t
 }
 
 hipError_t SKL_CAT(launch_fwd_pp, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile>), dim3((unsigned)nblocks), dim3(512), 0, st, a);
+  hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, kFwdPPTile<SKL_T>>), dim3((unsigned)nblocks), dim3(512), 0,
+                     st, a);
   return hipGetLastError();
 }
 
