@@ -97,8 +97,9 @@ struct Tile {
 // bytes [16L, 16L+16) of it), so each lane fetches the global chunk that
 // belongs at that swizzled spot; those per-lane byte offsets are fixed for the
 // kernel.  Per tile only the buffer resource changes (scalar work): its base
-// is the tile's first row and its size the bytes left in the tensor, so rows
-// past the end read as zeros.
+// is the tile's first row and its size the tile's rows that exist (at most
+// ROWS rows, so it always fits the 32-bit size field), so rows past the end
+// read as zeros.
 template <typename T, int D, int ROWS, int NW>
 struct TileLoader {
   using F = Tile<T, D>;
@@ -118,7 +119,7 @@ struct TileLoader {
   // rows [r0, r0 + ROWS) of g (a tensor with nrows rows) into `tile`
   __device__ inline void issue(T* tile, const T* g, int r0, int nrows) const {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer-resource type exists only in the device pass
-    const int left = nrows - r0;
+    const int left = min(nrows - r0, ROWS);
     const uint32_t bytes = left > 0 ? (uint32_t)left * (uint32_t)(D * sizeof(T)) : 0u;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(g + (int64_t)r0 * D), (short)0, (int)bytes, 0x00020000);

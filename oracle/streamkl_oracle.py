@@ -135,12 +135,14 @@ def _dS(setting: int, p1, p2, logp1, logp2, kl_rows, g_rows, mask):
 
 
 def head_backward(setting: int, q1, k1, q2, k2, causal: bool, g,
-                  scale1=None, scale2=None, rows=None, block: int = 512):
+                  scale1=None, scale2=None, rows=None, block: int = 512, want_dk: bool = True):
     """Gradients of sum_i g[i] KL[i] for one head.
 
     setting 1 -> (dQ2[rows], dK2 contribution of those rows), P1 held fixed.
     setting 2 -> (dQ1[rows], dK1 contribution of those rows), P2 held fixed.
     With rows=None every row is used and dK is the full gradient.
+    want_dk=False skips the dK product and returns None in its place (for
+    key ranges whose [N_K, d] fp64 dK would not fit in memory).
     The KL used in setting 2 is recomputed here from the definition (the
     GPU path uses its stored forward value; both equal the same number).
     """
@@ -154,7 +156,7 @@ def head_backward(setting: int, q1, k1, q2, k2, causal: bool, g,
         raise ValueError("setting must be 1 or 2")
     qs, ks, ss = (q2, k2, s2) if setting == 1 else (q1, k1, s1)
     dq = np.empty((len(rows), qs.shape[1]))
-    dk = np.zeros((n_k, ks.shape[1]))
+    dk = np.zeros((n_k, ks.shape[1])) if want_dk else None
     pos = 0
     for rb in _block_rows(rows, block):
         mask = valid_mask(rb, n_q, n_k, causal)
@@ -166,7 +168,8 @@ def head_backward(setting: int, q1, k1, q2, k2, causal: bool, g,
             kl_rows = (p1 * np.where(mask, logp1 - logp2, 0.0)).sum(axis=1)
         dS = _dS(setting, p1, p2, logp1, logp2, kl_rows, g[rb], mask)
         dq[pos:pos + len(rb)] = ss * (dS @ ks)
-        dk += ss * (dS.T @ qs[rb])
+        if want_dk:
+            dk += ss * (dS.T @ qs[rb])
         pos += len(rb)
     return dq, dk
 

@@ -1,0 +1,43 @@
+"""The largest key range the boundary accepts (2^24 keys), bf16, d = 128.
+
+Each K row is 256 bytes, so the whole range is 2^32 bytes: the direct-to-LDS
+tile loaders must size their buffers by the tile, not by the rows left (a
+size of 2^32 wraps to 0 and the tile reads as zeros).  The first key tile is
+made to dominate rows 0 and 17 (keys 0-31 and 32-63 are 3x those rows'
+queries, in both models), so losing it moves their LSE by about 17.  The
+forward (split over the keys) and the dQ kernel stream every key tile; those
+rows and an ordinary one are compared with the fp64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from attention_kl_divergence_amd import streamkl as sk
+from parity import check_forward_rows, check_grad, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def test_longest_key_range(cuda_device):
+    w = workloads.Workload("nk-2^24-d128-bf16", 1, 1, 40, 1 << 24, 128, 128, "bf16", False, 0.5, False, 13)
+    print(f"generate {w.name}", flush=True)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    for q, k in ((q1, k1), (q2, k2)):
+        k[0, 0, 0:32] = (3 * q[0, 0, 0].float()).to(k.dtype)
+        k[0, 0, 32:64] = (3 * q[0, 0, 17].float()).to(k.dtype)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    print("forward", flush=True)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal)
+    print("dQ", flush=True)
+    dq, _ = sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g, bwd_mode=sk.BWD_DQ_ONLY)
+    torch.cuda.synchronize()
+    rows = np.array([0, 17, 39])
+    print("oracle", flush=True)
+    hi = [to_np(t[0, 0]) for t in (q1, k1, q2, k2)]
+    ref = oracle.head_forward(*hi, w.causal, rows=rows, block=4)
+    check_forward_rows(w.name, to_np(kl[0, 0])[rows], to_np(l1[0, 0])[rows], to_np(l2[0, 0])[rows], ref,
+                       w.torch_dtype)
+    rdq, _ = oracle.head_backward(1, *hi, w.causal, to_np(g[0, 0]), rows=rows, block=4, want_dk=False)
+    check_grad(f"{w.name} dQ", to_np(dq[0, 0])[rows], rdq)
