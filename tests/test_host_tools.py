@@ -23,6 +23,7 @@ DK = "_ZN8streamkl13bwd_dk_kernelIDF16bLi128ELi128ELi1ELb0ELi64EEEvNS_7BwdArgsE"
 DK_FUSED = "_ZN8streamkl13bwd_dk_kernelIDF16bLi128ELi128ELi1ELb1ELi64EEEvNS_7BwdArgsE"
 FWD_PP = "_ZN8streamkl13fwd_pp_kernelIDF16bLi128ELi128ELi64EEEvNS_7FwdArgsE"
 FWD = "_ZN8streamkl10fwd_kernelIDF16bLi128ELi128ELi64EEEvNS_7FwdArgsE"
+DEC = "void streamkl::fwd_decode_kernel<128, 128>(streamkl::FwdArgs)"
 
 
 def write_csv(path, counter, rows):
@@ -44,10 +45,10 @@ def test_traffic_calibration(tmp_path):
     write = tmp_path / "w.csv"
     write_csv(fetch, "FETCH_SIZE", [(1, MUL, [100.0]), (2, MUL, [262144.0, 262144.0]),
                                     (3, DK, [1000.0]), (4, DK, [3000.0]), (5, FWD_PP, [50.0]),
-                                    (6, DK_FUSED, [7.0]), (7, FWD, [9.0])])
+                                    (6, DK_FUSED, [7.0]), (7, FWD, [9.0]), (8, DEC, [11.0])])
     write_csv(write, "WRITE_SIZE", [(1, MUL, [10.0]), (2, MUL, [1048576.0]),
                                     (3, DK, [64.0]), (4, DK, [64.0]), (5, FWD_PP, [2.0]),
-                                    (6, DK_FUSED, [1.0]), (7, FWD, [3.0])])
+                                    (6, DK_FUSED, [1.0]), (7, FWD, [3.0]), (8, DEC, [5.0])])
     res, factors = profiling.traffic(str(fetch), str(write), 1024)
     assert factors["FETCH_SIZE"] == pytest.approx(2.0)
     assert factors["WRITE_SIZE"] == pytest.approx(1.0)
@@ -58,6 +59,9 @@ def test_traffic_calibration(tmp_path):
     # the fused key-outer kernel and the plain forward get their own labels
     assert res["bwd_dk_kernel<FUSED>"]["fetch_bytes"] == pytest.approx(2.0 * 7.0 * 1024)
     assert res["fwd_kernel"]["write_bytes"] == pytest.approx(3.0 * 1024)
+    # the decode forward (demangled name) is not taken for the plain forward
+    assert res["fwd_decode_kernel"]["fetch_bytes"] == pytest.approx(2.0 * 11.0 * 1024)
+    assert res["fwd_kernel"]["launches"] == 1
 
 
 def test_traffic_needs_a_reference_copy(tmp_path):
