@@ -146,6 +146,13 @@ def test_workload_8k_causal_both_settings(cuda_device):
     run_sampled(w, cuda_device, settings=(1, 2), heads=[0, 13, 31], nrows=256)
 
 
+def test_workload_8k_causal_fused_mode(cuda_device):
+    """The fused backward (dQ by fp32 atomics from the key-outer kernel) at a
+    full workload size, both settings."""
+    w = workloads.WORKLOADS["h32-n8k-d128-bf16-causal"]
+    run_sampled(w, cuda_device, settings=(1, 2), heads=[0, 31], nrows=128, mode=sk.BWD_FUSED)
+
+
 def test_workload_64k_causal_setting1(cuda_device):
     w = workloads.WORKLOADS["h32-n64k-d128-bf16-causal"]
     run_sampled(w, cuda_device, settings=(1,))
