@@ -338,6 +338,72 @@ __device__ inline void sched_mfma_lds() {
   }
 }
 // ---------------------------------------------------------------------------
+// Per-lane maxima of raw logits: chains of max(max(acc, a), b), one v_max3
+// per two values.
+template <int NKB>
+__device__ inline void fwd_tile_max(const f32x16 (&s1)[NKB], const f32x16 (&s2)[NKB], float& mx1, float& mx2) {
+  float mx1a = kNegInf, mx1b = kNegInf, mx2a = kNegInf, mx2b = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      mx1a = fmaxf(fmaxf(mx1a, s1[kb][e]), s1[kb][e + 1]);
+      mx1b = fmaxf(fmaxf(mx1b, s1[kb][e + 2]), s1[kb][e + 3]);
+      mx2a = fmaxf(fmaxf(mx2a, s2[kb][e]), s2[kb][e + 1]);
+      mx2b = fmaxf(fmaxf(mx2b, s2[kb][e + 2]), s2[kb][e + 3]);
+    }
+  mx1 = fmaxf(mx1a, mx1b);
+  mx2 = fmaxf(mx2a, mx2b);
+}
+
+// An unmasked tile's update in two halves.  fwd_pre runs where the logits
+// were computed: new offsets, rescale factors, and the logits turned in place
+// into t_t = y_t - M_t'.  fwd_post sums 2^t over the tile and folds the sums
+// into the state.  Together they equal fwd_update<false>.
+struct FwdPre {
+  float M1n, M2n, al1, al2;
+};
+template <int NKB>
+__device__ inline FwdPre fwd_pre(const RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], float c1, float c2) {
+  float mx1, mx2;
+  fwd_tile_max<NKB>(s1, s2, mx1, mx2);
+  FwdPre p;
+  p.M1n = fmaxf(st.M1, mx1 * c1);
+  p.M2n = fmaxf(st.M2, mx2 * c2);
+  p.al1 = exp2_fast(st.M1 - p.M1n);
+  p.al2 = exp2_fast(st.M2 - p.M2n);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s1[kb][e] = fmaf(s1[kb][e], c1, -p.M1n);
+      s2[kb][e] = fmaf(s2[kb][e], c2, -p.M2n);
+    }
+  return p;
+}
+template <int NKB>
+__device__ inline void fwd_post(RowState& st, const f32x16 (&t1)[NKB], const f32x16 (&t2)[NKB], const FwdPre& p) {
+  float tl1[4] = {0.f, 0.f, 0.f, 0.f}, tl2[4] = {0.f, 0.f, 0.f, 0.f}, tA[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p1 = exp2_fast(t1[kb][e]);
+      const float p2 = exp2_fast(t2[kb][e]);
+      tl1[e & 3] += p1;
+      tl2[e & 3] += p2;
+      tA[e & 3] = fmaf(p1, t1[kb][e] - t2[kb][e], tA[e & 3]);
+    }
+  const float sl1 = (tl1[0] + tl1[1]) + (tl1[2] + tl1[3]);
+  const float sl2 = (tl2[0] + tl2[1]) + (tl2[2] + tl2[3]);
+  const float sA = (tA[0] + tA[1]) + (tA[2] + tA[3]);
+  st.l1 = fmaf(p.al1, st.l1, sl1);
+  st.l2 = fmaf(p.al2, st.l2, sl2);
+  st.A = fmaf(p.al1, st.A, fmaf(p.M1n - p.M2n, sl1, sA));
+  st.M1 = p.M1n;
+  st.M2 = p.M2n;
+}
+
 // Forward online update of one lane's running state with NKB 32-key blocks of
 // raw dot products (s1, s2).  MASK: keys past `lim` are excluded.
 template <bool MASK, int NKB>
@@ -353,19 +419,10 @@ __device__ inline void fwd_update(RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[
         s2[kb][e] = out ? kNegInf : s2[kb][e];
       }
   }
-  // running maxima as chains of max(max(acc, a), b): one v_max3 per two values
-  float mx1a = kNegInf, mx1b = kNegInf, mx2a = kNegInf, mx2b = kNegInf;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int e = 0; e < 16; e += 4) {
-      mx1a = fmaxf(fmaxf(mx1a, s1[kb][e]), s1[kb][e + 1]);
-      mx1b = fmaxf(fmaxf(mx1b, s1[kb][e + 2]), s1[kb][e + 3]);
-      mx2a = fmaxf(fmaxf(mx2a, s2[kb][e]), s2[kb][e + 1]);
-      mx2b = fmaxf(fmaxf(mx2b, s2[kb][e + 2]), s2[kb][e + 3]);
-    }
-  const float M1n = fmaxf(st.M1, fmaxf(mx1a, mx1b) * c1);
-  const float M2n = fmaxf(st.M2, fmaxf(mx2a, mx2b) * c2);
+  float mx1, mx2;
+  fwd_tile_max<NKB>(s1, s2, mx1, mx2);
+  const float M1n = fmaxf(st.M1, mx1 * c1);
+  const float M2n = fmaxf(st.M2, mx2 * c2);
   const float m1 = MASK ? finite_or_zero(M1n) : M1n;
   const float m2 = MASK ? finite_or_zero(M2n) : M2n;
   const float al1 = exp2_fast(st.M1 - m1), al2 = exp2_fast(st.M2 - m2);
@@ -731,12 +788,22 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const float c1 = a.c1, c2 = a.c2;
   const int lim_row = a.causal ? min(kend - 1, qrow + off) : kend - 1;
   f32x16 s1[NKB], s2[NKB];
+  FwdPre pre = {0.f, 0.f, 0.f, 0.f};
 
+  // An unmasked tile's update is split: the logits phase, whose wave's VALU
+  // is mostly idle, takes the maxima, offsets and t = y - M (fwd_pre); the
+  // update phase, the longer one, keeps the exponentials and sums (fwd_post).
+  // Forward 37.1 -> 35.2 ms at 64K causal against the whole update in the
+  // update phase (36.2 ms with only the maxima moved).
+  auto masked = [&](int k0) { return (k0 + BK > kend) || (a.causal && k0 + BK - 1 > q0 + off); };
+  auto logits = [&](const T* sK1, const T* sK2, int k0) {
+    fwd_logits<T, D1, D2, NKB>(s1, s2, sK1, sK2, qf1, qf2, col, grp);
+    if (!masked(k0)) pre = fwd_pre<NKB>(st, s1, s2, c1, c2);
+  };
   auto update = [&](int k0) {
     if (!wave_rows || k0 > wave_kmax) return;
-    const bool need_mask = (k0 + BK > kend) || (a.causal && k0 + BK - 1 > q0 + off);
-    if (need_mask) fwd_update<true, NKB>(st, s1, s2, c1, c2, k0, lim_row, grp);
-    else fwd_update<false, NKB>(st, s1, s2, c1, c2, k0, 0, grp);
+    if (masked(k0)) fwd_update<true, NKB>(st, s1, s2, c1, c2, k0, lim_row, grp);
+    else fwd_post<NKB>(st, s1, s2, pre);
   };
 
   for (int t = 0; t < ntiles; ++t) {
@@ -752,7 +819,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     const T* sK2 = sK1 + BK * D1;
     const bool active = wave_rows && k0 <= wave_kmax;
     if (group == 0) {
-      if (active) fwd_logits<T, D1, D2, NKB>(s1, s2, sK1, sK2, qf1, qf2, col, grp);
+      if (active) logits(sK1, sK2, k0);
     } else if (t > 0) {
       update(k0 - BK);
     }
@@ -760,7 +827,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     if (group == 0) {
       update(k0);
     } else if (active) {
-      fwd_logits<T, D1, D2, NKB>(s1, s2, sK1, sK2, qf1, qf2, col, grp);
+      logits(sK1, sK2, k0);
     }
   }
   if (group == 1 && ntiles > 0) update((ntiles - 1) * BK);
