@@ -159,6 +159,70 @@ def kernel_summary(stats_csv, bench_log, workload, command):
     return "\n".join(lines)
 
 
+# SQ counter sets for `counters`, one rocprofv3 --pmc pass each (at most 8 SQ
+# counters per pass)
+COUNTER_SETS = [
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
+    "SQ_VALU_MFMA_BUSY_CYCLES",
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_VALU_MFMA_COEXEC_CYCLES "
+    "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_INSTS_VALU_TRANS_F32",
+]
+
+
+def _gpu_topology(agent_csv):
+    for r in _rows(agent_csv):
+        if r["Agent_Type"] == "GPU":
+            cus = int(r["Cu_Count"])
+            return {"cus": cus, "simds": cus * int(r["Simd_Per_Cu"]), "ses": int(r["Num_Shader_Banks"])}
+    raise SystemExit(f"no GPU agent in {agent_csv}")
+
+
+def counters(csvs, agent_csv):
+    """Per-kernel SQ counter averages per dispatch and derived utilisations.
+
+    SQ_BUSY_CYCLES sums over shader engines, so /SEs is the dispatch length in
+    cycles (T).  SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES sum
+    over SIMDs: /SIMDs/T is the fraction of the dispatch the matrix cores are
+    busy, resp. busy while the VALU also issues.  VALU issue rate: non-MFMA
+    VALU instructions per SIMD per cycle (a wave64 fp32 VALU op occupies a
+    SIMD for at least 4 cycles, so 0.25 is the ceiling)."""
+    topo = _gpu_topology(agent_csv)
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for path in csvs:
+        for r in _rows(path):
+            lab = _label(r["Kernel_Name"])
+            if not lab:
+                continue
+            agg[lab][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[(lab, path)].add(r["Dispatch_Id"])
+    out = {}
+    for lab, c in agg.items():
+        n = {}
+        for path in csvs:
+            if disp.get((lab, path)):
+                n[path] = len(disp[(lab, path)])
+        # every pass ran the same launches; average per dispatch of its own pass
+        per = {}
+        for name, v in c.items():
+            cnt = max(n.values()) if n else 1
+            per[name] = v / cnt
+        t = per.get("SQ_BUSY_CYCLES", 0.0) / topo["ses"]
+        d = {"dispatch_cycles": t}
+        if t > 0:
+            d["mfma_busy"] = per.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / topo["simds"] / t
+            d["mfma_valu_coexec"] = per.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / topo["simds"] / t
+            valu = per.get("SQ_INSTS_VALU", 0.0) - per.get("SQ_INSTS_MFMA", 0.0)
+            d["valu_issue_per_simd_cycle"] = valu / topo["simds"] / t
+        if per.get("SQ_WAVE_CYCLES"):
+            d["lds_wait_share"] = per.get("SQ_WAIT_INST_LDS", 0.0) / per["SQ_WAVE_CYCLES"]
+        for k in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+            if k in per:
+                d[k] = per[k]
+        out[lab] = d
+    return out, topo
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -175,8 +239,38 @@ def main(argv=None):
     t.add_argument("--workload", required=True)
     t.add_argument("--command", required=True, help="the commands that produced the two csv files")
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", nargs="+", required=True, help="run_counter_collection.csv of each pass")
+    c.add_argument("--agent", required=True, help="run_agent_info.csv of any pass")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
     sub.add_parser("digest")
     args = ap.parse_args(argv)
+    if args.cmd == "counters":
+        res, topo = counters(args.csv, args.agent)
+        lines = [f"# SQ counters per kernel, workload {args.workload}", "",
+                 "Commands (run from /tmp with TMPDIR=/tmp on one MI355X; one rocprofv3 --pmc pass per set):", "",
+                 "```", args.command, "```", "",
+                 f"Topology from the agent info: {topo['cus']} CUs, {topo['simds']} SIMDs, {topo['ses']} shader "
+                 "engines.  Per dispatch: T = SQ_BUSY_CYCLES / engines; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                 "SIMDs / T; co-exec = SQ_VALU_MFMA_COEXEC_CYCLES / SIMDs / T (matrix cores busy while the VALU "
+                 "issues); VALU issue = non-MFMA VALU instructions / SIMDs / T (ceiling 0.25 for fp32 wave64); "
+                 "LDS wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES.", "",
+                 "| kernel | T (cycles) | MFMA busy | co-exec | VALU issue / SIMD-cycle | LDS wait | MFMA instr | "
+                 "VALU instr | exp2 instr | LDS instr |", "|---|---|---|---|---|---|---|---|---|---|"]
+        for lab, d in sorted(res.items()):
+            f = lambda k, fmt="{:.1%}": fmt.format(d[k]) if k in d else "-"  # noqa: E731
+            lines.append(f"| {lab} | {d['dispatch_cycles']:.0f} | {f('mfma_busy')} | {f('mfma_valu_coexec')} | "
+                         f"{f('valu_issue_per_simd_cycle', '{:.3f}')} | {f('lds_wait_share')} | "
+                         f"{f('SQ_INSTS_MFMA', '{:.3g}')} | {f('SQ_INSTS_VALU', '{:.3g}')} | "
+                         f"{f('SQ_INSTS_VALU_TRANS_F32', '{:.3g}')} | {f('SQ_INSTS_LDS', '{:.3g}')} |")
+        lines += ["", "```json", json.dumps({"workload": args.workload, "source_digest": kernel_source_digest(),
+                                              "kernels": res}, indent=1), "```", ""]
+        with open(args.out, "w") as fo:
+            fo.write("\n".join(lines))
+        print(args.out)
+        return 0
     if args.cmd == "digest":
         print(kernel_source_digest())
         return 0
