@@ -109,3 +109,36 @@ def test_bench_refuses_more_than_one_gpu():
     assert p.returncode == 2
     msg = json.loads(p.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_counter_utilisations(tmp_path):
+    # 4 CUs x 4 SIMDs, 2 shader engines; one dK dispatch per pass
+    agent = tmp_path / "agent.csv"
+    with open(agent, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Agent_Type", "Cu_Count", "Simd_Per_Cu", "Num_Shader_Banks"])
+        w.writeheader()
+        w.writerow({"Agent_Type": "CPU", "Cu_Count": 0, "Simd_Per_Cu": 0, "Num_Shader_Banks": 0})
+        w.writerow({"Agent_Type": "GPU", "Cu_Count": 4, "Simd_Per_Cu": 4, "Num_Shader_Banks": 2})
+    p1 = tmp_path / "p1.csv"
+    p2 = tmp_path / "p2.csv"
+    with open(p1, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for name, v in (("SQ_BUSY_CYCLES", 2000.0), ("SQ_VALU_MFMA_BUSY_CYCLES", 8000.0), ("SQ_INSTS_MFMA", 250.0),
+                        ("SQ_INSTS_VALU", 1050.0), ("SQ_WAVE_CYCLES", 4000.0)):
+            w.writerow({k: 0 for k in FIELDS} | {"Dispatch_Id": 3, "Kernel_Name": DK, "Counter_Name": name,
+                                                 "Counter_Value": v})
+    with open(p2, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for name, v in (("SQ_VALU_MFMA_COEXEC_CYCLES", 1600.0), ("SQ_WAIT_INST_LDS", 400.0)):
+            w.writerow({k: 0 for k in FIELDS} | {"Dispatch_Id": 3, "Kernel_Name": DK, "Counter_Name": name,
+                                                 "Counter_Value": v})
+    res, topo = profiling.counters([str(p1), str(p2)], str(agent))
+    assert topo == {"cus": 4, "simds": 16, "ses": 2}
+    d = res["bwd_dk_kernel"]
+    assert d["dispatch_cycles"] == pytest.approx(1000.0)          # 2000 / 2 engines
+    assert d["mfma_busy"] == pytest.approx(0.5)                   # 8000 / 16 SIMDs / 1000
+    assert d["mfma_valu_coexec"] == pytest.approx(0.1)
+    assert d["valu_issue_per_simd_cycle"] == pytest.approx(0.05)  # (1050 - 250) / 16 / 1000
+    assert d["lds_wait_share"] == pytest.approx(0.1)
