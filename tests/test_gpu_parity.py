@@ -70,6 +70,8 @@ SMALL = [
     ("bf16-n1", "bf16", 128, 128, False, 1, 2, 1, 1),
     ("bf16-n17-c", "bf16", 128, 128, True, 1, 2, 17, 17),
     ("bf16-q1-k1000", "bf16", 128, 128, False, 1, 3, 1, 1000),
+    ("bf16-d128-nc-tall", "bf16", 128, 128, False, 1, 2, 400, 130),
+    ("f32-d128x64-nc-tall", "f32", 128, 64, False, 1, 1, 150, 40),
     # query ranges of at most 32 rows: the one-wave-per-split decode kernel
     ("bf16-dec-q16-k2000", "bf16", 128, 128, False, 1, 2, 16, 2000),
     ("bf16-dec-q32-k1500-c", "bf16", 128, 128, True, 1, 2, 32, 1500),
