@@ -120,9 +120,26 @@ DkLaunch pick_dk(int dtype, int d1, int d2) {
   return nullptr;
 }
 
+DecBwdLaunch pick_dec_bwd(int dtype, int d1, int d2) {
+#define SKL_PICK(tn, a, b) if (d1 == a && d2 == b) return launch_bwd_dec_##tn##_##a##_##b;
+  if (dtype == STREAMKL_BF16) { SKL_PICK(bf16, 64, 64) SKL_PICK(bf16, 64, 128) SKL_PICK(bf16, 128, 64) SKL_PICK(bf16, 128, 128) }
+#undef SKL_PICK
+  return nullptr;
+}
+
 // bf16 query ranges that fit one wave's 32 rows run the decode forward, in
-// which every wave is one key split.
+// which every wave is one key split, and the decode backward, in which one
+// workgroup keeps every query row.
 bool decode_shape(const streamkl_shape* s) { return s->dtype == STREAMKL_BF16 && s->n_q <= kDecRows; }
+
+// Workgroups per head of the decode backward: one per CU in all (its LDS
+// tiles allow one per CU), at most one per key tile.
+int plan_dec_bwd_splits(const streamkl_shape* s, int cus) {
+  const int64_t tiles = cdiv(s->n_k, kDecBwdTile);
+  int64_t sp = cus / (s->B * s->H);
+  if (sp > tiles) sp = tiles;
+  return (int)(sp < 1 ? 1 : sp);
+}
 
 // Key-split plan.  Split-K (Method 3 of the technical summary) is for shapes
 // whose query blocks alone cannot fill the chip.  Decode shapes: about 4
@@ -164,6 +181,9 @@ size_t ws_bytes(const streamkl_shape* s, int splits) {
 // mode cannot fill the chip (few query rows, long key ranges).
 int plan_bwd(const streamkl_shape* s, int causal, int setting, const streamkl_launch* l, int cus) {
   if (l && l->bwd_mode != STREAMKL_BWD_AUTO) return l->bwd_mode;
+  // decode shapes: the fused decode kernel reads each key tile once and adds
+  // to dQ once per wave; the separate dQ kernel would get one workgroup per head
+  if (decode_shape(s)) return STREAMKL_BWD_FUSED;
   const double ds = setting == 1 ? s->d2 : s->d1;
   const double pairs = causal ? (double)s->n_q * (s->n_q + 1) / 2 + (double)s->n_q * (s->n_k - s->n_q)
                               : (double)s->n_q * s->n_k;
@@ -334,12 +354,17 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
   const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
   if (mode == STREAMKL_BWD_FUSED) {
     const int ds = setting == 1 ? shape->d2 : shape->d1;
+    const DecBwdLaunch fd = decode_shape(shape) ? pick_dec_bwd(shape->dtype, shape->d1, shape->d2) : nullptr;
     const int64_t n4 = a.BH * a.n_q * ds / 4;
     int64_t fb = cdiv(n4, 256);
     if (fb > 65536) fb = 65536;
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)fb), dim3(256), 0, s, reinterpret_cast<float4*>(dQ), n4);
     st = hip_status(hipGetLastError());
     if (st != STREAMKL_OK) return st;
+    if (fd) {
+      a.nblk = plan_dec_bwd_splits(shape, dev.cus);
+      return hip_status(fd(a, setting, a.BH * a.nblk, s));
+    }
     a.nblk = (int)nkb;
     return hip_status(fk(a, setting, true, a.BH * nkb, s));
   }

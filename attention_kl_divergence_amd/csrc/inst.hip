@@ -1,6 +1,6 @@
 // One translation unit per (dtype, d1, d2): compiled several times with
 // -DSKL_T=<type> -DSKL_TN=<tag> -DSKL_D1=<d1> -DSKL_D2=<d2> so the kernel
-// instantiations build in parallel.  Each exports five launchers with
+// instantiations build in parallel.  Each exports six launchers with
 // C++ linkage, named launch_<kind>_<tag>_<d1>_<d2>.
 #include "kernels.hpp"
 #include "launch.hpp"
@@ -50,6 +50,19 @@ hipError_t SKL_CAT(launch_bwd_dk, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int 
     else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, false, kBwdQTile<SKL_T>>), g, b, 0, st, a);
   }
   return hipGetLastError();
+}
+
+hipError_t SKL_CAT(launch_bwd_dec, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, int64_t nblocks,
+                                                            hipStream_t st) {
+  if constexpr (sizeof(SKL_T) != 2) {
+    return hipErrorInvalidValue;  // bf16 only
+  } else {
+    if (setting == 1)
+      hipLaunchKernelGGL((bwd_decode_kernel<SKL_D1, SKL_D2, 1>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_decode_kernel<SKL_D1, SKL_D2, 2>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
 }
 
 }  // namespace streamkl

@@ -65,7 +65,7 @@ struct BwdArgs {
   float* dk;
   int64_t BH;
   int n_q, n_k;
-  int nblk;            // query blocks (dQ kernel) or key blocks (dK kernel) per head
+  int nblk;            // query blocks (dQ kernel), key blocks (dK kernel) or workgroups (decode backward) per head
   int causal;
   float c1, c2;        // scale_t * log2(e)
   float scale_s;       // scale of the model that receives gradients
@@ -1381,5 +1381,168 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
     }
 }
 
-}  // namespace streamkl
 
+// ---------------------------------------------------------------------------
+// Decode-shaped backward (at most 32 query rows, long key ranges).  Each key
+// tile is visited once, as in the fused mode of Method 2, but the query rows
+// are few enough that a workgroup keeps all of them: dK_s is written
+// directly and dQ_s is summed over the workgroup's key tiles in registers,
+// then added to the caller's cleared dQ once at the end (one fp32 atomic
+// per element and wave, instead of one per element and key block).  The
+// workgroups of a head split its key tiles between them (split-K, Method 3):
+// workgroup z takes tiles z, z + nsplit, ..., so the workgroups running at a
+// time sweep through the keys together.
+//
+// Orientation as in the decode forward: S^T = K Q^T, so an accumulator
+// column is one query row and each lane's row statistics are constants.
+// Per wave and 32-key block of a tile:
+//   dQ_s^T += K_s^T dS^T   A = K_s read down the tile's rows with the
+//                          transpose read (keys in accumulator order),
+//                          B = dS^T straight from the accumulator
+//   dK_s    = dS^T Q_s     A = dS^T read back from a wave-private LDS tile
+//                          [query][key] with the transpose read, B = Q_s
+//                          columns, held in registers for the whole kernel
+// K1 and K2 tiles (32 keys per wave) are double-buffered in LDS.
+template <int D1, int D2, int SETTING>
+__global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
+  using MF = Mfma<bf16>;
+  constexpr int NW = 4, BK = 32 * NW;
+  constexpr int DS = SETTING == 1 ? D2 : D1;
+  constexpr int S1 = D1 / 16, S2 = D2 / 16, NB = DS / 32;
+  constexpr int TS = BK * (D1 + D2);  // elements of one tile stage (K1 then K2)
+  constexpr int QE = 32 * (D1 + D2);  // Q1 and Q2, 32 rows each
+  constexpr int DSE = 32 * 32;        // one wave's dS^T tile
+  // one array: separate __shared__ objects get separate alias scopes, and the
+  // tile reads would then wait for the next tile's direct loads in flight
+  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * TS + QE + NW * DSE];
+  bf16* sQ1 = lds + 2 * TS;
+  bf16* sQ2 = sQ1 + 32 * D1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, grp = lane >> 5;
+  bf16* sdS = lds + 2 * TS + QE + wave * DSE;
+  const int64_t bh = blockIdx.x / a.nblk;
+  const int z = (int)(blockIdx.x % a.nblk);
+  const int off = a.n_k - a.n_q;
+
+  const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.n_q * D1;
+  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + bh * (int64_t)a.n_k * D1;
+  const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.n_q * D2;
+  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + bh * (int64_t)a.n_k * D2;
+
+  const int ntile = (a.n_k + BK - 1) / BK;
+  const int count = z < ntile ? (ntile - z + a.nblk - 1) / a.nblk : 0;
+  const TileLoader<bf16, D1, BK, NW> ld1(wave, lane);
+  const TileLoader<bf16, D2, BK, NW> ld2(wave, lane);
+  auto issue = [&](int t, int buf) {
+    const int k0 = (z + t * a.nblk) * BK;
+    bf16* s = lds + buf * TS;
+    ld1.issue(s, K1, k0, a.n_k);
+    ld2.issue(s + BK * D1, K2, k0, a.n_k);
+  };
+  if (count > 0) issue(0, 0);
+  dec_stage_q<D1>(sQ1, Q1, a.n_q, tid);
+  dec_stage_q<D2>(sQ2, Q2, a.n_q, tid);
+  // lane column col is query row col: its statistics are fixed for the kernel
+  const bool qv = col < a.n_q;
+  const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.n_q + col, qv);
+  const float c1 = a.c1, c2 = a.c2;
+  // last key this lane's query sees, and the last key of which every query
+  // of a wave block is visible (beyond it blocks take the element mask)
+  const int lim = a.causal ? col + off : a.n_k - 1;
+  const int mask_from = a.causal ? off : a.n_k - 1;
+  __syncthreads();
+
+  // B operand of dK_s = dS^T Q_s: Q_s columns, k = query rows in natural order
+  const bf16* sQS = SETTING == 1 ? sQ2 : sQ1;
+  bf16x8 qcol[2][NB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) qcol[h][nb] = fragcol_nat_bf16<DS>(sQS, 0, 32 * nb, h, lane);
+
+  f32x16 dqa[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) dqa[nb] = zero16();
+
+  auto tile = [&](const bf16* __restrict__ sK1, const bf16* __restrict__ sK2, const bf16* __restrict__ sQa,
+                  const bf16* __restrict__ sQb, int kw) {
+    f32x16 s1 = zero16(), s2 = zero16();
+    constexpr int SM = S1 > S2 ? S1 : S2;
+#pragma unroll
+    for (int s = 0; s < SM; ++s) {
+      if (s < S1)
+        s1 = MF::run(frag_tile<bf16, D1>(sK1, 32 * wave + col, s < S1 ? s : 0, grp),
+                     frag_tile<bf16, D1>(sQa, col, s < S1 ? s : 0, grp), s1);
+      if (s < S2)
+        s2 = MF::run(frag_tile<bf16, D2>(sK2, 32 * wave + col, s < S2 ? s : 0, grp),
+                     frag_tile<bf16, D2>(sQb, col, s < S2 ? s : 0, grp), s2);
+    }
+    // dS^T in s1 (element e: key kw + acc_row(e, grp), query col)
+    const bool need_mask = kw + 31 > mask_from;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float ds = dS_elem<SETTING>(s1[e], s2[e], c1, c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
+      if (need_mask) ds = kw + acc_row(e, grp) <= lim ? ds : 0.f;
+      s1[e] = qv ? ds : 0.f;
+    }
+    const bf16* sKS = SETTING == 1 ? sK2 : sK1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 b = frag_from_acc(s1, h, bf16());
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        dqa[nb] = MF::run(fragcol_acc_bf16<DS>(sKS, 32 * wave, 32 * nb, h, lane), b, dqa[nb]);
+    }
+    // dS^T to the wave's own [query][key] tile: 4 consecutive keys per store
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 v;
+      v[0] = (bf16)s1[4 * i]; v[1] = (bf16)s1[4 * i + 1]; v[2] = (bf16)s1[4 * i + 2]; v[3] = (bf16)s1[4 * i + 3];
+      *reinterpret_cast<bf16x4*>(sdS + Tile<bf16, 32>::off(col, 8 * i + 4 * grp)) = v;
+    }
+    // one wave writes and reads its tile; LDS serves a wave's accesses in order
+    asm volatile("" ::: "memory");
+    f32x16 dka[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) dka[nb] = zero16();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 af = fragcol_nat_bf16<32>(sdS, 0, 0, h, lane);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dka[nb] = MF::run(af, qcol[h][nb], dka[nb]);
+    }
+    float* dk = a.dk + (bh * a.n_k + kw) * (int64_t)DS + col;
+    const int kleft = a.n_k - kw;
+    if (kleft >= 32) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dk[acc_row(e, grp) * DS + 32 * nb] = dka[nb][e];
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (acc_row(e, grp) < kleft) dk[acc_row(e, grp) * DS + 32 * nb] = dka[nb][e];
+    }
+  };
+
+  for (int t = 0; t < count; ++t) {
+    wait_loads();
+    __syncthreads();
+    if (t + 1 < count) issue(t + 1, (t + 1) & 1);
+    const bf16* sK1 = lds + (t & 1) * TS;
+    const int kw = (z + t * a.nblk) * BK + 32 * wave;
+    if (kw < a.n_k) tile(sK1, sK1 + BK * D1, sQ1, sQ2, kw);
+  }
+
+  if (qv) {
+    float* dq = a.dq + (bh * a.n_q + col) * (int64_t)DS;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) atomicAdd(dq + 32 * nb + acc_row(e, grp), dqa[nb][e]);
+  }
+}
+
+}  // namespace streamkl

@@ -22,19 +22,22 @@ constexpr int kDecBlock = 32;     // key rows per decode-forward block
 constexpr int kBwdQRows = 128;    // query rows per dQ workgroup
 constexpr int kBwdKeyTile = 64;   // key rows per dQ-kernel LDS tile
 constexpr int kBwdKRows = 128;    // key rows per dK workgroup (4 waves x 32)
+constexpr int kDecBwdTile = 128;  // key rows per tile of the decode backward (4 waves x 32)
 // query rows per LDS tile of the dK kernel (fp32 tiles are twice as large)
 template <typename T> constexpr int kBwdQTile = sizeof(T) == 2 ? 64 : 32;
 
 using FwdLaunch = hipError_t (*)(const FwdArgs&, int64_t, hipStream_t);
 using DqLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t);
 using DkLaunch = hipError_t (*)(const BwdArgs&, int, bool, int64_t, hipStream_t);
+using DecBwdLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t);
 
 #define SKL_DECL(tn, d1, d2)                                                                   \
   hipError_t launch_fwd_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);              \
   hipError_t launch_fwd_pp_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);           \
   hipError_t launch_fwd_dec_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);          \
   hipError_t launch_bwd_dq_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t);      \
-  hipError_t launch_bwd_dk_##tn##_##d1##_##d2(const BwdArgs&, int, bool, int64_t, hipStream_t);
+  hipError_t launch_bwd_dk_##tn##_##d1##_##d2(const BwdArgs&, int, bool, int64_t, hipStream_t);     \
+  hipError_t launch_bwd_dec_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t);
 SKL_DECL(f32, 64, 64)
 SKL_DECL(f32, 64, 128)
 SKL_DECL(f32, 128, 64)

@@ -51,10 +51,12 @@ def pairs_of(w):
     return w.B * w.H * (n_q * (n_q + 1) // 2 + n_q * (n_k - n_q))
 
 
-def cpu_baseline(w, rows_wanted):
+def cpu_baseline(w, rows_wanted, head_bytes=None):
     """The fp64 oracle on the host: forward + setting-1 backward for a bounded
     sample (the last rows of head 0, which see the full key range), reported
-    as algorithmic TFLOP/s like the GPU value."""
+    as algorithmic TFLOP/s like the GPU value.  With head_bytes (the
+    algorithmic HBM bytes of one head's step, for the bandwidth-bound decode
+    shapes) the sample must be whole heads and the rate is in GB/s."""
     import numpy as np
     import torch
     import oracle
@@ -78,6 +80,12 @@ def cpu_baseline(w, rows_wanted):
     vis = oracle.valid_mask(rows, w.n_q, w.n_k, w.causal).sum()
     qk = 2 * (w.d1 + w.d2)
     flops = float(vis) * (qk + sum(qk + 4 * (w.d2 if st == 1 else w.d1) for st in w.settings))
+    if head_bytes is not None and len(rows) == w.n_q:
+        return {"value": head_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+                "seconds": dt,
+                "sample": "numpy fp64 oracle, forward" + "".join(f" + setting-{st} backward" for st in w.settings)
+                          + f" of one whole head ({w.n_q} query rows over {w.n_k} keys), rated by that head's"
+                          " algorithmic HBM bytes"}
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": dt,
             "sample": f"numpy fp64 oracle, forward" + "".join(f" + setting-{st} backward" for st in w.settings)
@@ -184,17 +192,31 @@ def main():
         fwd_kernel = "fwd_pp_kernel"
     else:
         fwd_kernel = "fwd_kernel"
+    # decode shapes (bf16, at most 32 query rows): the split-K forward and the
+    # decode backward, both bound by HBM bandwidth
+    decode = w.dtype == "bf16" and w.n_q <= 32
     kernel_names = {"fwd": fwd_kernel}
     for setting in w.settings:
-        kernel_names[f"bwd{setting}_fused"] = "bwd_dk_kernel<FUSED>"
+        kernel_names[f"bwd{setting}_fused"] = "bwd_decode_kernel" if decode else "bwd_dk_kernel<FUSED>"
         kernel_names[f"bwd{setting}_dk"] = "bwd_dk_kernel"
         kernel_names[f"bwd{setting}_dq"] = "bwd_dq_kernel"
-    decode = not w.settings and w.n_q <= 16
+    # algorithmic HBM bytes of each call: every input read once, every output
+    # written once (the backward reads K1, K2, Q1, Q2 and four row vectors and
+    # writes dQ_s and dK_s in fp32)
+    nbytes = {"fwd": fwd_bytes}
+    for setting in w.settings:
+        ds = w.d2 if setting == 1 else w.d1
+        b = w.B * w.H * ((w.n_q + w.n_k) * (w.d1 + w.d2) * esz + 16 * w.n_q + (w.n_q + w.n_k) * ds * 4)
+        nbytes[f"bwd{setting}_fused"] = b
     if decode:
-        ach = fwd_bytes / (per_call["fwd"] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": kernel_names["fwd"] + (" + splitk_merge_kernel" if splits > 1 else ""),
+        dname = max((n for n, _ in calls), key=lambda n: per_call[n])
+        ach = nbytes[dname] / (per_call[dname] * 1e-3) / 1e9
+        kn = kernel_names[dname]
+        if dname == "fwd" and splits > 1:
+            kn += " + splitk_merge_kernel"
+        roof = {"bound": "hbm", "kernel": kn,
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": None, "avg_ms": round(per_call["fwd"], 4)}
+                "traffic": None, "avg_ms": round(per_call[dname], 4)}
     else:
         ach = credit[dom] / (per_call[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": kernel_names[dom], "achieved": round(ach, 2), "peak": peak,
@@ -216,8 +238,9 @@ def main():
     headline = w.name == "h32-n64k-d128-bf16-causal"
     out = {
         "metric": ("attn-KL fwd/bwd TFLOP/s + % bf16 MFMA peak, H32 d128 causal 64K" if headline
-                   else ("attn-KL split-K forward HBM GB/s" if decode else "attn-KL fwd/bwd TFLOP/s")),
-        "value": round(fwd_bytes / (ms_step * 1e-3) / 1e9, 1) if decode else round(value, 2),
+                   else (("attn-KL decode forward + backward HBM GB/s" if w.settings
+                          else "attn-KL split-K forward HBM GB/s") if decode else "attn-KL fwd/bwd TFLOP/s")),
+        "value": round(sum(nbytes[n] for n, _ in calls) / (ms_step * 1e-3) / 1e9, 1) if decode else round(value, 2),
         "unit": "GB/s" if decode else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -258,7 +281,8 @@ def main():
         out["alt_bwd_ms"] = alt
     if not args.no_cpu_baseline:
         # about 4e8 visible pairs of oracle work (10-20 s on the host) at most
-        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, max(1, int(4e8 // w.n_k))))
+        hb = sum(nbytes[n] for n, _ in calls) / (w.B * w.H) if decode else None
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, max(1, int(4e8 // w.n_k))), hb)
     print(json.dumps(out))
     return 0
 

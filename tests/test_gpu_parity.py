@@ -77,6 +77,11 @@ SMALL = [
     ("bf16-dec-q32-k1500-c", "bf16", 128, 128, True, 1, 2, 32, 1500),
     ("bf16-dec-d128x64-q5-k777-c", "bf16", 128, 64, True, 1, 2, 5, 777),
     ("bf16-dec-d64x128-q31-k300", "bf16", 64, 128, False, 2, 1, 31, 300),
+    # decode backward with several key tiles per workgroup: 8 workgroups per
+    # head at 32 heads (5 tiles each, ragged tail), and one workgroup per head
+    # at 256 heads (24 tiles, causal)
+    ("bf16-dec-h32-q16-k5000", "bf16", 128, 128, False, 1, 32, 16, 5000),
+    ("bf16-dec-b4h64-q7-k3000-c", "bf16", 128, 128, True, 4, 64, 7, 3000),
 ]
 
 
@@ -187,6 +192,34 @@ def test_workload_decode_splitk(name, cuda_device):
     # the split count changes only fp32 rounding
     for sp in (1, 2, 7, 64):
         assert np.abs(res[sp][0] - res[0][0]).max() < 1e-4
+
+
+@pytest.mark.parametrize("name", ["decode-bwd-h32-q1-k512k-d128-bf16", "decode-bwd-h32-q16-k512k-d128-bf16"])
+def test_workload_decode_backward(name, cuda_device):
+    """Decode-shaped backward at full size, both settings, in the launch
+    configuration the benchmark uses (the decode backward kernel: every key
+    tile once, dQ summed per workgroup).  Two heads are compared with the
+    oracle on every query row and every key's dK."""
+    w = workloads.WORKLOADS[name]
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    shp = sk.shape_of(q1, k1, q2, k2)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal)
+    grads = {}
+    for s in (1, 2):
+        assert sk.bwd_plan(shp, w.causal, s) == sk.BWD_FUSED
+        _say(f"bwd {name} setting {s}")
+        dq, dk = sk.streamkl_bwd(s, q1, k1, q2, k2, w.causal, kl, l1, l2, g)
+        torch.cuda.synchronize()
+        grads[s] = (dq, dk)
+    gn = to_np(g)
+    for h in (0, w.H - 1):
+        hi = head_inputs(q1, k1, q2, k2, 0, h)
+        for s in (1, 2):
+            _say(f"oracle {name} head {h} setting {s}")
+            rdq, rdk = oracle.head_backward(s, *hi, w.causal, gn[0, h], block=16)
+            check_grad(f"{name} h{h} s{s} dQ", to_np(grads[s][0][0, h]), rdq)
+            check_grad(f"{name} h{h} s{s} dK", to_np(grads[s][1][0, h]), rdk)
 
 
 def test_workload_512k_two_head_dims_setting2(cuda_device):

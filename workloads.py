@@ -55,6 +55,9 @@ WORKLOADS = {
         Workload("decode-h32-q16-k128k-d128-bf16", 1, 32, 16, 131072, 128, 128, "bf16", False, 0.5, False, 4, ()),
         Workload("decode-h32-q1-k512k-d128-bf16", 1, 32, 1, 524288, 128, 128, "bf16", False, 0.5, False, 4, ()),
         Workload("decode-h32-q16-k512k-d128-bf16", 1, 32, 16, 524288, 128, 128, "bf16", False, 0.5, False, 4, ()),
+        # the decode-shaped forward followed by the backward of one setting
+        Workload("decode-bwd-h32-q1-k512k-d128-bf16", 1, 32, 1, 524288, 128, 128, "bf16", False, 0.5, False, 4, (1,)),
+        Workload("decode-bwd-h32-q16-k512k-d128-bf16", 1, 32, 16, 524288, 128, 128, "bf16", False, 0.5, False, 4, (1,)),
         Workload("h32-n512k-d128x64-bf16-causal", 1, 32, 524288, 524288, 128, 64, "bf16", True, 0.0, True, 5, (2,)),
     ]
 }
