@@ -40,6 +40,7 @@ KERNELS = [
     ("bwd_dk_kernel", r"bwd_dk_kernel(I.*Lb0E|<[^>]*false)"),
     ("bwd_dk_kernel<FUSED>", r"bwd_dk_kernel(I.*Lb1E|<[^>]*true)"),
     ("bwd_dq_kernel", r"bwd_dq_kernel"),
+    ("bwd_decode_kernel", r"bwd_decode_kernel"),
     ("splitk_merge_kernel", r"splitk_merge_kernel"),
 ]
 # the reference copy: torch.mul(src, 1.0, out=dst), the last such dispatch
