@@ -61,7 +61,9 @@ typedef enum { STREAMKL_F32 = 0, STREAMKL_BF16 = 1 } streamkl_dtype;
 
 typedef enum {
   STREAMKL_BWD_AUTO = 0,     /* choose by the cost model of streamkl_bwd_plan */
-  STREAMKL_BWD_FUSED = 1,    /* one kernel per key block, dQ by fp32 atomics */
+  STREAMKL_BWD_FUSED = 1,    /* one kernel visits each key tile once, dQ by fp32 atomics; bf16 with
+                                n_q <= 32: one workgroup keeps every query row, sums dQ over its key
+                                tiles and adds it once (the auto choice for those shapes) */
   STREAMKL_BWD_SEPARATE = 2, /* a key-outer dK kernel, then a query-outer dQ kernel */
   STREAMKL_BWD_DK_ONLY = 3,  /* only the key-outer dK kernel; dQ is not touched (may be NULL) */
   STREAMKL_BWD_DQ_ONLY = 4   /* only the query-outer dQ kernel; dK is not touched (may be NULL) */
