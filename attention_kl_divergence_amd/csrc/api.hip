@@ -339,7 +339,7 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
   if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
   const int mode = plan_bwd(shape, causal, setting, launch, dev.cus);
 
-  BwdArgs a;
+  BwdArgs a = {};
   a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
   a.kl = kl; a.lse1 = lse1; a.lse2 = lse2; a.g = d_kl;
   a.dq = dQ; a.dk = dK;
@@ -376,6 +376,69 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
   if (mode == STREAMKL_BWD_DK_ONLY) return STREAMKL_OK;
   a.nblk = (int)nqb;
   return hip_status(fq(a, setting, a.BH * nqb, s));
+}
+
+streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                                   float scale1, float scale2, const float* kl, const float* lse1, const float* lse2,
+                                   const float* d_kl, float* dQ1, float* dK1, float* dQ2, float* dK2,
+                                   const streamkl_shape* shape, const streamkl_launch* launch, void* stream) {
+  streamkl_status st = check_shape(shape, causal);
+  if (st != STREAMKL_OK) return st;
+  if (launch && (launch->num_splits < 0 || launch->bwd_mode < 0 || launch->bwd_mode > 4)) return STREAMKL_ERR_INVALID;
+  const int req = launch ? launch->bwd_mode : STREAMKL_BWD_AUTO;
+  const bool need_dq = req != STREAMKL_BWD_DK_ONLY, need_dk = req != STREAMKL_BWD_DQ_ONLY;
+  if (!Q1 || !K1 || !Q2 || !K2 || !kl || !lse1 || !lse2 || !d_kl) return STREAMKL_ERR_INVALID;
+  if ((need_dq && (!dQ1 || !dQ2)) || (need_dk && (!dK1 || !dK2))) return STREAMKL_ERR_INVALID;
+  if (!aligned(Q1, 16) || !aligned(K1, 16) || !aligned(Q2, 16) || !aligned(K2, 16)) return STREAMKL_ERR_INVALID;
+  if (!aligned(kl, 4) || !aligned(lse1, 4) || !aligned(lse2, 4) || !aligned(d_kl, 4)) return STREAMKL_ERR_INVALID;
+  if ((dQ1 && !aligned(dQ1, 16)) || (dQ2 && !aligned(dQ2, 16)) || (dK1 && !aligned(dK1, 4)) ||
+      (dK2 && !aligned(dK2, 4)))
+    return STREAMKL_ERR_INVALID;
+  if (!(scale1 == scale1) || !(scale2 == scale2)) return STREAMKL_ERR_INVALID;
+  DeviceInfo dev;
+  st = device_info(&dev);
+  if (st != STREAMKL_OK) return st;
+  const int mode = plan_bwd(shape, causal, 1, launch, dev.cus);
+  if (shape->dtype != STREAMKL_BF16 || mode == STREAMKL_BWD_FUSED) {
+    // one pass per setting (every argument above is what each pass checks)
+    st = streamkl_bwd(2, Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ1, dK1, shape, launch, stream);
+    if (st != STREAMKL_OK) return st;
+    return streamkl_bwd(1, Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ2, dK2, shape, launch,
+                        stream);
+  }
+  DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
+  DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
+  if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
+
+  BwdArgs a = {};
+  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
+  a.kl = kl; a.lse1 = lse1; a.lse2 = lse2; a.g = d_kl;
+  a.dk = dK1; a.dk2 = dK2;
+  a.BH = shape->B * shape->H;
+  a.n_q = (int)shape->n_q;
+  a.n_k = (int)shape->n_k;
+  a.causal = causal ? 1 : 0;
+  a.c1 = log2e_scale(scale1, shape->d1);
+  a.c2 = log2e_scale(scale2, shape->d2);
+  a.scale_s = plain_scale(scale1, shape->d1);
+  a.scale_s2 = plain_scale(scale2, shape->d2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
+  if (mode != STREAMKL_BWD_DQ_ONLY) {
+    a.nblk = (int)nkb;
+    st = hip_status(fk(a, 3, false, a.BH * nkb, s));
+    if (st != STREAMKL_OK || mode == STREAMKL_BWD_DK_ONLY) return st;
+  }
+  // dQ1 and dQ2: the query-outer kernel once per setting (one kernel holding
+  // both accumulators needs more registers than two waves per SIMD allow, and
+  // measured slower than these two)
+  a.nblk = (int)nqb;
+  a.dq = dQ1;
+  st = hip_status(fq(a, 2, a.BH * nqb, s));
+  if (st != STREAMKL_OK) return st;
+  a.dq = dQ2;
+  a.scale_s = a.scale_s2;
+  return hip_status(fq(a, 1, a.BH * nqb, s));
 }
 
 }  // extern "C"

@@ -10,6 +10,23 @@
 
 namespace streamkl {
 
+// The joint dK kernel (setting 3) exists for bf16 only and has no fused
+// form; a template, so the fp32 kernel is never instantiated.  Internal
+// linkage and the head dims as parameters: every translation unit defines its
+// own.
+namespace {
+template <typename T, int D1, int D2>
+hipError_t launch_joint_dk(const BwdArgs& a, dim3 g, dim3 b, hipStream_t st, bool fused) {
+  if constexpr (sizeof(T) != 2) {
+    return hipErrorInvalidValue;
+  } else {
+    if (fused) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dk_kernel<T, D1, D2, 3, false, kBwdQTile<T>>), g, b, 0, st, a);
+    return hipGetLastError();
+  }
+}
+}  // namespace
+
 hipError_t SKL_CAT(launch_fwd, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
   hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
   return hipGetLastError();
@@ -32,10 +49,10 @@ hipError_t SKL_CAT(launch_fwd_dec, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int
 
 hipError_t SKL_CAT(launch_bwd_dq, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, int64_t nblocks,
                                                            hipStream_t st) {
-  if (setting == 1)
-    hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 1, kBwdKeyTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 2, kBwdKeyTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  const dim3 g((unsigned)nblocks), b(256);
+  if (setting == 1) hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 1, kBwdKeyTile>), g, b, 0, st, a);
+  else if (setting == 2) hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 2, kBwdKeyTile>), g, b, 0, st, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -45,9 +62,11 @@ hipError_t SKL_CAT(launch_bwd_dk, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int 
   if (setting == 1) {
     if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, true, kBwdQTile<SKL_T>>), g, b, 0, st, a);
     else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, false, kBwdQTile<SKL_T>>), g, b, 0, st, a);
-  } else {
+  } else if (setting == 2) {
     if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, true, kBwdQTile<SKL_T>>), g, b, 0, st, a);
     else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, false, kBwdQTile<SKL_T>>), g, b, 0, st, a);
+  } else {
+    return launch_joint_dk<SKL_T, SKL_D1, SKL_D2>(a, g, b, st, fused);
   }
   return hipGetLastError();
 }

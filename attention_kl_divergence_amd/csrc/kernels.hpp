@@ -61,14 +61,16 @@ struct BwdArgs {
   const float* lse1;
   const float* lse2;
   const float* g;
-  float* dq;
-  float* dk;
+  float* dq;           // setting 1: dQ2; setting 2: dQ1
+  float* dk;           // setting 1: dK2; settings 2 and 3 (joint): dK1
+  float* dk2;          // joint: dK2
   int64_t BH;
   int n_q, n_k;
   int nblk;            // query blocks (dQ kernel), key blocks (dK kernel) or workgroups (decode backward) per head
   int causal;
   float c1, c2;        // scale_t * log2(e)
-  float scale_s;       // scale of the model that receives gradients
+  float scale_s;       // scale of the model that receives gradients (joint: model 1)
+  float scale_s2;      // joint: scale of model 2
 };
 
 typedef __bf16 bf16x4_lds __attribute__((ext_vector_type(4)));
@@ -860,13 +862,17 @@ __device__ inline RawRowGrad load_rowgrad_raw(const BwdArgs& a, int64_t r, bool 
   o.lse1 = a.lse1[r];
   o.lse2 = a.lse2[r];
   o.g = a.g[r];
-  if constexpr (SETTING == 2) o.kl = a.kl[r];
+  if constexpr (SETTING >= 2) o.kl = a.kl[r];
   return o;
 }
 
 // Setting 1 folds |gs| into the exponent offsets: L_t = LSE_t log2(e) -
 // log2|gs|, so exp2(y_t - L_t) is |gs| P_t and gs is replaced by its sign
 // (a zero gs gives +inf offsets and an exactly zero dS row).
+//
+// Joint (SETTING 3, gradients to both models): the offsets are not folded;
+// gs = g * scale_2 for dS2 = gs (P2 - P1), and a, b come from g * scale_1
+// for dS1.
 template <int SETTING>
 __device__ inline RowGrad scale_rowgrad(const BwdArgs& a, const RawRowGrad& w) {
   RowGrad o;
@@ -884,6 +890,7 @@ __device__ inline RowGrad scale_rowgrad(const BwdArgs& a, const RawRowGrad& w) {
   } else {
     o.a = gs * kLn2;
     o.b = gs * w.kl;
+    if constexpr (SETTING == 3) o.gs = w.g * a.scale_s2;
   }
   return o;
 }
@@ -915,6 +922,18 @@ template <int SETTING>
 __device__ inline float dS_elem_row(float s1, float s2, float c1, float c2, const RowGrad& rg) {
   if constexpr (SETTING == 1) return exp2_fast(fmaf(s2, c2, -rg.L2)) - exp2_fast(fmaf(s1, c1, -rg.L1));
   else return dS_elem<SETTING>(s1, s2, c1, c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
+}
+
+// Joint: dS1 (setting 2) and dS2 (setting 1) of one element from the raw
+// dot products, sharing P1 (see RowGrad).
+__device__ inline void dS_joint(float s1, float s2, float c1, float c2, float L1, float L2, float gs, float ra,
+                                float rb, float& ds1, float& ds2) {
+  const float t1 = fmaf(s1, c1, -L1);
+  const float t2 = fmaf(s2, c2, -L2);
+  const float p1 = exp2_fast(t1);
+  const float p2 = exp2_fast(t2);
+  ds1 = p1 * fmaf(ra, t1 - t2, -rb);
+  ds2 = gs * (p2 - p1);
 }
 
 
@@ -954,6 +973,34 @@ __device__ inline void dS_rows_keyouter(f32x16& s1, const f32x16& s2, const floa
         ds = ((q >= qlo) & (q < n_q)) ? ds : 0.f;
       }
       s1[e] = ds;
+    }
+  }
+}
+
+// Joint version: dS1 overwrites s1 and dS2 overwrites s2 (stats L1, L2, gs,
+// a, b per query).
+template <bool MASK, int BQ>
+__device__ inline void dS_rows_keyouter_joint(f32x16& s1, f32x16& s2, const float* st, int ql0, int qb0, int grp,
+                                              float c1, float c2, int qlo, int n_q, int lane_off) {
+  auto at = [&](int k, int i) {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(st + k * BQ + ql0 + 8 * i) + lane_off);
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 L1 = at(0, i), L2 = at(1, i), GS = at(2, i), RA = at(3, i), RB = at(4, i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * i + j;
+      float d1, d2;
+      dS_joint(s1[e], s2[e], c1, c2, L1[j], L2[j], GS[j], RA[j], RB[j], d1, d2);
+      if constexpr (MASK) {
+        const int q = qb0 + 8 * i + 4 * grp + j;
+        const bool v = (q >= qlo) & (q < n_q);
+        d1 = v ? d1 : 0.f;
+        d2 = v ? d2 : 0.f;
+      }
+      s1[e] = d1;
+      s2[e] = d2;
     }
   }
 }
@@ -1116,16 +1163,20 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 // is read down the query rows of its tile.  FUSED additionally forms dQ_s for
 // every query tile from the same dS (staged in LDS as [key][query]) and adds it
 // to global dQ_s with fp32 atomics, so each query-key pair is visited once.
+// SETTING 3 (joint, not fused) forms dS1 and dS2 from the same logits and
+// accumulates dK1 (dk) and dK2 (dk2).
 template <typename T, int D1, int D2, int SETTING, bool FUSED, int BQ>
 __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
+  constexpr bool JOINT = SETTING == 3;
+  static_assert(!(JOINT && FUSED), "the joint backward has no fused form");
   constexpr int NW = 4, BKW = 32 * NW;
   constexpr int DS = SETTING == 1 ? D2 : D1;
   constexpr int S1 = D1 / MF::KSTEP, S2 = D2 / MF::KSTEP;
-  constexpr int NB = DS / 32, HS = 32 / MF::KSTEP, NQB = BQ / 32, HK = BKW / MF::KSTEP;
+  constexpr int NB = DS / 32, NB2 = D2 / 32, HS = 32 / MF::KSTEP, NQB = BQ / 32, HK = BKW / MF::KSTEP;
   constexpr int TS = BQ * (D1 + D2);
-  constexpr int NSTAT = SETTING == 2 ? 5 : 3;
+  constexpr int NSTAT = SETTING >= 2 ? 5 : 3;
   // One LDS array holds the two tile buffers, the dS^T staging tile (FUSED)
   // and the two per-query stats buffers: separate __shared__ objects would
   // get distinct alias scopes, and then every tile read would be made to wait
@@ -1178,7 +1229,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
       sstat[buf][0][tid] = rg.L1;
       sstat[buf][1][tid] = rg.L2;
       sstat[buf][2][tid] = rg.gs;
-      if constexpr (SETTING == 2) {
+      if constexpr (SETTING >= 2) {
         sstat[buf][3][tid] = rg.a;
         sstat[buf][4][tid] = rg.b;
       }
@@ -1225,9 +1276,11 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
     }
   }
 
-  f32x16 dka[NB];
+  f32x16 dka[NB], dka2[JOINT ? NB2 : 1];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dka[nb] = zero16();
+#pragma unroll
+  for (int nb = 0; nb < (JOINT ? NB2 : 1); ++nb) dka2[nb] = zero16();
   const bool wave_has_keys = kwave < a.n_k;
   // queries that see this lane's key: [qlo, n_q)
   const int qlo = kv ? (a.causal ? krow - off : 0) : 0x3fffffff;
@@ -1238,6 +1291,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   using RF1 = std::conditional_t<BF, RowFragOffsets<D1, S1>, NoOffsets>;
   using RF2 = std::conditional_t<BF, RowFragOffsets<D2, S2>, NoOffsets>;
   using CF = std::conditional_t<BF, ColFragOffsets<DS, NB>, NoOffsets>;
+  using CF2 = std::conditional_t<BF && JOINT, ColFragOffsets<D2, NB2>, NoOffsets>;
   RF1 rf1(col, grp);
   // per-lane byte offset of the stats reads (16 * grp), kept opaque like
   // the offset tables so each stats read is this register plus an immediate
@@ -1256,9 +1310,14 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
     else return frag_tile<T, D2>(tile, 32 * blk + col, s, grp);
   };
   CF cf(lane);
+  CF2 cf2(lane);
   auto colop = [&](const T* tile, int blk, int nb, int h) -> frag {
     if constexpr (BF) return cf.read(tile, blk, nb, h);
     else return fragcol_acc<T, DS>(tile, 32 * blk, 32 * nb, h, lane);
+  };
+  auto colop2 = [&](const T* tile, int blk, int nb, int h) -> frag {
+    if constexpr (BF && JOINT) return cf2.read(tile, blk, nb, h);
+    else return fragcol_acc<T, D2>(tile, 32 * blk, 32 * nb, h, lane);
   };
 
   // One query tile.  P is the tile's buffer (t & 1): tiles alternate between
@@ -1299,6 +1358,21 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
         }
         sched_mfma_lds<S1 + S2, 1, 4>();
         const bool need_mask = (qb0 + 32 > a.n_q) || (kwave + 32 > a.n_k) || (a.causal && kwave + 31 > qb0 + off);
+        if constexpr (JOINT) {
+          if (need_mask) dS_rows_keyouter_joint<true, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q, stat_off);
+          else dS_rows_keyouter_joint<false, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q, stat_off);
+#pragma unroll
+          for (int h = 0; h < HS; ++h) {
+            const frag af1 = frag_from_acc(s1, h, T());
+            const frag af2 = frag_from_acc(s2, h, T());
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) dka[nb] = MF::run(af1, colop(sQ1, qb, nb, h), dka[nb]);
+#pragma unroll
+            for (int nb = 0; nb < NB2; ++nb) dka2[nb] = MF::run(af2, colop2(sQ2, qb, nb, h), dka2[nb]);
+          }
+          sched_mfma_lds<HS * (NB + NB2), MF::KPL == 1 ? 1 : 2, 2>();
+          continue;
+        }
         if (SETTING == 2 || tile_signed) {
           if (need_mask) dS_rows_keyouter<SETTING, true, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q, stat_off);
           else dS_rows_keyouter<SETTING, false, BQ>(s1, s2, st, 32 * qb, qb0, grp, a.c1, a.c2, qlo, a.n_q, stat_off);
@@ -1367,6 +1441,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
     rf1.touch();
     if constexpr (!std::is_same_v<RF1, RF2>) rf2.touch();
     cf.touch();
+    cf2.touch();
     asm volatile("" : "+v"(stat_off));
     step(t, std::integral_constant<int, 0>());
     if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>());
@@ -1379,6 +1454,15 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
       const int key = kwave + acc_row(e, grp);
       if (key < a.n_k) a.dk[(bh * a.n_k + key) * DS + nb * 32 + col] = dka[nb][e];
     }
+  if constexpr (JOINT) {
+#pragma unroll
+    for (int nb = 0; nb < NB2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kwave + acc_row(e, grp);
+        if (key < a.n_k) a.dk2[(bh * a.n_k + key) * D2 + nb * 32 + col] = dka2[nb][e];
+      }
+  }
 }
 
 

@@ -37,6 +37,7 @@ KERNELS = [
     ("fwd_decode_kernel", r"fwd_decode_kernel"),
     ("fwd_pp_kernel", r"fwd_pp_kernel"),
     ("fwd_kernel", r"fwd_kernel"),
+    ("bwd_dk_kernel<JOINT>", r"bwd_dk_kernel(I.*Li3ELb0E|<[^>]*, 3, false)"),
     ("bwd_dk_kernel", r"bwd_dk_kernel(I.*Lb0E|<[^>]*false)"),
     ("bwd_dk_kernel<FUSED>", r"bwd_dk_kernel(I.*Lb1E|<[^>]*true)"),
     ("bwd_dq_kernel", r"bwd_dq_kernel"),

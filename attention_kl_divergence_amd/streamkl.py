@@ -55,6 +55,8 @@ def _lib():
         lib.streamkl_fwd.restype = i32
         lib.streamkl_bwd.argtypes = [i32, vp, vp, vp, vp, i32, f32, f32, vp, vp, vp, vp, vp, vp, sp, lp, vp]
         lib.streamkl_bwd.restype = i32
+        lib.streamkl_bwd_joint.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, vp, vp, vp, vp, vp, vp, sp, lp, vp]
+        lib.streamkl_bwd_joint.restype = i32
         lib.streamkl_fwd_workspace_bytes.argtypes = [sp, i32, lp]
         lib.streamkl_fwd_workspace_bytes.restype = sz
         lib.streamkl_fwd_plan.argtypes = [sp, i32, lp]
@@ -191,6 +193,33 @@ def streamkl_bwd(setting: int, q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_k
     return dq, dk
 
 
+def streamkl_bwd_joint(q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
+                       scale1: float = 0.0, scale2: float = 0.0, bwd_mode: int = BWD_AUTO, out=None):
+    """Joint backward: returns (dQ1, dK1, dQ2, dK2) in fp32, the gradients to
+    both models in one pass (equal to setting 2 and setting 1 of streamkl_bwd)."""
+    shp = shape_of(q1, k1, q2, k2)
+    dev = q1.device
+    if out is None:
+        kw = dict(device=dev, dtype=torch.float32)
+        nq = bwd_mode == BWD_DK_ONLY
+        nk = bwd_mode == BWD_DQ_ONLY
+        out = (None if nq else torch.empty((shp.B, shp.H, shp.n_q, shp.d1), **kw),
+               None if nk else torch.empty((shp.B, shp.H, shp.n_k, shp.d1), **kw),
+               None if nq else torch.empty((shp.B, shp.H, shp.n_q, shp.d2), **kw),
+               None if nk else torch.empty((shp.B, shp.H, shp.n_k, shp.d2), **kw))
+    for t in (kl, lse1, lse2, d_kl):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != shp.B * shp.H * shp.n_q:
+            raise ValueError("kl, lse1, lse2, d_kl must be contiguous fp32 [B, H, n_q]")
+    ln = Launch(0, bwd_mode, None, 0)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    st = _lib().streamkl_bwd_joint(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), int(causal),
+                                   float(scale1), float(scale2), kl.data_ptr(), lse1.data_ptr(), lse2.data_ptr(),
+                                   d_kl.data_ptr(), *(ptr(t) for t in out), ctypes.byref(shp), ctypes.byref(ln),
+                                   _stream(dev))
+    _check(st, "streamkl_bwd_joint")
+    return tuple(out)
+
+
 class _KLFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q1, k1, q2, k2, causal, scale1, scale2, bwd_mode):
@@ -204,11 +233,17 @@ class _KLFunction(torch.autograd.Function):
         q1, k1, q2, k2, kl, lse1, lse2 = ctx.saved_tensors
         g = g.contiguous().to(torch.float32)
         grads = [None, None, None, None]
-        if ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
+        teacher = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
+        student = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
+        if teacher and student:
+            dq1, dk1, dq2, dk2 = streamkl_bwd_joint(q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1,
+                                                    ctx.scale2, ctx.bwd_mode)
+            return (dq1.to(q1.dtype), dk1.to(k1.dtype), dq2.to(q2.dtype), dk2.to(k2.dtype), None, None, None, None)
+        if student:
             dq2, dk2 = streamkl_bwd(1, q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1, ctx.scale2,
                                     ctx.bwd_mode)
             grads[2], grads[3] = dq2.to(q2.dtype), dk2.to(k2.dtype)
-        if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
+        if teacher:
             dq1, dk1 = streamkl_bwd(2, q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1, ctx.scale2,
                                     ctx.bwd_mode)
             grads[0], grads[1] = dq1.to(q1.dtype), dk1.to(k1.dtype)
@@ -221,6 +256,7 @@ def attention_kl(q1, k1, q2, k2, causal: bool = False, scale1: float = 0.0, scal
 
     Gradients flow to whichever of (Q1, K1) / (Q2, K2) require grad: the
     student side uses setting 1 (teacher distribution held fixed), the
-    teacher side setting 2 (student distribution held fixed).
+    teacher side setting 2 (student distribution held fixed), and both
+    sides together the joint backward.
     """
     return _KLFunction.apply(q1, k1, q2, k2, causal, scale1, scale2, bwd_mode)

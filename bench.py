@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--workload", default="h32-n64k-d128-bf16-causal")
     ap.add_argument("--bwd-mode", default="auto", choices=["auto", "fused", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--joint", action="store_true",
+                    help="for workloads that train both models (settings 1 and 2), run the joint backward "
+                         "(one key-outer pass for dK1 and dK2, then dQ1 and dQ2) instead of two backward calls")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="query rows of the oracle sample")
     ap.add_argument("--compare-modes", action="store_true",
                     help="after the timed steps, time each backward setting once in the mode the plan "
@@ -122,7 +125,15 @@ def main():
     # stream bracket exactly one kernel (split-K adds its merge kernel).
     calls = [("fwd", lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, out=(kl, l1, l2), workspace=ws))]
     modes = {}
-    for setting in w.settings:
+    joint = args.joint and tuple(sorted(w.settings)) == (1, 2)
+    if joint:
+        jo = (torch.empty((w.B, w.H, w.n_q, w.d1), **f32), torch.empty((w.B, w.H, w.n_k, w.d1), **f32),
+              torch.empty((w.B, w.H, w.n_q, w.d2), **f32), torch.empty((w.B, w.H, w.n_k, w.d2), **f32))
+        calls.append(("bwdj_dk", lambda: sk.streamkl_bwd_joint(q1, k1, q2, k2, w.causal, kl, l1, l2, g,
+                                                                bwd_mode=sk.BWD_DK_ONLY, out=(None, jo[1], None, jo[3]))))
+        calls.append(("bwdj_dq", lambda: sk.streamkl_bwd_joint(q1, k1, q2, k2, w.causal, kl, l1, l2, g,
+                                                                bwd_mode=sk.BWD_DQ_ONLY, out=(jo[0], None, jo[2], None))))
+    for setting in (() if joint else w.settings):
         ds = w.d2 if setting == 1 else w.d1
         dq = torch.empty((w.B, w.H, w.n_q, ds), **f32)
         dk = torch.empty((w.B, w.H, w.n_k, ds), **f32)
@@ -177,6 +188,8 @@ def main():
         credit[f"bwd{setting}_fused"] = (qk + 4 * ds) * pairs
         credit[f"bwd{setting}_dk"] = (qk + 2 * ds) * pairs
         credit[f"bwd{setting}_dq"] = 2 * ds * pairs
+    credit["bwdj_dk"] = (qk + 2 * (w.d1 + w.d2)) * pairs
+    credit["bwdj_dq"] = 2 * (w.d1 + w.d2) * pairs
     flops_step = sum(credit[n] for n, _ in calls)
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -195,7 +208,7 @@ def main():
     # decode shapes (bf16, at most 32 query rows): the split-K forward and the
     # decode backward, both bound by HBM bandwidth
     decode = w.dtype == "bf16" and w.n_q <= 32
-    kernel_names = {"fwd": fwd_kernel}
+    kernel_names = {"fwd": fwd_kernel, "bwdj_dk": "bwd_dk_kernel<JOINT>", "bwdj_dq": "bwd_dq_kernel"}
     for setting in w.settings:
         kernel_names[f"bwd{setting}_fused"] = "bwd_decode_kernel" if decode else "bwd_dk_kernel<FUSED>"
         kernel_names[f"bwd{setting}_dk"] = "bwd_dk_kernel"
@@ -253,7 +266,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "n_q": w.n_q, "n_k": w.n_k, "d1": w.d1, "d2": w.d2,
                    "causal": w.causal, "bwd_settings": list(w.settings),
-                   "bwd_modes": {str(k): names[v] for k, v in modes.items()},
+                   "bwd_modes": {str(k): names[v] for k, v in modes.items()} if not joint else {"1+2": "joint"},
                    "fwd_splits": splits, "parallelism": "single GPU"},
         "pct_of_mfma_peak": round(100 * value / peak, 2),
         "per_kernel_ms": {k: round(v, 4) for k, v in per_call.items()},

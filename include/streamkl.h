@@ -144,6 +144,29 @@ streamkl_status streamkl_bwd(int setting,
                              const streamkl_shape* shape, const streamkl_launch* launch,
                              void* stream);
 
+/*
+ * Joint backward: the gradients of sum_i d_kl[i] * KL[i] with respect to
+ * both models at once (when teacher and student are both trained), equal to
+ * setting 2 (dQ1 [B,H,n_q,d1], dK1 [B,H,n_k,d1]) and setting 1 (dQ2, dK2,
+ * with d2) of streamkl_bwd.  Both settings need S1, S2 and P1 per tile
+ * (Method 2): the key-outer kernel recomputes them once per tile pair and
+ * forms dS1 and dS2 from them, accumulating dK1 and dK2 together
+ * (2(d1+d2) + 2(d1+d2) matrix FLOPs per visible pair instead of twice
+ * 2(d1+d2) + 2 d_s); dQ1 and dQ2 come from the query-outer kernel of each
+ * setting.  bf16 in the separate mode only; fp32 inputs, and shapes whose
+ * plan is the fused mode (few query rows), run the two settings one after the
+ * other.  kl is required.  dQ1, dQ2 must be 16-byte aligned.
+ * launch->bwd_mode DK_ONLY (DQ_ONLY) computes dK1 and dK2 (dQ1 and dQ2) only.
+ * Every argument is checked before anything is enqueued; all four outputs are
+ * fully overwritten.
+ */
+streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q2, const void* K2,
+                                   int causal, float scale1, float scale2,
+                                   const float* kl, const float* lse1, const float* lse2,
+                                   const float* d_kl, float* dQ1, float* dK1, float* dQ2, float* dK2,
+                                   const streamkl_shape* shape, const streamkl_launch* launch,
+                                   void* stream);
+
 /* Static text for a status code. */
 const char* streamkl_status_string(int status);
 

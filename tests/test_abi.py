@@ -57,6 +57,14 @@ def _bwd(setting, shape, ptr=0, causal=0):
                             ctypes.byref(shape) if shape is not None else None, None, None)
 
 
+def _joint(shape, ptr=0, causal=0, launch=None):
+    lib = sk.library()
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.streamkl_bwd_joint(p, p, p, p, causal, 0.0, 0.0, p, p, p, p, p, p, p, p,
+                                  ctypes.byref(shape) if shape is not None else None,
+                                  ctypes.byref(launch) if launch is not None else None, None)
+
+
 GOOD = dict(B=1, H=2, n_q=64, n_k=64, d1=128, d2=128, dtype=sk.BF16)
 
 
@@ -70,6 +78,8 @@ def test_null_pointers_are_invalid():
     assert _fwd(shape()) == sk.ERR_INVALID
     assert _bwd(1, shape()) == sk.ERR_INVALID
     assert _fwd(None) == sk.ERR_INVALID
+    assert _joint(shape()) == sk.ERR_INVALID
+    assert _joint(None) == sk.ERR_INVALID
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -82,6 +92,7 @@ def test_bad_shapes(kw, code):
     # misaligned fake pointer: shape errors are reported first, the pointer is never used
     assert _fwd(shape(**kw), ptr=8) == code
     assert _bwd(2, shape(**kw), ptr=8) == code
+    assert _joint(shape(**kw), ptr=8) == code
 
 
 def test_causal_needs_nq_le_nk():
@@ -94,6 +105,9 @@ def test_bad_setting_and_alignment():
     # 8-byte aligned tensor pointers are rejected (16 is required) before any device call
     assert _fwd(shape(), ptr=8) == sk.ERR_INVALID
     assert _bwd(1, shape(), ptr=8) == sk.ERR_INVALID
+    assert _joint(shape(), ptr=8) == sk.ERR_INVALID
+    assert _joint(shape(), ptr=16, launch=sk.Launch(0, 9, None, 0)) == sk.ERR_INVALID
+    assert _joint(shape(n_q=65, n_k=64), ptr=16, causal=1) == sk.ERR_INVALID
 
 
 def test_bad_launch_options():
