@@ -275,6 +275,37 @@ def main():
         "materialised_bytes_avoided": 2 * w.B * w.H * w.n_q * w.n_k * 2,
         "roofline": roof,
     }
+    if decode:
+        # the pages' two ablations on decode shapes: the split-K forward against
+        # one workgroup sweep per query block (num_splits = 1), and the fused
+        # backward against the separate dK + dQ kernels
+        def once(fn):
+            fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+        abl = {"fwd_split_ms": round(per_call["fwd"], 4)}
+        t1 = once(lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, num_splits=1))
+        abl["fwd_one_split_ms"] = round(t1, 4)
+        abl["split_speedup"] = round(t1 / per_call["fwd"], 2)
+        for setting in w.settings:
+            name = f"bwd{setting}_fused"
+            if name in per_call:
+                t2 = once(lambda: sk.streamkl_bwd(setting, q1, k1, q2, k2, w.causal, kl, l1, l2, g,
+                                                  bwd_mode=sk.BWD_SEPARATE))
+                abl[f"bwd{setting}_separate_ms"] = round(t2, 4)
+                abl[f"bwd{setting}_fused_speedup"] = round(t2 / per_call[name], 2)
+        out["ablation"] = abl
+    # device memory the library takes beyond the caller's buffers: none (it
+    # never allocates); checked with the driver's free-memory count around a step
+    free0 = torch.cuda.mem_get_info(dev)[0]
+    for _, c in calls:
+        c()
+    torch.cuda.synchronize()
+    out["library_device_allocation_bytes"] = int(free0 - torch.cuda.mem_get_info(dev)[0])
     if args.compare_modes:
         alt = {}
         for setting in w.settings:

@@ -130,3 +130,34 @@ def test_failed_call_writes_nothing(cuda_device):
         sk.streamkl_fwd(q1, k1, q2, k2, False, num_splits=-1, out=out)
     torch.cuda.synchronize()
     assert all((o == 7.0).all() for o in out)
+
+
+@pytest.mark.parametrize("n_q,n_k", [(300, 300), (16, 20000)], ids=["prefill", "decode"])
+def test_library_allocates_no_device_memory(n_q, n_k, cuda_device):
+    """Every call runs in the caller's buffers: the driver's free-memory count
+    is the same before and after forward (split and unsplit), both settings
+    in both modes and the joint backward, once each has been launched once."""
+    w = W("alloc", causal=False, n_q=n_q, n_k=n_k)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    shp = sk.shape_of(q1, k1, q2, k2)
+    f32 = dict(device=cuda_device, dtype=torch.float32)
+    kl, l1, l2 = (torch.empty((1, w.H, n_q), **f32) for _ in range(3))
+    ws = torch.empty(max(sk.fwd_workspace_bytes(shp, False, 8), 1), dtype=torch.uint8, device=cuda_device)
+    dq1, dq2 = torch.empty((1, w.H, n_q, 128), **f32), torch.empty((1, w.H, n_q, 128), **f32)
+    dk1, dk2 = torch.empty((1, w.H, n_k, 128), **f32), torch.empty((1, w.H, n_k, 128), **f32)
+
+    def step():
+        sk.streamkl_fwd(q1, k1, q2, k2, False, out=(kl, l1, l2), workspace=ws, num_splits=8)
+        sk.streamkl_fwd(q1, k1, q2, k2, False, out=(kl, l1, l2), num_splits=1)
+        for s in (1, 2):
+            for m in (sk.BWD_FUSED, sk.BWD_SEPARATE):
+                sk.streamkl_bwd(s, q1, k1, q2, k2, False, kl, l1, l2, g, bwd_mode=m, out=(dq2, dk2))
+        sk.streamkl_bwd_joint(q1, k1, q2, k2, False, kl, l1, l2, g, out=(dq1, dk1, dq2, dk2))
+        torch.cuda.synchronize()
+
+    step()
+    free0 = torch.cuda.mem_get_info(cuda_device)[0]
+    for _ in range(3):
+        step()
+    assert torch.cuda.mem_get_info(cuda_device)[0] == free0
