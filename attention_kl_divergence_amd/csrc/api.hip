@@ -79,8 +79,16 @@ streamkl_status check_shape(const streamkl_shape* s, int causal) {
   if (s->B > (int64_t(1) << 20) || s->H > (int64_t(1) << 20) || s->B * s->H > (int64_t(1) << 20))
     return STREAMKL_ERR_UNSUPPORTED;
   if (causal && s->n_q > s->n_k) return STREAMKL_ERR_INVALID;
+  // grouped key heads: each count divides H (0 = H)
+  for (const int32_t kv : {s->kv_heads1, s->kv_heads2})
+    if (kv < 0 || (kv > 0 && s->H % kv != 0)) return STREAMKL_ERR_INVALID;
   return STREAMKL_OK;
 }
+
+// query heads per key head of each model
+int group1(const streamkl_shape* s) { return s->kv_heads1 > 0 ? (int)(s->H / s->kv_heads1) : 1; }
+int group2(const streamkl_shape* s) { return s->kv_heads2 > 0 ? (int)(s->H / s->kv_heads2) : 1; }
+
 
 float log2e_scale(float scale, int d) { return (scale > 0.f ? scale : 1.0f / sqrtf((float)d)) * kLog2e; }
 float plain_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
@@ -207,6 +215,23 @@ streamkl_status hip_status(hipError_t e) {
   return STREAMKL_ERR_HIP;
 }
 
+// Clears n floats (a multiple of 4) on the stream.
+streamkl_status fill_zero(float* p, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  int64_t fb = cdiv(n4, 256);
+  if (fb > 65536) fb = 65536;
+  if (fb < 1) fb = 1;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)fb), dim3(256), 0, s, reinterpret_cast<float4*>(p), n4);
+  return hip_status(hipGetLastError());
+}
+
+// dK of a model whose key heads are shared is summed with atomics: clear it
+// first.  ds: its head dim, g: query heads per key head.
+streamkl_status clear_shared_dk(float* dK, const streamkl_shape* sh, int ds, int g, hipStream_t s) {
+  if (g <= 1) return STREAMKL_OK;
+  return fill_zero(dK, sh->B * (sh->H / g) * sh->n_k * (int64_t)ds, s);
+}
+
 }  // namespace
 }  // namespace streamkl
 
@@ -214,7 +239,7 @@ using namespace streamkl;
 
 extern "C" {
 
-int streamkl_version(void) { return 1; }
+int streamkl_version(void) { return 2; }
 
 const char* streamkl_status_string(int status) {
   switch (status) {
@@ -282,7 +307,7 @@ streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, con
                       : pick_fwd(shape->dtype, shape->d1, shape->d2);
   if (!fn) return STREAMKL_ERR_UNSUPPORTED;
 
-  FwdArgs a;
+  FwdArgs a = {};
   a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
   a.kl = out_kl; a.lse1 = out_lse1; a.lse2 = out_lse2;
   a.ws = splits > 1 ? static_cast<float*>(launch->workspace) : nullptr;
@@ -296,6 +321,8 @@ streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, con
   a.causal = causal ? 1 : 0;
   a.c1 = log2e_scale(scale1, shape->d1);
   a.c2 = log2e_scale(scale2, shape->d2);
+  a.g1 = group1(shape);
+  a.g2 = group2(shape);
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = hip_status(fn(a, dec ? a.BH * cdiv(splits, 4) : a.BH * a.nqb * splits, s));
   if (st != STREAMKL_OK || splits == 1) return st;
@@ -350,16 +377,18 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
   a.c1 = log2e_scale(scale1, shape->d1);
   a.c2 = log2e_scale(scale2, shape->d2);
   a.scale_s = setting == 1 ? plain_scale(scale2, shape->d2) : plain_scale(scale1, shape->d1);
+  a.g1 = group1(shape);
+  a.g2 = group2(shape);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
+  const int ds = setting == 1 ? shape->d2 : shape->d1;
+  if (mode != STREAMKL_BWD_DQ_ONLY) {
+    st = clear_shared_dk(dK, shape, ds, setting == 1 ? a.g2 : a.g1, s);
+    if (st != STREAMKL_OK) return st;
+  }
   if (mode == STREAMKL_BWD_FUSED) {
-    const int ds = setting == 1 ? shape->d2 : shape->d1;
     const DecBwdLaunch fd = decode_shape(shape) ? pick_dec_bwd(shape->dtype, shape->d1, shape->d2) : nullptr;
-    const int64_t n4 = a.BH * a.n_q * ds / 4;
-    int64_t fb = cdiv(n4, 256);
-    if (fb > 65536) fb = 65536;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)fb), dim3(256), 0, s, reinterpret_cast<float4*>(dQ), n4);
-    st = hip_status(hipGetLastError());
+    st = fill_zero(dQ, a.BH * a.n_q * (int64_t)ds, s);
     if (st != STREAMKL_OK) return st;
     if (fd) {
       a.nblk = plan_dec_bwd_splits(shape, dev.cus);
@@ -422,9 +451,14 @@ streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q
   a.c2 = log2e_scale(scale2, shape->d2);
   a.scale_s = plain_scale(scale1, shape->d1);
   a.scale_s2 = plain_scale(scale2, shape->d2);
+  a.g1 = group1(shape);
+  a.g2 = group2(shape);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
   if (mode != STREAMKL_BWD_DQ_ONLY) {
+    st = clear_shared_dk(dK1, shape, shape->d1, a.g1, s);
+    if (st == STREAMKL_OK) st = clear_shared_dk(dK2, shape, shape->d2, a.g2, s);
+    if (st != STREAMKL_OK) return st;
     a.nblk = (int)nkb;
     st = hip_status(fk(a, 3, false, a.BH * nkb, s));
     if (st != STREAMKL_OK || mode == STREAMKL_BWD_DK_ONLY) return st;

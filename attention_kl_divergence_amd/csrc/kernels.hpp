@@ -50,6 +50,7 @@ struct FwdArgs {
   int nqb;             // query blocks per head
   int causal;
   float c1, c2;        // scale_t * log2(e)
+  int g1, g2;          // query heads per key head of each model (1: no sharing)
 };
 
 struct BwdArgs {
@@ -71,6 +72,7 @@ struct BwdArgs {
   float c1, c2;        // scale_t * log2(e)
   float scale_s;       // scale of the model that receives gradients (joint: model 1)
   float scale_s2;      // joint: scale of model 2
+  int g1, g2;          // query heads per key head of each model (1: no sharing)
 };
 
 typedef __bf16 bf16x4_lds __attribute__((ext_vector_type(4)));
@@ -511,9 +513,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + bh * (int64_t)a.n_k * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
   const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + bh * (int64_t)a.n_k * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
 
   const int kbeg = z * a.keys_per_split;
   int kend = min(a.n_k, kbeg + a.keys_per_split);
@@ -632,9 +634,9 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + bh * (int64_t)a.n_k * D1;
+  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
   const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + bh * (int64_t)a.n_k * D2;
+  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
   dec_stage_q<D1>(sQ1, Q1, a.n_q, tid);
   dec_stage_q<D2>(sQ2, Q2, a.n_q, tid);
   __syncthreads();
@@ -764,9 +766,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + bh * (int64_t)a.n_k * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
   const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + bh * (int64_t)a.n_k * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
 
   int kend = a.n_k;
   if (a.causal) kend = min(kend, min(a.n_q, qwg0 + 32 * NW) - 1 + off + 1);
@@ -1032,9 +1034,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + bh * (int64_t)a.n_k * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
   const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + bh * (int64_t)a.n_k * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
 
   int kend = a.n_k;
   if (a.causal) kend = min(kend, min(a.n_q, qb * 32 * NW + 32 * NW) - 1 + off + 1);
@@ -1201,9 +1203,9 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + bh * (int64_t)a.n_k * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
   const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + bh * (int64_t)a.n_k * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
   const T* KS = SETTING == 1 ? K2 : K1;
 
   // Query tiles are visited from the last one down: under a causal mask every
@@ -1447,21 +1449,26 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
     if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>());
   }
 
+  // dK_s of key head bh / g_s: the query heads that share a key head add
+  // their parts with fp32 atomics into the cleared output (once per key and
+  // query head); without sharing each element is stored once
+  auto put = [&](float* dk, int g, int D, int nb, int e, float v) {
+    const int key = kwave + acc_row(e, grp);
+    if (key >= a.n_k) return;
+    float* p = dk + ((bh / g) * a.n_k + key) * D + nb * 32 + col;
+    if (g > 1) atomicAdd(p, v);
+    else *p = v;
+  };
+  const int gs = SETTING == 1 ? a.g2 : a.g1;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kwave + acc_row(e, grp);
-      if (key < a.n_k) a.dk[(bh * a.n_k + key) * DS + nb * 32 + col] = dka[nb][e];
-    }
+    for (int e = 0; e < 16; ++e) put(a.dk, gs, DS, nb, e, dka[nb][e]);
   if constexpr (JOINT) {
 #pragma unroll
     for (int nb = 0; nb < NB2; ++nb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kwave + acc_row(e, grp);
-        if (key < a.n_k) a.dk2[(bh * a.n_k + key) * D2 + nb * 32 + col] = dka2[nb][e];
-      }
+      for (int e = 0; e < 16; ++e) put(a.dk2, a.g2, D2, nb, e, dka2[nb][e]);
   }
 }
 
@@ -1509,9 +1516,9 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + bh * (int64_t)a.n_k * D1;
+  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
   const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + bh * (int64_t)a.n_k * D2;
+  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
 
   const int ntile = (a.n_k + BK - 1) / BK;
   const int count = z < ntile ? (ntile - z + a.nblk - 1) / a.nblk : 0;
@@ -1595,9 +1602,17 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) dka[nb] = MF::run(af, qcol[h][nb], dka[nb]);
     }
-    float* dk = a.dk + (bh * a.n_k + kw) * (int64_t)DS + col;
+    const int gs = SETTING == 1 ? a.g2 : a.g1;
+    float* dk = a.dk + ((bh / gs) * a.n_k + kw) * (int64_t)DS + col;
     const int kleft = a.n_k - kw;
-    if (kleft >= 32) {
+    if (gs > 1) {
+      // query heads sharing a key head add their parts into the cleared dK
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (acc_row(e, grp) < kleft) atomicAdd(dk + acc_row(e, grp) * DS + 32 * nb, dka[nb][e]);
+    } else if (kleft >= 32) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll

@@ -31,8 +31,13 @@ class StreamKLError(RuntimeError):
 
 
 class Shape(ctypes.Structure):
+    # kv_heads1/kv_heads2: key heads of each model (0 = H, one per query head)
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("n_q", ctypes.c_int64), ("n_k", ctypes.c_int64),
-                ("d1", ctypes.c_int32), ("d2", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("d1", ctypes.c_int32), ("d2", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("kv_heads1", ctypes.c_int32), ("kv_heads2", ctypes.c_int32)]
+
+
+ABI_VERSION = 2
 
 
 class Launch(ctypes.Structure):
@@ -69,6 +74,9 @@ def _lib():
         lib.streamkl_last_hip_error.restype = i32
         lib.streamkl_version.argtypes = []
         lib.streamkl_version.restype = i32
+        if lib.streamkl_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {lib.streamkl_version()}, this binding needs "
+                               f"{ABI_VERSION}: rebuild it")
         _LIB = lib
     return _LIB
 
@@ -86,9 +94,9 @@ def _dtype_code(t: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {t}; expected float32 or bfloat16")
 
 
-def make_shape(B, H, n_q, n_k, d1, d2, dtype) -> Shape:
+def make_shape(B, H, n_q, n_k, d1, d2, dtype, kv_heads1=0, kv_heads2=0) -> Shape:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
-    return Shape(B, H, n_q, n_k, d1, d2, code)
+    return Shape(B, H, n_q, n_k, d1, d2, code, kv_heads1, kv_heads2)
 
 
 def shape_of(q1, k1, q2, k2) -> Shape:
@@ -104,9 +112,18 @@ def shape_of(q1, k1, q2, k2) -> Shape:
     B, H, n_q, d1 = q1.shape
     n_k = k1.shape[2]
     d2 = q2.shape[3]
-    if tuple(k1.shape) != (B, H, n_k, d1) or tuple(q2.shape) != (B, H, n_q, d2) or tuple(k2.shape) != (B, H, n_k, d2):
+    # K_t may have fewer heads than Q_t (grouped key heads): [B, kv_heads_t, n_k, d_t]
+    kv1, kv2 = k1.shape[1], k2.shape[1]
+    if (tuple(k1.shape) != (B, kv1, n_k, d1) or tuple(q2.shape) != (B, H, n_q, d2)
+            or tuple(k2.shape) != (B, kv2, n_k, d2) or H % kv1 or H % kv2):
         raise ValueError("inconsistent Q/K shapes")
-    return make_shape(B, H, n_q, n_k, d1, d2, q1.dtype)
+    return make_shape(B, H, n_q, n_k, d1, d2, q1.dtype, 0 if kv1 == H else kv1, 0 if kv2 == H else kv2)
+
+
+def _kv(shp: Shape, model: int) -> int:
+    """Key heads of model 1 or 2."""
+    kv = shp.kv_heads1 if model == 1 else shp.kv_heads2
+    return kv if kv > 0 else shp.H
 
 
 def _stream(device) -> int:
@@ -178,7 +195,8 @@ def streamkl_bwd(setting: int, q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_k
     if out is None:
         kw = dict(device=dev, dtype=torch.float32)
         out = (None if bwd_mode == BWD_DK_ONLY else torch.empty((shp.B, shp.H, shp.n_q, ds), **kw),
-               None if bwd_mode == BWD_DQ_ONLY else torch.empty((shp.B, shp.H, shp.n_k, ds), **kw))
+               None if bwd_mode == BWD_DQ_ONLY else torch.empty((shp.B, _kv(shp, 2 if setting == 1 else 1), shp.n_k, ds),
+                                                                **kw))
     dq, dk = out
     for t in (lse1, lse2, d_kl) + ((kl,) if kl is not None else ()):
         if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != shp.B * shp.H * shp.n_q:
@@ -204,9 +222,9 @@ def streamkl_bwd_joint(q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
         nq = bwd_mode == BWD_DK_ONLY
         nk = bwd_mode == BWD_DQ_ONLY
         out = (None if nq else torch.empty((shp.B, shp.H, shp.n_q, shp.d1), **kw),
-               None if nk else torch.empty((shp.B, shp.H, shp.n_k, shp.d1), **kw),
+               None if nk else torch.empty((shp.B, _kv(shp, 1), shp.n_k, shp.d1), **kw),
                None if nq else torch.empty((shp.B, shp.H, shp.n_q, shp.d2), **kw),
-               None if nk else torch.empty((shp.B, shp.H, shp.n_k, shp.d2), **kw))
+               None if nk else torch.empty((shp.B, _kv(shp, 2), shp.n_k, shp.d2), **kw))
     for t in (kl, lse1, lse2, d_kl):
         if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != shp.B * shp.H * shp.n_q:
             raise ValueError("kl, lse1, lse2, d_kl must be contiguous fp32 [B, H, n_q]")

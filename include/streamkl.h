@@ -20,7 +20,8 @@
  * - Tensor pointers are DEVICE pointers (HIP device memory of the current
  *   device), 16-byte aligned.  Descriptor pointers (streamkl_shape,
  *   streamkl_launch) are HOST pointers, read during the call only.
- * - Q_t is [B, H, n_q, d_t] and K_t is [B, H, n_k, d_t], row-major and
+ * - Q_t is [B, H, n_q, d_t] and K_t is [B, H, n_k, d_t] (or [B, kv_heads_t,
+ *   n_k, d_t] with grouped key heads, see streamkl_shape), row-major and
  *   contiguous, all four in the dtype of shape->dtype (fp32 or bf16).
  *   Supported head dims: d_t in {64, 128}; d1 and d2 may differ.
  * - Per-row vectors (kl, lse1, lse2, d_kl) are fp32 [B, H, n_q].
@@ -74,6 +75,12 @@ typedef struct {
   int64_t B, H, n_q, n_k;
   int32_t d1, d2;   /* head dims of model 1 (teacher) and model 2 (student) */
   int32_t dtype;    /* streamkl_dtype */
+  /* Key heads of model 1 and model 2 (grouped-query attention): K_t is
+   * [B, kv_heads_t, n_k, d_t] and query head h reads key head
+   * h / (H / kv_heads_t).  0 means H (every query head has its own keys).
+   * kv_heads_t must divide H.  dK_t is then [B, kv_heads_t, n_k, d_t], the
+   * sum over the query heads that share each key head. */
+  int32_t kv_heads1, kv_heads2;
 } streamkl_shape;
 
 /* Launch options (host struct; a NULL pointer means all defaults). */
@@ -173,7 +180,8 @@ const char* streamkl_status_string(int status);
 /* hipError_t of the last STREAMKL_ERR_HIP returned on this thread (0 if none). */
 int streamkl_last_hip_error(void);
 
-/* Library version, for the Python binding's load check. */
+/* Library version, for the Python binding's load check (2: streamkl_shape
+ * carries kv_heads1, kv_heads2). */
 int streamkl_version(void);
 
 #ifdef __cplusplus

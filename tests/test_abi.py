@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = sk.library()
-    assert lib.streamkl_version() >= 1
+    assert lib.streamkl_version() == sk.ABI_VERSION == 2
     assert lib.streamkl_status_string(0) == b"ok"
     assert lib.streamkl_status_string(4) == b"HIP runtime error"
     assert lib.streamkl_status_string(99) == b"unknown status"
@@ -93,6 +93,15 @@ def test_bad_shapes(kw, code):
     assert _fwd(shape(**kw), ptr=8) == code
     assert _bwd(2, shape(**kw), ptr=8) == code
     assert _joint(shape(**kw), ptr=8) == code
+
+
+@pytest.mark.parametrize("kv1,kv2", [(3, 0), (0, 5), (-1, 0), (0, 64)])
+def test_key_head_counts_must_divide_h(kv1, kv2):
+    s = shape(H=32)
+    s.kv_heads1, s.kv_heads2 = kv1, kv2
+    assert _fwd(s, ptr=16) == sk.ERR_INVALID
+    assert _bwd(1, s, ptr=16) == sk.ERR_INVALID
+    assert _joint(s, ptr=16) == sk.ERR_INVALID
 
 
 def test_causal_needs_nq_le_nk():
