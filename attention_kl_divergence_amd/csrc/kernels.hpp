@@ -136,6 +136,10 @@ struct TileLoader {
   }
 };
 
+// Key head of query head bh (of B*H < 2^20) when g query heads share one:
+// a 32-bit division, far shorter than a 64-bit one.
+__device__ inline int64_t key_head(int64_t bh, int g) { return (int64_t)((uint32_t)bh / (uint32_t)g); }
+
 __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Work item (head, block) of workgroup `lin` of a grid of BH * nblk.
@@ -513,9 +517,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
   const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
 
   const int kbeg = z * a.keys_per_split;
   int kend = min(a.n_k, kbeg + a.keys_per_split);
@@ -634,9 +638,9 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
+  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
   const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
+  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
   dec_stage_q<D1>(sQ1, Q1, a.n_q, tid);
   dec_stage_q<D2>(sQ2, Q2, a.n_q, tid);
   __syncthreads();
@@ -766,9 +770,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
   const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
 
   int kend = a.n_k;
   if (a.causal) kend = min(kend, min(a.n_q, qwg0 + 32 * NW) - 1 + off + 1);
@@ -1034,9 +1038,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
   const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
 
   int kend = a.n_k;
   if (a.causal) kend = min(kend, min(a.n_q, qb * 32 * NW + 32 * NW) - 1 + off + 1);
@@ -1203,9 +1207,9 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
   const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
   const T* KS = SETTING == 1 ? K2 : K1;
 
   // Query tiles are visited from the last one down: under a causal mask every
@@ -1452,24 +1456,29 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   // dK_s of key head bh / g_s: the query heads that share a key head add
   // their parts with fp32 atomics into the cleared output (once per key and
   // query head); without sharing each element is stored once
-  auto put = [&](float* dk, int g, int D, int nb, int e, float v) {
-    const int key = kwave + acc_row(e, grp);
-    if (key >= a.n_k) return;
-    float* p = dk + ((bh / g) * a.n_k + key) * D + nb * 32 + col;
-    if (g > 1) atomicAdd(p, v);
-    else *p = v;
+  auto put = [&](float* dk, int g, const f32x16* acc, auto D_) {
+    constexpr int D = decltype(D_)::value;
+    float* base = dk + key_head(bh, g) * a.n_k * D + col;
+    if (g > 1) {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kwave + acc_row(e, grp);
+          if (key < a.n_k) atomicAdd(base + key * D + nb * 32, acc[nb][e]);
+        }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kwave + acc_row(e, grp);
+          if (key < a.n_k) base[key * D + nb * 32] = acc[nb][e];
+        }
+    }
   };
-  const int gs = SETTING == 1 ? a.g2 : a.g1;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) put(a.dk, gs, DS, nb, e, dka[nb][e]);
-  if constexpr (JOINT) {
-#pragma unroll
-    for (int nb = 0; nb < NB2; ++nb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) put(a.dk2, a.g2, D2, nb, e, dka2[nb][e]);
-  }
+  put(a.dk, SETTING == 1 ? a.g2 : a.g1, dka, std::integral_constant<int, DS>());
+  if constexpr (JOINT) put(a.dk2, a.g2, dka2, std::integral_constant<int, D2>());
 }
 
 
@@ -1516,9 +1525,9 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
   const int off = a.n_k - a.n_q;
 
   const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + (bh / a.g1) * (int64_t)a.n_k * D1;
+  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
   const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + (bh / a.g2) * (int64_t)a.n_k * D2;
+  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
 
   const int ntile = (a.n_k + BK - 1) / BK;
   const int count = z < ntile ? (ntile - z + a.nblk - 1) / a.nblk : 0;
@@ -1603,7 +1612,7 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
       for (int nb = 0; nb < NB; ++nb) dka[nb] = MF::run(af, qcol[h][nb], dka[nb]);
     }
     const int gs = SETTING == 1 ? a.g2 : a.g1;
-    float* dk = a.dk + ((bh / gs) * a.n_k + kw) * (int64_t)DS + col;
+    float* dk = a.dk + (key_head(bh, gs) * a.n_k + kw) * (int64_t)DS + col;
     const int kleft = a.n_k - kw;
     if (gs > 1) {
       // query heads sharing a key head add their parts into the cleared dK
