@@ -18,5 +18,6 @@ from .streamkl import (  # noqa: F401
     make_shape,
     shape_of,
     streamkl_bwd,
+    streamkl_bwd_joint,
     streamkl_fwd,
 )
