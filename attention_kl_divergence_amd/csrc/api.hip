@@ -1,8 +1,10 @@
 // C ABI of the StreamKL library: argument validation, launch planning
 // (key-split count, fused or separate backward) and kernel launches on the
 // caller's stream.  Declared in include/streamkl.h.
+#include <algorithm>
 #include <mutex>
 #include <string.h>
+#include <type_traits>
 
 #include "../../include/streamkl.h"
 #include "kernels.hpp"
@@ -12,11 +14,12 @@ namespace streamkl {
 
 // Merge of the split partial states, then the epilogue (one thread per row).
 __global__ __launch_bounds__(256) void splitk_merge_kernel(const float* __restrict__ ws, float* kl, float* lse1,
-                                                           float* lse2, int64_t BH, int n_q, int nsplit) {
+                                                           float* lse2, int64_t BH, int n_q, int nsplit, int qs) {
   const int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x;
   if (i >= BH * n_q) return;
   const int64_t bh = i / n_q;
   const int q = (int)(i % n_q);
+  const int64_t r = bh * qs + q;  // output row (qs rows per head in memory)
   const int64_t fs = BH * (int64_t)nsplit * n_q;
   RowState st = empty_state();
   for (int z = 0; z < nsplit; ++z) {
@@ -24,12 +27,17 @@ __global__ __launch_bounds__(256) void splitk_merge_kernel(const float* __restri
     RowState p = {ws[o], ws[o + fs], ws[o + 2 * fs], ws[o + 3 * fs], ws[o + 4 * fs]};
     st = merge_state(st, p);
   }
-  finish_state(st, kl + i, lse1 + i, lse2 + i);
+  finish_state(st, kl + r, lse1 + r, lse2 + r);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, int64_t n4) {
   for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// the same for any alignment and count
+__global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
 namespace {
@@ -66,6 +74,8 @@ streamkl_status device_info(DeviceInfo* out) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+bool ragged(const streamkl_shape* s);
+
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Shape checks that need no device.  Sizes are bounded so every in-head
@@ -79,6 +89,16 @@ streamkl_status check_shape(const streamkl_shape* s, int causal) {
   if (s->B > (int64_t(1) << 20) || s->H > (int64_t(1) << 20) || s->B * s->H > (int64_t(1) << 20))
     return STREAMKL_ERR_UNSUPPORTED;
   if (causal && s->n_q > s->n_k) return STREAMKL_ERR_INVALID;
+  if (ragged(s)) {
+    // every batch element: lengths within the padded sizes, some key for
+    // every query row, bottom-right causal alignment needs q <= k
+    for (int64_t b = 0; b < s->B; ++b) {
+      const int64_t q = s->q_len ? s->q_len[b] : s->n_q, k = s->k_len ? s->k_len[b] : s->n_k;
+      if (q < 0 || q > s->n_q || k < 0 || k > s->n_k) return STREAMKL_ERR_INVALID;
+      if (q > 0 && k == 0) return STREAMKL_ERR_INVALID;
+      if (causal && q > k) return STREAMKL_ERR_INVALID;
+    }
+  }
   // grouped key heads: each count divides H (0 = H)
   for (const int32_t kv : {s->kv_heads1, s->kv_heads2})
     if (kv < 0 || (kv > 0 && s->H % kv != 0)) return STREAMKL_ERR_INVALID;
@@ -215,21 +235,52 @@ streamkl_status hip_status(hipError_t e) {
   return STREAMKL_ERR_HIP;
 }
 
-// Clears n floats (a multiple of 4) on the stream.
+// Clears n floats on the stream (16-byte stores when p and n allow them).
 streamkl_status fill_zero(float* p, int64_t n, hipStream_t s) {
-  const int64_t n4 = n / 4;
-  int64_t fb = cdiv(n4, 256);
+  if (n <= 0) return STREAMKL_OK;
+  const bool vec = aligned(p, 16) && n % 4 == 0;
+  const int64_t m = vec ? n / 4 : n;
+  int64_t fb = cdiv(m, 256);
   if (fb > 65536) fb = 65536;
-  if (fb < 1) fb = 1;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)fb), dim3(256), 0, s, reinterpret_cast<float4*>(p), n4);
+  if (vec) hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)fb), dim3(256), 0, s, reinterpret_cast<float4*>(p), m);
+  else hipLaunchKernelGGL(fill_zero_f32_kernel, dim3((unsigned)fb), dim3(256), 0, s, p, m);
   return hip_status(hipGetLastError());
 }
 
 // dK of a model whose key heads are shared is summed with atomics: clear it
-// first.  ds: its head dim, g: query heads per key head.
-streamkl_status clear_shared_dk(float* dK, const streamkl_shape* sh, int ds, int g, hipStream_t s) {
+// first.  ds: its head dim, g: query heads per key head, ks: key rows per
+// head in memory.
+streamkl_status clear_shared_dk(float* dK, const streamkl_shape* sh, int ds, int g, int64_t ks, hipStream_t s) {
   if (g <= 1) return STREAMKL_OK;
-  return fill_zero(dK, sh->B * (sh->H / g) * sh->n_k * (int64_t)ds, s);
+  return fill_zero(dK, sh->B * (sh->H / g) * ks * (int64_t)ds, s);
+}
+
+// ---- ragged batches: per batch element lengths inside padded tensors ----
+
+bool ragged(const streamkl_shape* s) { return s->q_len || s->k_len; }
+
+// Batch element b as a problem of its own: B = 1, its lengths, no length arrays.
+streamkl_shape element_shape(const streamkl_shape* s, int64_t b) {
+  streamkl_shape e = *s;
+  e.B = 1;
+  e.n_q = s->q_len ? s->q_len[b] : s->n_q;
+  e.n_k = s->k_len ? s->k_len[b] : s->n_k;
+  e.q_len = nullptr;
+  e.k_len = nullptr;
+  return e;
+}
+
+int64_t kv_heads(const streamkl_shape* s, int model) {
+  const int32_t kv = model == 1 ? s->kv_heads1 : s->kv_heads2;
+  return kv > 0 ? kv : s->H;
+}
+
+// Element b's part of a tensor: rows_per_elem = heads * rows per head.
+template <typename P>
+P elem(P p, int64_t b, int64_t rows_per_elem, int64_t bytes_per_row) {
+  if (!p) return p;
+  using C = std::conditional_t<std::is_const_v<std::remove_pointer_t<P>>, const char*, char*>;
+  return reinterpret_cast<P>(reinterpret_cast<C>(p) + b * rows_per_elem * bytes_per_row);
 }
 
 }  // namespace
@@ -239,7 +290,7 @@ using namespace streamkl;
 
 extern "C" {
 
-int streamkl_version(void) { return 2; }
+int streamkl_version(void) { return 3; }
 
 const char* streamkl_status_string(int status) {
   switch (status) {
@@ -259,11 +310,20 @@ int streamkl_fwd_plan(const streamkl_shape* shape, int causal, const streamkl_la
   if (launch && launch->num_splits < 0) return 0;
   DeviceInfo d;
   const int cus = device_info(&d) == STREAMKL_OK ? d.cus : 256;
-  int sp = plan_splits(shape, causal, launch, cus);
-  if (sp > 1 && (!launch || launch->num_splits == 0) &&
-      (!launch || !launch->workspace || launch->workspace_bytes < ws_bytes(shape, sp)))
-    sp = 1;
-  return sp;
+  auto plan = [&](const streamkl_shape* e) {
+    int sp = plan_splits(e, causal, launch, cus);
+    if (sp > 1 && (!launch || launch->num_splits == 0) &&
+        (!launch || !launch->workspace || launch->workspace_bytes < ws_bytes(e, sp)))
+      sp = 1;
+    return sp;
+  };
+  if (!ragged(shape)) return plan(shape);
+  int most = 1;  // ragged batches: the largest split count of any element
+  for (int64_t b = 0; b < shape->B; ++b) {
+    const streamkl_shape e = element_shape(shape, b);
+    if (e.n_q > 0) most = std::max(most, plan(&e));
+  }
+  return most;
 }
 
 size_t streamkl_fwd_workspace_bytes(const streamkl_shape* shape, int causal, const streamkl_launch* launch) {
@@ -271,23 +331,27 @@ size_t streamkl_fwd_workspace_bytes(const streamkl_shape* shape, int causal, con
   if (launch && launch->num_splits < 0) return 0;
   DeviceInfo d;
   const int cus = device_info(&d) == STREAMKL_OK ? d.cus : 256;
-  return ws_bytes(shape, plan_splits(shape, causal, launch, cus));
+  if (!ragged(shape)) return ws_bytes(shape, plan_splits(shape, causal, launch, cus));
+  // ragged batches run one element at a time and reuse the workspace
+  size_t most = 0;
+  for (int64_t b = 0; b < shape->B; ++b) {
+    const streamkl_shape e = element_shape(shape, b);
+    if (e.n_q > 0) most = std::max(most, ws_bytes(&e, plan_splits(&e, causal, launch, cus)));
+  }
+  return most;
 }
 
-streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
-                             float scale1, float scale2, float* out_kl, float* out_lse1, float* out_lse2,
-                             const streamkl_shape* shape, const streamkl_launch* launch, void* stream) {
-  streamkl_status st = check_shape(shape, causal);
-  if (st != STREAMKL_OK) return st;
-  if (!Q1 || !K1 || !Q2 || !K2 || !out_kl || !out_lse1 || !out_lse2) return STREAMKL_ERR_INVALID;
-  if (!aligned(Q1, 16) || !aligned(K1, 16) || !aligned(Q2, 16) || !aligned(K2, 16)) return STREAMKL_ERR_INVALID;
-  if (!aligned(out_kl, 4) || !aligned(out_lse1, 4) || !aligned(out_lse2, 4)) return STREAMKL_ERR_INVALID;
-  if (!(scale1 == scale1) || !(scale2 == scale2)) return STREAMKL_ERR_INVALID;
-  if (launch && (launch->num_splits < 0 || launch->bwd_mode < 0 || launch->bwd_mode > 4)) return STREAMKL_ERR_INVALID;
-  DeviceInfo dev;
-  st = device_info(&dev);
-  if (st != STREAMKL_OK) return st;
+}  // extern "C"
 
+namespace streamkl {
+namespace {
+
+// The forward of one problem (validated): qs, ks are the rows per head in
+// memory (the padded lengths), sh->n_q, sh->n_k the rows used.
+streamkl_status fwd_launch(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal, float scale1,
+                           float scale2, float* out_kl, float* out_lse1, float* out_lse2, const streamkl_shape* shape,
+                           int64_t qs, int64_t ks, const streamkl_launch* launch, const DeviceInfo& dev,
+                           hipStream_t s) {
   int splits = plan_splits(shape, causal, launch, dev.cus);
   const size_t need = ws_bytes(shape, splits);
   if (splits > 1) {
@@ -314,6 +378,8 @@ streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, con
   a.BH = shape->B * shape->H;
   a.n_q = (int)shape->n_q;
   a.n_k = (int)shape->n_k;
+  a.qs = (int)qs;
+  a.ks = (int)ks;
   a.nsplit = splits;
   const int unit = dec ? kDecBlock : kFwdTile;
   a.keys_per_split = (int)(cdiv(cdiv(shape->n_k, unit), splits) * unit);
@@ -323,13 +389,156 @@ streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, con
   a.c2 = log2e_scale(scale2, shape->d2);
   a.g1 = group1(shape);
   a.g2 = group2(shape);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(fn(a, dec ? a.BH * cdiv(splits, 4) : a.BH * a.nqb * splits, s));
+  streamkl_status st = hip_status(fn(a, dec ? a.BH * cdiv(splits, 4) : a.BH * a.nqb * splits, s));
   if (st != STREAMKL_OK || splits == 1) return st;
   const int64_t rows = a.BH * a.n_q;
   hipLaunchKernelGGL(splitk_merge_kernel, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, s,
-                     (const float*)a.ws, out_kl, out_lse1, out_lse2, a.BH, a.n_q, splits);
+                     (const float*)a.ws, out_kl, out_lse1, out_lse2, a.BH, a.n_q, splits, a.qs);
   return hip_status(hipGetLastError());
+}
+
+// One backward setting of one problem (validated), rows per head qs, ks.
+streamkl_status bwd_launch(int setting, const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                           float scale1, float scale2, const float* kl, const float* lse1, const float* lse2,
+                           const float* d_kl, float* dQ, float* dK, const streamkl_shape* shape, int64_t qs,
+                           int64_t ks, const streamkl_launch* launch, const DeviceInfo& dev, hipStream_t s) {
+  DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
+  DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
+  if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
+  const int mode = plan_bwd(shape, causal, setting, launch, dev.cus);
+
+  BwdArgs a = {};
+  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
+  a.kl = kl; a.lse1 = lse1; a.lse2 = lse2; a.g = d_kl;
+  a.dq = dQ; a.dk = dK;
+  a.BH = shape->B * shape->H;
+  a.n_q = (int)shape->n_q;
+  a.n_k = (int)shape->n_k;
+  a.qs = (int)qs;
+  a.ks = (int)ks;
+  a.causal = causal ? 1 : 0;
+  a.c1 = log2e_scale(scale1, shape->d1);
+  a.c2 = log2e_scale(scale2, shape->d2);
+  a.scale_s = setting == 1 ? plain_scale(scale2, shape->d2) : plain_scale(scale1, shape->d1);
+  a.g1 = group1(shape);
+  a.g2 = group2(shape);
+  const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
+  const int ds = setting == 1 ? shape->d2 : shape->d1;
+  streamkl_status st;
+  if (mode != STREAMKL_BWD_DQ_ONLY) {
+    st = clear_shared_dk(dK, shape, ds, setting == 1 ? a.g2 : a.g1, ks, s);
+    if (st != STREAMKL_OK) return st;
+  }
+  if (mode == STREAMKL_BWD_FUSED) {
+    const DecBwdLaunch fd = decode_shape(shape) ? pick_dec_bwd(shape->dtype, shape->d1, shape->d2) : nullptr;
+    st = fill_zero(dQ, a.BH * qs * (int64_t)ds, s);
+    if (st != STREAMKL_OK) return st;
+    if (fd) {
+      a.nblk = plan_dec_bwd_splits(shape, dev.cus);
+      return hip_status(fd(a, setting, a.BH * a.nblk, s));
+    }
+    a.nblk = (int)nkb;
+    return hip_status(fk(a, setting, true, a.BH * nkb, s));
+  }
+  if (mode != STREAMKL_BWD_DQ_ONLY) {
+    a.nblk = (int)nkb;
+    st = hip_status(fk(a, setting, false, a.BH * nkb, s));
+    if (st != STREAMKL_OK) return st;
+  }
+  if (mode == STREAMKL_BWD_DK_ONLY) return STREAMKL_OK;
+  a.nblk = (int)nqb;
+  return hip_status(fq(a, setting, a.BH * nqb, s));
+}
+
+// The joint kernels for one problem (validated, bf16), rows per head qs, ks.
+streamkl_status joint_launch(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal, float scale1,
+                             float scale2, const float* kl, const float* lse1, const float* lse2, const float* d_kl,
+                             float* dQ1, float* dK1, float* dQ2, float* dK2, const streamkl_shape* shape, int64_t qs,
+                             int64_t ks, int mode, hipStream_t s) {
+  DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
+  DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
+  if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
+  BwdArgs a = {};
+  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
+  a.kl = kl; a.lse1 = lse1; a.lse2 = lse2; a.g = d_kl;
+  a.dk = dK1; a.dk2 = dK2;
+  a.BH = shape->B * shape->H;
+  a.n_q = (int)shape->n_q;
+  a.n_k = (int)shape->n_k;
+  a.qs = (int)qs;
+  a.ks = (int)ks;
+  a.causal = causal ? 1 : 0;
+  a.c1 = log2e_scale(scale1, shape->d1);
+  a.c2 = log2e_scale(scale2, shape->d2);
+  a.scale_s = plain_scale(scale1, shape->d1);
+  a.scale_s2 = plain_scale(scale2, shape->d2);
+  a.g1 = group1(shape);
+  a.g2 = group2(shape);
+  const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
+  streamkl_status st;
+  if (mode != STREAMKL_BWD_DQ_ONLY) {
+    st = clear_shared_dk(dK1, shape, shape->d1, a.g1, ks, s);
+    if (st == STREAMKL_OK) st = clear_shared_dk(dK2, shape, shape->d2, a.g2, ks, s);
+    if (st != STREAMKL_OK) return st;
+    a.nblk = (int)nkb;
+    st = hip_status(fk(a, 3, false, a.BH * nkb, s));
+    if (st != STREAMKL_OK || mode == STREAMKL_BWD_DK_ONLY) return st;
+  }
+  // dQ1 and dQ2: the query-outer kernel once per setting (one kernel holding
+  // both accumulators needs more registers than two waves per SIMD allow, and
+  // measured slower than these two)
+  a.nblk = (int)nqb;
+  a.dq = dQ1;
+  st = hip_status(fq(a, 2, a.BH * nqb, s));
+  if (st != STREAMKL_OK) return st;
+  a.dq = dQ2;
+  a.scale_s = a.scale_s2;
+  return hip_status(fq(a, 1, a.BH * nqb, s));
+}
+
+}  // namespace
+}  // namespace streamkl
+
+extern "C" {
+
+streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                             float scale1, float scale2, float* out_kl, float* out_lse1, float* out_lse2,
+                             const streamkl_shape* shape, const streamkl_launch* launch, void* stream) {
+  streamkl_status st = check_shape(shape, causal);
+  if (st != STREAMKL_OK) return st;
+  if (!Q1 || !K1 || !Q2 || !K2 || !out_kl || !out_lse1 || !out_lse2) return STREAMKL_ERR_INVALID;
+  if (!aligned(Q1, 16) || !aligned(K1, 16) || !aligned(Q2, 16) || !aligned(K2, 16)) return STREAMKL_ERR_INVALID;
+  if (!aligned(out_kl, 4) || !aligned(out_lse1, 4) || !aligned(out_lse2, 4)) return STREAMKL_ERR_INVALID;
+  if (!(scale1 == scale1) || !(scale2 == scale2)) return STREAMKL_ERR_INVALID;
+  if (launch && (launch->num_splits < 0 || launch->bwd_mode < 0 || launch->bwd_mode > 4)) return STREAMKL_ERR_INVALID;
+  DeviceInfo dev;
+  st = device_info(&dev);
+  if (st != STREAMKL_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!ragged(shape))
+    return fwd_launch(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, shape->n_q,
+                      shape->n_k, launch, dev, s);
+  // ragged batch: rows past an element's query length read 0; each element
+  // runs as a problem of its own in the padded tensors
+  if (launch && launch->num_splits > 1 && (!launch->workspace ||
+      launch->workspace_bytes < streamkl_fwd_workspace_bytes(shape, causal, launch)))
+    return STREAMKL_ERR_WORKSPACE;
+  const int64_t rows = shape->B * shape->H * shape->n_q;
+  for (float* o : {out_kl, out_lse1, out_lse2}) {
+    st = fill_zero(o, rows, s);
+    if (st != STREAMKL_OK) return st;
+  }
+  const int64_t es = shape->dtype == STREAMKL_BF16 ? 2 : 4;
+  const int64_t qr = shape->H * shape->n_q, k1r = kv_heads(shape, 1) * shape->n_k, k2r = kv_heads(shape, 2) * shape->n_k;
+  for (int64_t b = 0; b < shape->B; ++b) {
+    const streamkl_shape e = element_shape(shape, b);
+    if (e.n_q == 0) continue;
+    st = fwd_launch(elem(Q1, b, qr, es * e.d1), elem(K1, b, k1r, es * e.d1), elem(Q2, b, qr, es * e.d2),
+                    elem(K2, b, k2r, es * e.d2), causal, scale1, scale2, elem(out_kl, b, qr, 4),
+                    elem(out_lse1, b, qr, 4), elem(out_lse2, b, qr, 4), &e, shape->n_q, shape->n_k, launch, dev, s);
+    if (st != STREAMKL_OK) return st;
+  }
+  return STREAMKL_OK;
 }
 
 int streamkl_bwd_plan(const streamkl_shape* shape, int causal, int setting, const streamkl_launch* launch) {
@@ -361,50 +570,31 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
   DeviceInfo dev;
   st = device_info(&dev);
   if (st != STREAMKL_OK) return st;
-  DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
-  DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
-  if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
-  const int mode = plan_bwd(shape, causal, setting, launch, dev.cus);
-
-  BwdArgs a = {};
-  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
-  a.kl = kl; a.lse1 = lse1; a.lse2 = lse2; a.g = d_kl;
-  a.dq = dQ; a.dk = dK;
-  a.BH = shape->B * shape->H;
-  a.n_q = (int)shape->n_q;
-  a.n_k = (int)shape->n_k;
-  a.causal = causal ? 1 : 0;
-  a.c1 = log2e_scale(scale1, shape->d1);
-  a.c2 = log2e_scale(scale2, shape->d2);
-  a.scale_s = setting == 1 ? plain_scale(scale2, shape->d2) : plain_scale(scale1, shape->d1);
-  a.g1 = group1(shape);
-  a.g2 = group2(shape);
+  if (!pick_dq(shape->dtype, shape->d1, shape->d2) || !pick_dk(shape->dtype, shape->d1, shape->d2))
+    return STREAMKL_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
+  if (!ragged(shape))
+    return bwd_launch(setting, Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ, dK, shape,
+                      shape->n_q, shape->n_k, launch, dev, s);
+  // ragged batch: padded rows of dQ and dK are zero; each element runs as a
+  // problem of its own in the padded tensors
   const int ds = setting == 1 ? shape->d2 : shape->d1;
-  if (mode != STREAMKL_BWD_DQ_ONLY) {
-    st = clear_shared_dk(dK, shape, ds, setting == 1 ? a.g2 : a.g1, s);
+  const int64_t kvs = kv_heads(shape, setting == 1 ? 2 : 1);
+  if (need_dq) st = fill_zero(dQ, shape->B * shape->H * shape->n_q * (int64_t)ds, s);
+  if (st == STREAMKL_OK && need_dk) st = fill_zero(dK, shape->B * kvs * shape->n_k * (int64_t)ds, s);
+  if (st != STREAMKL_OK) return st;
+  const int64_t es = shape->dtype == STREAMKL_BF16 ? 2 : 4;
+  const int64_t qr = shape->H * shape->n_q, k1r = kv_heads(shape, 1) * shape->n_k, k2r = kv_heads(shape, 2) * shape->n_k;
+  for (int64_t b = 0; b < shape->B; ++b) {
+    const streamkl_shape e = element_shape(shape, b);
+    if (e.n_q == 0) continue;
+    st = bwd_launch(setting, elem(Q1, b, qr, es * e.d1), elem(K1, b, k1r, es * e.d1), elem(Q2, b, qr, es * e.d2),
+                    elem(K2, b, k2r, es * e.d2), causal, scale1, scale2, elem(kl, b, qr, 4), elem(lse1, b, qr, 4),
+                    elem(lse2, b, qr, 4), elem(d_kl, b, qr, 4), elem(dQ, b, qr, 4 * ds),
+                    elem(dK, b, kvs * shape->n_k, 4 * ds), &e, shape->n_q, shape->n_k, launch, dev, s);
     if (st != STREAMKL_OK) return st;
   }
-  if (mode == STREAMKL_BWD_FUSED) {
-    const DecBwdLaunch fd = decode_shape(shape) ? pick_dec_bwd(shape->dtype, shape->d1, shape->d2) : nullptr;
-    st = fill_zero(dQ, a.BH * a.n_q * (int64_t)ds, s);
-    if (st != STREAMKL_OK) return st;
-    if (fd) {
-      a.nblk = plan_dec_bwd_splits(shape, dev.cus);
-      return hip_status(fd(a, setting, a.BH * a.nblk, s));
-    }
-    a.nblk = (int)nkb;
-    return hip_status(fk(a, setting, true, a.BH * nkb, s));
-  }
-  if (mode != STREAMKL_BWD_DQ_ONLY) {
-    a.nblk = (int)nkb;
-    st = hip_status(fk(a, setting, false, a.BH * nkb, s));
-    if (st != STREAMKL_OK) return st;
-  }
-  if (mode == STREAMKL_BWD_DK_ONLY) return STREAMKL_OK;
-  a.nblk = (int)nqb;
-  return hip_status(fq(a, setting, a.BH * nqb, s));
+  return STREAMKL_OK;
 }
 
 streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
@@ -435,44 +625,34 @@ streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q
     return streamkl_bwd(1, Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ2, dK2, shape, launch,
                         stream);
   }
-  DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
-  DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
-  if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
-
-  BwdArgs a = {};
-  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
-  a.kl = kl; a.lse1 = lse1; a.lse2 = lse2; a.g = d_kl;
-  a.dk = dK1; a.dk2 = dK2;
-  a.BH = shape->B * shape->H;
-  a.n_q = (int)shape->n_q;
-  a.n_k = (int)shape->n_k;
-  a.causal = causal ? 1 : 0;
-  a.c1 = log2e_scale(scale1, shape->d1);
-  a.c2 = log2e_scale(scale2, shape->d2);
-  a.scale_s = plain_scale(scale1, shape->d1);
-  a.scale_s2 = plain_scale(scale2, shape->d2);
-  a.g1 = group1(shape);
-  a.g2 = group2(shape);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
-  if (mode != STREAMKL_BWD_DQ_ONLY) {
-    st = clear_shared_dk(dK1, shape, shape->d1, a.g1, s);
-    if (st == STREAMKL_OK) st = clear_shared_dk(dK2, shape, shape->d2, a.g2, s);
-    if (st != STREAMKL_OK) return st;
-    a.nblk = (int)nkb;
-    st = hip_status(fk(a, 3, false, a.BH * nkb, s));
-    if (st != STREAMKL_OK || mode == STREAMKL_BWD_DK_ONLY) return st;
+  if (!ragged(shape))
+    return joint_launch(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ1, dK1, dQ2, dK2, shape,
+                        shape->n_q, shape->n_k, mode, s);
+  const int64_t kv1 = kv_heads(shape, 1), kv2 = kv_heads(shape, 2);
+  const int64_t BHQ = shape->B * shape->H * shape->n_q;
+  if (need_dq) {
+    st = fill_zero(dQ1, BHQ * shape->d1, s);
+    if (st == STREAMKL_OK) st = fill_zero(dQ2, BHQ * shape->d2, s);
   }
-  // dQ1 and dQ2: the query-outer kernel once per setting (one kernel holding
-  // both accumulators needs more registers than two waves per SIMD allow, and
-  // measured slower than these two)
-  a.nblk = (int)nqb;
-  a.dq = dQ1;
-  st = hip_status(fq(a, 2, a.BH * nqb, s));
+  if (st == STREAMKL_OK && need_dk) {
+    st = fill_zero(dK1, shape->B * kv1 * shape->n_k * shape->d1, s);
+    if (st == STREAMKL_OK) st = fill_zero(dK2, shape->B * kv2 * shape->n_k * shape->d2, s);
+  }
   if (st != STREAMKL_OK) return st;
-  a.dq = dQ2;
-  a.scale_s = a.scale_s2;
-  return hip_status(fq(a, 1, a.BH * nqb, s));
+  const int64_t es = 2;
+  const int64_t qr = shape->H * shape->n_q, k1r = kv1 * shape->n_k, k2r = kv2 * shape->n_k;
+  const int d1 = shape->d1, d2 = shape->d2;
+  for (int64_t b = 0; b < shape->B; ++b) {
+    const streamkl_shape e = element_shape(shape, b);
+    if (e.n_q == 0) continue;
+    st = joint_launch(elem(Q1, b, qr, es * d1), elem(K1, b, k1r, es * d1), elem(Q2, b, qr, es * d2),
+                      elem(K2, b, k2r, es * d2), causal, scale1, scale2, elem(kl, b, qr, 4), elem(lse1, b, qr, 4),
+                      elem(lse2, b, qr, 4), elem(d_kl, b, qr, 4), elem(dQ1, b, qr, 4 * d1), elem(dK1, b, k1r, 4 * d1),
+                      elem(dQ2, b, qr, 4 * d2), elem(dK2, b, k2r, 4 * d2), &e, shape->n_q, shape->n_k, mode, s);
+    if (st != STREAMKL_OK) return st;
+  }
+  return STREAMKL_OK;
 }
 
 }  // extern "C"

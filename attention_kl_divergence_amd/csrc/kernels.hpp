@@ -51,6 +51,8 @@ struct FwdArgs {
   int causal;
   float c1, c2;        // scale_t * log2(e)
   int g1, g2;          // query heads per key head of each model (1: no sharing)
+  int qs, ks;          // rows per head in memory of Q (and the per-row vectors) and of K: n_q and
+                       // n_k, or more when the batch element's lengths are padded
 };
 
 struct BwdArgs {
@@ -73,6 +75,7 @@ struct BwdArgs {
   float scale_s;       // scale of the model that receives gradients (joint: model 1)
   float scale_s2;      // joint: scale of model 2
   int g1, g2;          // query heads per key head of each model (1: no sharing)
+  int qs, ks;          // rows per head in memory of Q, dQ and the per-row vectors, and of K and dK
 };
 
 typedef __bf16 bf16x4_lds __attribute__((ext_vector_type(4)));
@@ -516,10 +519,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int qrow = q0 + col;
   const int off = a.n_k - a.n_q;
 
-  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
-  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
+  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.qs * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
+  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.qs * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
 
   const int kbeg = z * a.keys_per_split;
   int kend = min(a.n_k, kbeg + a.keys_per_split);
@@ -569,7 +572,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   st = merge_state(st, shfl_xor_state(st, 32));
   if (grp == 0 && qrow < a.n_q) {
-    const int64_t r = bh * a.n_q + qrow;
+    const int64_t r = bh * a.qs + qrow;
     if (a.nsplit == 1) {
       finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
     } else {
@@ -637,10 +640,10 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
   const int z = (int)(blockIdx.x % nwg) * 4 + wave;
   const int off = a.n_k - a.n_q;
 
-  const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
-  const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
+  const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.qs * D1;
+  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
+  const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.qs * D2;
+  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
   dec_stage_q<D1>(sQ1, Q1, a.n_q, tid);
   dec_stage_q<D2>(sQ2, Q2, a.n_q, tid);
   __syncthreads();
@@ -769,10 +772,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const int qrow = q0 + col;
   const int off = a.n_k - a.n_q;
 
-  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
-  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
+  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.qs * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
+  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.qs * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
 
   int kend = a.n_k;
   if (a.causal) kend = min(kend, min(a.n_q, qwg0 + 32 * NW) - 1 + off + 1);
@@ -842,7 +845,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   st = merge_state(st, shfl_xor_state(st, 32));
   if (grp == 0 && qrow < a.n_q) {
-    const int64_t r = bh * a.n_q + qrow;
+    const int64_t r = bh * a.qs + qrow;
     finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
   }
 }
@@ -1037,10 +1040,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int qrow = q0 + col;
   const int off = a.n_k - a.n_q;
 
-  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
-  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
+  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.qs * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
+  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.qs * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
 
   int kend = a.n_k;
   if (a.causal) kend = min(kend, min(a.n_q, qb * 32 * NW + 32 * NW) - 1 + off + 1);
@@ -1059,7 +1062,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   for (int s = 0; s < S1; ++s) qf1[s] = frag_global<T, D1>(Q1, qrow, a.n_q - 1, qv, s, grp);
 #pragma unroll
   for (int s = 0; s < S2; ++s) qf2[s] = frag_global<T, D2>(Q2, qrow, a.n_q - 1, qv, s, grp);
-  const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.n_q + qrow, qv);
+  const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.qs + qrow, qv);
   const float row_sign = SETTING == 1 ? rg.gs : 1.f;
 
   f32x16 dqa[NB];
@@ -1156,7 +1159,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       const int r = acc_row(e, grp);
       const int q = q0 + r;
       const float v = ((neg >> r) & 1) ? -dqa[nb][e] : dqa[nb][e];
-      if (q < a.n_q) a.dq[(bh * a.n_q + q) * DS + nb * 32 + col] = v;
+      if (q < a.n_q) a.dq[(bh * a.qs + q) * DS + nb * 32 + col] = v;
     }
 }
 
@@ -1206,10 +1209,10 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   const int krow = kwave + col;
   const int off = a.n_k - a.n_q;
 
-  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
-  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
+  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.qs * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
+  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.qs * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
   const T* KS = SETTING == 1 ? K2 : K1;
 
   // Query tiles are visited from the last one down: under a causal mask every
@@ -1225,7 +1228,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   // they are scaled and stored to LDS after the tile's compute, behind a
   // scheduling barrier, so their load latency overlaps the whole tile
   auto load_stats = [&](int q0, RawRowGrad& r) {
-    r = load_rowgrad_raw<SETTING>(a, bh * a.n_q + q0 + tid, tid < BQ && q0 + tid < a.n_q);
+    r = load_rowgrad_raw<SETTING>(a, bh * a.qs + q0 + tid, tid < BQ && q0 + tid < a.n_q);
   };
   auto store_stats = [&](int buf, const RawRowGrad& raw) {
     const RowGrad rg = scale_rowgrad<SETTING>(a, raw);
@@ -1437,7 +1440,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int q = qb0 + acc_row(e, grp);
-          if (q < a.n_q) atomicAdd(a.dq + (bh * a.n_q + q) * DS + dcol, dqa[e]);
+          if (q < a.n_q) atomicAdd(a.dq + (bh * a.qs + q) * DS + dcol, dqa[e]);
         }
       }
     }
@@ -1458,7 +1461,7 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
   // query head); without sharing each element is stored once
   auto put = [&](float* dk, int g, const f32x16* acc, auto D_) {
     constexpr int D = decltype(D_)::value;
-    float* base = dk + key_head(bh, g) * a.n_k * D + col;
+    float* base = dk + key_head(bh, g) * a.ks * D + col;
     if (g > 1) {
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb)
@@ -1524,10 +1527,10 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
   const int z = (int)(blockIdx.x % a.nblk);
   const int off = a.n_k - a.n_q;
 
-  const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.n_q * D1;
-  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.n_k * D1;
-  const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.n_q * D2;
-  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.n_k * D2;
+  const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.qs * D1;
+  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
+  const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.qs * D2;
+  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
 
   const int ntile = (a.n_k + BK - 1) / BK;
   const int count = z < ntile ? (ntile - z + a.nblk - 1) / a.nblk : 0;
@@ -1544,7 +1547,7 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
   dec_stage_q<D2>(sQ2, Q2, a.n_q, tid);
   // lane column col is query row col: its statistics are fixed for the kernel
   const bool qv = col < a.n_q;
-  const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.n_q + col, qv);
+  const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.qs + col, qv);
   const float c1 = a.c1, c2 = a.c2;
   // last key this lane's query sees, and the last key of which every query
   // of a wave block is visible (beyond it blocks take the element mask)
@@ -1612,7 +1615,7 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
       for (int nb = 0; nb < NB; ++nb) dka[nb] = MF::run(af, qcol[h][nb], dka[nb]);
     }
     const int gs = SETTING == 1 ? a.g2 : a.g1;
-    float* dk = a.dk + (key_head(bh, gs) * a.n_k + kw) * (int64_t)DS + col;
+    float* dk = a.dk + (key_head(bh, gs) * a.ks + kw) * (int64_t)DS + col;
     const int kleft = a.n_k - kw;
     if (gs > 1) {
       // query heads sharing a key head add their parts into the cleared dK
@@ -1645,7 +1648,7 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
   }
 
   if (qv) {
-    float* dq = a.dq + (bh * a.n_q + col) * (int64_t)DS;
+    float* dq = a.dq + (bh * a.qs + col) * (int64_t)DS;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll

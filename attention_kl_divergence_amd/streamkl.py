@@ -31,13 +31,30 @@ class StreamKLError(RuntimeError):
 
 
 class Shape(ctypes.Structure):
-    # kv_heads1/kv_heads2: key heads of each model (0 = H, one per query head)
+    # kv_heads1/kv_heads2: key heads of each model (0 = H, one per query head);
+    # q_len/k_len: host arrays of B lengths for ragged batches (NULL = full)
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("n_q", ctypes.c_int64), ("n_k", ctypes.c_int64),
                 ("d1", ctypes.c_int32), ("d2", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("kv_heads1", ctypes.c_int32), ("kv_heads2", ctypes.c_int32)]
+                ("kv_heads1", ctypes.c_int32), ("kv_heads2", ctypes.c_int32),
+                ("q_len", ctypes.POINTER(ctypes.c_int64)), ("k_len", ctypes.POINTER(ctypes.c_int64))]
+
+    def set_lengths(self, q_len=None, k_len=None):
+        """Ragged batch: per batch element query and key lengths (sequences of
+        B ints, or None for the padded sizes).  The arrays live on this object."""
+        for name, v in (("q_len", q_len), ("k_len", k_len)):
+            if v is None:
+                setattr(self, name, None)
+                continue
+            v = [int(x) for x in v]
+            if len(v) != self.B:
+                raise ValueError(f"{name} needs {self.B} lengths")
+            arr = (ctypes.c_int64 * len(v))(*v)
+            setattr(self, "_" + name, arr)  # keep the array alive
+            setattr(self, name, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+        return self
 
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class Launch(ctypes.Structure):
@@ -156,14 +173,14 @@ def bwd_plan(shape: Shape, causal: bool, setting: int, bwd_mode: int = BWD_AUTO)
 
 
 def streamkl_fwd(q1, k1, q2, k2, causal: bool, scale1: float = 0.0, scale2: float = 0.0,
-                 num_splits: int = 0, out=None, workspace=None):
+                 num_splits: int = 0, out=None, workspace=None, q_len=None, k_len=None):
     """Forward: returns (kl, lse1, lse2), fp32 [B, H, n_q].
 
     num_splits: 0 = library's choice, 1 = no key split, k = k key splits.
     out: optional preallocated (kl, lse1, lse2).  workspace: optional uint8
     device tensor (allocated here when a split needs one and none is given).
     """
-    shp = shape_of(q1, k1, q2, k2)
+    shp = shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
     dev = q1.device
     if out is None:
         kw = dict(device=dev, dtype=torch.float32)
@@ -184,12 +201,14 @@ def streamkl_fwd(q1, k1, q2, k2, causal: bool, scale1: float = 0.0, scale2: floa
 
 
 def streamkl_bwd(setting: int, q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
-                 scale1: float = 0.0, scale2: float = 0.0, bwd_mode: int = BWD_AUTO, out=None):
+                 scale1: float = 0.0, scale2: float = 0.0, bwd_mode: int = BWD_AUTO, out=None,
+                 q_len=None, k_len=None):
     """Backward: returns (dQ, dK) in fp32 for the trained model.
 
     setting 1 -> (dQ2, dK2) with P1 fixed; setting 2 -> (dQ1, dK1) with P2 fixed.
+    q_len, k_len: ragged-batch lengths, as given to the forward.
     """
-    shp = shape_of(q1, k1, q2, k2)
+    shp = shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
     dev = q1.device
     ds = shp.d2 if setting == 1 else shp.d1
     if out is None:
@@ -212,10 +231,11 @@ def streamkl_bwd(setting: int, q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_k
 
 
 def streamkl_bwd_joint(q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
-                       scale1: float = 0.0, scale2: float = 0.0, bwd_mode: int = BWD_AUTO, out=None):
+                       scale1: float = 0.0, scale2: float = 0.0, bwd_mode: int = BWD_AUTO, out=None,
+                       q_len=None, k_len=None):
     """Joint backward: returns (dQ1, dK1, dQ2, dK2) in fp32, the gradients to
     both models in one pass (equal to setting 2 and setting 1 of streamkl_bwd)."""
-    shp = shape_of(q1, k1, q2, k2)
+    shp = shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
     dev = q1.device
     if out is None:
         kw = dict(device=dev, dtype=torch.float32)
@@ -240,10 +260,11 @@ def streamkl_bwd_joint(q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
 
 class _KLFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q1, k1, q2, k2, causal, scale1, scale2, bwd_mode):
-        kl, lse1, lse2 = streamkl_fwd(q1, k1, q2, k2, causal, scale1, scale2)
+    def forward(ctx, q1, k1, q2, k2, causal, scale1, scale2, bwd_mode, q_len, k_len):
+        kl, lse1, lse2 = streamkl_fwd(q1, k1, q2, k2, causal, scale1, scale2, q_len=q_len, k_len=k_len)
         ctx.save_for_backward(q1, k1, q2, k2, kl, lse1, lse2)
         ctx.causal, ctx.scale1, ctx.scale2, ctx.bwd_mode = causal, scale1, scale2, bwd_mode
+        ctx.lens = dict(q_len=q_len, k_len=k_len)
         return kl
 
     @staticmethod
@@ -255,26 +276,28 @@ class _KLFunction(torch.autograd.Function):
         student = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
         if teacher and student:
             dq1, dk1, dq2, dk2 = streamkl_bwd_joint(q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1,
-                                                    ctx.scale2, ctx.bwd_mode)
-            return (dq1.to(q1.dtype), dk1.to(k1.dtype), dq2.to(q2.dtype), dk2.to(k2.dtype), None, None, None, None)
+                                                    ctx.scale2, ctx.bwd_mode, **ctx.lens)
+            return (dq1.to(q1.dtype), dk1.to(k1.dtype), dq2.to(q2.dtype), dk2.to(k2.dtype),
+                    None, None, None, None, None, None)
         if student:
             dq2, dk2 = streamkl_bwd(1, q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1, ctx.scale2,
-                                    ctx.bwd_mode)
+                                    ctx.bwd_mode, **ctx.lens)
             grads[2], grads[3] = dq2.to(q2.dtype), dk2.to(k2.dtype)
         if teacher:
             dq1, dk1 = streamkl_bwd(2, q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1, ctx.scale2,
-                                    ctx.bwd_mode)
+                                    ctx.bwd_mode, **ctx.lens)
             grads[0], grads[1] = dq1.to(q1.dtype), dk1.to(k1.dtype)
-        return (*grads, None, None, None, None)
+        return (*grads, None, None, None, None, None, None)
 
 
 def attention_kl(q1, k1, q2, k2, causal: bool = False, scale1: float = 0.0, scale2: float = 0.0,
-                 bwd_mode: int = BWD_AUTO):
+                 bwd_mode: int = BWD_AUTO, q_len=None, k_len=None):
     """Per-row KL(P1 || P2) as an autograd function (gradients by streamkl_bwd).
 
     Gradients flow to whichever of (Q1, K1) / (Q2, K2) require grad: the
     student side uses setting 1 (teacher distribution held fixed), the
     teacher side setting 2 (student distribution held fixed), and both
-    sides together the joint backward.
+    sides together the joint backward.  q_len, k_len: per batch element
+    lengths of a ragged batch in padded tensors (padded rows give 0).
     """
-    return _KLFunction.apply(q1, k1, q2, k2, causal, scale1, scale2, bwd_mode)
+    return _KLFunction.apply(q1, k1, q2, k2, causal, scale1, scale2, bwd_mode, q_len, k_len)

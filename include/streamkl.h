@@ -81,6 +81,15 @@ typedef struct {
    * kv_heads_t must divide H.  dK_t is then [B, kv_heads_t, n_k, d_t], the
    * sum over the query heads that share each key head. */
   int32_t kv_heads1, kv_heads2;
+  /* Ragged batches (HOST arrays of B lengths, or NULL for all n_q / n_k):
+   * batch element b uses its first q_len[b] query rows and k_len[b] key rows
+   * of the padded tensors (n_q, n_k rows per head in memory), with
+   * 0 <= q_len[b] <= n_q, 0 <= k_len[b] <= n_k, k_len[b] >= 1 when
+   * q_len[b] >= 1, and q_len[b] <= k_len[b] under a causal mask (aligned
+   * bottom-right within the element).  Outputs of padded rows (KL, LSE, dQ,
+   * dK) are 0.  Read during the call only. */
+  const int64_t* q_len;
+  const int64_t* k_len;
 } streamkl_shape;
 
 /* Launch options (host struct; a NULL pointer means all defaults). */
@@ -180,8 +189,8 @@ const char* streamkl_status_string(int status);
 /* hipError_t of the last STREAMKL_ERR_HIP returned on this thread (0 if none). */
 int streamkl_last_hip_error(void);
 
-/* Library version, for the Python binding's load check (2: streamkl_shape
- * carries kv_heads1, kv_heads2). */
+/* Library version, for the Python binding's load check (3: streamkl_shape
+ * carries kv_heads1, kv_heads2 and the ragged-batch lengths). */
 int streamkl_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = sk.library()
-    assert lib.streamkl_version() == sk.ABI_VERSION == 2
+    assert lib.streamkl_version() == sk.ABI_VERSION == 3
     assert lib.streamkl_status_string(0) == b"ok"
     assert lib.streamkl_status_string(4) == b"HIP runtime error"
     assert lib.streamkl_status_string(99) == b"unknown status"
@@ -102,6 +102,19 @@ def test_key_head_counts_must_divide_h(kv1, kv2):
     assert _fwd(s, ptr=16) == sk.ERR_INVALID
     assert _bwd(1, s, ptr=16) == sk.ERR_INVALID
     assert _joint(s, ptr=16) == sk.ERR_INVALID
+
+
+@pytest.mark.parametrize("q_len,k_len,causal", [
+    ([64, 65], None, 0),   # past the padded query count
+    (None, [64, -1], 0),   # negative key length
+    ([10, 5], [0, 64], 0),  # query rows without any key
+    ([40, 64], [30, 64], 1),  # causal needs q_len <= k_len
+])
+def test_ragged_lengths_are_checked(q_len, k_len, causal):
+    s = shape(B=2).set_lengths(q_len, k_len)
+    assert _fwd(s, ptr=16, causal=causal) == sk.ERR_INVALID
+    assert _bwd(1, s, ptr=16, causal=causal) == sk.ERR_INVALID
+    assert _joint(s, ptr=16, causal=causal) == sk.ERR_INVALID
 
 
 def test_causal_needs_nq_le_nk():
