@@ -19,5 +19,6 @@ from .streamkl import (  # noqa: F401
     shape_of,
     streamkl_bwd,
     streamkl_bwd_joint,
+    kl_loss,
     streamkl_fwd,
 )

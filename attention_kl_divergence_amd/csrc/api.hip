@@ -35,6 +35,23 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, 
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// The distillation loss from the per-row KL: sum_i w_i KL_i (w = 1/rows
+// when weights is NULL), in one workgroup so the summation order is fixed:
+// each thread sums a strided subset in fp64, then a tree over the threads.
+__global__ __launch_bounds__(1024) void kl_loss_kernel(const float* __restrict__ kl, const float* __restrict__ w,
+                                                      int64_t rows, float* out) {
+  __shared__ double part[1024];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < rows; i += 1024) acc += (double)kl[i] * (w ? (double)w[i] : 1.0);
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int n = 512; n > 0; n >>= 1) {
+    if ((int)threadIdx.x < n) part[threadIdx.x] += part[threadIdx.x + n];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = (float)(w ? part[0] : part[0] / (double)rows);
+}
+
 // the same for any alignment and count
 __global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* __restrict__ p, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
@@ -653,6 +670,16 @@ streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q
     if (st != STREAMKL_OK) return st;
   }
   return STREAMKL_OK;
+}
+
+streamkl_status streamkl_kl_loss(const float* kl, const float* weights, int64_t rows, float* out, void* stream) {
+  if (!kl || !out || rows < 1) return STREAMKL_ERR_INVALID;
+  if (!aligned(kl, 4) || !aligned(out, 4) || (weights && !aligned(weights, 4))) return STREAMKL_ERR_INVALID;
+  DeviceInfo dev;
+  streamkl_status st = device_info(&dev);
+  if (st != STREAMKL_OK) return st;
+  hipLaunchKernelGGL(kl_loss_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), kl, weights, rows, out);
+  return hip_status(hipGetLastError());
 }
 
 }  // extern "C"

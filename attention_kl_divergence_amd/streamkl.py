@@ -79,6 +79,8 @@ def _lib():
         lib.streamkl_bwd.restype = i32
         lib.streamkl_bwd_joint.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, vp, vp, vp, vp, vp, vp, sp, lp, vp]
         lib.streamkl_bwd_joint.restype = i32
+        lib.streamkl_kl_loss.argtypes = [vp, vp, ctypes.c_int64, vp, vp]
+        lib.streamkl_kl_loss.restype = i32
         lib.streamkl_fwd_workspace_bytes.argtypes = [sp, i32, lp]
         lib.streamkl_fwd_workspace_bytes.restype = sz
         lib.streamkl_fwd_plan.argtypes = [sp, i32, lp]
@@ -256,6 +258,22 @@ def streamkl_bwd_joint(q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
                                    _stream(dev))
     _check(st, "streamkl_bwd_joint")
     return tuple(out)
+
+
+def kl_loss(kl, weights=None, out=None):
+    """sum_i w_i KL_i over every row of kl (the mean KL when weights is None),
+    as a 0-dim fp32 tensor computed by the library (deterministic)."""
+    if kl.dtype != torch.float32 or not kl.is_contiguous():
+        raise ValueError("kl must be contiguous fp32")
+    if weights is not None and (weights.dtype != torch.float32 or not weights.is_contiguous()
+                                or weights.numel() != kl.numel() or weights.device != kl.device):
+        raise ValueError("weights must be contiguous fp32 with one value per row of kl")
+    if out is None:
+        out = torch.empty((), device=kl.device, dtype=torch.float32)
+    st = _lib().streamkl_kl_loss(kl.data_ptr(), weights.data_ptr() if weights is not None else None,
+                                 kl.numel(), out.data_ptr(), _stream(kl.device))
+    _check(st, "streamkl_kl_loss")
+    return out
 
 
 class _KLFunction(torch.autograd.Function):

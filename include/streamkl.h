@@ -183,6 +183,18 @@ streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q
                                    const streamkl_shape* shape, const streamkl_launch* launch,
                                    void* stream);
 
+/*
+ * Distillation loss from the forward's per-row KL: *out = sum_i w_i KL_i
+ * over rows = B*H*n_q rows, or the mean KL when weights is NULL (device
+ * pointers: kl and weights fp32 [rows], out one fp32).  Deterministic: one
+ * workgroup sums in a fixed order, in fp64.  Its gradient with respect to
+ * KL_i is w_i (or 1/rows), the d_kl that streamkl_bwd takes.  The loss is
+ * the quantity the pages distil with; the fused kernels above keep it per
+ * row so callers can weight, mask or reduce it as they need.
+ */
+streamkl_status streamkl_kl_loss(const float* kl, const float* weights, int64_t rows, float* out,
+                                 void* stream);
+
 /* Static text for a status code. */
 const char* streamkl_status_string(int status);
 

@@ -117,6 +117,15 @@ def test_ragged_lengths_are_checked(q_len, k_len, causal):
     assert _joint(s, ptr=16, causal=causal) == sk.ERR_INVALID
 
 
+def test_kl_loss_checks_arguments():
+    lib = sk.library()
+    p = ctypes.c_void_p(16)
+    assert lib.streamkl_kl_loss(None, None, 10, p, None) == sk.ERR_INVALID
+    assert lib.streamkl_kl_loss(p, None, 0, p, None) == sk.ERR_INVALID
+    assert lib.streamkl_kl_loss(p, None, 10, None, None) == sk.ERR_INVALID
+    assert lib.streamkl_kl_loss(ctypes.c_void_p(18), None, 10, p, None) == sk.ERR_INVALID
+
+
 def test_causal_needs_nq_le_nk():
     assert _fwd(shape(n_q=65, n_k=64), ptr=8, causal=1) == sk.ERR_INVALID
 

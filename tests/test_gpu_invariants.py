@@ -161,3 +161,21 @@ def test_library_allocates_no_device_memory(n_q, n_k, cuda_device):
     for _ in range(3):
         step()
     assert torch.cuda.mem_get_info(cuda_device)[0] == free0
+
+
+def test_kl_loss_reduction(cuda_device):
+    """streamkl_kl_loss: the weighted sum and the mean of the per-row KL match
+    an fp64 sum on the host, and repeated calls are bitwise equal."""
+    w = W("loss", n_q=700, n_k=700, H=3)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    kl, _, _ = sk.streamkl_fwd(q1, k1, q2, k2, True)
+    wt = workloads.upstream_grad(w, cuda_device, "random")
+    klh, wth = to_np(kl).ravel(), to_np(wt).ravel()
+    s = sk.kl_loss(kl, wt)
+    m = sk.kl_loss(kl)
+    assert abs(s.item() - float((klh * wth).sum())) <= 1e-6 * max(1.0, abs(float((klh * wth).sum())))
+    assert abs(m.item() - float(klh.mean())) <= 1e-6 * max(1.0, float(klh.mean()))
+    assert torch.equal(s, sk.kl_loss(kl, wt)) and torch.equal(m, sk.kl_loss(kl))
+    # one row: the value itself
+    one = torch.tensor([0.25], device=cuda_device)
+    assert sk.kl_loss(one).item() == 0.25
