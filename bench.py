@@ -308,7 +308,7 @@ def main():
     out["library_device_allocation_bytes"] = int(free0 - torch.cuda.mem_get_info(dev)[0])
     if args.compare_modes:
         alt = {}
-        for setting in w.settings:
+        for setting in (() if joint else w.settings):
             ds = w.d2 if setting == 1 else w.d1
             other = sk.BWD_SEPARATE if modes[setting] == sk.BWD_FUSED else sk.BWD_FUSED
             dq = torch.empty((w.B, w.H, w.n_q, ds), **f32)
