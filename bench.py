@@ -48,6 +48,8 @@ def parse():
 
 
 def pairs_of(w):
+    if w.lengths:  # ragged batch: each element with its own length (query = key)
+        return sum(w.H * (n * (n + 1) // 2 if w.causal else n * n) for n in w.lengths)
     n_q, n_k = w.n_q, w.n_k
     if not w.causal:
         return w.B * w.H * n_q * n_k
@@ -69,7 +71,7 @@ def cpu_baseline(w, rows_wanted, head_bytes=None):
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    small = w.with_(H=1)
+    small = w.with_(H=1, B=1, lengths=(), kv_heads=0)
     q1, k1, q2, k2 = workloads.generate(small, "cpu")
     g = workloads.upstream_grad(small, "cpu", "mean")
     hi = [t[0, 0].float().numpy().astype(np.float64) for t in (q1, k1, q2, k2)]
@@ -112,7 +114,10 @@ def main():
     torch.cuda.set_device(dev)
     q1, k1, q2, k2 = workloads.generate(w, dev)
     g = workloads.upstream_grad(w, dev, "mean")
-    shp = sk.shape_of(q1, k1, q2, k2)
+    # ragged workloads: the same lengths for queries and keys of each element
+    lens = dict(q_len=list(w.lengths), k_len=list(w.lengths)) if w.lengths else {}
+    shp = sk.shape_of(q1, k1, q2, k2).set_lengths(**lens)
+    kv = k1.shape[1]
     mode = {"auto": sk.BWD_AUTO, "fused": sk.BWD_FUSED, "separate": sk.BWD_SEPARATE}[args.bwd_mode]
     splits = sk.fwd_plan(shp, w.causal)
 
@@ -123,25 +128,27 @@ def main():
 
     # Each kernel is launched by its own ABI call so HIP events on the launch
     # stream bracket exactly one kernel (split-K adds its merge kernel).
-    calls = [("fwd", lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, out=(kl, l1, l2), workspace=ws))]
+    calls = [("fwd", lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, out=(kl, l1, l2), workspace=ws, **lens))]
     modes = {}
     joint = args.joint and tuple(sorted(w.settings)) == (1, 2)
     if joint:
-        jo = (torch.empty((w.B, w.H, w.n_q, w.d1), **f32), torch.empty((w.B, w.H, w.n_k, w.d1), **f32),
-              torch.empty((w.B, w.H, w.n_q, w.d2), **f32), torch.empty((w.B, w.H, w.n_k, w.d2), **f32))
+        jo = (torch.empty((w.B, w.H, w.n_q, w.d1), **f32), torch.empty((w.B, kv, w.n_k, w.d1), **f32),
+              torch.empty((w.B, w.H, w.n_q, w.d2), **f32), torch.empty((w.B, kv, w.n_k, w.d2), **f32))
         calls.append(("bwdj_dk", lambda: sk.streamkl_bwd_joint(q1, k1, q2, k2, w.causal, kl, l1, l2, g,
-                                                                bwd_mode=sk.BWD_DK_ONLY, out=(None, jo[1], None, jo[3]))))
+                                                                bwd_mode=sk.BWD_DK_ONLY, out=(None, jo[1], None, jo[3]),
+                                                                **lens)))
         calls.append(("bwdj_dq", lambda: sk.streamkl_bwd_joint(q1, k1, q2, k2, w.causal, kl, l1, l2, g,
-                                                                bwd_mode=sk.BWD_DQ_ONLY, out=(jo[0], None, jo[2], None))))
+                                                                bwd_mode=sk.BWD_DQ_ONLY, out=(jo[0], None, jo[2], None),
+                                                                **lens)))
     for setting in (() if joint else w.settings):
         ds = w.d2 if setting == 1 else w.d1
         dq = torch.empty((w.B, w.H, w.n_q, ds), **f32)
-        dk = torch.empty((w.B, w.H, w.n_k, ds), **f32)
+        dk = torch.empty((w.B, kv, w.n_k, ds), **f32)
         plan = sk.bwd_plan(shp, w.causal, setting, mode)
         modes[setting] = plan
 
         def mk(m, o, st=setting):
-            return lambda: sk.streamkl_bwd(st, q1, k1, q2, k2, w.causal, kl, l1, l2, g, bwd_mode=m, out=o)
+            return lambda: sk.streamkl_bwd(st, q1, k1, q2, k2, w.causal, kl, l1, l2, g, bwd_mode=m, out=o, **lens)
         if plan == sk.BWD_FUSED:
             calls.append((f"bwd{setting}_fused", mk(sk.BWD_FUSED, (dq, dk))))
         else:
@@ -267,7 +274,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "n_q": w.n_q, "n_k": w.n_k, "d1": w.d1, "d2": w.d2,
                    "causal": w.causal, "bwd_settings": list(w.settings),
                    "bwd_modes": {str(k): names[v] for k, v in modes.items()} if not joint else {"1+2": "joint"},
-                   "fwd_splits": splits, "parallelism": "single GPU"},
+                   "fwd_splits": splits, "parallelism": "single GPU",
+                   **({"kv_heads": kv} if kv != w.H else {}),
+                   **({"lengths": list(w.lengths)} if w.lengths else {})},
         "pct_of_mfma_peak": round(100 * value / peak, 2),
         "per_kernel_ms": {k: round(v, 4) for k, v in per_call.items()},
         "algorithmic_tflop_per_step": round(flops_step / 1e12, 4),
@@ -288,14 +297,14 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1)
         abl = {"fwd_split_ms": round(per_call["fwd"], 4)}
-        t1 = once(lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, num_splits=1))
+        t1 = once(lambda: sk.streamkl_fwd(q1, k1, q2, k2, w.causal, num_splits=1, **lens))
         abl["fwd_one_split_ms"] = round(t1, 4)
         abl["split_speedup"] = round(t1 / per_call["fwd"], 2)
         for setting in w.settings:
             name = f"bwd{setting}_fused"
             if name in per_call:
                 t2 = once(lambda: sk.streamkl_bwd(setting, q1, k1, q2, k2, w.causal, kl, l1, l2, g,
-                                                  bwd_mode=sk.BWD_SEPARATE))
+                                                  bwd_mode=sk.BWD_SEPARATE, **lens))
                 abl[f"bwd{setting}_separate_ms"] = round(t2, 4)
                 abl[f"bwd{setting}_fused_speedup"] = round(t2 / per_call[name], 2)
         out["ablation"] = abl
@@ -312,9 +321,9 @@ def main():
             ds = w.d2 if setting == 1 else w.d1
             other = sk.BWD_SEPARATE if modes[setting] == sk.BWD_FUSED else sk.BWD_FUSED
             dq = torch.empty((w.B, w.H, w.n_q, ds), **f32)
-            dk = torch.empty((w.B, w.H, w.n_k, ds), **f32)
+            dk = torch.empty((w.B, kv, w.n_k, ds), **f32)
             run = lambda: sk.streamkl_bwd(setting, q1, k1, q2, k2, w.causal, kl, l1, l2, g,  # noqa: E731
-                                          bwd_mode=other, out=(dq, dk))
+                                          bwd_mode=other, out=(dq, dk), **lens)
             run()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)

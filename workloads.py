@@ -34,6 +34,8 @@ class Workload:
     independent: bool   # draw the student independently (different head dims)
     seed: int
     settings: tuple = (1,)  # backward settings one step runs (empty: forward only)
+    kv_heads: int = 0       # key heads of both models (0: one per query head)
+    lengths: tuple = ()     # ragged batch: per batch element lengths (query = key), () for none
 
     @property
     def torch_dtype(self):
@@ -59,12 +61,19 @@ WORKLOADS = {
         Workload("decode-bwd-h32-q1-k512k-d128-bf16", 1, 32, 1, 524288, 128, 128, "bf16", False, 0.5, False, 4, (1,)),
         Workload("decode-bwd-h32-q16-k512k-d128-bf16", 1, 32, 16, 524288, 128, 128, "bf16", False, 0.5, False, 4, (1,)),
         Workload("h32-n512k-d128x64-bf16-causal", 1, 32, 524288, 524288, 128, 64, "bf16", True, 0.0, True, 5, (2,)),
+        # grouped key heads: 32 query heads read 8 key heads
+        Workload("h32-kv8-n64k-d128-bf16-causal", 1, 32, 65536, 65536, 128, 128, "bf16", True, 0.5, False, 3,
+                 kv_heads=8),
+        # ragged batch: four sequences padded to 32K
+        Workload("ragged-b4-h32-n32k-d128-bf16-causal", 4, 32, 32768, 32768, 128, 128, "bf16", True, 0.5, False, 6,
+                 lengths=(8192, 16384, 4096, 32768)),
     ]
 }
 
 
 def generate(w: Workload, device="cpu"):
-    """Return (q1, k1, q2, k2) for workload ``w`` on ``device``."""
+    """Return (q1, k1, q2, k2) for workload ``w`` on ``device`` (K with
+    ``kv_heads`` heads when set; ragged workloads are drawn at the padded size)."""
     dev = torch.device(device)
     gt = torch.Generator(device=dev).manual_seed(w.seed)
     gn = torch.Generator(device=dev).manual_seed(100 + w.seed)
@@ -73,16 +82,17 @@ def generate(w: Workload, device="cpu"):
     def randn(shape, gen):
         return torch.randn(shape, generator=gen, device=dev, dtype=f32)
 
-    shp = lambda n, d: (w.B, w.H, n, d)  # noqa: E731
+    shp = lambda n, d, h=w.H: (w.B, h, n, d)  # noqa: E731
+    kv = w.kv_heads or w.H
     q1 = randn(shp(w.n_q, w.d1), gt)
-    k1 = randn(shp(w.n_k, w.d1), gt)
+    k1 = randn(shp(w.n_k, w.d1, kv), gt)
     if w.independent:
         q2 = randn(shp(w.n_q, w.d2), gn)
-        k2 = randn(shp(w.n_k, w.d2), gn)
+        k2 = randn(shp(w.n_k, w.d2, kv), gn)
     else:
         assert w.d1 == w.d2
         q2 = q1 + w.noise * randn(shp(w.n_q, w.d2), gn)
-        k2 = k1 + w.noise * randn(shp(w.n_k, w.d2), gn)
+        k2 = k1 + w.noise * randn(shp(w.n_k, w.d2, kv), gn)
     dt = w.torch_dtype
     return (q1.to(dt).contiguous(), k1.to(dt).contiguous(),
             q2.to(dt).contiguous(), k2.to(dt).contiguous())
