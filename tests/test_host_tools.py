@@ -142,3 +142,19 @@ def test_counter_utilisations(tmp_path):
     assert d["mfma_valu_coexec"] == pytest.approx(0.1)
     assert d["valu_issue_per_simd_cycle"] == pytest.approx(0.05)  # (1050 - 250) / 16 / 1000
     assert d["lds_wait_share"] == pytest.approx(0.1)
+
+
+@pytest.mark.parametrize("name,label", [
+    ("_ZN8streamkl13bwd_dk_kernelIDF16bLi128ELi128ELi3ELb0ELi64EEEvNS_7BwdArgsE", "bwd_dk_kernel<JOINT>"),
+    ("void streamkl::bwd_dk_kernel<__bf16, 128, 128, 3, false, 64>(streamkl::BwdArgs)", "bwd_dk_kernel<JOINT>"),
+    ("void streamkl::bwd_dk_kernel<__bf16, 128, 128, 1, false, 64>(streamkl::BwdArgs)", "bwd_dk_kernel"),
+    ("void streamkl::bwd_dk_kernel<__bf16, 128, 128, 2, true, 64>(streamkl::BwdArgs)", "bwd_dk_kernel<FUSED>"),
+    ("void streamkl::bwd_decode_kernel<128, 128, 1>(streamkl::BwdArgs)", "bwd_decode_kernel"),
+    ("void streamkl::fwd_decode_kernel<128, 128>(streamkl::FwdArgs)", "fwd_decode_kernel"),
+    ("_ZN8streamkl13bwd_dq_kernelIDF16bLi128ELi128ELi1ELi64EEEvNS_7BwdArgsE", "bwd_dq_kernel"),
+])
+def test_kernel_labels(name, label):
+    """Each library kernel's profiler name maps to the label its traffic and
+    time are reported under (the joint and fused dK kernels apart from the
+    plain one)."""
+    assert profiling._label(name) == label
