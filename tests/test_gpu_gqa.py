@@ -88,3 +88,36 @@ def test_grouped_key_heads(case, cuda_device):
                 check_grad(f"{w.name} s{s} out{i} h{h} dQ", dq[0, h], ref_dq[(s, h)])
             for kh in range(ref_dk[s].shape[0]):
                 check_grad(f"{w.name} s{s} out{i} key head {kh} dK", dk[0, kh], ref_dk[s][kh])
+
+
+def test_grouped_key_heads_64k_workload(cuda_device):
+    """The 64K causal workload with 32 query heads on 8 key heads, in the
+    configuration the benchmark times: sampled query rows (forward, dQ) of
+    two query heads, and the last 1024 keys' dK of two key heads summed over
+    their four query heads, against the oracle."""
+    w = workloads.WORKLOADS["h32-kv8-n64k-d128-bf16-causal"]
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    G = w.H // w.kv_heads
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    print("gqa 64k forward", flush=True)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, True)
+    print("gqa 64k backward", flush=True)
+    dq, dk = sk.streamkl_bwd(1, q1, k1, q2, k2, True, kl, l1, l2, g)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, w.n_q - 1], rng.choice(w.n_q, 61, replace=False)]))
+    keys = np.arange(w.n_k - 1024, w.n_k)
+    gn = to_np(g)
+    hin = lambda h: [to_np(q1[0, h]), to_np(k1[0, h // G]), to_np(q2[0, h]), to_np(k2[0, h // G])]  # noqa: E731
+    for h in (0, 31):
+        print(f"oracle head {h}", flush=True)
+        ref = oracle.head_forward(*hin(h), True, rows=rows, block=64)
+        check_forward_rows(f"64k gqa h{h}", to_np(kl[0, h])[rows], to_np(l1[0, h])[rows], to_np(l2[0, h])[rows],
+                           ref, w.torch_dtype)
+        rdq, _ = oracle.head_backward(1, *hin(h), True, gn[0, h], rows=rows, block=64)
+        check_grad(f"64k gqa h{h} dQ rows", to_np(dq[0, h])[rows], rdq)
+    for kh in (0, w.kv_heads - 1):
+        print(f"oracle key head {kh}", flush=True)
+        rdk = sum(oracle.head_backward_dk_rows(1, *hin(h), True, gn[0, h], key_rows=keys, block=128)
+                  for h in range(kh * G, (kh + 1) * G))
+        check_grad(f"64k gqa key head {kh} dK tail", to_np(dk[0, kh])[keys], rdk)

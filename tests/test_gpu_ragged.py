@@ -102,3 +102,31 @@ def test_ragged_batch(case, cuda_device):
                     check_grad(f"{w.name} b{b} s{s} out{i} h{h} dQ", dq[b, h, :nq], ref_dq[(s, h)])
                 for kh in range(ref_dk[s].shape[0]):
                     check_grad(f"{w.name} b{b} s{s} out{i} kh{kh} dK", dk[b, kh, :nk], ref_dk[s][kh])
+
+
+def test_ragged_workload_full_size(cuda_device):
+    """The ragged benchmark workload (four causal sequences of 8K, 16K, 4K and
+    32K rows padded to 32K, 32 heads) in the configuration the benchmark
+    times: sampled rows of every sequence on two heads, forward and dQ,
+    against the oracle on the trimmed tensors; padded rows are 0."""
+    w = workloads.WORKLOADS["ragged-b4-h32-n32k-d128-bf16-causal"]
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    L = list(w.lengths)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    print("ragged workload forward", flush=True)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, True, q_len=L, k_len=L)
+    dq, dk = sk.streamkl_bwd(1, q1, k1, q2, k2, True, kl, l1, l2, g, q_len=L, k_len=L)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    gn = to_np(g)
+    for b, n in enumerate(L):
+        assert (kl[b, :, n:] == 0).all() and (dq[b, :, n:] == 0).all() and (dk[b, :, n:] == 0).all()
+        rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 30, replace=False)]))
+        for h in (0, 31):
+            print(f"oracle sequence {b} head {h}", flush=True)
+            hi = [to_np(t[b, h, :n]) for t in (q1, k1, q2, k2)]
+            ref = oracle.head_forward(*hi, True, rows=rows, block=64)
+            check_forward_rows(f"ragged b{b}h{h}", to_np(kl[b, h])[rows], to_np(l1[b, h])[rows],
+                               to_np(l2[b, h])[rows], ref, w.torch_dtype)
+            rdq, _ = oracle.head_backward(1, *hi, True, gn[b, h, :n], rows=rows, block=64)
+            check_grad(f"ragged b{b}h{h} dQ rows", to_np(dq[b, h])[rows], rdq)
