@@ -458,8 +458,9 @@ streamkl_status bwd_launch(int setting, const void* Q1, const void* K1, const vo
     return hip_status(fk(a, setting, true, a.BH * nkb, s));
   }
   if (mode != STREAMKL_BWD_DQ_ONLY) {
-    a.nblk = (int)nkb;
-    st = hip_status(fk(a, setting, false, a.BH * nkb, s));
+    const int64_t nkb8 = cdiv(a.n_k, kBwdKRowsSep);  // the separate dK kernel's 8-wave key blocks
+    a.nblk = (int)nkb8;
+    st = hip_status(fk(a, setting, false, a.BH * nkb8, s));
     if (st != STREAMKL_OK) return st;
   }
   if (mode == STREAMKL_BWD_DK_ONLY) return STREAMKL_OK;

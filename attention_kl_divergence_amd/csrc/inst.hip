@@ -58,13 +58,14 @@ hipError_t SKL_CAT(launch_bwd_dq, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int 
 
 hipError_t SKL_CAT(launch_bwd_dk, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, bool fused, int64_t nblocks,
                                                            hipStream_t st) {
-  const dim3 g((unsigned)nblocks), b(256);
+  const dim3 g((unsigned)nblocks), b(256), b8(64 * kBwdKWaves);
+  constexpr int W = kBwdKWaves;
   if (setting == 1) {
     if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, true, kBwdQTile<SKL_T>>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, false, kBwdQTile<SKL_T>>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, false, kBwdQTile<SKL_T>, W>), g, b8, 0, st, a);
   } else if (setting == 2) {
     if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, true, kBwdQTile<SKL_T>>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, false, kBwdQTile<SKL_T>>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, false, kBwdQTile<SKL_T>, W>), g, b8, 0, st, a);
   } else {
     return launch_joint_dk<SKL_T, SKL_D1, SKL_D2>(a, g, b, st, fused);
   }

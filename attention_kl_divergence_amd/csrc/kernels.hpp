@@ -1174,13 +1174,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 // to global dQ_s with fp32 atomics, so each query-key pair is visited once.
 // SETTING 3 (joint, not fused) forms dS1 and dS2 from the same logits and
 // accumulates dK1 (dk) and dK2 (dk2).
-template <typename T, int D1, int D2, int SETTING, bool FUSED, int BQ>
-__global__ __launch_bounds__(256) void bwd_dk_kernel(BwdArgs a) {
+template <typename T, int D1, int D2, int SETTING, bool FUSED, int BQ, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr bool JOINT = SETTING == 3;
   static_assert(!(JOINT && FUSED), "the joint backward has no fused form");
-  constexpr int NW = 4, BKW = 32 * NW;
+  static_assert(NW == 4 || !FUSED, "the fused form maps its dQ columns onto 4 waves");
+  constexpr int BKW = 32 * NW;
   constexpr int DS = SETTING == 1 ? D2 : D1;
   constexpr int S1 = D1 / MF::KSTEP, S2 = D2 / MF::KSTEP;
   constexpr int NB = DS / 32, NB2 = D2 / 32, HS = 32 / MF::KSTEP, NQB = BQ / 32, HK = BKW / MF::KSTEP;

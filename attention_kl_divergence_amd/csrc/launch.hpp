@@ -21,7 +21,9 @@ constexpr int kDecRows = 32;      // longest query range of the decode forward (
 constexpr int kDecBlock = 32;     // key rows per decode-forward block
 constexpr int kBwdQRows = 128;    // query rows per dQ workgroup
 constexpr int kBwdKeyTile = 64;   // key rows per dQ-kernel LDS tile
-constexpr int kBwdKRows = 128;    // key rows per dK workgroup (4 waves x 32)
+constexpr int kBwdKRows = 128;    // key rows per dK workgroup (4 waves x 32): fused and joint forms
+constexpr int kBwdKWaves = 8;     // waves of the separate single-setting dK workgroup
+constexpr int kBwdKRowsSep = 32 * kBwdKWaves;  // its key rows
 constexpr int kDecBwdTile = 128;  // key rows per tile of the decode backward (4 waves x 32)
 // query rows per LDS tile of the dK kernel (fp32 tiles are twice as large)
 template <typename T> constexpr int kBwdQTile = sizeof(T) == 2 ? 64 : 32;
