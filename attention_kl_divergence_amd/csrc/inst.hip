@@ -49,9 +49,10 @@ hipError_t SKL_CAT(launch_fwd_dec, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int
 
 hipError_t SKL_CAT(launch_bwd_dq, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, int64_t nblocks,
                                                            hipStream_t st) {
-  const dim3 g((unsigned)nblocks), b(256);
-  if (setting == 1) hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 1, kBwdKeyTile>), g, b, 0, st, a);
-  else if (setting == 2) hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 2, kBwdKeyTile>), g, b, 0, st, a);
+  const dim3 g((unsigned)nblocks), b(64 * kBwdQWaves);
+  constexpr int W = kBwdQWaves;
+  if (setting == 1) hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 1, kBwdKeyTile, W>), g, b, 0, st, a);
+  else if (setting == 2) hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 2, kBwdKeyTile, W>), g, b, 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -1020,11 +1020,10 @@ __device__ inline void dS_rows_keyouter_joint(f32x16& s1, f32x16& s2, const floa
 // one query row, so dS from the accumulators is directly the A operand of
 // dQ = dS K_s; K_s's B operand is read down the key rows of its tile.
 // Deterministic; no atomics.
-template <typename T, int D1, int D2, int SETTING, int BK>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+template <typename T, int D1, int D2, int SETTING, int BK, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
-  constexpr int NW = 4;
   constexpr int DS = SETTING == 1 ? D2 : D1;
   constexpr int S1 = D1 / MF::KSTEP, S2 = D2 / MF::KSTEP;
   constexpr int NKB = BK / 32, NB = DS / 32, HS = 32 / MF::KSTEP;

@@ -19,7 +19,8 @@ constexpr int kFwdTile = 64;      // key rows per forward LDS tile
 template <typename T> constexpr int kFwdPPTile = sizeof(T) == 2 ? 128 : 64;
 constexpr int kDecRows = 32;      // longest query range of the decode forward (one wave's rows)
 constexpr int kDecBlock = 32;     // key rows per decode-forward block
-constexpr int kBwdQRows = 128;    // query rows per dQ workgroup
+constexpr int kBwdQWaves = 8;     // waves per dQ workgroup
+constexpr int kBwdQRows = 32 * kBwdQWaves;  // query rows per dQ workgroup
 constexpr int kBwdKeyTile = 64;   // key rows per dQ-kernel LDS tile
 constexpr int kBwdKRows = 128;    // key rows per dK workgroup (4 waves x 32): fused and joint forms
 constexpr int kBwdKWaves = 8;     // waves of the separate single-setting dK workgroup
