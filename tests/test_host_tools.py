@@ -158,3 +158,20 @@ def test_kernel_labels(name, label):
     time are reported under (the joint and fused dK kernels apart from the
     plain one)."""
     assert profiling._label(name) == label
+
+
+def test_bench_pair_counts():
+    """Visible pairs: causal N(N+1)/2 per head, rectangular bottom-right
+    causal, and per-sequence lengths for ragged workloads."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads
+    w = workloads.WORKLOADS["h32-n64k-d128-bf16-causal"]
+    assert bench.pairs_of(w) == 32 * 65536 * 65537 // 2
+    r = w.with_(n_q=100, n_k=333)
+    assert bench.pairs_of(r) == 32 * (100 * 101 // 2 + 100 * 233)
+    assert bench.pairs_of(w.with_(causal=False, n_q=7, n_k=9)) == 32 * 63
+    rag = workloads.WORKLOADS["ragged-b4-h32-n32k-d128-bf16-causal"]
+    assert bench.pairs_of(rag) == 32 * sum(n * (n + 1) // 2 for n in (8192, 16384, 4096, 32768))
+    # grouped key heads do not change the pairs
+    assert bench.pairs_of(workloads.WORKLOADS["h32-kv8-n64k-d128-bf16-causal"]) == bench.pairs_of(w)
