@@ -225,6 +225,49 @@ def counters(csvs, agent_csv):
     return out, topo
 
 
+def copy_bandwidth() -> str:
+    """Markdown table of plain device copies and one-directional streams on
+    cuda:0: the practical ceiling of a kernel that reads and writes in equal
+    amounts.  HIP events around 5 back-to-back launches; bytes = read + write."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 5
+
+    rows = []
+    for gib in (1, 4, 8):
+        n = gib * (1 << 30) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty(n, device=dev)
+        for name, fn in (("`dst.copy_(src)`", lambda: dst.copy_(src)),
+                         ("`torch.mul(src, 1.0, out=dst)`", lambda: torch.mul(src, 1.0, out=dst))):
+            ms = timed(fn)
+            rows.append(f"| {name} | {gib} GiB | {ms:.3f} | {2 * n * 4 / ms / 1e6:.0f} |")
+        del src, dst
+    n = 8 * (1 << 30) // 4
+    x = torch.ones(n, device=dev)
+    ms = timed(lambda: x.sum())
+    rows.append(f"| `x.sum()` (read only) | 8 GiB | {ms:.3f} | {n * 4 / ms / 1e6:.0f} |")
+    ms = timed(lambda: x.fill_(1.0))
+    rows.append(f"| `x.fill_(1.0)` (write only) | 8 GiB | {ms:.3f} | {n * 4 / ms / 1e6:.0f} |")
+    return "\n".join([
+        "# Plain device copies on one MI355X (the ceiling of a 1:1 read/write stream)", "",
+        "Command: `python -m attention_kl_divergence_amd.profiling copybw --out profiles/copy_bandwidth.md`",
+        "(torch ops on fp32 tensors; HIP events around 5 back-to-back launches, bytes = read + write).", "",
+        "| op | size | ms | GB/s |", "|---|---|---|---|", *rows, "",
+        "The decode backward reads K1 and K2 (bf16) and writes dK (fp32) in equal",
+        "byte counts, the mix of the elementwise `mul` above.", ""])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -248,7 +291,16 @@ def main(argv=None):
     c.add_argument("--command", required=True)
     c.add_argument("--out", required=True)
     sub.add_parser("digest")
+    cb = sub.add_parser("copybw", help="read+write bandwidth of plain device copies (needs a GPU)")
+    cb.add_argument("--out", default=None)
     args = ap.parse_args(argv)
+    if args.cmd == "copybw":
+        text = copy_bandwidth()
+        if args.out:
+            with open(args.out, "w") as fo:
+                fo.write(text)
+        print(text)
+        return 0
     if args.cmd == "counters":
         res, topo = counters(args.csv, args.agent)
         lines = [f"# SQ counters per kernel, workload {args.workload}", "",
