@@ -1015,8 +1015,9 @@ __device__ inline void dS_rows_keyouter_joint(f32x16& s1, f32x16& s2, const floa
 }
 
 // ---------------------------------------------------------------------------
-// Query-outer backward: dQ_s for 32 query rows per wave (4 waves), key tiles
-// of BK rows of K1 and K2 streamed through LDS.  S^T = K Q^T keeps a lane on
+// Query-outer backward: dQ_s for 32 query rows per wave (NW waves), key tiles
+// of BK rows of K1 and K2 streamed through LDS.  The more waves share a
+// workgroup, the fewer times each head's key tiles are read.  S^T = K Q^T keeps a lane on
 // one query row, so dS from the accumulators is directly the A operand of
 // dQ = dS K_s; K_s's B operand is read down the key rows of its tile.
 // Deterministic; no atomics.
@@ -1163,8 +1164,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Key-outer backward: each wave owns 32 key rows (workgroup: 4 waves, 128
-// keys), keeps K1, K2 in registers and accumulates dK_s in registers while
+// Key-outer backward: each wave owns 32 key rows (workgroup: NW waves, 32 NW
+// keys; the more keys a workgroup owns, the fewer times each head's query
+// tiles are read), keeps K1, K2 in registers and accumulates dK_s in registers while
 // query tiles of BQ rows of Q1 and Q2 stream through LDS.  The logits are
 // computed as S = Q K^T so a lane's accumulator column is one key and dS from
 // the accumulators is directly the A operand of dK = dS^T Q_s; Q_s's B operand
