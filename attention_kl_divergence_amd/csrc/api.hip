@@ -235,12 +235,17 @@ int plan_bwd(const streamkl_shape* s, int causal, int setting, const streamkl_la
   const double heads = (double)(s->B * s->H);
   const double rate = 1.0e15;  // sustained MFMA FLOP/s assumed for these kernels
   const double f_qk = 2.0 * (s->d1 + s->d2), f_grad = 2.0 * ds;
-  const double wg_dk = heads * cdiv(s->n_k, kBwdKRows), wg_dq = heads * cdiv(s->n_q, kBwdQRows);
-  const double full = 2.0 * cus;
-  const double u_dk = wg_dk < full ? wg_dk / full : 1.0, u_dq = wg_dq < full ? wg_dq / full : 1.0;
-  const double t_sep = heads * pairs * (f_qk + f_grad) / (rate * u_dk) + heads * pairs * (f_qk + f_grad) / (rate * u_dq);
+  // workgroups of each kernel against what the chip holds at once: the
+  // separate dK and dQ kernels run one 8-wave workgroup (256 rows) per CU,
+  // the fused key-outer kernel one 4-wave workgroup (128 keys) per CU
+  const double wg_dk = heads * cdiv(s->n_k, kBwdKRowsSep), wg_dq = heads * cdiv(s->n_q, kBwdQRows);
+  const double wg_fk = heads * cdiv(s->n_k, kBwdKRows);
+  const double full = cus;
+  auto use = [&](double wg) { return wg < full ? wg / full : 1.0; };
+  const double t_sep = heads * pairs * (f_qk + f_grad) / (rate * use(wg_dk)) +
+                       heads * pairs * (f_qk + f_grad) / (rate * use(wg_dq));
   const double atomic_bytes = heads * pairs * 4.0 * ds / kBwdKRows;
-  double t_fused = heads * pairs * (f_qk + 2 * f_grad) / (rate * u_dk);
+  double t_fused = heads * pairs * (f_qk + 2 * f_grad) / (rate * use(wg_fk));
   const double t_atomic = atomic_bytes / 1.2e12;
   if (t_atomic > t_fused) t_fused = t_atomic;
   return t_fused < t_sep ? STREAMKL_BWD_FUSED : STREAMKL_BWD_SEPARATE;
