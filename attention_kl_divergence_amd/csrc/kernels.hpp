@@ -1630,7 +1630,8 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dk[acc_row(e, grp) * DS + 32 * nb] = dka[nb][e];
+        // dK is written once and not read again here: non-temporal stores
+        for (int e = 0; e < 16; ++e) __builtin_nontemporal_store(dka[nb][e], dk + acc_row(e, grp) * DS + 32 * nb);
     } else {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
