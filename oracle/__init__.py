@@ -9,6 +9,7 @@ from .streamkl_oracle import (  # noqa: F401
     head_forward,
     head_backward,
     head_backward_dk_rows,
+    head_dk_keys,
     materialised_bytes,
     pair_count,
 )

@@ -47,6 +47,7 @@ __all__ = [
     "head_forward",
     "head_backward",
     "head_backward_dk_rows",
+    "head_dk_keys",
     "materialised_bytes",
     "pair_count",
 ]
@@ -192,6 +193,48 @@ def head_backward_dk_rows(setting: int, q1, k1, q2, k2, causal: bool, g,
     _, dk = head_backward(setting, q1, k1, q2, k2, causal, g, scale1, scale2,
                           rows=rows, block=block)
     return dk[key_rows]
+
+
+def head_dk_keys(setting: int, q1, k1, q2, k2, causal: bool, g, key_rows, row_stats,
+                 scale1=None, scale2=None, block: int = 512):
+    """dK_s[key_rows] of sum_i g[i] KL[i] for one head, from the definition
+    restricted to those key columns.
+
+    ``row_stats`` = (kl, lse1, lse2) for EVERY query row of the head, as
+    ``head_forward`` returns them (the LSE runs over all visible keys, so it
+    cannot come from the selected columns).  Then for each selected key j:
+    P_t[i, j] = exp(S_t[i, j] - LSE_t[i]) (technical summary, Method 2:
+    probabilities regenerated from the stored LSE), dS as in ``_dS`` and
+    dK_s[j] = scale_s * sum_i dS[i, j] Q_s[i].  Only len(key_rows) columns of
+    the logits are formed, so the cost is O(N_Q * len(key_rows) * d) beyond
+    the row statistics.
+    """
+    q1, k1, q2, k2 = _f64(q1), _f64(k1), _f64(q2), _f64(k2)
+    g = _f64(g)
+    n_q, n_k = q1.shape[0], k1.shape[0]
+    s1 = _default_scale(q1.shape[1], scale1)
+    s2 = _default_scale(q2.shape[1], scale2)
+    if setting not in (1, 2):
+        raise ValueError("setting must be 1 or 2")
+    kl, lse1, lse2 = (_f64(x) for x in row_stats)
+    if kl.shape != (n_q,) or lse1.shape != (n_q,) or lse2.shape != (n_q,):
+        raise ValueError("row_stats must hold kl, lse1, lse2 for every query row")
+    key_rows = np.asarray(key_rows, dtype=np.int64)
+    qs, ss = (q2, s2) if setting == 1 else (q1, s1)
+    dk = np.zeros((len(key_rows), qs.shape[1]))
+    rows = np.arange(n_q)
+    for rb in _block_rows(rows, block):
+        mask = valid_mask(rb, n_q, n_k, causal)[:, key_rows]
+        if not mask.any():
+            continue
+        with np.errstate(invalid="ignore"):
+            logp1 = np.where(mask, scores(q1[rb], k1[key_rows], s1), -np.inf) - lse1[rb][:, None]
+            logp2 = np.where(mask, scores(q2[rb], k2[key_rows], s2), -np.inf) - lse2[rb][:, None]
+        p1 = np.exp(logp1)
+        p2 = np.exp(logp2)
+        dS = _dS(setting, p1, p2, logp1, logp2, kl[rb], g[rb], mask)
+        dk += ss * (dS.T @ qs[rb])
+    return dk
 
 
 def pair_count(B: int, H: int, n_q: int, n_k: int, causal: bool) -> int:

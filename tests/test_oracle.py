@@ -285,6 +285,26 @@ def test_rows_and_dk_rows_consistent_with_full():
         np.testing.assert_allclose(dkt, dk[[7, 8, 9]], rtol=1e-12, atol=1e-16)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("setting", [1, 2])
+@pytest.mark.parametrize("dims", [(4, 4), (6, 3)])
+def test_dk_keys_equals_full_dk(setting, causal, dims):
+    """head_dk_keys (selected key columns, row statistics over all keys) gives
+    the same dK rows as the full materialised backward, which the finite
+    differences pin; with row statistics that are off by a constant it does not."""
+    d1, d2 = dims
+    q1, k1, q2, k2 = rand_case(20 + setting, n_q=9, n_k=13, d1=d1, d2=d2)
+    g = np.random.default_rng(5).normal(size=9)
+    stats = oracle.head_forward(q1, k1, q2, k2, causal)
+    _, dk = oracle.head_backward(setting, q1, k1, q2, k2, causal, g)
+    keys = np.array([12, 0, 5, 4, 12])
+    got = oracle.head_dk_keys(setting, q1, k1, q2, k2, causal, g, keys, stats, block=4)
+    np.testing.assert_allclose(got, dk[keys], rtol=1e-12, atol=1e-15)
+    kl, l1, l2 = stats
+    off = oracle.head_dk_keys(setting, q1, k1, q2, k2, causal, g, keys, (kl, l1 + 0.01, l2), block=4)
+    assert np.abs(off - dk[keys]).max() > 1e-6
+
+
 # --------------------------------------------------------------------------- setting-2 stability
 
 def test_setting2_underflow_gives_zero_not_nan():
