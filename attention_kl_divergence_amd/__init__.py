@@ -12,7 +12,9 @@ from .streamkl import (  # noqa: F401
     StreamKLError,
     attention_kl,
     bwd_plan,
+    bwd_workspace_bytes,
     fwd_plan,
+    fwd_loss_workspace_bytes,
     fwd_workspace_bytes,
     library,
     make_shape,
@@ -21,4 +23,5 @@ from .streamkl import (  # noqa: F401
     streamkl_bwd_joint,
     kl_loss,
     streamkl_fwd,
+    streamkl_fwd_loss,
 )

@@ -62,7 +62,9 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
                      "-c", os.path.join(CSRC, "inst.hip"), "-o", obj])
         objs.append(obj)
     api_obj = os.path.join(BUILD, "api.o")
-    cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "api.hip"), "-o", api_obj])
+    # the host layer checks float arguments for NaN: it keeps IEEE NaN semantics
+    cmds.append([HIPCC, *[f for f in FLAGS if f != "-fno-honor-nans"], "-c", os.path.join(CSRC, "api.hip"),
+                 "-o", api_obj])
     objs.append(api_obj)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         outs = list(ex.map(_run, cmds))

@@ -5,6 +5,7 @@
 #include <mutex>
 #include <string.h>
 #include <type_traits>
+#include <vector>
 
 #include "../../include/streamkl.h"
 #include "kernels.hpp"
@@ -12,22 +13,46 @@
 
 namespace streamkl {
 
-// Merge of the split partial states, then the epilogue (one thread per row).
+// Merge of the split partial states, then the epilogue (one thread per row);
+// with the fused loss each workgroup also writes its rows' sum of w_i KL_i.
 __global__ __launch_bounds__(256) void splitk_merge_kernel(const float* __restrict__ ws, float* kl, float* lse1,
-                                                           float* lse2, int64_t BH, int n_q, int nsplit, int qs) {
+                                                           float* lse2, int64_t BH, int n_q, int nsplit, int qs,
+                                                           const float* __restrict__ lw, double* lpart) {
+  __shared__ double red[4];
   const int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x;
-  if (i >= BH * n_q) return;
-  const int64_t bh = i / n_q;
-  const int q = (int)(i % n_q);
-  const int64_t r = bh * qs + q;  // output row (qs rows per head in memory)
-  const int64_t fs = BH * (int64_t)nsplit * n_q;
-  RowState st = empty_state();
-  for (int z = 0; z < nsplit; ++z) {
-    const int64_t o = (bh * nsplit + z) * (int64_t)n_q + q;
-    RowState p = {ws[o], ws[o + fs], ws[o + 2 * fs], ws[o + 3 * fs], ws[o + 4 * fs]};
-    st = merge_state(st, p);
+  double lv = 0.0;
+  if (i < BH * n_q) {
+    const int64_t bh = i / n_q;
+    const int q = (int)(i % n_q);
+    const int64_t r = bh * qs + q;  // output row (qs rows per head in memory)
+    const int64_t fs = BH * (int64_t)nsplit * n_q;
+    RowState st = empty_state();
+    for (int z = 0; z < nsplit; ++z) {
+      const int64_t o = (bh * nsplit + z) * (int64_t)n_q + q;
+      RowState p = {ws[o], ws[o + fs], ws[o + 2 * fs], ws[o + 3 * fs], ws[o + 4 * fs]};
+      st = merge_state(st, p);
+    }
+    const float k = finish_state(st, kl + r, lse1 + r, lse2 + r);
+    lv = lw ? (double)lw[r] * (double)k : (double)k;
   }
-  finish_state(st, kl + r, lse1 + r, lse2 + r);
+  if (lpart) loss_partial<4>(lv, red, lpart + blockIdx.x, threadIdx.x);
+}
+
+// The fused loss from the forward's per-workgroup partials: their sum in a
+// fixed order (strided per thread, then a tree), divided by the row count
+// for the mean (count > 0) or taken as is (weighted sum, count = 0).
+__global__ __launch_bounds__(1024) void loss_reduce_kernel(const double* __restrict__ part, int64_t n, double count,
+                                                          float* out) {
+  __shared__ double red[1024];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) acc += part[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int m = 512; m > 0; m >>= 1) {
+    if ((int)threadIdx.x < m) red[threadIdx.x] += red[threadIdx.x + m];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = (float)(count > 0 ? red[0] / count : red[0]);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, int64_t n4) {
@@ -90,6 +115,14 @@ streamkl_status device_info(DeviceInfo* out) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// A scale must be a finite number (<= 0 selects the default).  Tested on the
+// bits, so no floating-point flag can fold the test away.
+bool finite_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (u & 0x7fffffffu) < 0x7f800000u;
+}
 
 bool ragged(const streamkl_shape* s);
 
@@ -219,6 +252,33 @@ size_t ws_bytes(const streamkl_shape* s, int splits) {
   return splits > 1 ? (size_t)20 * (size_t)(s->B * s->H) * (size_t)s->n_q * (size_t)splits : 0;
 }
 
+// How the forward of one problem runs.  Workspace sizing and the launches
+// both take it from make_fwd_plan, so the bytes reported are the bytes used.
+struct FwdPlan {
+  int splits;           // key splits
+  bool pp, dec;         // the ping-pong kernel (long unsplit query ranges) / the decode kernel
+  int64_t nqb;          // query blocks per head
+  int64_t grid;         // workgroups of the forward kernel
+  size_t split_bytes;   // split partials (at the start of the workspace)
+  int64_t loss_slots;   // workgroups that finalize rows: one fused-loss partial each
+};
+
+FwdPlan make_fwd_plan(const streamkl_shape* s, int splits) {
+  FwdPlan p;
+  const int64_t BH = s->B * s->H;
+  p.splits = splits;
+  p.pp = splits == 1 && s->n_q > kFwdRows;
+  p.dec = splits > 1 && decode_shape(s);
+  p.nqb = cdiv(s->n_q, p.pp ? kFwdPPRows : kFwdRows);
+  p.grid = p.dec ? BH * cdiv(splits, 4) : BH * p.nqb * splits;
+  p.split_bytes = ws_bytes(s, splits);
+  // unsplit: the forward kernel finalizes rows; split: the merge kernel (256 rows per workgroup)
+  p.loss_slots = splits > 1 ? cdiv(BH * s->n_q, 256) : p.grid;
+  return p;
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
 // Backward mode plan.  The fused kernel (Method 2: each query-key tile pair
 // visited once, dQ by atomics) moves 4*d_s bytes of fp32 atomics per query
 // row and 128-key block; on gfx950 device-scope fp32 atomics sustain about
@@ -305,6 +365,84 @@ P elem(P p, int64_t b, int64_t rows_per_elem, int64_t bytes_per_row) {
   return reinterpret_cast<P>(reinterpret_cast<C>(p) + b * rows_per_elem * bytes_per_row);
 }
 
+// ---- the problems of one forward call and their workspace ----
+
+constexpr size_t kInvalidBytes = ~(size_t)0;  // workspace queries with invalid arguments
+
+// Problem b of a call: the shape itself, or batch element b of a ragged batch.
+int64_t problems(const streamkl_shape* s) { return ragged(s) ? s->B : 1; }
+streamkl_shape problem(const streamkl_shape* s, int64_t b) { return ragged(s) ? element_shape(s, b) : *s; }
+
+struct FwdCall {
+  size_t split_region = 0;  // bytes of split partials: the largest of any problem (they run one after another)
+  int64_t loss_slots = 0;   // fused-loss partials of all problems (consecutive, after the split region)
+  double rows = 0;          // query rows the call finalizes (the mean's divisor)
+};
+
+FwdCall summarize(const streamkl_shape* s, const std::vector<int>& splits) {
+  FwdCall c;
+  for (int64_t b = 0; b < problems(s); ++b) {
+    const streamkl_shape e = problem(s, b);
+    if (e.n_q == 0) continue;
+    const FwdPlan p = make_fwd_plan(&e, splits[b]);
+    c.split_region = std::max(c.split_region, p.split_bytes);
+    c.loss_slots += p.loss_slots;
+    c.rows += (double)(e.B * e.H * e.n_q);
+  }
+  return c;
+}
+
+size_t loss_base(const FwdCall& c) { return round256(c.split_region); }
+size_t loss_call_bytes(const FwdCall& c) { return loss_base(c) + 8 * (size_t)c.loss_slots; }
+
+// The split count of every problem (0 for empty ones) as the plan asks, or one split.
+std::vector<int> planned_splits(const streamkl_shape* s, int causal, const streamkl_launch* l, int cus, bool one) {
+  std::vector<int> sp((size_t)problems(s), 0);
+  for (int64_t b = 0; b < problems(s); ++b) {
+    const streamkl_shape e = problem(s, b);
+    if (e.n_q > 0) sp[b] = one ? 1 : plan_splits(&e, causal, l, cus);
+  }
+  return sp;
+}
+
+// Workspace a call needs with the planned split counts (or one split each):
+// the split partials alone, or (loss) the split region then the loss partials.
+size_t call_bytes(const streamkl_shape* s, int causal, const streamkl_launch* l, int cus, bool loss, bool one) {
+  const FwdCall c = summarize(s, planned_splits(s, causal, l, cus, one));
+  return loss ? loss_call_bytes(c) : c.split_region;
+}
+
+// The split count of every problem given the workspace the caller offers
+// (`avail` bytes at `ws`), decided before anything is enqueued.  Without
+// the loss, a problem whose split partials do not fit falls back to one
+// split (auto) or fails (explicit split count); with the loss, the whole
+// call falls back to one split when both kinds of partials do not fit, and
+// fails if the loss partials alone do not fit.
+streamkl_status plan_call(const streamkl_shape* s, int causal, const streamkl_launch* l, int cus, bool loss,
+                          const void* ws, size_t avail, std::vector<int>& splits, FwdCall& c) {
+  const bool expl = l && l->num_splits > 1;
+  splits = planned_splits(s, causal, l, cus, false);
+  if (!loss) {
+    const bool usable = ws && aligned(ws, 4);
+    for (int64_t b = 0; b < problems(s); ++b) {
+      if (splits[b] <= 1) continue;
+      const streamkl_shape e = problem(s, b);
+      if (usable && ws_bytes(&e, splits[b]) <= avail) continue;
+      if (expl) return STREAMKL_ERR_WORKSPACE;
+      splits[b] = 1;
+    }
+    c = summarize(s, splits);
+    return STREAMKL_OK;
+  }
+  if (!ws || !aligned(ws, 16)) return STREAMKL_ERR_WORKSPACE;
+  c = summarize(s, splits);
+  if (loss_call_bytes(c) <= avail) return STREAMKL_OK;
+  if (expl) return STREAMKL_ERR_WORKSPACE;
+  splits = planned_splits(s, causal, l, cus, true);
+  c = summarize(s, splits);
+  return loss_call_bytes(c) <= avail ? STREAMKL_OK : STREAMKL_ERR_WORKSPACE;
+}
+
 }  // namespace
 }  // namespace streamkl
 
@@ -312,7 +450,7 @@ using namespace streamkl;
 
 extern "C" {
 
-int streamkl_version(void) { return 3; }
+int streamkl_version(void) { return 4; }
 
 const char* streamkl_status_string(int status) {
   switch (status) {
@@ -332,35 +470,37 @@ int streamkl_fwd_plan(const streamkl_shape* shape, int causal, const streamkl_la
   if (launch && launch->num_splits < 0) return 0;
   DeviceInfo d;
   const int cus = device_info(&d) == STREAMKL_OK ? d.cus : 256;
-  auto plan = [&](const streamkl_shape* e) {
-    int sp = plan_splits(e, causal, launch, cus);
-    if (sp > 1 && (!launch || launch->num_splits == 0) &&
-        (!launch || !launch->workspace || launch->workspace_bytes < ws_bytes(e, sp)))
-      sp = 1;
-    return sp;
-  };
-  if (!ragged(shape)) return plan(shape);
+  const void* ws = launch ? launch->workspace : nullptr;
+  const size_t avail = launch && ws ? launch->workspace_bytes : 0;
+  std::vector<int> splits;
+  FwdCall c;
+  if (plan_call(shape, causal, launch, cus, false, ws, avail, splits, c) != STREAMKL_OK) return 0;
   int most = 1;  // ragged batches: the largest split count of any element
-  for (int64_t b = 0; b < shape->B; ++b) {
-    const streamkl_shape e = element_shape(shape, b);
-    if (e.n_q > 0) most = std::max(most, plan(&e));
-  }
+  for (int sp : splits) most = std::max(most, sp);
   return most;
 }
 
 size_t streamkl_fwd_workspace_bytes(const streamkl_shape* shape, int causal, const streamkl_launch* launch) {
-  if (check_shape(shape, causal) != STREAMKL_OK) return 0;
-  if (launch && launch->num_splits < 0) return 0;
+  if (check_shape(shape, causal) != STREAMKL_OK) return kInvalidBytes;
+  if (launch && launch->num_splits < 0) return kInvalidBytes;
   DeviceInfo d;
   const int cus = device_info(&d) == STREAMKL_OK ? d.cus : 256;
-  if (!ragged(shape)) return ws_bytes(shape, plan_splits(shape, causal, launch, cus));
-  // ragged batches run one element at a time and reuse the workspace
-  size_t most = 0;
-  for (int64_t b = 0; b < shape->B; ++b) {
-    const streamkl_shape e = element_shape(shape, b);
-    if (e.n_q > 0) most = std::max(most, ws_bytes(&e, plan_splits(&e, causal, launch, cus)));
-  }
-  return most;
+  return call_bytes(shape, causal, launch, cus, false, false);
+}
+
+size_t streamkl_fwd_loss_workspace_bytes(const streamkl_shape* shape, int causal, const streamkl_launch* launch) {
+  if (check_shape(shape, causal) != STREAMKL_OK) return kInvalidBytes;
+  if (launch && launch->num_splits < 0) return kInvalidBytes;
+  DeviceInfo d;
+  const int cus = device_info(&d) == STREAMKL_OK ? d.cus : 256;
+  return call_bytes(shape, causal, launch, cus, true, false);
+}
+
+size_t streamkl_bwd_workspace_bytes(const streamkl_shape* shape, int causal, int setting,
+                                    const streamkl_launch* launch) {
+  if (check_shape(shape, causal) != STREAMKL_OK || (setting != 1 && setting != 2)) return kInvalidBytes;
+  if (launch && (launch->num_splits < 0 || launch->bwd_mode < 0 || launch->bwd_mode > 4)) return kInvalidBytes;
+  return 0;  // every backward mode runs in the caller's inputs and outputs
 }
 
 }  // extern "C"
@@ -368,54 +508,104 @@ size_t streamkl_fwd_workspace_bytes(const streamkl_shape* shape, int causal, con
 namespace streamkl {
 namespace {
 
-// The forward of one problem (validated): qs, ks are the rows per head in
-// memory (the padded lengths), sh->n_q, sh->n_k the rows used.
+// The forward of one problem, validated and planned: qs, ks are the rows per
+// head in memory (the padded lengths), sh->n_q, sh->n_k the rows used; split
+// partials go to `ws`, fused-loss partials (when lpart is set) to lpart.
 streamkl_status fwd_launch(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal, float scale1,
                            float scale2, float* out_kl, float* out_lse1, float* out_lse2, const streamkl_shape* shape,
-                           int64_t qs, int64_t ks, const streamkl_launch* launch, const DeviceInfo& dev,
+                           int64_t qs, int64_t ks, const FwdPlan& p, float* ws, const float* lw, double* lpart,
                            hipStream_t s) {
-  int splits = plan_splits(shape, causal, launch, dev.cus);
-  const size_t need = ws_bytes(shape, splits);
-  if (splits > 1) {
-    const bool have = launch && launch->workspace && launch->workspace_bytes >= need &&
-                      aligned(launch->workspace, 4);
-    if (!have) {
-      if (launch && launch->num_splits > 1) return STREAMKL_ERR_WORKSPACE;
-      splits = 1;
-    }
-  }
   // Without a key split, long query ranges use the 8-wave ping-pong kernel;
   // split short bf16 query ranges use the decode kernel.
-  const bool pp = splits == 1 && shape->n_q > kFwdRows;
-  const bool dec = splits > 1 && decode_shape(shape);
-  FwdLaunch fn = dec  ? pick_fwd_dec(shape->dtype, shape->d1, shape->d2)
-                 : pp ? pick_fwd_pp(shape->dtype, shape->d1, shape->d2)
-                      : pick_fwd(shape->dtype, shape->d1, shape->d2);
+  FwdLaunch fn = p.dec  ? pick_fwd_dec(shape->dtype, shape->d1, shape->d2)
+                 : p.pp ? pick_fwd_pp(shape->dtype, shape->d1, shape->d2)
+                        : pick_fwd(shape->dtype, shape->d1, shape->d2);
   if (!fn) return STREAMKL_ERR_UNSUPPORTED;
 
   FwdArgs a = {};
   a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
   a.kl = out_kl; a.lse1 = out_lse1; a.lse2 = out_lse2;
-  a.ws = splits > 1 ? static_cast<float*>(launch->workspace) : nullptr;
+  a.ws = p.splits > 1 ? ws : nullptr;
+  a.lw = lw;
+  a.lpart = p.splits > 1 ? nullptr : lpart;  // split: the merge kernel finalizes the rows
   a.BH = shape->B * shape->H;
   a.n_q = (int)shape->n_q;
   a.n_k = (int)shape->n_k;
   a.qs = (int)qs;
   a.ks = (int)ks;
-  a.nsplit = splits;
-  const int unit = dec ? kDecBlock : kFwdTile;
-  a.keys_per_split = (int)(cdiv(cdiv(shape->n_k, unit), splits) * unit);
-  a.nqb = (int)cdiv(shape->n_q, pp ? kFwdPPRows : kFwdRows);
+  a.nsplit = p.splits;
+  const int unit = p.dec ? kDecBlock : kFwdTile;
+  a.keys_per_split = (int)(cdiv(cdiv(shape->n_k, unit), p.splits) * unit);
+  a.nqb = (int)p.nqb;
   a.causal = causal ? 1 : 0;
   a.c1 = log2e_scale(scale1, shape->d1);
   a.c2 = log2e_scale(scale2, shape->d2);
   a.g1 = group1(shape);
   a.g2 = group2(shape);
-  streamkl_status st = hip_status(fn(a, dec ? a.BH * cdiv(splits, 4) : a.BH * a.nqb * splits, s));
-  if (st != STREAMKL_OK || splits == 1) return st;
+  streamkl_status st = hip_status(fn(a, p.grid, s));
+  if (st != STREAMKL_OK || p.splits == 1) return st;
   const int64_t rows = a.BH * a.n_q;
-  hipLaunchKernelGGL(splitk_merge_kernel, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, s,
-                     (const float*)a.ws, out_kl, out_lse1, out_lse2, a.BH, a.n_q, splits, a.qs);
+  hipLaunchKernelGGL(splitk_merge_kernel, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, s, (const float*)a.ws,
+                     out_kl, out_lse1, out_lse2, a.BH, a.n_q, p.splits, a.qs, lw, lpart);
+  return hip_status(hipGetLastError());
+}
+
+// A whole forward call: every argument and the workspace are checked, and
+// every problem planned, before anything is enqueued.  out_loss set: the
+// fused loss, sum_i w_i KL_i (or the mean KL without weights) over the rows.
+streamkl_status fwd_call(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal, float scale1,
+                         float scale2, const float* weights, float* out_kl, float* out_lse1, float* out_lse2,
+                         float* out_loss, const streamkl_shape* shape, const streamkl_launch* launch, void* ws,
+                         size_t avail, void* stream) {
+  streamkl_status st = check_shape(shape, causal);
+  if (st != STREAMKL_OK) return st;
+  if (!Q1 || !K1 || !Q2 || !K2 || !out_kl || !out_lse1 || !out_lse2) return STREAMKL_ERR_INVALID;
+  if (!aligned(Q1, 16) || !aligned(K1, 16) || !aligned(Q2, 16) || !aligned(K2, 16)) return STREAMKL_ERR_INVALID;
+  if (!aligned(out_kl, 4) || !aligned(out_lse1, 4) || !aligned(out_lse2, 4)) return STREAMKL_ERR_INVALID;
+  if ((out_loss && !aligned(out_loss, 4)) || (weights && !aligned(weights, 4))) return STREAMKL_ERR_INVALID;
+  if (!finite_bits(scale1) || !finite_bits(scale2)) return STREAMKL_ERR_INVALID;
+  if (launch && (launch->num_splits < 0 || launch->bwd_mode < 0 || launch->bwd_mode > 4)) return STREAMKL_ERR_INVALID;
+  DeviceInfo dev;
+  st = device_info(&dev);
+  if (st != STREAMKL_OK) return st;
+  const bool loss = out_loss != nullptr;
+  std::vector<int> splits;
+  FwdCall c;
+  st = plan_call(shape, causal, launch, dev.cus, loss, ws, ws ? avail : 0, splits, c);
+  if (st != STREAMKL_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* split_ws = static_cast<float*>(ws);
+  double* lpart = loss ? reinterpret_cast<double*>(static_cast<char*>(ws) + loss_base(c)) : nullptr;
+  if (!ragged(shape)) {
+    st = fwd_launch(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, shape->n_q,
+                    shape->n_k, make_fwd_plan(shape, splits[0]), split_ws, weights, lpart, s);
+  } else {
+    // ragged batch: rows past an element's query length read 0; each element
+    // runs as a problem of its own in the padded tensors
+    const int64_t rows = shape->B * shape->H * shape->n_q;
+    for (float* o : {out_kl, out_lse1, out_lse2}) {
+      st = fill_zero(o, rows, s);
+      if (st != STREAMKL_OK) return st;
+    }
+    const int64_t es = shape->dtype == STREAMKL_BF16 ? 2 : 4;
+    const int64_t qr = shape->H * shape->n_q, k1r = kv_heads(shape, 1) * shape->n_k,
+                  k2r = kv_heads(shape, 2) * shape->n_k;
+    int64_t slot = 0;
+    for (int64_t b = 0; b < shape->B && st == STREAMKL_OK; ++b) {
+      const streamkl_shape e = element_shape(shape, b);
+      if (e.n_q == 0) continue;
+      const FwdPlan p = make_fwd_plan(&e, splits[b]);
+      st = fwd_launch(elem(Q1, b, qr, es * e.d1), elem(K1, b, k1r, es * e.d1), elem(Q2, b, qr, es * e.d2),
+                      elem(K2, b, k2r, es * e.d2), causal, scale1, scale2, elem(out_kl, b, qr, 4),
+                      elem(out_lse1, b, qr, 4), elem(out_lse2, b, qr, 4), &e, shape->n_q, shape->n_k, p, split_ws,
+                      elem(weights, b, qr, 4), lpart ? lpart + slot : nullptr, s);
+      slot += p.loss_slots;
+    }
+  }
+  if (st != STREAMKL_OK || !loss) return st;
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, s, (const double*)lpart, c.loss_slots,
+                     weights ? 0.0 : c.rows, out_loss);
   return hip_status(hipGetLastError());
 }
 
@@ -527,41 +717,16 @@ extern "C" {
 streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
                              float scale1, float scale2, float* out_kl, float* out_lse1, float* out_lse2,
                              const streamkl_shape* shape, const streamkl_launch* launch, void* stream) {
-  streamkl_status st = check_shape(shape, causal);
-  if (st != STREAMKL_OK) return st;
-  if (!Q1 || !K1 || !Q2 || !K2 || !out_kl || !out_lse1 || !out_lse2) return STREAMKL_ERR_INVALID;
-  if (!aligned(Q1, 16) || !aligned(K1, 16) || !aligned(Q2, 16) || !aligned(K2, 16)) return STREAMKL_ERR_INVALID;
-  if (!aligned(out_kl, 4) || !aligned(out_lse1, 4) || !aligned(out_lse2, 4)) return STREAMKL_ERR_INVALID;
-  if (!(scale1 == scale1) || !(scale2 == scale2)) return STREAMKL_ERR_INVALID;
-  if (launch && (launch->num_splits < 0 || launch->bwd_mode < 0 || launch->bwd_mode > 4)) return STREAMKL_ERR_INVALID;
-  DeviceInfo dev;
-  st = device_info(&dev);
-  if (st != STREAMKL_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!ragged(shape))
-    return fwd_launch(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, shape->n_q,
-                      shape->n_k, launch, dev, s);
-  // ragged batch: rows past an element's query length read 0; each element
-  // runs as a problem of its own in the padded tensors
-  if (launch && launch->num_splits > 1 && (!launch->workspace ||
-      launch->workspace_bytes < streamkl_fwd_workspace_bytes(shape, causal, launch)))
-    return STREAMKL_ERR_WORKSPACE;
-  const int64_t rows = shape->B * shape->H * shape->n_q;
-  for (float* o : {out_kl, out_lse1, out_lse2}) {
-    st = fill_zero(o, rows, s);
-    if (st != STREAMKL_OK) return st;
-  }
-  const int64_t es = shape->dtype == STREAMKL_BF16 ? 2 : 4;
-  const int64_t qr = shape->H * shape->n_q, k1r = kv_heads(shape, 1) * shape->n_k, k2r = kv_heads(shape, 2) * shape->n_k;
-  for (int64_t b = 0; b < shape->B; ++b) {
-    const streamkl_shape e = element_shape(shape, b);
-    if (e.n_q == 0) continue;
-    st = fwd_launch(elem(Q1, b, qr, es * e.d1), elem(K1, b, k1r, es * e.d1), elem(Q2, b, qr, es * e.d2),
-                    elem(K2, b, k2r, es * e.d2), causal, scale1, scale2, elem(out_kl, b, qr, 4),
-                    elem(out_lse1, b, qr, 4), elem(out_lse2, b, qr, 4), &e, shape->n_q, shape->n_k, launch, dev, s);
-    if (st != STREAMKL_OK) return st;
-  }
-  return STREAMKL_OK;
+  return fwd_call(Q1, K1, Q2, K2, causal, scale1, scale2, nullptr, out_kl, out_lse1, out_lse2, nullptr, shape, launch,
+                  launch ? launch->workspace : nullptr, launch ? launch->workspace_bytes : 0, stream);
+}
+
+streamkl_status streamkl_fwd_loss(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                                  float scale1, float scale2, const float* weights, float* out_kl, float* out_lse1,
+                                  float* out_lse2, float* out_loss, const streamkl_shape* shape,
+                                  const streamkl_launch* launch, void* stream) {
+  return fwd_call(Q1, K1, Q2, K2, causal, scale1, scale2, weights, out_kl, out_lse1, out_lse2, out_loss, shape, launch,
+                  launch ? launch->workspace : nullptr, launch ? launch->workspace_bytes : 0, stream);
 }
 
 int streamkl_bwd_plan(const streamkl_shape* shape, int causal, int setting, const streamkl_launch* launch) {
@@ -589,7 +754,7 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
   if (!aligned(lse1, 4) || !aligned(lse2, 4) || !aligned(d_kl, 4) || (kl && !aligned(kl, 4)))
     return STREAMKL_ERR_INVALID;
   if ((dQ && !aligned(dQ, 16)) || (dK && !aligned(dK, 4))) return STREAMKL_ERR_INVALID;
-  if (!(scale1 == scale1) || !(scale2 == scale2)) return STREAMKL_ERR_INVALID;
+  if (!finite_bits(scale1) || !finite_bits(scale2)) return STREAMKL_ERR_INVALID;
   DeviceInfo dev;
   st = device_info(&dev);
   if (st != STREAMKL_OK) return st;
@@ -636,7 +801,7 @@ streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q
   if ((dQ1 && !aligned(dQ1, 16)) || (dQ2 && !aligned(dQ2, 16)) || (dK1 && !aligned(dK1, 4)) ||
       (dK2 && !aligned(dK2, 4)))
     return STREAMKL_ERR_INVALID;
-  if (!(scale1 == scale1) || !(scale2 == scale2)) return STREAMKL_ERR_INVALID;
+  if (!finite_bits(scale1) || !finite_bits(scale2)) return STREAMKL_ERR_INVALID;
   DeviceInfo dev;
   st = device_info(&dev);
   if (st != STREAMKL_OK) return st;

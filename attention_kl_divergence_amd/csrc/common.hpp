@@ -95,12 +95,15 @@ __device__ inline RowState merge_state(const RowState& a, const RowState& b) {
 
 // KL, LSE1, LSE2 (natural units) from a complete row state:
 // KL = ln2 * (A / l1 + LSE2_2 - LSE1_2), LSE_t = ln2 * (M_t + log2 l_t).
-__device__ inline void finish_state(const RowState& s, float* kl, float* lse1, float* lse2) {
+// Returns the KL it stored.
+__device__ inline float finish_state(const RowState& s, float* kl, float* lse1, float* lse2) {
   const float L1 = s.M1 + log2f(s.l1);
   const float L2 = s.M2 + log2f(s.l2);
-  *kl = kLn2 * (s.A / s.l1 + (L2 - L1));
+  const float k = kLn2 * (s.A / s.l1 + (L2 - L1));
+  *kl = k;
   *lse1 = kLn2 * L1;
   *lse2 = kLn2 * L2;
+  return k;
 }
 
 __device__ inline RowState shfl_xor_state(const RowState& s, int mask) {

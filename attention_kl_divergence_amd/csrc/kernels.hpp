@@ -43,6 +43,8 @@ struct FwdArgs {
   float* lse1;
   float* lse2;
   float* ws;           // split partials [5][BH][nsplit][n_q], used when nsplit > 1
+  const float* lw;     // fused loss: per-row weights [BH][qs] (NULL: weight 1)
+  double* lpart;       // fused loss: one partial sum per finalizing workgroup (NULL: no loss)
   int64_t BH;
   int n_q, n_k;
   int nsplit;
@@ -164,6 +166,30 @@ __device__ inline WorkItem work_item(int64_t lin, int64_t BH, int nblk) {
     return {v / nblk, (int)(v % nblk)};
   }
   return {lin % BH, (int)(lin / BH)};
+}
+
+// Fused loss (the distillation objective sum_i w_i KL_i): each workgroup that
+// finalizes rows writes the sum of w_i KL_i over its rows to its own slot, in
+// a fixed order (a butterfly over the wave's lanes, which leaves the same bits
+// in every lane, then the waves in index order), so the result does not depend
+// on scheduling.  v is this thread's w_i KL_i (0 if it finalized no row).
+// `red` is NW doubles of LDS the caller has made free for this.
+template <int NW>
+__device__ inline void loss_partial(double v, double* red, double* slot, int tid) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += red[w];
+    *slot = t;
+  }
+}
+
+__device__ inline double loss_term(const FwdArgs& a, int64_t r, float kl) {
+  return a.lw ? (double)a.lw[r] * (double)kl : (double)kl;
 }
 
 // Barrier between the compute phases of a ping-pong loop.  It orders no
@@ -332,6 +358,52 @@ __device__ inline typename Mfma<T>::frag frag_global(const T* g, int row, int rm
   return valid ? f : zero_frag<T>();
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 dQ under a key offset shared by every key.  Every row of dS sums to
+// zero (setting 1: sum_j (P2 - P1) = 0; setting 2: sum_j P1 (r - KL) = 0,
+// Method 2), so dQ_i = sum_j dS_ij K_j = sum_j dS_ij (K_j - kbar) for any
+// vector kbar.  The matrix instruction takes dS rounded to bf16, and those
+// rounding errors do not sum to zero: a component u common to all keys
+// would reach dQ as (sum_j bf16(dS_ij)) u, however large u is against the
+// spread of the keys.  The dQ paths therefore either subtract
+// r_i kbar with r_i = sum_j bf16(dS_ij) (the exact values fed to the
+// product), or feed K_j - kbar to the product; either way the rounding error
+// is relative to K - kbar instead of K.  kbar is the mean of the head's first
+// min(64, n_k) key rows, summed in row order by ref_key_col, so every
+// workgroup that adds into one dQ row gets bitwise the same kbar.
+constexpr int kRefKeys = 64;
+
+__device__ inline float ref_key_col(const bf16* K, int D, int n_k, int c) {
+  float s = 0.f;
+  if (n_k >= kRefKeys) {  // unrolled so the loads go out together; the same row order
+#pragma unroll 16
+    for (int j = 0; j < kRefKeys; ++j) s += (float)K[(int64_t)j * D + c];
+    return s * (1.f / kRefKeys);
+  }
+  for (int j = 0; j < n_k; ++j) s += (float)K[(int64_t)j * D + c];
+  return s / (float)n_k;
+}
+
+// kbar[c] for every column c < D, spread over nthreads threads (the caller
+// publishes it with a barrier)
+template <int D>
+__device__ inline void ref_key(float* kbar, const bf16* K, int n_k, int tid, int nthreads) {
+  for (int c = tid; c < D; c += nthreads) kbar[c] = ref_key_col(K, D, n_k, c);
+}
+
+// acc + the sum of the eight bf16 values of an operand fragment (exact
+// products with 1.0, fp32 accumulation)
+__device__ inline float sum_frag(const bf16x8& f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[0], f[1]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[2], f[3]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[4], f[5]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[6], f[7]}, one, acc, false);
+  return acc;
+}
+__device__ inline float sum_frag(float, float acc) { return acc; }
 
 // Scheduling pattern for a run of N matrix instructions that each consume R
 // LDS reads: issue the reads for the first AHEAD instructions, then alternate
@@ -571,10 +643,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 
   st = merge_state(st, shfl_xor_state(st, 32));
+  double lv = 0.0;
   if (grp == 0 && qrow < a.n_q) {
     const int64_t r = bh * a.qs + qrow;
     if (a.nsplit == 1) {
-      finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
+      const float klv = finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
+      if (a.lpart) lv = loss_term(a, r, klv);
     } else {
       const int64_t fs = a.BH * (int64_t)a.nsplit * a.n_q;
       const int64_t o = (bh * a.nsplit + z) * (int64_t)a.n_q + qrow;
@@ -584,6 +658,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       a.ws[o + 3 * fs] = st.M2;
       a.ws[o + 4 * fs] = st.l2;
     }
+  }
+  if (a.lpart && a.nsplit == 1) {
+    __syncthreads();  // every wave is past its last tile read: the tile buffer is free
+    loss_partial<NW>(lv, reinterpret_cast<double*>(lds), a.lpart + blockIdx.x, tid);
   }
 }
 
@@ -844,9 +922,15 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   if (group == 1 && ntiles > 0) update((ntiles - 1) * BK);
 
   st = merge_state(st, shfl_xor_state(st, 32));
+  double lv = 0.0;
   if (grp == 0 && qrow < a.n_q) {
     const int64_t r = bh * a.qs + qrow;
-    finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
+    const float klv = finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
+    if (a.lpart) lv = loss_term(a, r, klv);
+  }
+  if (a.lpart) {
+    __syncthreads();  // group 1 may still read the last tile until here
+    loss_partial<NW>(lv, reinterpret_cast<double*>(lds), a.lpart + blockIdx.x, tid);
   }
 }
 
@@ -1029,7 +1113,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   constexpr int S1 = D1 / MF::KSTEP, S2 = D2 / MF::KSTEP;
   constexpr int NKB = BK / 32, NB = DS / 32, HS = 32 / MF::KSTEP;
   constexpr int TS = BK * (D1 + D2);
-  __shared__ __attribute__((aligned(1024))) T lds[2 * TS];
+  constexpr bool BF = sizeof(T) == 2;
+  // two tile buffers, then (bf16) the reference key kbar: DS floats
+  __shared__ __attribute__((aligned(1024))) T lds[2 * TS + (BF ? 2 * DS : 0)];
+  float* kbar = reinterpret_cast<float*>(lds + 2 * TS);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
@@ -1055,6 +1142,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   const TileLoader<T, D2, BK, NW> ld2(wave, lane);
   ld1.issue(lds, K1, 0, a.n_k);
   ld2.issue(lds + BK * D1, K2, 0, a.n_k);
+  // the first tile's barrier publishes kbar
+  if constexpr (BF) ref_key<DS>(kbar, reinterpret_cast<const bf16*>(SETTING == 1 ? K2 : K1), a.n_k, tid, 64 * NW);
 
   frag qf1[S1], qf2[S2];
   const bool qv = qrow < a.n_q;
@@ -1068,10 +1157,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   f32x16 dqa[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dqa[nb] = zero16();
+  float rsum = 0.f;  // bf16: this lane's part of r for query qrow, the sum of the bf16 dS it fed
 
   // bf16: per-lane LDS offsets computed once (K1/K2 rows share them when
   // d1 == d2); fp32 computes addresses per read
-  constexpr bool BF = sizeof(T) == 2;
   using RF1 = std::conditional_t<BF, RowFragOffsets<D1, S1>, NoOffsets>;
   using RF2 = std::conditional_t<BF, RowFragOffsets<D2, S2>, NoOffsets>;
   using CF = std::conditional_t<BF, ColFragOffsets<DS, NB>, NoOffsets>;
@@ -1125,6 +1214,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int h = 0; h < HS; ++h) {
         const frag af = frag_from_acc(s1, h, T());
+        if constexpr (BF) rsum = sum_frag(af, rsum);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) dqa[nb] = MF::run(af, colop(sKS, kb, nb, h), dqa[nb]);
       }
@@ -1150,7 +1240,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   }
 
   // dQ accumulator rows are queries q0 + acc_row(e, grp); lane r < 32 holds
-  // query q0 + r's sign
+  // query q0 + r's sign (and, once the lane groups' key halves are added, its r)
+  if constexpr (BF) {
+    rsum += __shfl_xor(rsum, 32);
+    float kb[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) kb[nb] = kbar[nb * 32 + col];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float rq = __shfl(rsum, acc_row(e, grp));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dqa[nb][e] = fmaf(-rq, kb[nb], dqa[nb][e]);
+    }
+  }
   const uint64_t neg = __ballot(row_sign < 0.f);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -1271,6 +1373,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a) {
   frag kcf[FUSED ? HK : 1];
   if constexpr (FUSED) {
     const int dcol = 32 * (wave % NBF) + col;
+    // bf16: the operand is K_s - kbar (see ref_key_col), the same kbar in
+    // every workgroup of the head
+    float kb = 0.f;
+    if constexpr (MF::KPL > 1) kb = ref_key_col(reinterpret_cast<const bf16*>(KS), DS, a.n_k, dcol);
 #pragma unroll
     for (int h = 0; h < HK; ++h) {
       if constexpr (MF::KPL == 1) {
@@ -1280,8 +1386,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < MF::KPL; ++e) {
           const int key = kw0 + h * MF::KSTEP + grp * MF::KPL + e;
-          kcf[h][e] = KS[(int64_t)min(key, a.n_k - 1) * DS + dcol];
-          if (key >= a.n_k) kcf[h][e] = (T)0.f;
+          const float v = (float)KS[(int64_t)min(key, a.n_k - 1) * DS + dcol] - kb;
+          kcf[h][e] = key < a.n_k ? (T)v : (T)0.f;
         }
       }
     }
@@ -1518,13 +1624,15 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
   constexpr int QE = 32 * (D1 + D2);  // Q1 and Q2, 32 rows each
   constexpr int DSE = 32 * 32;        // one wave's dS^T tile
   // one array: separate __shared__ objects get separate alias scopes, and the
-  // tile reads would then wait for the next tile's direct loads in flight
-  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * TS + QE + NW * DSE];
+  // tile reads would then wait for the next tile's direct loads in flight;
+  // the reference key kbar (DS floats) at the end
+  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * TS + QE + NW * DSE + 2 * DS];
   bf16* sQ1 = lds + 2 * TS;
   bf16* sQ2 = sQ1 + 32 * D1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
   bf16* sdS = lds + 2 * TS + QE + wave * DSE;
+  float* kbar = reinterpret_cast<float*>(lds + 2 * TS + QE + NW * DSE);
   const int64_t bh = blockIdx.x / a.nblk;
   const int z = (int)(blockIdx.x % a.nblk);
   const int off = a.n_k - a.n_q;
@@ -1547,6 +1655,7 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
   if (count > 0) issue(0, 0);
   dec_stage_q<D1>(sQ1, Q1, a.n_q, tid);
   dec_stage_q<D2>(sQ2, Q2, a.n_q, tid);
+  ref_key<DS>(kbar, SETTING == 1 ? K2 : K1, a.n_k, tid, 256);
   // lane column col is query row col: its statistics are fixed for the kernel
   const bool qv = col < a.n_q;
   const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.qs + col, qv);
@@ -1568,6 +1677,7 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
   f32x16 dqa[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dqa[nb] = zero16();
+  float rsum = 0.f;  // this lane's part of r for query col: the sum of the bf16 dS it fed
 
   auto tile = [&](const bf16* __restrict__ sK1, const bf16* __restrict__ sK2, const bf16* __restrict__ sQa,
                   const bf16* __restrict__ sQb, int kw) {
@@ -1594,6 +1704,7 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const bf16x8 b = frag_from_acc(s1, h, bf16());
+      rsum = sum_frag(b, rsum);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         dqa[nb] = MF::run(fragcol_acc_bf16<DS>(sKS, 32 * wave, 32 * nb, h, lane), b, dqa[nb]);
@@ -1650,12 +1761,22 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
     if (kw < a.n_k) tile(sK1, sK1 + BK * D1, sQ1, sQ2, kw);
   }
 
+  // the workgroups of a head add r kbar for their own key tiles, with the
+  // same kbar: the sum over them is the row's r kbar
+  rsum += __shfl_xor(rsum, 32);
   if (qv) {
     float* dq = a.dq + (bh * a.qs + col) * (int64_t)DS;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) atomicAdd(dq + 32 * nb + acc_row(e, grp), dqa[nb][e]);
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 kb = *reinterpret_cast<const f32x4*>(kbar + 32 * nb + 8 * i + 4 * grp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * i + j;
+          atomicAdd(dq + 32 * nb + acc_row(e, grp), fmaf(-rsum, kb[j], dqa[nb][e]));
+        }
+      }
   }
 }
 

@@ -54,7 +54,8 @@ class Shape(ctypes.Structure):
         return self
 
 
-ABI_VERSION = 3
+ABI_VERSION = 4
+INVALID_BYTES = (1 << 64) - 1  # STREAMKL_INVALID_BYTES
 
 
 class Launch(ctypes.Structure):
@@ -81,8 +82,14 @@ def _lib():
         lib.streamkl_bwd_joint.restype = i32
         lib.streamkl_kl_loss.argtypes = [vp, vp, ctypes.c_int64, vp, vp]
         lib.streamkl_kl_loss.restype = i32
+        lib.streamkl_fwd_loss.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, vp, vp, vp, sp, lp, vp]
+        lib.streamkl_fwd_loss.restype = i32
         lib.streamkl_fwd_workspace_bytes.argtypes = [sp, i32, lp]
         lib.streamkl_fwd_workspace_bytes.restype = sz
+        lib.streamkl_fwd_loss_workspace_bytes.argtypes = [sp, i32, lp]
+        lib.streamkl_fwd_loss_workspace_bytes.restype = sz
+        lib.streamkl_bwd_workspace_bytes.argtypes = [sp, i32, i32, lp]
+        lib.streamkl_bwd_workspace_bytes.restype = sz
         lib.streamkl_fwd_plan.argtypes = [sp, i32, lp]
         lib.streamkl_fwd_plan.restype = i32
         lib.streamkl_bwd_plan.argtypes = [sp, i32, i32, lp]
@@ -154,6 +161,40 @@ def _check(status: int, what: str):
         raise StreamKLError(status, what, _lib().streamkl_last_hip_error())
 
 
+def _check_out(t, shape, device, what):
+    """A caller-supplied output: fp32, contiguous, on the inputs' device, of the
+    exact shape the library writes (it sees only a pointer)."""
+    if t is None:
+        raise ValueError(f"{what}: missing output tensor")
+    if (t.dtype != torch.float32 or not t.is_contiguous() or t.device != device
+            or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{what} must be a contiguous fp32 tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _check_rows(t, shp: Shape, device, what):
+    """A per-row input vector: contiguous fp32 [B, H, n_q] on the device."""
+    if (t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != shp.B * shp.H * shp.n_q
+            or t.device != device):
+        raise ValueError(f"{what} must be contiguous fp32 [B, H, n_q] on {device}")
+
+
+def _bytes(n: int, what: str) -> int:
+    if n == INVALID_BYTES:
+        raise ValueError(f"{what}: invalid shape or launch options")
+    return n
+
+
+def _workspace(workspace, need: int, device):
+    """The caller's workspace if it is a large enough device tensor, else a new one."""
+    if workspace is not None:
+        if workspace.device != device or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {device}")
+        if workspace.numel() * workspace.element_size() >= need:
+            return workspace
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
 def fwd_plan(shape: Shape, causal: bool, num_splits: int = 0, with_workspace: bool = True) -> int:
     """Key-split count the forward would use."""
     lib = _lib()
@@ -166,7 +207,20 @@ def fwd_plan(shape: Shape, causal: bool, num_splits: int = 0, with_workspace: bo
 
 def fwd_workspace_bytes(shape: Shape, causal: bool, num_splits: int = 0) -> int:
     ln = Launch(num_splits, 0, None, 0)
-    return _lib().streamkl_fwd_workspace_bytes(ctypes.byref(shape), int(causal), ctypes.byref(ln))
+    return _bytes(_lib().streamkl_fwd_workspace_bytes(ctypes.byref(shape), int(causal), ctypes.byref(ln)),
+                  "streamkl_fwd_workspace_bytes")
+
+
+def fwd_loss_workspace_bytes(shape: Shape, causal: bool, num_splits: int = 0) -> int:
+    ln = Launch(num_splits, 0, None, 0)
+    return _bytes(_lib().streamkl_fwd_loss_workspace_bytes(ctypes.byref(shape), int(causal), ctypes.byref(ln)),
+                  "streamkl_fwd_loss_workspace_bytes")
+
+
+def bwd_workspace_bytes(shape: Shape, causal: bool, setting: int, bwd_mode: int = BWD_AUTO) -> int:
+    ln = Launch(0, bwd_mode, None, 0)
+    return _bytes(_lib().streamkl_bwd_workspace_bytes(ctypes.byref(shape), int(causal), int(setting),
+                                                      ctypes.byref(ln)), "streamkl_bwd_workspace_bytes")
 
 
 def bwd_plan(shape: Shape, causal: bool, setting: int, bwd_mode: int = BWD_AUTO) -> int:
@@ -184,15 +238,18 @@ def streamkl_fwd(q1, k1, q2, k2, causal: bool, scale1: float = 0.0, scale2: floa
     """
     shp = shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
     dev = q1.device
+    rows = (shp.B, shp.H, shp.n_q)
     if out is None:
         kw = dict(device=dev, dtype=torch.float32)
-        out = tuple(torch.empty((shp.B, shp.H, shp.n_q), **kw) for _ in range(3))
+        out = tuple(torch.empty(rows, **kw) for _ in range(3))
+    for t, n in zip(out, ("kl", "lse1", "lse2")):
+        _check_out(t, rows, dev, f"out {n}")
     kl, lse1, lse2 = out
     ln = Launch(num_splits, 0, None, 0)
-    need = _lib().streamkl_fwd_workspace_bytes(ctypes.byref(shp), int(causal), ctypes.byref(ln))
+    need = _bytes(_lib().streamkl_fwd_workspace_bytes(ctypes.byref(shp), int(causal), ctypes.byref(ln)),
+                  "streamkl_fwd")
     if need:
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _workspace(workspace, need, dev)
         ln.workspace = workspace.data_ptr()
         ln.workspace_bytes = workspace.numel() * workspace.element_size()
     st = _lib().streamkl_fwd(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), int(causal),
@@ -200,6 +257,40 @@ def streamkl_fwd(q1, k1, q2, k2, causal: bool, scale1: float = 0.0, scale2: floa
                              ctypes.byref(shp), ctypes.byref(ln), _stream(dev))
     _check(st, "streamkl_fwd")
     return kl, lse1, lse2
+
+
+def streamkl_fwd_loss(q1, k1, q2, k2, causal: bool, weights=None, scale1: float = 0.0, scale2: float = 0.0,
+                      num_splits: int = 0, out=None, workspace=None, q_len=None, k_len=None):
+    """Forward with the loss fused into its epilogue: returns (kl, lse1, lse2, loss).
+
+    loss is a 0-dim fp32 tensor: sum_i weights_i KL_i over every query row, or
+    the mean KL over the rows when weights is None (bitwise repeatable).
+    out: optional preallocated (kl, lse1, lse2, loss).
+    """
+    shp = shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
+    dev = q1.device
+    rows = (shp.B, shp.H, shp.n_q)
+    if out is None:
+        kw = dict(device=dev, dtype=torch.float32)
+        out = tuple(torch.empty(rows, **kw) for _ in range(3)) + (torch.empty((), **kw),)
+    for t, n in zip(out[:3], ("kl", "lse1", "lse2")):
+        _check_out(t, rows, dev, f"out {n}")
+    _check_out(out[3], (), dev, "out loss")
+    if weights is not None:
+        _check_rows(weights, shp, dev, "weights")
+    kl, lse1, lse2, loss = out
+    ln = Launch(num_splits, 0, None, 0)
+    need = _bytes(_lib().streamkl_fwd_loss_workspace_bytes(ctypes.byref(shp), int(causal), ctypes.byref(ln)),
+                  "streamkl_fwd_loss")
+    workspace = _workspace(workspace, need, dev)
+    ln.workspace = workspace.data_ptr()
+    ln.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = _lib().streamkl_fwd_loss(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), int(causal),
+                                  float(scale1), float(scale2), weights.data_ptr() if weights is not None else None,
+                                  kl.data_ptr(), lse1.data_ptr(), lse2.data_ptr(), loss.data_ptr(),
+                                  ctypes.byref(shp), ctypes.byref(ln), _stream(dev))
+    _check(st, "streamkl_fwd_loss")
+    return kl, lse1, lse2, loss
 
 
 def streamkl_bwd(setting: int, q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
@@ -219,9 +310,13 @@ def streamkl_bwd(setting: int, q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_k
                None if bwd_mode == BWD_DQ_ONLY else torch.empty((shp.B, _kv(shp, 2 if setting == 1 else 1), shp.n_k, ds),
                                                                 **kw))
     dq, dk = out
-    for t in (lse1, lse2, d_kl) + ((kl,) if kl is not None else ()):
-        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != shp.B * shp.H * shp.n_q:
-            raise ValueError("kl, lse1, lse2, d_kl must be contiguous fp32 [B, H, n_q]")
+    if bwd_mode != BWD_DK_ONLY:
+        _check_out(dq, (shp.B, shp.H, shp.n_q, ds), dev, "out dQ")
+    if bwd_mode != BWD_DQ_ONLY:
+        _check_out(dk, (shp.B, _kv(shp, 2 if setting == 1 else 1), shp.n_k, ds), dev, "out dK")
+    for t, n in zip((lse1, lse2, d_kl, kl), ("lse1", "lse2", "d_kl", "kl")):
+        if t is not None:
+            _check_rows(t, shp, dev, n)
     ln = Launch(0, bwd_mode, None, 0)
     st = _lib().streamkl_bwd(int(setting), q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), int(causal),
                              float(scale1), float(scale2), kl.data_ptr() if kl is not None else None,
@@ -247,9 +342,14 @@ def streamkl_bwd_joint(q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
                None if nk else torch.empty((shp.B, _kv(shp, 1), shp.n_k, shp.d1), **kw),
                None if nq else torch.empty((shp.B, shp.H, shp.n_q, shp.d2), **kw),
                None if nk else torch.empty((shp.B, _kv(shp, 2), shp.n_k, shp.d2), **kw))
-    for t in (kl, lse1, lse2, d_kl):
-        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != shp.B * shp.H * shp.n_q:
-            raise ValueError("kl, lse1, lse2, d_kl must be contiguous fp32 [B, H, n_q]")
+    shapes = ((shp.B, shp.H, shp.n_q, shp.d1), (shp.B, _kv(shp, 1), shp.n_k, shp.d1),
+              (shp.B, shp.H, shp.n_q, shp.d2), (shp.B, _kv(shp, 2), shp.n_k, shp.d2))
+    for i, (t, want, n) in enumerate(zip(out, shapes, ("dQ1", "dK1", "dQ2", "dK2"))):
+        if (bwd_mode == BWD_DK_ONLY and i % 2 == 0) or (bwd_mode == BWD_DQ_ONLY and i % 2 == 1):
+            continue
+        _check_out(t, want, dev, f"out {n}")
+    for t, n in zip((kl, lse1, lse2, d_kl), ("kl", "lse1", "lse2", "d_kl")):
+        _check_rows(t, shp, dev, n)
     ln = Launch(0, bwd_mode, None, 0)
     ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     st = _lib().streamkl_bwd_joint(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), int(causal),
@@ -270,6 +370,7 @@ def kl_loss(kl, weights=None, out=None):
         raise ValueError("weights must be contiguous fp32 with one value per row of kl")
     if out is None:
         out = torch.empty((), device=kl.device, dtype=torch.float32)
+    _check_out(out, (), kl.device, "out")
     st = _lib().streamkl_kl_loss(kl.data_ptr(), weights.data_ptr() if weights is not None else None,
                                  kl.numel(), out.data_ptr(), _stream(kl.device))
     _check(st, "streamkl_kl_loss")

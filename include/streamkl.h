@@ -28,7 +28,8 @@
  * - causal != 0 applies a bottom-right aligned mask: key j is visible to
  *   query i iff j <= i + (n_k - n_q); this requires n_q <= n_k.  Key tiles
  *   past the boundary are skipped (Method 1).
- * - scale_t <= 0 selects 1/sqrt(d_t).
+ * - scale_t must be a finite number; scale_t <= 0 selects 1/sqrt(d_t)
+ *   (NaN or an infinite scale returns STREAMKL_ERR_INVALID).
  * - LSE values are natural logarithms.
  * - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *   enqueues work: no host synchronisation, no device allocation, no
@@ -100,16 +101,40 @@ typedef struct {
   size_t workspace_bytes;
 } streamkl_launch;
 
+/* Returned by the workspace queries below for invalid arguments. */
+#define STREAMKL_INVALID_BYTES ((size_t)-1)
+
 /*
  * Bytes of workspace the forward needs for this shape and launch options
  * (0 when no key split is used).  With num_splits = 0 (auto) this is the
- * size for the split count the library would choose.  Returns 0 for
- * invalid shapes.  Split-K: the technical summary, Method 3 (GPU kernel
- * optimisations), partitions the key dimension across thread blocks for
- * small N_Q; each split leaves five fp32 partial scalars per row, so the
- * workspace is 20 * B * H * n_q * splits bytes.
+ * size for the split count the library would choose.  Returns
+ * STREAMKL_INVALID_BYTES for invalid arguments.  Split-K: the technical
+ * summary, Method 3 (GPU kernel optimisations), partitions the key
+ * dimension across thread blocks for small N_Q; each split leaves five fp32
+ * partial scalars per row, so the workspace is 20 * B * H * n_q * splits
+ * bytes (ragged batches: the largest of any element; they reuse it).
  */
 size_t streamkl_fwd_workspace_bytes(const streamkl_shape* shape, int causal,
+                                    const streamkl_launch* launch);
+
+/*
+ * Bytes of workspace streamkl_fwd_loss needs: the split partials above
+ * (rounded up to 256 bytes), then one fp64 partial sum per workgroup that
+ * finalizes query rows (for the fused loss).  STREAMKL_INVALID_BYTES for
+ * invalid arguments.
+ */
+size_t streamkl_fwd_loss_workspace_bytes(const streamkl_shape* shape, int causal,
+                                         const streamkl_launch* launch);
+
+/*
+ * Bytes of workspace the backward needs: 0 for every valid shape, setting
+ * and mode (Method 2, recomputation strategy: the backward regenerates P_t
+ * from the stored LSE tile by tile and keeps everything else in registers
+ * and LDS; the fused mode accumulates dQ in the caller's output).
+ * STREAMKL_INVALID_BYTES for an invalid shape, setting (not 1 or 2) or
+ * launch option.  Callers may size a backward workspace generically with it.
+ */
+size_t streamkl_bwd_workspace_bytes(const streamkl_shape* shape, int causal, int setting,
                                     const streamkl_launch* launch);
 
 /* The key-split count the forward will use (>= 1), or 0 for invalid input. */
@@ -129,6 +154,30 @@ streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, con
                              float* out_kl, float* out_lse1, float* out_lse2,
                              const streamkl_shape* shape, const streamkl_launch* launch,
                              void* stream);
+
+/*
+ * Forward with the distillation loss fused into its epilogue (the pages
+ * name attention distillation as what the KL serves: technical summary,
+ * Significance; the preprint's abstract).  Everything streamkl_fwd does,
+ * plus, when out_loss is not NULL, *out_loss = sum_i w_i KL_i over every
+ * query row (weights: device fp32 [B,H,n_q], or NULL for the mean KL over
+ * the rows; ragged batches count only each element's rows).  Each
+ * workgroup that finalizes rows writes the sum of its rows' w_i KL_i to the
+ * workspace and one small kernel adds those partials in a fixed order, so
+ * the loss is bitwise repeatable and no second pass reads the KL.  The
+ * loss's gradient with respect to KL_i is w_i (or 1 / rows): the d_kl that
+ * streamkl_bwd takes.  out_loss: device, one fp32, 4-byte aligned.
+ * The workspace (launch->workspace, 16-byte aligned) must hold
+ * streamkl_fwd_loss_workspace_bytes; with num_splits = 0 a smaller one
+ * that still holds the loss partials of an unsplit forward falls back to
+ * one split, otherwise the call returns STREAMKL_ERR_WORKSPACE.  With
+ * out_loss NULL the call is streamkl_fwd.
+ */
+streamkl_status streamkl_fwd_loss(const void* Q1, const void* K1, const void* Q2, const void* K2,
+                                  int causal, float scale1, float scale2, const float* weights,
+                                  float* out_kl, float* out_lse1, float* out_lse2, float* out_loss,
+                                  const streamkl_shape* shape, const streamkl_launch* launch,
+                                  void* stream);
 
 /* The backward mode streamkl_bwd will use (1 fused, 2 separate, or the
  * requested 3/4), 0 if invalid. */
@@ -150,7 +199,7 @@ int streamkl_bwd_plan(const streamkl_shape* shape, int causal, int setting,
  *   With bwd_mode DK_ONLY (DQ_ONLY) only dK (dQ) is computed and the other
  *   pointer may be NULL; these serve callers that train only keys or only
  *   queries, and per-kernel timing.
- * No workspace is needed.
+ * No workspace is needed (streamkl_bwd_workspace_bytes returns 0).
  */
 streamkl_status streamkl_bwd(int setting,
                              const void* Q1, const void* K1, const void* Q2, const void* K2,
@@ -202,7 +251,8 @@ const char* streamkl_status_string(int status);
 int streamkl_last_hip_error(void);
 
 /* Library version, for the Python binding's load check (3: streamkl_shape
- * carries kv_heads1, kv_heads2 and the ragged-batch lengths). */
+ * carries kv_heads1, kv_heads2 and the ragged-batch lengths; 4: the fused
+ * loss, the backward workspace query, STREAMKL_INVALID_BYTES). */
 int streamkl_version(void);
 
 #ifdef __cplusplus

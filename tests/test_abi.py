@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("streamkl_fwd", "streamkl_bwd", "streamkl_fwd_workspace_bytes", "streamkl_status_string"):
+    for n in ("streamkl_fwd", "streamkl_bwd", "streamkl_fwd_workspace_bytes", "streamkl_bwd_workspace_bytes",
+              "streamkl_fwd_loss", "streamkl_fwd_loss_workspace_bytes", "streamkl_status_string"):
         assert n in names
 
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = sk.library()
-    assert lib.streamkl_version() == sk.ABI_VERSION == 3
+    assert lib.streamkl_version() == sk.ABI_VERSION == 4
     assert lib.streamkl_status_string(0) == b"ok"
     assert lib.streamkl_status_string(4) == b"HIP runtime error"
     assert lib.streamkl_status_string(99) == b"unknown status"
@@ -145,8 +146,111 @@ def test_bad_launch_options():
     bad = sk.Launch(-1, 0, None, 0)
     assert _fwd(shape(), ptr=8, launch=bad) == sk.ERR_INVALID
     lib = sk.library()
-    assert lib.streamkl_fwd_workspace_bytes(ctypes.byref(shape()), 0, ctypes.byref(bad)) == 0
+    assert lib.streamkl_fwd_workspace_bytes(ctypes.byref(shape()), 0, ctypes.byref(bad)) == sk.INVALID_BYTES
+    assert lib.streamkl_fwd_loss_workspace_bytes(ctypes.byref(shape()), 0, ctypes.byref(bad)) == sk.INVALID_BYTES
     assert lib.streamkl_bwd_plan(ctypes.byref(shape()), 0, 5, None) == 0
+
+
+def _fwd_scales(s1, s2, loss=False):
+    lib = sk.library()
+    p = ctypes.c_void_p(256)
+    if loss:
+        return lib.streamkl_fwd_loss(p, p, p, p, 0, s1, s2, None, p, p, p, p, ctypes.byref(shape()), None, None)
+    return lib.streamkl_fwd(p, p, p, p, 0, s1, s2, p, p, p, ctypes.byref(shape()), None, None)
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf"), float("-inf")])
+def test_non_finite_scales_are_invalid(bad):
+    """A NaN or infinite scale is rejected on the host before any device call
+    (the host layer tests the float's bits, so no floating-point compiler
+    flag can fold the check away)."""
+    lib = sk.library()
+    p = ctypes.c_void_p(256)
+    for s1, s2 in ((bad, 0.0), (0.0, bad)):
+        assert _fwd_scales(s1, s2) == sk.ERR_INVALID
+        assert _fwd_scales(s1, s2, loss=True) == sk.ERR_INVALID
+        for setting in (1, 2):
+            assert lib.streamkl_bwd(setting, p, p, p, p, 0, s1, s2, p, p, p, p, p, p, ctypes.byref(shape()),
+                                    None, None) == sk.ERR_INVALID
+        assert lib.streamkl_bwd_joint(p, p, p, p, 0, s1, s2, p, p, p, p, p, p, p, p, ctypes.byref(shape()),
+                                      None, None) == sk.ERR_INVALID
+
+
+def test_backward_workspace_query():
+    """The backward needs no workspace: 0 for every valid shape, setting and
+    mode; STREAMKL_INVALID_BYTES for an invalid shape, setting or mode."""
+    lib = sk.library()
+    for setting in (1, 2):
+        for mode in range(5):
+            ln = sk.Launch(0, mode, None, 0)
+            assert lib.streamkl_bwd_workspace_bytes(ctypes.byref(shape()), 1, setting, ctypes.byref(ln)) == 0
+    assert sk.bwd_workspace_bytes(shape(H=32, n_q=16, n_k=131072), False, 1) == 0
+    assert lib.streamkl_bwd_workspace_bytes(ctypes.byref(shape(n_q=0)), 0, 1, None) == sk.INVALID_BYTES
+    assert lib.streamkl_bwd_workspace_bytes(ctypes.byref(shape(d1=96)), 0, 1, None) == sk.INVALID_BYTES
+    assert lib.streamkl_bwd_workspace_bytes(ctypes.byref(shape(n_q=65, n_k=64)), 1, 1, None) == sk.INVALID_BYTES
+    assert lib.streamkl_bwd_workspace_bytes(ctypes.byref(shape()), 0, 3, None) == sk.INVALID_BYTES
+    assert lib.streamkl_bwd_workspace_bytes(None, 0, 1, None) == sk.INVALID_BYTES
+    bad = sk.Launch(0, 7, None, 0)
+    assert lib.streamkl_bwd_workspace_bytes(ctypes.byref(shape()), 0, 1, ctypes.byref(bad)) == sk.INVALID_BYTES
+    with pytest.raises(ValueError):
+        sk.bwd_workspace_bytes(shape(n_q=0), False, 1)
+
+
+def test_loss_workspace_query():
+    """streamkl_fwd_loss_workspace_bytes: the split partials (rounded up to 256
+    bytes) then 8 bytes per workgroup that finalizes rows."""
+    # long prefill, no split: one partial per 256-row ping-pong workgroup
+    big = shape(H=32, n_q=65536, n_k=65536)
+    assert sk.fwd_loss_workspace_bytes(big, True) == 8 * 32 * (65536 // 256)
+    # short query range, no split: 128-row workgroups
+    assert sk.fwd_loss_workspace_bytes(shape(H=3, n_q=100, n_k=100), False) == 8 * 3
+    # decode shape, split: split partials, then one partial per 256 merged rows
+    dec = shape(H=32, n_q=16, n_k=131072)
+    split = sk.fwd_workspace_bytes(dec, False)
+    assert split > 0
+    assert sk.fwd_loss_workspace_bytes(dec, False) == (split + 255) // 256 * 256 + 8 * 2
+    # ragged: consecutive partials of every non-empty element after the
+    # largest split region; each element is planned as a problem of its own
+    lens = [600, 0, 100, 9000]
+    rag = shape(B=4, H=8, n_q=9000, n_k=9000).set_lengths(lens, lens)
+    slots = 0
+    for n in lens:
+        if n == 0:
+            continue
+        sp = sk.fwd_plan(shape(H=8, n_q=n, n_k=n), True)
+        slots += -(-8 * n // 256) if sp > 1 else 8 * -(-n // (256 if n > 128 else 128))
+    split = sk.fwd_workspace_bytes(rag, True)
+    assert sk.fwd_loss_workspace_bytes(rag, True) == (split + 255) // 256 * 256 + 8 * slots
+    with pytest.raises(ValueError):
+        sk.fwd_loss_workspace_bytes(shape(n_q=0), False)
+
+
+def test_binding_checks_output_buffers():
+    """The C ABI sees only pointers: the binding rejects output buffers of the
+    wrong dtype, shape, layout or device before calling the library."""
+    import torch
+    q = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16)
+    f32 = torch.float32
+    good = tuple(torch.empty((1, 2, 64), dtype=f32) for _ in range(3))
+    for bad in (torch.empty((1, 2, 63), dtype=f32), torch.empty((1, 2, 64), dtype=torch.float64),
+                torch.empty((1, 2, 128), dtype=f32)[..., ::2]):
+        with pytest.raises(ValueError):
+            sk.streamkl_fwd(q, q, q, q, False, out=(bad,) + good[1:])
+    with pytest.raises(ValueError):
+        sk.streamkl_fwd_loss(q, q, q, q, False, out=good + (torch.empty((1,), dtype=f32),))
+    rows = torch.zeros((1, 2, 64), dtype=f32)
+    for bad_dq in (torch.empty((1, 2, 64, 64), dtype=f32), torch.empty((1, 2, 64, 128), dtype=torch.bfloat16)):
+        with pytest.raises(ValueError):
+            sk.streamkl_bwd(1, q, q, q, q, False, rows, rows, rows, rows,
+                            out=(bad_dq, torch.empty((1, 2, 64, 128), dtype=f32)))
+    with pytest.raises(ValueError):
+        sk.streamkl_bwd(1, q, q, q, q, False, rows, rows, rows, rows.double())
+    with pytest.raises(ValueError):
+        sk.streamkl_bwd_joint(q, q, q, q, False, rows, rows, rows, rows,
+                              out=tuple(torch.empty((1, 2, 64, 128), dtype=f32) for _ in range(3)) +
+                              (torch.empty((1, 2, 64, 64), dtype=f32),))
+    with pytest.raises(ValueError):
+        sk.kl_loss(rows, out=torch.empty((2,), dtype=f32))
 
 
 def test_workspace_sizing_and_plans():

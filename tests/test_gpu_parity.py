@@ -107,9 +107,28 @@ def sample_rows(n, k=96, seed=0):
     return np.unique(np.concatenate([[0, 1, n - 1], extra]).clip(0, n - 1))
 
 
-def run_sampled(w, dev, settings, heads=None, mode=sk.BWD_AUTO, dk_tail=2048, nrows=96):
+def oracle_row_stats(hi, causal, block=64):
+    """oracle.head_forward over every query row of one head, row blocks in
+    parallel threads (BLAS one thread each), for checks that need the LSE of
+    all rows."""
+    import concurrent.futures as cf
+    import os
+
+    from threadpoolctl import threadpool_limits
+    n_q = hi[0].shape[0]
+    chunks = np.array_split(np.arange(n_q), max(1, n_q // 2048))
+    with threadpool_limits(limits=1):
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+            parts = list(ex.map(lambda rows: oracle.head_forward(*hi, causal, rows=rows, block=block), chunks))
+    return tuple(np.concatenate([p[i] for p in parts]) for i in range(3))
+
+
+def run_sampled(w, dev, settings, heads=None, mode=sk.BWD_AUTO, dk_tail=2048, nrows=96, key_shift=0.0):
     _say(f"generate {w.name}")
     q1, k1, q2, k2 = workloads.generate(w, dev)
+    if key_shift:
+        # a component shared by every key (KL and the gradients do not change)
+        k1, k2 = ((k.float() + key_shift).to(k.dtype) for k in (k1, k2))
     g = workloads.upstream_grad(w, dev, "random")
     _say(f"fwd {w.name}")
     kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal)
@@ -153,6 +172,14 @@ def test_workload_8k_causal_both_settings(cuda_device):
     run_sampled(w, cuda_device, settings=(1, 2), heads=[0, 13, 31], nrows=256)
 
 
+def test_workload_8k_causal_shifted_keys(cuda_device):
+    """The 8K workload with 32 added to every key coordinate, both settings,
+    separate mode: dQ stays within the 1e-2 bound (the bf16 rounding of dS
+    meets K - kbar, not the shifted K)."""
+    w = workloads.WORKLOADS["h32-n8k-d128-bf16-causal"]
+    run_sampled(w, cuda_device, settings=(1, 2), heads=[0, 31], nrows=128, key_shift=32.0)
+
+
 def test_workload_8k_causal_fused_mode(cuda_device):
     """The fused backward (dQ by fp32 atomics from the key-outer kernel) at a
     full workload size, both settings."""
@@ -166,8 +193,22 @@ def test_workload_64k_causal_setting1(cuda_device):
 
 
 def test_workload_64k_noncausal_setting1(cuda_device):
+    """The 64K non-causal workload: sampled rows of KL, LSE and dQ on two
+    heads, and dK of 256 sampled keys (first, last and random ones) of head 0
+    against the oracle over all 65536 query rows."""
     w = workloads.WORKLOADS["h32-n64k-d128-bf16"]
-    run_sampled(w, cuda_device, settings=(1,), dk_tail=0)
+    _, grads = run_sampled(w, cuda_device, settings=(1,), dk_tail=0)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    hi = head_inputs(q1, k1, q2, k2, 0, 0)
+    _say("oracle row statistics of head 0, all 65536 rows")
+    stats = oracle_row_stats(hi, False)
+    keys = sample_rows(w.n_k, 253, seed=3)
+    _say(f"oracle dK of {len(keys)} keys over all rows")
+    rdk = oracle.head_dk_keys(1, *hi, False, to_np(g[0, 0]), keys, stats, block=4096)
+    dk = to_np(grads[1][1][0, 0])[keys]
+    assert np.linalg.norm(dk) > 0
+    check_grad(f"{w.name} h0 s1 dK sampled keys", dk, rdk)
 
 
 @pytest.mark.parametrize("name", ["decode-h32-q1-k128k-d128-bf16", "decode-h32-q16-k128k-d128-bf16",
