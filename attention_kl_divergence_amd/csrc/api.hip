@@ -82,6 +82,14 @@ __global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* __restrict__ 
   for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
+// Partials of the forward for callers that cannot allocate device memory
+// (streamkl_fwd_loss_noalloc): split-K states and fused-loss sums live in
+// this array, one copy per device, held until the process ends.  Host code
+// never passes the name itself to a kernel (on the host it only stands for
+// the symbol): it takes each device's address from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -90,6 +98,7 @@ struct DeviceInfo {
   int checked = 0;
   int gfx950 = 0;
   int cus = 256;
+  void* scratch = nullptr;  // this device's copy of `scratch` (streamkl_fwd_loss_noalloc), once looked up
 };
 std::mutex g_dev_mutex;
 DeviceInfo g_dev[64];
@@ -112,6 +121,28 @@ streamkl_status device_info(DeviceInfo* out) {
   }
   *out = d;
   return d.gfx950 ? STREAMKL_OK : STREAMKL_ERR_UNSUPPORTED;
+}
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current (the first call of streamkl_fwd_loss_noalloc on it).
+streamkl_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { g_last_hip_error = (int)e; return STREAMKL_ERR_HIP; }
+  if (dev < 0 || dev >= 64) return STREAMKL_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_dev_mutex);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.scratch) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      g_last_hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return STREAMKL_ERR_HIP;
+    }
+    d.scratch = ptr;
+  }
+  *out = d.scratch;
+  return STREAMKL_OK;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -727,6 +758,27 @@ streamkl_status streamkl_fwd_loss(const void* Q1, const void* K1, const void* Q2
                                   const streamkl_launch* launch, void* stream) {
   return fwd_call(Q1, K1, Q2, K2, causal, scale1, scale2, weights, out_kl, out_lse1, out_lse2, out_loss, shape, launch,
                   launch ? launch->workspace : nullptr, launch ? launch->workspace_bytes : 0, stream);
+}
+
+streamkl_status streamkl_fwd_loss_noalloc(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                                          float scale1, float scale2, const float* weights, float* out_kl,
+                                          float* out_lse1, float* out_lse2, float* out_loss,
+                                          const streamkl_shape* shape, const streamkl_launch* launch, void* stream) {
+  // argument errors first (as every entry point), then this device's scratch
+  streamkl_status st = check_shape(shape, causal);
+  if (st != STREAMKL_OK) return st;
+  DeviceInfo dev;
+  st = device_info(&dev);
+  if (st != STREAMKL_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != STREAMKL_OK) return st;
+  // the caller's workspace fields are not used: the library's scratch replaces them
+  streamkl_launch l = launch ? *launch : streamkl_launch{0, 0, nullptr, 0};
+  l.workspace = nullptr;
+  l.workspace_bytes = 0;
+  return fwd_call(Q1, K1, Q2, K2, causal, scale1, scale2, weights, out_kl, out_lse1, out_lse2, out_loss, shape, &l, ws,
+                  kScratchBytes, stream);
 }
 
 int streamkl_bwd_plan(const streamkl_shape* shape, int causal, int setting, const streamkl_launch* launch) {

@@ -179,6 +179,33 @@ streamkl_status streamkl_fwd_loss(const void* Q1, const void* K1, const void* Q2
                                   const streamkl_shape* shape, const streamkl_launch* launch,
                                   void* stream);
 
+/*
+ * streamkl_fwd_loss for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the split-K partial states and the fused-loss partial sums go
+ * to a scratch array inside the library instead of a caller workspace.  The
+ * array holds STREAMKL_NOALLOC_SCRATCH_BYTES (4 MiB) on every device the
+ * library runs on, from the library's first use on that device (when its
+ * code is loaded there) until the process ends; the call allocates and
+ * frees nothing.  Arguments, outputs and
+ * semantics are those of streamkl_fwd_loss (out_loss may be NULL: the plain
+ * forward), except that launch->workspace and launch->workspace_bytes are
+ * ignored.  If the partials the plan needs do not fit in the scratch, an
+ * automatic split count falls back to fewer partials (one split) and
+ * otherwise the call returns STREAMKL_ERR_WORKSPACE having written nothing
+ * (e.g. an explicit split count whose 20 * B * H * n_q * splits bytes exceed
+ * it).  Every call on one device shares its scratch: calls that overlap in
+ * time on one device (other streams, other threads) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing in the scratch
+ * needs clearing: every partial is written before it is read.
+ */
+#define STREAMKL_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+streamkl_status streamkl_fwd_loss_noalloc(const void* Q1, const void* K1, const void* Q2, const void* K2,
+                                          int causal, float scale1, float scale2, const float* weights,
+                                          float* out_kl, float* out_lse1, float* out_lse2, float* out_loss,
+                                          const streamkl_shape* shape, const streamkl_launch* launch,
+                                          void* stream);
+
 /* The backward mode streamkl_bwd will use (1 fused, 2 separate, or the
  * requested 3/4), 0 if invalid. */
 int streamkl_bwd_plan(const streamkl_shape* shape, int causal, int setting,

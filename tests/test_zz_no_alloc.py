@@ -1,0 +1,97 @@
+"""The allocation-free forward (streamkl_fwd_loss_noalloc) against the entry
+point it is a variant of (streamkl_fwd_loss with a caller workspace),
+through the C ABI: two calls in a row, the second with a smaller input,
+then the plain forward through it, then a request too large for its scratch."""
+import ctypes
+
+import pytest
+import torch
+
+import workloads
+from attention_kl_divergence_amd import streamkl as sk
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _lib():
+    lib = sk.library()
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.streamkl_fwd_loss_noalloc.argtypes = [vp, vp, vp, vp, i32, f32, f32, vp, vp, vp, vp, vp,
+                                              ctypes.POINTER(sk.Shape), ctypes.POINTER(sk.Launch), vp]
+    lib.streamkl_fwd_loss_noalloc.restype = i32
+    return lib
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def _outs(w, dev, fill=7.0):
+    f32 = dict(device=dev, dtype=torch.float32)
+    return tuple(torch.full((w.B, w.H, w.n_q), fill, **f32) for _ in range(3)) + (torch.full((), fill, **f32),)
+
+
+def _noalloc(lib, q1, k1, q2, k2, causal, weights, out, num_splits=0, with_loss=True):
+    shp = sk.shape_of(q1, k1, q2, k2)
+    ln = sk.Launch(num_splits, 0, None, 0)
+    return lib.streamkl_fwd_loss_noalloc(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), int(causal), 0.0, 0.0,
+                                         _ptr(weights), *(_ptr(t) for t in out[:3]),
+                                         _ptr(out[3]) if with_loss else None, ctypes.byref(shp), ctypes.byref(ln),
+                                         sk._stream(q1.device))
+
+
+def test_noalloc_matches_workspace_entry_point(cuda_device):
+    lib = _lib()
+    # a split-K decode shape (split partials and loss partials in the scratch),
+    # then a smaller unsplit shape, then a split shape with weights
+    cases = [
+        workloads.Workload("na-dec", 1, 32, 16, 20000, 128, 128, "bf16", False, 0.5, False, 21),
+        workloads.Workload("na-small", 1, 2, 100, 300, 64, 64, "f32", True, 0.5, False, 22),
+        workloads.Workload("na-split", 1, 3, 200, 5000, 128, 64, "bf16", False, 0.5, True, 23),
+    ]
+    for i, w in enumerate(cases):
+        q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+        wt = workloads.upstream_grad(w, cuda_device, "random") if i == 2 else None
+        shp = sk.shape_of(q1, k1, q2, k2)
+        _say(f"call {i}: {w.name} splits {sk.fwd_plan(shp, w.causal)}")
+        ref = sk.streamkl_fwd_loss(q1, k1, q2, k2, w.causal, wt)
+        out = _outs(w, cuda_device)
+        torch.cuda.synchronize()
+        # free device memory around the call alone (every tensor exists already)
+        free0 = torch.cuda.mem_get_info(cuda_device)[0]
+        assert _noalloc(lib, q1, k1, q2, k2, w.causal, wt, out) == sk.OK
+        torch.cuda.synchronize()
+        assert torch.cuda.mem_get_info(cuda_device)[0] == free0, f"{w.name}: the call changed free device memory"
+        for a, b, n in zip(out, ref, ("kl", "lse1", "lse2", "loss")):
+            assert torch.equal(a, b), f"{w.name}: {n} differs from streamkl_fwd_loss"
+    # the plain forward through it (no loss): the same rows as streamkl_fwd
+    w = cases[0]
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    out = _outs(w, cuda_device)
+    assert _noalloc(lib, q1, k1, q2, k2, False, None, out, with_loss=False) == sk.OK
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, False)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], kl) and torch.equal(out[1], l1) and torch.equal(out[2], l2)
+    assert (out[3] == 7.0).all()  # no loss requested: not written
+
+
+def test_noalloc_rejects_requests_beyond_its_scratch(cuda_device):
+    """An explicit split count whose partials exceed the 4 MiB scratch returns
+    STREAMKL_ERR_WORKSPACE and writes nothing; an automatic one falls back."""
+    lib = _lib()
+    w = workloads.Workload("na-big", 1, 32, 32, 100000, 128, 128, "bf16", False, 0.5, False, 24)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    out = _outs(w, cuda_device)
+    splits = 2048  # 20 B * 32 heads * 32 rows * 2048 splits = 40 MiB of partials
+    assert _noalloc(lib, q1, k1, q2, k2, False, None, out, num_splits=splits) == sk.ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert all((t == 7.0).all() for t in out)
+    assert _noalloc(lib, q1, k1, q2, k2, False, None, out) == sk.OK
+    ref = sk.streamkl_fwd_loss(q1, k1, q2, k2, False)
+    torch.cuda.synchronize()
+    for a, b in zip(out, ref):
+        assert torch.equal(a, b)
