@@ -20,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libstreamkl.so")
+# device probes of the measurement side (matrix-core, exponential and atomic
+# rates), a library of their own so the product's ABI stays the header's
+PROBES = os.path.join(HERE, "libstreamkl_probes.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -75,6 +78,10 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     shutil.move(tmp, LIB)
+    tmp = PROBES + ".tmp"
+    _run([HIPCC, *[f for f in FLAGS if f != "-fno-honor-nans"], "-shared", os.path.join(CSRC, "probes.hip"),
+          "-o", tmp])
+    shutil.move(tmp, PROBES)
     return LIB
 
 

@@ -44,7 +44,7 @@ template <> struct Mfma<float> {
   }
 };
 
-__device__ inline f32x16 zero16() {
+__device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
   for (int e = 0; e < 16; ++e) z[e] = 0.f;
@@ -52,20 +52,20 @@ __device__ inline f32x16 zero16() {
 }
 
 // Row (within a 32-row block) held by accumulator element e of lane group grp.
-__device__ inline int acc_row(int e, int grp) { return 8 * (e >> 2) + 4 * grp + (e & 3); }
+__device__ __forceinline__ int acc_row(int e, int grp) { return 8 * (e >> 2) + 4 * grp + (e & 3); }
 
 // A-operand fragment built from a 32x32 accumulator whose lane column is the
 // operand's row; contraction runs over the accumulator's rows in the order
 // acc_row(h*KPL + e', grp).
-__device__ inline bf16x8 frag_from_acc(const f32x16& c, int h, bf16) {
+__device__ __forceinline__ bf16x8 frag_from_acc(const f32x16& c, int h, bf16) {
   bf16x8 f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] = (bf16)c[8 * h + e];
   return f;
 }
-__device__ inline float frag_from_acc(const f32x16& c, int h, float) { return c[h]; }
+__device__ __forceinline__ float frag_from_acc(const f32x16& c, int h, float) { return c[h]; }
 
-__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 
 // The five running scalars of one (partial) row, in base-2 units:
@@ -75,12 +75,12 @@ struct RowState {
   float M1, l1, A, M2, l2;
 };
 
-__device__ inline RowState empty_state() { return {kNegInf, 0.f, 0.f, kNegInf, 0.f}; }
+__device__ __forceinline__ RowState empty_state() { return {kNegInf, 0.f, 0.f, kNegInf, 0.f}; }
 
-__device__ inline float finite_or_zero(float m) { return m == kNegInf ? 0.f : m; }
+__device__ __forceinline__ float finite_or_zero(float m) { return m == kNegInf ? 0.f : m; }
 
 // Associative merge of two partial states over disjoint key sets.
-__device__ inline RowState merge_state(const RowState& a, const RowState& b) {
+__device__ __forceinline__ RowState merge_state(const RowState& a, const RowState& b) {
   RowState r;
   r.M1 = fmaxf(a.M1, b.M1);
   r.M2 = fmaxf(a.M2, b.M2);
@@ -96,7 +96,7 @@ __device__ inline RowState merge_state(const RowState& a, const RowState& b) {
 // KL, LSE1, LSE2 (natural units) from a complete row state:
 // KL = ln2 * (A / l1 + LSE2_2 - LSE1_2), LSE_t = ln2 * (M_t + log2 l_t).
 // Returns the KL it stored.
-__device__ inline float finish_state(const RowState& s, float* kl, float* lse1, float* lse2) {
+__device__ __forceinline__ float finish_state(const RowState& s, float* kl, float* lse1, float* lse2) {
   const float L1 = s.M1 + log2f(s.l1);
   const float L2 = s.M2 + log2f(s.l2);
   const float k = kLn2 * (s.A / s.l1 + (L2 - L1));
@@ -106,7 +106,7 @@ __device__ inline float finish_state(const RowState& s, float* kl, float* lse1, 
   return k;
 }
 
-__device__ inline RowState shfl_xor_state(const RowState& s, int mask) {
+__device__ __forceinline__ RowState shfl_xor_state(const RowState& s, int mask) {
   RowState o;
   o.M1 = __shfl_xor(s.M1, mask);
   o.l1 = __shfl_xor(s.l1, mask);

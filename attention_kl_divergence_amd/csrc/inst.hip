@@ -27,14 +27,23 @@ hipError_t launch_joint_dk(const BwdArgs& a, dim3 g, dim3 b, hipStream_t st, boo
 }
 }  // namespace
 
+// a.lpart set: the fused-loss instantiation (only unsplit launches finalize rows here)
 hipError_t SKL_CAT(launch_fwd, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+  if (a.lpart && a.nsplit == 1)
+    hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile, true>), dim3((unsigned)nblocks), dim3(256), 0, st,
+                       a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t SKL_CAT(launch_fwd_pp, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, kFwdPPTile<SKL_T>>), dim3((unsigned)nblocks), dim3(512), 0,
-                     st, a);
+  if (a.lpart)
+    hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, kFwdPPTile<SKL_T>, true>), dim3((unsigned)nblocks),
+                       dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, kFwdPPTile<SKL_T>>), dim3((unsigned)nblocks), dim3(512),
+                       0, st, a);
   return hipGetLastError();
 }
 

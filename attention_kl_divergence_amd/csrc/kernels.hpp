@@ -117,7 +117,7 @@ struct TileLoader {
   static_assert(NI * 64 == ROWS * F::CPR, "a tile must be whole 1 KB blocks");
   int voff[PER];
   int wave;
-  __device__ inline TileLoader(int wave_, int lane) : wave(wave_) {
+  __device__ __forceinline__ TileLoader(int wave_, int lane) : wave(wave_) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int P = (wave * PER + i) * 64 + lane;
@@ -126,7 +126,7 @@ struct TileLoader {
     }
   }
   // rows [r0, r0 + ROWS) of g (a tensor with nrows rows) into `tile`
-  __device__ inline void issue(T* tile, const T* g, int r0, int nrows) const {
+  __device__ __forceinline__ void issue(T* tile, const T* g, int r0, int nrows) const {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer-resource type exists only in the device pass
     const int left = min(nrows - r0, ROWS);
     const uint32_t bytes = left > 0 ? (uint32_t)left * (uint32_t)(D * sizeof(T)) : 0u;
@@ -143,9 +143,9 @@ struct TileLoader {
 
 // Key head of query head bh (of B*H < 2^20) when g query heads share one:
 // a 32-bit division, far shorter than a 64-bit one.
-__device__ inline int64_t key_head(int64_t bh, int g) { return (int64_t)((uint32_t)bh / (uint32_t)g); }
+__device__ __forceinline__ int64_t key_head(int64_t bh, int g) { return (int64_t)((uint32_t)bh / (uint32_t)g); }
 
-__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Work item (head, block) of workgroup `lin` of a grid of BH * nblk.
 // Workgroups go to the 8 XCDs round-robin (workgroup i runs on XCD i % 8) and
@@ -158,7 +158,7 @@ struct WorkItem {
   int64_t bh;
   int blk;
 };
-__device__ inline WorkItem work_item(int64_t lin, int64_t BH, int nblk) {
+__device__ __forceinline__ WorkItem work_item(int64_t lin, int64_t BH, int nblk) {
   constexpr int X = 8;
   if (BH % X == 0) {
     const int64_t per = BH / X * nblk;
@@ -175,7 +175,7 @@ __device__ inline WorkItem work_item(int64_t lin, int64_t BH, int nblk) {
 // on scheduling.  v is this thread's w_i KL_i (0 if it finalized no row).
 // `red` is NW doubles of LDS the caller has made free for this.
 template <int NW>
-__device__ inline void loss_partial(double v, double* red, double* slot, int tid) {
+__device__ __forceinline__ void loss_partial(double v, double* red, double* slot, int tid) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
   if ((tid & 63) == 0) red[tid >> 6] = v;
@@ -188,14 +188,14 @@ __device__ inline void loss_partial(double v, double* red, double* slot, int tid
   }
 }
 
-__device__ inline double loss_term(const FwdArgs& a, int64_t r, float kl) {
+__device__ __forceinline__ double loss_term(const FwdArgs& a, int64_t r, float kl) {
   return a.lw ? (double)a.lw[r] * (double)kl : (double)kl;
 }
 
 // Barrier between the compute phases of a ping-pong loop.  It orders no
 // memory (each phase reads data a tile barrier already published), so unlike
 // __syncthreads it does not wait for the direct-to-LDS tile loads in flight.
-__device__ inline void phase_barrier() {
+__device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -203,7 +203,7 @@ __device__ inline void phase_barrier() {
 
 // Barrier that publishes this wave's LDS stores to the workgroup, again
 // without waiting for the tile loads in flight.
-__device__ inline void lds_barrier() {
+__device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -211,7 +211,7 @@ __device__ inline void lds_barrier() {
 
 // MFMA operand with lane row = `row`, k from `k0`: natural layout read.
 template <typename T, int D>
-__device__ inline typename Mfma<T>::frag frag_tile(const T* tile, int row, int s, int grp) {
+__device__ __forceinline__ typename Mfma<T>::frag frag_tile(const T* tile, int row, int s, int grp) {
   const int k = s * Mfma<T>::KSTEP + grp * Mfma<T>::KPL;
   return *reinterpret_cast<const typename Mfma<T>::frag*>(tile + Tile<T, D>::off(row, k));
 }
@@ -220,7 +220,7 @@ __device__ inline typename Mfma<T>::frag frag_tile(const T* tile, int row, int s
 // values run down the rows of a row-major tile, in accumulator order
 // (k = acc_row(h*KPL + e', grp) + kb0).  bf16 uses two transpose reads.
 template <int D>
-__device__ inline bf16x8 fragcol_acc_bf16(const bf16* __restrict__ tile, int kb0, int n0, int h, int lane) {
+__device__ __forceinline__ bf16x8 fragcol_acc_bf16(const bf16* __restrict__ tile, int kb0, int n0, int h, int lane) {
   using F = Tile<bf16, D>;
   const int grp = lane >> 5, sub = (lane >> 4) & 1, r = lane & 15;
   const int n = n0 + 16 * sub + 4 * (r & 3);
@@ -237,7 +237,7 @@ __device__ inline bf16x8 fragcol_acc_bf16(const bf16* __restrict__ tile, int kb0
 
 // Same, natural k order (k = kb0 + 16h + 8grp + e').
 template <int D>
-__device__ inline bf16x8 fragcol_nat_bf16(const bf16* __restrict__ tile, int kb0, int n0, int h, int lane) {
+__device__ __forceinline__ bf16x8 fragcol_nat_bf16(const bf16* __restrict__ tile, int kb0, int n0, int h, int lane) {
   using F = Tile<bf16, D>;
   const int grp = lane >> 5, sub = (lane >> 4) & 1, r = lane & 15;
   const int n = n0 + 16 * sub + 4 * (r & 3);
@@ -254,21 +254,21 @@ __device__ inline bf16x8 fragcol_nat_bf16(const bf16* __restrict__ tile, int kb0
 
 // fp32 versions: one element per lane, k = acc_row(h, grp) (+kb0) or 2h + grp.
 template <int D>
-__device__ inline float fragcol_acc_f32(const float* tile, int kb0, int n0, int h, int lane) {
+__device__ __forceinline__ float fragcol_acc_f32(const float* tile, int kb0, int n0, int h, int lane) {
   return tile[Tile<float, D>::off(kb0 + acc_row(h, lane >> 5), n0 + (lane & 31))];
 }
 template <int D>
-__device__ inline float fragcol_nat_f32(const float* tile, int kb0, int n0, int h, int lane) {
+__device__ __forceinline__ float fragcol_nat_f32(const float* tile, int kb0, int n0, int h, int lane) {
   return tile[Tile<float, D>::off(kb0 + 2 * h + (lane >> 5), n0 + (lane & 31))];
 }
 
 template <typename T, int D>
-__device__ inline typename Mfma<T>::frag fragcol_acc(const T* tile, int kb0, int n0, int h, int lane) {
+__device__ __forceinline__ typename Mfma<T>::frag fragcol_acc(const T* tile, int kb0, int n0, int h, int lane) {
   if constexpr (Mfma<T>::KPL == 1) return fragcol_acc_f32<D>(tile, kb0, n0, h, lane);
   else return fragcol_acc_bf16<D>(tile, kb0, n0, h, lane);
 }
 template <typename T, int D>
-__device__ inline typename Mfma<T>::frag fragcol_nat(const T* tile, int kb0, int n0, int h, int lane) {
+__device__ __forceinline__ typename Mfma<T>::frag fragcol_nat(const T* tile, int kb0, int n0, int h, int lane) {
   if constexpr (Mfma<T>::KPL == 1) return fragcol_nat_f32<D>(tile, kb0, n0, h, lane);
   else return fragcol_nat_bf16<D>(tile, kb0, n0, h, lane);
 }
@@ -282,19 +282,19 @@ __device__ inline typename Mfma<T>::frag fragcol_nat(const T* tile, int kb0, int
 template <int D, int S>
 struct RowFragOffsets {  // operand rows: frag_tile(tile, 32 * blk + col, s, grp)
   int o[S];
-  __device__ inline RowFragOffsets(int col, int grp) {
+  __device__ __forceinline__ RowFragOffsets(int col, int grp) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       o[s] = Tile<bf16, D>::off(col, s * Mfma<bf16>::KSTEP + grp * Mfma<bf16>::KPL) * (int)sizeof(bf16);
       asm volatile("" : "+v"(o[s]));
     }
   }
-  __device__ inline bf16x8 read(const bf16* tile, int blk, int s) const {
+  __device__ __forceinline__ bf16x8 read(const bf16* tile, int blk, int s) const {
     return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile + 32 * blk * D) + o[s]);
   }
   // called once per loop iteration: the offsets then look loop-variant, so
   // the optimiser does not hoist tile base + offset sums into extra registers
-  __device__ inline void touch() {
+  __device__ __forceinline__ void touch() {
 #pragma unroll
     for (int s = 0; s < S; ++s) asm volatile("" : "+v"(o[s]));
   }
@@ -303,7 +303,7 @@ struct RowFragOffsets {  // operand rows: frag_tile(tile, 32 * blk + col, s, grp
 template <int D, int NB>
 struct ColFragOffsets {  // column operands: fragcol_acc_bf16(tile, 32 * blk, 32 * nb, h, lane)
   int lo[NB], hi[NB];
-  __device__ inline ColFragOffsets(int lane) {
+  __device__ __forceinline__ ColFragOffsets(int lane) {
     const int grp = lane >> 5, sub = (lane >> 4) & 1, r = lane & 15;
     const int ka = 4 * grp + (r >> 2);
 #pragma unroll
@@ -314,7 +314,7 @@ struct ColFragOffsets {  // column operands: fragcol_acc_bf16(tile, 32 * blk, 32
       asm volatile("" : "+v"(lo[nb]), "+v"(hi[nb]));
     }
   }
-  __device__ inline bf16x8 read(const bf16* __restrict__ tile, int blk, int nb, int h) const {
+  __device__ __forceinline__ bf16x8 read(const bf16* __restrict__ tile, int blk, int nb, int h) const {
     const char* b = reinterpret_cast<const char*>(tile + (32 * blk + 16 * h) * D);
     const bf16x4_lds l = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
         (bf16x4_lds __attribute__((address_space(3)))*)(b + lo[nb]));
@@ -325,20 +325,20 @@ struct ColFragOffsets {  // column operands: fragcol_acc_bf16(tile, 32 * blk, 32
     f[4] = u[0]; f[5] = u[1]; f[6] = u[2]; f[7] = u[3];
     return f;
   }
-  __device__ inline void touch() {
+  __device__ __forceinline__ void touch() {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(lo[nb]), "+v"(hi[nb]));
   }
 };
 
 struct NoOffsets {  // stand-in for the offset tables where they are not used (fp32 tiles)
-  __device__ inline NoOffsets(int) {}
-  __device__ inline NoOffsets(int, int) {}
-  __device__ inline void touch() {}
+  __device__ __forceinline__ NoOffsets(int) {}
+  __device__ __forceinline__ NoOffsets(int, int) {}
+  __device__ __forceinline__ void touch() {}
 };
 
 template <typename T>
-__device__ inline typename Mfma<T>::frag zero_frag() {
+__device__ __forceinline__ typename Mfma<T>::frag zero_frag() {
   typename Mfma<T>::frag f;
   if constexpr (Mfma<T>::KPL == 1) {
     f = 0.f;
@@ -352,7 +352,7 @@ __device__ inline typename Mfma<T>::frag zero_frag() {
 // Fragment of a row of a global row-major [*, D] tensor (row clamped to a
 // valid one; `valid` false gives zeros).
 template <typename T, int D>
-__device__ inline typename Mfma<T>::frag frag_global(const T* g, int row, int rmax, bool valid, int s, int grp) {
+__device__ __forceinline__ typename Mfma<T>::frag frag_global(const T* g, int row, int rmax, bool valid, int s, int grp) {
   const T* p = g + (int64_t)min(row, rmax) * D + s * Mfma<T>::KSTEP + grp * Mfma<T>::KPL;
   typename Mfma<T>::frag f = *reinterpret_cast<const typename Mfma<T>::frag*>(p);
   return valid ? f : zero_frag<T>();
@@ -374,7 +374,7 @@ __device__ inline typename Mfma<T>::frag frag_global(const T* g, int row, int rm
 // workgroup that adds into one dQ row gets bitwise the same kbar.
 constexpr int kRefKeys = 64;
 
-__device__ inline float ref_key_col(const bf16* K, int D, int n_k, int c) {
+__device__ __forceinline__ float ref_key_col(const bf16* K, int D, int n_k, int c) {
   float s = 0.f;
   if (n_k >= kRefKeys) {  // unrolled so the loads go out together; the same row order
 #pragma unroll 16
@@ -388,13 +388,13 @@ __device__ inline float ref_key_col(const bf16* K, int D, int n_k, int c) {
 // kbar[c] for every column c < D, spread over nthreads threads (the caller
 // publishes it with a barrier)
 template <int D>
-__device__ inline void ref_key(float* kbar, const bf16* K, int n_k, int tid, int nthreads) {
+__device__ __forceinline__ void ref_key(float* kbar, const bf16* K, int n_k, int tid, int nthreads) {
   for (int c = tid; c < D; c += nthreads) kbar[c] = ref_key_col(K, D, n_k, c);
 }
 
 // acc + the sum of the eight bf16 values of an operand fragment (exact
 // products with 1.0, fp32 accumulation)
-__device__ inline float sum_frag(const bf16x8& f, float acc) {
+__device__ __forceinline__ float sum_frag(const bf16x8& f, float acc) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = {(bf16)1.f, (bf16)1.f};
   acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[0], f[1]}, one, acc, false);
@@ -403,7 +403,7 @@ __device__ inline float sum_frag(const bf16x8& f, float acc) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[6], f[7]}, one, acc, false);
   return acc;
 }
-__device__ inline float sum_frag(float, float acc) { return acc; }
+__device__ __forceinline__ float sum_frag(float, float acc) { return acc; }
 
 // Scheduling pattern for a run of N matrix instructions that each consume R
 // LDS reads: issue the reads for the first AHEAD instructions, then alternate
@@ -411,7 +411,7 @@ __device__ inline float sum_frag(float, float acc) { return acc; }
 // LDS latency hides behind the matrix pipeline.  Placed after the code it
 // orders, inside the same basic block.
 template <int N, int R, int AHEAD>
-__device__ inline void sched_mfma_lds() {
+__device__ __forceinline__ void sched_mfma_lds() {
   constexpr int PRE = AHEAD < N ? AHEAD : N;
   __builtin_amdgcn_sched_group_barrier(0x100, PRE * R, 0);
 #pragma unroll
@@ -424,7 +424,7 @@ __device__ inline void sched_mfma_lds() {
 // Per-lane maxima of raw logits: chains of max(max(acc, a), b), one v_max3
 // per two values.
 template <int NKB>
-__device__ inline void fwd_tile_max(const f32x16 (&s1)[NKB], const f32x16 (&s2)[NKB], float& mx1, float& mx2) {
+__device__ __forceinline__ void fwd_tile_max(const f32x16 (&s1)[NKB], const f32x16 (&s2)[NKB], float& mx1, float& mx2) {
   float mx1a = kNegInf, mx1b = kNegInf, mx2a = kNegInf, mx2b = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -447,7 +447,7 @@ struct FwdPre {
   float M1n, M2n, al1, al2;
 };
 template <int NKB>
-__device__ inline FwdPre fwd_pre(const RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], float c1, float c2) {
+__device__ __forceinline__ FwdPre fwd_pre(const RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], float c1, float c2) {
   float mx1, mx2;
   fwd_tile_max<NKB>(s1, s2, mx1, mx2);
   FwdPre p;
@@ -465,7 +465,7 @@ __device__ inline FwdPre fwd_pre(const RowState& st, f32x16 (&s1)[NKB], f32x16 (
   return p;
 }
 template <int NKB>
-__device__ inline void fwd_post(RowState& st, const f32x16 (&t1)[NKB], const f32x16 (&t2)[NKB], const FwdPre& p) {
+__device__ __forceinline__ void fwd_post(RowState& st, const f32x16 (&t1)[NKB], const f32x16 (&t2)[NKB], const FwdPre& p) {
   float tl1[4] = {0.f, 0.f, 0.f, 0.f}, tl2[4] = {0.f, 0.f, 0.f, 0.f}, tA[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -490,7 +490,7 @@ __device__ inline void fwd_post(RowState& st, const f32x16 (&t1)[NKB], const f32
 // Forward online update of one lane's running state with NKB 32-key blocks of
 // raw dot products (s1, s2).  MASK: keys past `lim` are excluded.
 template <bool MASK, int NKB>
-__device__ inline void fwd_update(RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], float c1, float c2, int k0,
+__device__ __forceinline__ void fwd_update(RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], float c1, float c2, int k0,
                                   int lim, int grp) {
   if constexpr (MASK) {
 #pragma unroll
@@ -539,7 +539,7 @@ __device__ inline void fwd_update(RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[
 // are computed on the matrix cores while the VALU runs the online update of
 // block kb (the scheduling groups interleave the two streams).
 template <typename T, int D1, int D2, int NKB, bool MASK>
-__device__ inline void fwd_tile(RowState& st, const T* sK1, const T* sK2, const typename Mfma<T>::frag* qf1,
+__device__ __forceinline__ void fwd_tile(RowState& st, const T* sK1, const T* sK2, const typename Mfma<T>::frag* qf1,
                                 const typename Mfma<T>::frag* qf2, float c1, float c2, int k0, int lim, int col,
                                 int grp) {
   using MF = Mfma<T>;
@@ -569,7 +569,9 @@ __device__ inline void fwd_tile(RowState& st, const T* sK1, const T* sK2, const 
 // lane's accumulator column is one query row: lane (col, grp) keeps its own
 // running state over the keys acc_row(., grp) of every 32-key block, and the
 // two lane groups merge once at the end.
-template <typename T, int D1, int D2, int BK>
+// LOSS: the fused-loss form (a.lpart set); a separate instantiation so the
+// plain forward's code is untouched by it.
+template <typename T, int D1, int D2, int BK, bool LOSS = false>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
@@ -648,7 +650,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const int64_t r = bh * a.qs + qrow;
     if (a.nsplit == 1) {
       const float klv = finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
-      if (a.lpart) lv = loss_term(a, r, klv);
+      if constexpr (LOSS) lv = loss_term(a, r, klv);
     } else {
       const int64_t fs = a.BH * (int64_t)a.nsplit * a.n_q;
       const int64_t o = (bh * a.nsplit + z) * (int64_t)a.n_q + qrow;
@@ -659,7 +661,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       a.ws[o + 4 * fs] = st.l2;
     }
   }
-  if (a.lpart && a.nsplit == 1) {
+  if (LOSS && a.nsplit == 1) {
     __syncthreads();  // every wave is past its last tile read: the tile buffer is free
     loss_partial<NW>(lv, reinterpret_cast<double*>(lds), a.lpart + blockIdx.x, tid);
   }
@@ -682,7 +684,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 // s, the natural order, so each load instruction reads 32 bytes of each of
 // 32 key rows.
 template <int D>
-__device__ inline void dec_load_row(bf16x8 (&f)[D / 16], const bf16* base, int64_t row, int grp) {
+__device__ __forceinline__ void dec_load_row(bf16x8 (&f)[D / 16], const bf16* base, int64_t row, int grp) {
   constexpr int S = D / 16;
   const bf16x8* p = reinterpret_cast<const bf16x8*>(base + row * D) + grp;
 #pragma unroll
@@ -692,7 +694,7 @@ __device__ inline void dec_load_row(bf16x8 (&f)[D / 16], const bf16* base, int64
 // rows [0, 32) of a [n_q, D] query tensor into a swizzled LDS tile (zeros
 // past n_q), 16-byte chunks spread over the workgroup's 256 threads
 template <int D>
-__device__ inline void dec_stage_q(bf16* tile, const bf16* q, int n_q, int tid) {
+__device__ __forceinline__ void dec_stage_q(bf16* tile, const bf16* q, int n_q, int tid) {
   constexpr int CPR = D / 8;
 #pragma unroll
   for (int i = tid; i < 32 * CPR; i += 256) {
@@ -801,7 +803,7 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
 // Logits of one key tile for one wave: s_t[kb] = K_t[kb*32 .. +32) Q_t^T for
 // the wave's 32 query rows (raw dot products), 2*NKB independent chains.
 template <typename T, int D1, int D2, int NKB>
-__device__ inline void fwd_logits(f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], const T* sK1, const T* sK2,
+__device__ __forceinline__ void fwd_logits(f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], const T* sK1, const T* sK2,
                                   const typename Mfma<T>::frag* qf1, const typename Mfma<T>::frag* qf2, int col,
                                   int grp) {
   using MF = Mfma<T>;
@@ -829,7 +831,7 @@ __device__ inline void fwd_logits(f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], const T*
 // (waves 4-7, the other wave on each SIMD) runs the online update of tile
 // t-1; after a barrier the roles swap.  Each SIMD thus keeps one wave on the
 // matrix cores and one on the VALU.
-template <typename T, int D1, int D2, int BK>
+template <typename T, int D1, int D2, int BK, bool LOSS = false>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
@@ -926,9 +928,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   if (grp == 0 && qrow < a.n_q) {
     const int64_t r = bh * a.qs + qrow;
     const float klv = finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
-    if (a.lpart) lv = loss_term(a, r, klv);
+    if constexpr (LOSS) lv = loss_term(a, r, klv);
   }
-  if (a.lpart) {
+  if constexpr (LOSS) {
     __syncthreads();  // group 1 may still read the last tile until here
     loss_partial<NW>(lv, reinterpret_cast<double*>(lds), a.lpart + blockIdx.x, tid);
   }
@@ -949,7 +951,7 @@ struct RawRowGrad {
 };
 
 template <int SETTING>
-__device__ inline RawRowGrad load_rowgrad_raw(const BwdArgs& a, int64_t r, bool valid) {
+__device__ __forceinline__ RawRowGrad load_rowgrad_raw(const BwdArgs& a, int64_t r, bool valid) {
   RawRowGrad o = {0.f, 0.f, 0.f, 0.f};
   if (!valid) return o;
   o.lse1 = a.lse1[r];
@@ -967,7 +969,7 @@ __device__ inline RawRowGrad load_rowgrad_raw(const BwdArgs& a, int64_t r, bool 
 // gs = g * scale_2 for dS2 = gs (P2 - P1), and a, b come from g * scale_1
 // for dS1.
 template <int SETTING>
-__device__ inline RowGrad scale_rowgrad(const BwdArgs& a, const RawRowGrad& w) {
+__device__ __forceinline__ RowGrad scale_rowgrad(const BwdArgs& a, const RawRowGrad& w) {
   RowGrad o;
   const float gs = w.g * a.scale_s;
   o.L1 = w.lse1 * kLog2e;
@@ -989,13 +991,13 @@ __device__ inline RowGrad scale_rowgrad(const BwdArgs& a, const RawRowGrad& w) {
 }
 
 template <int SETTING>
-__device__ inline RowGrad load_rowgrad(const BwdArgs& a, int64_t r, bool valid) {
+__device__ __forceinline__ RowGrad load_rowgrad(const BwdArgs& a, int64_t r, bool valid) {
   return scale_rowgrad<SETTING>(a, load_rowgrad_raw<SETTING>(a, r, valid));
 }
 
 // dS for one element from the raw dot products s1, s2 (see RowGrad).
 template <int SETTING>
-__device__ inline float dS_elem(float s1, float s2, float c1, float c2, float L1, float L2, float gs, float ra,
+__device__ __forceinline__ float dS_elem(float s1, float s2, float c1, float c2, float L1, float L2, float gs, float ra,
                                 float rb) {
   const float t1 = fmaf(s1, c1, -L1);
   const float t2 = fmaf(s2, c2, -L2);
@@ -1012,14 +1014,14 @@ __device__ inline float dS_elem(float s1, float s2, float c1, float c2, float L1
 // row: for setting 1 the row's sign (gs = +-1) is left out here and applied
 // to the row's dQ once at the end.
 template <int SETTING>
-__device__ inline float dS_elem_row(float s1, float s2, float c1, float c2, const RowGrad& rg) {
+__device__ __forceinline__ float dS_elem_row(float s1, float s2, float c1, float c2, const RowGrad& rg) {
   if constexpr (SETTING == 1) return exp2_fast(fmaf(s2, c2, -rg.L2)) - exp2_fast(fmaf(s1, c1, -rg.L1));
   else return dS_elem<SETTING>(s1, s2, c1, c2, rg.L1, rg.L2, rg.gs, rg.a, rg.b);
 }
 
 // Joint: dS1 (setting 2) and dS2 (setting 1) of one element from the raw
 // dot products, sharing P1 (see RowGrad).
-__device__ inline void dS_joint(float s1, float s2, float c1, float c2, float L1, float L2, float gs, float ra,
+__device__ __forceinline__ void dS_joint(float s1, float s2, float c1, float c2, float L1, float L2, float gs, float ra,
                                 float rb, float& ds1, float& ds2) {
   const float t1 = fmaf(s1, c1, -L1);
   const float t2 = fmaf(s2, c2, -L2);
@@ -1036,7 +1038,7 @@ __device__ inline void dS_joint(float s1, float s2, float c1, float c2, float L1
 // (setting 1, no negative gradient in the tile) skips gs, which is then +1.
 // MASK: queries outside [qlo, n_q) get dS = 0.  Result overwrites s1.
 template <int SETTING, bool MASK, int BQ, bool SIGNED = true>
-__device__ inline void dS_rows_keyouter(f32x16& s1, const f32x16& s2, const float* st, int ql0, int qb0, int grp,
+__device__ __forceinline__ void dS_rows_keyouter(f32x16& s1, const f32x16& s2, const float* st, int ql0, int qb0, int grp,
                                         float c1, float c2, int qlo, int n_q, int lane_off) {
   // st[k*BQ + q] for q = ql0 + 8i + 4grp + j; lane_off = 16 * grp bytes
   auto at = [&](int k, int i) {
@@ -1073,7 +1075,7 @@ __device__ inline void dS_rows_keyouter(f32x16& s1, const f32x16& s2, const floa
 // Joint version: dS1 overwrites s1 and dS2 overwrites s2 (stats L1, L2, gs,
 // a, b per query).
 template <bool MASK, int BQ>
-__device__ inline void dS_rows_keyouter_joint(f32x16& s1, f32x16& s2, const float* st, int ql0, int qb0, int grp,
+__device__ __forceinline__ void dS_rows_keyouter_joint(f32x16& s1, f32x16& s2, const float* st, int ql0, int qb0, int grp,
                                               float c1, float c2, int qlo, int n_q, int lane_off) {
   auto at = [&](int k, int i) {
     return *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(st + k * BQ + ql0 + 8 * i) + lane_off);

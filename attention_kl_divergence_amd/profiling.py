@@ -225,6 +225,140 @@ def counters(csvs, agent_csv):
     return out, topo
 
 
+# ---- device probes (libstreamkl_probes.so): the part's own rates ----
+
+MFMA_FLOP = 2 * 32 * 32 * 16  # one v_mfma_f32_32x32x16_bf16
+
+
+def _probes():
+    import ctypes
+    path = os.path.join(HERE, "libstreamkl_probes.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m attention_kl_divergence_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32
+    lib.streamkl_probe_mfma.argtypes = [vp, vp, i32, i32, vp]
+    lib.streamkl_probe_exp.argtypes = [vp, i32, i32, vp]
+    lib.streamkl_probe_atomic.argtypes = [vp, u32, i32, i32, vp]
+    lib.streamkl_probe_wall_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int)]
+    for f in (lib.streamkl_probe_mfma, lib.streamkl_probe_exp, lib.streamkl_probe_atomic,
+              lib.streamkl_probe_wall_clock_khz):
+        f.restype = i32
+    return lib
+
+
+def _timed_launch(launch):
+    """ms of one launch (after one warm-up launch), HIP events on the stream."""
+    import torch
+    launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launch()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def probe_mfma(waves_per_simd: int = 1, iters: int = 200000) -> dict:
+    """bf16 matrix-core rate with no operand traffic (TFLOP/s over the whole
+    chip) and the shader clock it ran at (MHz, median over workgroups)."""
+    import ctypes
+
+    import torch
+    lib = _probes()
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = cus * waves_per_simd  # 4-wave workgroups: one wave per SIMD each
+    out = torch.empty(blocks * 256, device=dev)
+    clk = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def run():
+        e = lib.streamkl_probe_mfma(out.data_ptr(), clk.data_ptr(), blocks, iters, stream)
+        if e:
+            raise RuntimeError(f"streamkl_probe_mfma: hipError {e}")
+    ms = _timed_launch(run)
+    khz = ctypes.c_int(0)
+    if lib.streamkl_probe_wall_clock_khz(ctypes.byref(khz)) or khz.value <= 0:
+        raise RuntimeError("wall clock rate unavailable")
+    c = clk.view(-1, 2).double().cpu()
+    mhz = (c[:, 0] / (c[:, 1] / (khz.value * 1e3))).median().item() / 1e6
+    flops = blocks * 4 * iters * 4 * MFMA_FLOP
+    return {"tflops": flops / ms / 1e9, "sclk_mhz": mhz, "ms": ms, "waves_per_simd": waves_per_simd,
+            "cycles_per_mfma": mhz * 1e6 * ms * 1e-3 / (iters * 4 * waves_per_simd)}
+
+
+def probe_exp(waves_per_simd: int = 2, iters: int = 40000) -> dict:
+    """v_exp_f32 throughput over the whole chip (exponentials per ns)."""
+    import torch
+    lib = _probes()
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = cus * waves_per_simd
+    out = torch.empty(blocks * 256, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def run():
+        e = lib.streamkl_probe_exp(out.data_ptr(), blocks, iters, stream)
+        if e:
+            raise RuntimeError(f"streamkl_probe_exp: hipError {e}")
+    ms = _timed_launch(run)
+    n = blocks * 256 * iters * 8
+    return {"exp_per_ns": n / ms / 1e6, "ms": ms, "waves_per_simd": waves_per_simd}
+
+
+def probe_atomic(window_mib: int, iters: int = 2000) -> dict:
+    """fp32 device-scope atomic adds, 64 consecutive floats per wave at
+    scattered 256-byte slots of a window: payload GB/s."""
+    import torch
+    lib = _probes()
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    slots = window_mib * (1 << 20) // 256
+    win = torch.zeros(slots * 64, device=dev)
+    blocks = cus * 8
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def run():
+        e = lib.streamkl_probe_atomic(win.data_ptr(), slots, blocks, iters, stream)
+        if e:
+            raise RuntimeError(f"streamkl_probe_atomic: hipError {e}")
+    ms = _timed_launch(run)
+    return {"gbs": blocks * 256 * iters * 4 / ms / 1e6, "ms": ms, "window_mib": window_mib}
+
+
+def device_probes() -> str:
+    """Markdown summary of the probes (matrix-core rate and clock, exponential
+    rate, atomic payload rate)."""
+    m1, m2 = probe_mfma(1), probe_mfma(2)
+    e1, e2 = probe_exp(1), probe_exp(2)
+    at = [probe_atomic(w) for w in (1, 64, 1024)]
+    cus = 256
+    rows = [
+        f"| bf16 MFMA 32x32x16, no operand traffic, 1 wave per SIMD | {m1['tflops']:.1f} TFLOP/s | "
+        f"sclk {m1['sclk_mhz']:.0f} MHz, {m1['cycles_per_mfma']:.1f} cycles per MFMA |",
+        f"| same, 2 waves per SIMD | {m2['tflops']:.1f} TFLOP/s | sclk {m2['sclk_mhz']:.0f} MHz, "
+        f"{m2['cycles_per_mfma']:.1f} cycles per MFMA issued on a SIMD |",
+        f"| spec bf16 dense peak scaled to that clock (2516.6 x sclk / 2400 MHz) | "
+        f"{2516.6 * m1['sclk_mhz'] / 2400:.1f} TFLOP/s | |",
+        f"| v_exp_f32, 8 chains per lane, 1 wave per SIMD | {e1['exp_per_ns']:.0f} exp/ns | "
+        f"{e1['exp_per_ns'] / (cus * 4) / (m1['sclk_mhz'] / 1e3):.2f} exp per SIMD-cycle at that sclk |",
+        f"| same, 2 waves per SIMD | {e2['exp_per_ns']:.0f} exp/ns | "
+        f"{e2['exp_per_ns'] / (cus * 4) / (m1['sclk_mhz'] / 1e3):.2f} exp per SIMD-cycle |",
+    ] + [f"| fp32 atomic add, 64 floats per wave at scattered 256 B slots, {a['window_mib']} MiB window | "
+         f"{a['gbs']:.0f} GB/s payload | |" for a in at]
+    return "\n".join([
+        "# Device probes on one MI355X", "",
+        "Command: `python -m attention_kl_divergence_amd.profiling probes --out profiles/device_probes.md`",
+        "(kernels in `attention_kl_divergence_amd/csrc/probes.hip`; HIP events around one launch",
+        "after one warm-up launch; the shader clock is the shader-cycle counter against the",
+        "constant-rate wall clock over wave 0's matrix loop of each workgroup, median).", "",
+        "| probe | rate | notes |", "|---|---|---|", *rows, "",
+        "```json", json.dumps({"mfma_1": m1, "mfma_2": m2, "exp_1": e1, "exp_2": e2, "atomic": at}, indent=1),
+        "```", ""])
+
+
 def copy_bandwidth() -> str:
     """Markdown table of plain device copies and one-directional streams on
     cuda:0: the practical ceiling of a kernel that reads and writes in equal
@@ -293,7 +427,16 @@ def main(argv=None):
     sub.add_parser("digest")
     cb = sub.add_parser("copybw", help="read+write bandwidth of plain device copies (needs a GPU)")
     cb.add_argument("--out", default=None)
+    pb = sub.add_parser("probes", help="matrix-core, exponential and atomic rates of the part (needs a GPU)")
+    pb.add_argument("--out", default=None)
     args = ap.parse_args(argv)
+    if args.cmd == "probes":
+        text = device_probes()
+        if args.out:
+            with open(args.out, "w") as fo:
+                fo.write(text)
+        print(text)
+        return 0
     if args.cmd == "copybw":
         text = copy_bandwidth()
         if args.out:

@@ -56,46 +56,65 @@ def pairs_of(w):
     return w.B * w.H * (n_q * (n_q + 1) // 2 + n_q * (n_k - n_q))
 
 
-def cpu_baseline(w, rows_wanted, head_bytes=None):
-    """The fp64 oracle on the host: forward + setting-1 backward for a bounded
-    sample (the last rows of head 0, which see the full key range), reported
-    as algorithmic TFLOP/s like the GPU value.  With head_bytes (the
-    algorithmic HBM bytes of one head's step, for the bandwidth-bound decode
-    shapes) the sample must be whole heads and the rate is in GB/s."""
+def cpu_baseline(w, rows_wanted, head_bytes=None, gpu=None):
+    """The fp64 oracle on the host: forward + backward of the step's settings
+    for a bounded sample (the last rows of head 0, which see the full key
+    range), reported as algorithmic TFLOP/s like the GPU value.  With
+    head_bytes (the algorithmic HBM bytes of one head's step, for the
+    bandwidth-bound decode shapes) the sample must be whole heads and the rate
+    is in GB/s.  gpu: head 0's inputs as the GPU received them and its outputs
+    ({"inputs": [q1, k1, q2, k2], "kl", "lse1", "lse2", "dq": {setting: array}},
+    host arrays); the oracle runs on those inputs and the errors of the GPU's
+    rows against it are returned too."""
     import numpy as np
-    import torch
     import oracle
-    import workloads
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    small = w.with_(H=1, B=1, lengths=(), kv_heads=0)
-    q1, k1, q2, k2 = workloads.generate(small, "cpu")
-    g = workloads.upstream_grad(small, "cpu", "mean")
-    hi = [t[0, 0].float().numpy().astype(np.float64) for t in (q1, k1, q2, k2)]
-    rows = np.arange(max(0, w.n_q - rows_wanted), w.n_q)
-    block = max(1, min(64, (1 << 22) // w.n_k))
+    hi = gpu["inputs"]
+    n_q, n_k = hi[0].shape[0], hi[1].shape[0]
+    g = np.full(n_q, 1.0 / n_q)  # the step's upstream gradient (mean KL)
+    rows = np.arange(max(0, n_q - rows_wanted), n_q)
+    block = max(1, min(64, (1 << 22) // n_k))
     t0 = time.perf_counter()
-    oracle.head_forward(*hi, w.causal, rows=rows, block=block)
+    ref = oracle.head_forward(*hi, w.causal, rows=rows, block=block)
+    rdq = {}
     for setting in w.settings:
-        oracle.head_backward(setting, *hi, w.causal, g[0, 0].numpy(), rows=rows, block=block)
+        rdq[setting], _ = oracle.head_backward(setting, *hi, w.causal, g, rows=rows, block=block)
     dt = time.perf_counter() - t0
-    vis = oracle.valid_mask(rows, w.n_q, w.n_k, w.causal).sum()
+    vis = oracle.valid_mask(rows, n_q, n_k, w.causal).sum()
     qk = 2 * (w.d1 + w.d2)
     flops = float(vis) * (qk + sum(qk + 4 * (w.d2 if st == 1 else w.d1) for st in w.settings))
-    if head_bytes is not None and len(rows) == w.n_q:
-        return {"value": head_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-                "seconds": dt,
-                "sample": "numpy fp64 oracle, forward" + "".join(f" + setting-{st} backward" for st in w.settings)
-                          + f" of one whole head ({w.n_q} query rows over {w.n_k} keys), rated by that head's"
-                          " algorithmic HBM bytes"}
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"numpy fp64 oracle, forward" + "".join(f" + setting-{st} backward" for st in w.settings)
-                      + f" of the last {len(rows)} query rows of one head over all {w.n_k} keys"
-                      f" ({int(vis)} visible pairs)"}
+    steps = "".join(f" + setting-{st} backward" for st in w.settings)
+    if head_bytes is not None and len(rows) == n_q:
+        res = {"value": head_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+               "seconds": dt,
+               "sample": f"numpy fp64 oracle, forward{steps} of one whole head ({n_q} query rows over {n_k} keys),"
+                         " rated by that head's algorithmic HBM bytes"}
+    else:
+        res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+               "seconds": dt,
+               "sample": f"numpy fp64 oracle, forward{steps} of the last {len(rows)} query rows of head 0 over all"
+                         f" {n_k} keys ({int(vis)} visible pairs)"}
+    # the GPU's rows against the oracle: max and 99th percentile of the
+    # per-row errors, and the largest ratio to the tolerance (<= 1 passes)
+    a, r = (1e-4, 1e-3) if w.dtype == "f32" else (1e-3, 1e-2)
+    dkl = np.abs(gpu["kl"][rows] - ref[0])
+    err = {"rows": int(len(rows)),
+           "kl_abs_max": float(dkl.max()), "kl_abs_p99": float(np.percentile(dkl, 99)),
+           "kl_tol_ratio_max": float((dkl / (a + r * np.abs(ref[0]))).max())}
+    for name, i in (("lse1", 1), ("lse2", 2)):
+        d = np.abs(gpu[name][rows] - ref[i])
+        err[f"{name}_abs_max"], err[f"{name}_abs_p99"] = float(d.max()), float(np.percentile(d, 99))
+    for setting, dq in gpu["dq"].items():
+        got, want = dq[rows], rdq[setting]
+        rowerr = np.linalg.norm(got - want, axis=1) / np.maximum(np.linalg.norm(want, axis=1), 1e-300)
+        err[f"dq{setting}_rel_l2"] = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+        err[f"dq{setting}_row_rel_max"] = float(rowerr.max())
+        err[f"dq{setting}_row_rel_p99"] = float(np.percentile(rowerr, 99))
+    return res, err
 
 
 def main():
@@ -140,10 +159,14 @@ def main():
         calls.append(("bwdj_dq", lambda: sk.streamkl_bwd_joint(q1, k1, q2, k2, w.causal, kl, l1, l2, g,
                                                                 bwd_mode=sk.BWD_DQ_ONLY, out=(jo[0], None, jo[2], None),
                                                                 **lens)))
+    grads = {}  # setting -> (dQ, dK) buffers of the timed calls
+    if joint:
+        grads = {2: (jo[0], jo[1]), 1: (jo[2], jo[3])}
     for setting in (() if joint else w.settings):
         ds = w.d2 if setting == 1 else w.d1
         dq = torch.empty((w.B, w.H, w.n_q, ds), **f32)
         dk = torch.empty((w.B, kv, w.n_k, ds), **f32)
+        grads[setting] = (dq, dk)
         plan = sk.bwd_plan(shp, w.causal, setting, mode)
         modes[setting] = plan
 
@@ -163,6 +186,19 @@ def main():
         torch.mul(src, 1.0, out=dst)  # reads and writes copy_ref_mib MiB
         torch.cuda.synchronize()
         del src, dst
+
+    # the part's own rates, measured before the timed region: the bf16
+    # matrix-core rate with no operand traffic and the shader clock it holds,
+    # and the v_exp_f32 rate (attention_kl_divergence_amd/csrc/probes.hip)
+    from attention_kl_divergence_amd import profiling
+    try:
+        pm = profiling.probe_mfma(1, iters=100000)
+        pe = profiling.probe_exp(2, iters=20000)
+        probe = {"mfma_bf16_tflops": round(pm["tflops"], 1), "sclk_mhz": round(pm["sclk_mhz"]),
+                 "spec_peak_at_sclk_tflops": round(MFMA_BF16_PEAK_TFLOPS * pm["sclk_mhz"] / 2400.0, 1),
+                 "exp_per_ns": round(pe["exp_per_ns"], 1)}
+    except Exception as e:  # the bench line still reports the spec peaks
+        probe = {"error": str(e)}
 
     for _ in range(args.warmup):
         for _, c in calls:
@@ -245,7 +281,6 @@ def main():
 
     # measured HBM bytes per launch of that kernel (calibrated TCC counters),
     # valid only for the kernel sources they were taken with
-    from attention_kl_divergence_amd import profiling
     summ = profiling.load_summary(w.name)
     kname = roof["kernel"].split(" + ")[0]
     if summ and summ.get("source_digest") == profiling.kernel_source_digest() and kname in summ["kernels"]:
@@ -283,7 +318,22 @@ def main():
         "extra_hbm_bytes": extra_hbm,
         "materialised_bytes_avoided": 2 * w.B * w.H * w.n_q * w.n_k * 2,
         "roofline": roof,
+        "device_probe": probe,
     }
+    if "mfma_bf16_tflops" in probe and not decode:
+        out["pct_of_measured_mfma_peak"] = round(100 * value / probe["mfma_bf16_tflops"], 2)
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / probe["mfma_bf16_tflops"], 4)
+    # exponentials each call evaluates per visible pair (P1 and P2, or P1
+    # alone in setting 2) against the measured v_exp_f32 rate
+    exps = {"fwd": 2, "bwdj_dk": 2, "bwdj_dq": 3}
+    for setting in w.settings:
+        for kind in ("fused", "dk", "dq"):
+            exps[f"bwd{setting}_{kind}"] = 2 if setting == 1 else 1
+    if "exp_per_ns" in probe:
+        out["transcendental"] = {
+            n: {"exp_per_ns": round(exps[n] * pairs / (per_call[n] * 1e6), 1),
+                "frac": round(exps[n] * pairs / (per_call[n] * 1e6) / probe["exp_per_ns"], 4)}
+            for n in per_call if n in exps}
     if decode:
         # the pages' two ablations on decode shapes: the split-K forward against
         # one workgroup sweep per query block (num_splits = 1), and the fused
@@ -335,7 +385,14 @@ def main():
     if not args.no_cpu_baseline:
         # about 4e8 visible pairs of oracle work (10-20 s on the host) at most
         hb = sum(nbytes[n] for n, _ in calls) / (w.B * w.H) if decode else None
-        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, max(1, int(4e8 // w.n_k))), hb)
+        n0 = w.lengths[0] if w.lengths else w.n_q  # rows (= keys of a ragged element) of batch element 0
+        nk0 = w.lengths[0] if w.lengths else w.n_k
+        host = lambda t, n: t.float().cpu().numpy().astype("float64")[:n]  # noqa: E731
+        gpu = {"inputs": [host(q1[0, 0], n0), host(k1[0, 0], nk0), host(q2[0, 0], n0), host(k2[0, 0], nk0)],
+               "kl": host(kl[0, 0], n0), "lse1": host(l1[0, 0], n0), "lse2": host(l2[0, 0], n0),
+               "dq": {st: host(grads[st][0][0, 0], n0) for st in w.settings if st in grads}}
+        out["cpu_baseline"], out["oracle_errors"] = cpu_baseline(w, min(args.cpu_rows, max(1, int(4e8 // nk0))),
+                                                                 hb, gpu)
     print(json.dumps(out))
     return 0
 
