@@ -1120,7 +1120,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) T lds[2 * TS + (BF ? 2 * DS : 0)];
   float* kbar = reinterpret_cast<float*>(lds + 2 * TS);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: the per-block conditions on this wave's rows
+  // become scalar branches instead of exec-mask branches
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
   const WorkItem wi = work_item(blockIdx.x, a.BH, a.nblk);
   const int64_t bh = wi.bh;
@@ -1305,7 +1307,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a) {
   float(*sstat)[NSTAT][BQ] = reinterpret_cast<float(*)[NSTAT][BQ]>(smem + STAT_OFF);
   int* sneg = reinterpret_cast<int*>(smem + FLAG_OFF);  // per stats buffer: a row has gs < 0
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: the per-block conditions on this wave's rows
+  // become scalar branches instead of exec-mask branches
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
   const WorkItem wi = work_item(blockIdx.x, a.BH, a.nblk);
   const int64_t bh = wi.bh;
