@@ -402,6 +402,75 @@ def copy_bandwidth() -> str:
         "byte counts, the mix of the elementwise `mul` above.", ""])
 
 
+# Shapes of the backward mode sweep: (H, n_q, n_k, causal, setting), d = 128
+# bf16.  Causal prefill from 512 to 32K rows, non-causal, short query ranges
+# against long key ranges (where the fused mode's dQ working set is small),
+# and fewer heads.
+MODE_SWEEP = [
+    (32, 512, 512, True, 1), (32, 1024, 1024, True, 1), (32, 2048, 2048, True, 1),
+    (32, 4096, 4096, True, 1), (32, 8192, 8192, True, 1), (32, 8192, 8192, True, 2),
+    (32, 16384, 16384, True, 1), (32, 32768, 32768, True, 1),
+    (32, 4096, 4096, False, 1), (32, 16384, 16384, False, 1),
+    (32, 16, 65536, False, 1), (32, 64, 65536, False, 1), (32, 256, 65536, False, 1),
+    (32, 1024, 65536, False, 1), (8, 8192, 8192, True, 1), (4, 32768, 32768, True, 1),
+]
+
+
+def mode_sweep(shapes=MODE_SWEEP) -> str:
+    """Markdown table: the fused and separate backward timed on cuda:0 for each
+    shape (best of 3 launches, HIP events on the launch stream), the mode the
+    library's plan picks, and what that pick costs against the faster one."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import workloads
+    from . import streamkl as sk
+    dev = torch.device("cuda:0")
+
+    def best_ms(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    name = {sk.BWD_FUSED: "fused", sk.BWD_SEPARATE: "separate"}
+    rows, regrets = [], []
+    for H, n_q, n_k, causal, setting in shapes:
+        w = workloads.Workload("mode-sweep", 1, H, n_q, n_k, 128, 128, "bf16", causal, 0.5, False, 7, (setting,))
+        q1, k1, q2, k2 = workloads.generate(w, dev)
+        g = workloads.upstream_grad(w, dev, "mean")
+        kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, causal)
+        t = {}
+        for m in (sk.BWD_FUSED, sk.BWD_SEPARATE):
+            t[m] = best_ms(lambda m=m: sk.streamkl_bwd(setting, q1, k1, q2, k2, causal, kl, l1, l2, g, bwd_mode=m))
+        pick = sk.bwd_plan(sk.shape_of(q1, k1, q2, k2), causal, setting)
+        fast = min(t, key=t.get)
+        regret = t[pick] / t[fast] - 1.0
+        regrets.append(regret)
+        rows.append(f"| {H} | {n_q} | {n_k} | {'yes' if causal else 'no'} | {setting} | {t[sk.BWD_FUSED]:.3f} | "
+                    f"{t[sk.BWD_SEPARATE]:.3f} | {name[pick]} | {name[fast]} | {100 * regret:.1f}% |")
+        del q1, k1, q2, k2, g, kl, l1, l2
+        torch.cuda.empty_cache()
+    hit = sum(r == 0.0 for r in regrets)
+    return "\n".join([
+        "# Backward mode plan against measurement, one MI355X", "",
+        "Command: `python -m attention_kl_divergence_amd.profiling modes --out profiles/bwd_mode_plan.md`", "",
+        "d1 = d2 = 128, bf16, B = 1, inputs from `workloads.generate` (seed 7, student = teacher + 0.5 noise),",
+        "upstream gradient 1/N_Q per row.  Each mode is the best of 3 launches (HIP events on the launch",
+        "stream).  The plan (`streamkl_bwd_plan`, the cost model that AUTO runs) sees only the shape and the",
+        "CU count; query ranges of at most 32 rows run the decode kernel in the fused mode.", "",
+        "| H | N_Q | N_K | causal | setting | fused ms | separate ms | plan picks | faster | cost of the pick |",
+        "|---|---|---|---|---|---|---|---|---|---|", *rows, "",
+        f"The plan picks the faster mode on {hit} of {len(rows)} shapes; the largest cost of a pick is "
+        f"{100 * max(regrets):.1f}%.", ""])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -429,7 +498,16 @@ def main(argv=None):
     cb.add_argument("--out", default=None)
     pb = sub.add_parser("probes", help="matrix-core, exponential and atomic rates of the part (needs a GPU)")
     pb.add_argument("--out", default=None)
+    md = sub.add_parser("modes", help="fused vs separate backward over a sweep of shapes, against the plan (needs a GPU)")
+    md.add_argument("--out", default=None)
     args = ap.parse_args(argv)
+    if args.cmd == "modes":
+        text = mode_sweep()
+        if args.out:
+            with open(args.out, "w") as fo:
+                fo.write(text)
+        print(text)
+        return 0
     if args.cmd == "probes":
         text = device_probes()
         if args.out:
