@@ -570,9 +570,10 @@ __device__ __forceinline__ void fwd_tile(RowState& st, const T* sK1, const T* sK
 // running state over the keys acc_row(., grp) of every 32-key block, and the
 // two lane groups merge once at the end.
 // LOSS: the fused-loss form (a.lpart set); a separate instantiation so the
-// plain forward's code is untouched by it.
+// plain forward's code is untouched by it.  Two workgroups per CU, except
+// fp32 with d1 = d2 = 128, whose operand fragments leave room for one.
 template <typename T, int D1, int D2, int BK, bool LOSS = false>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, (sizeof(T) == 2 || D1 + D2 < 256) ? 2 : 1) void fwd_kernel(FwdArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr int NW = 4;
@@ -1543,10 +1544,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a) {
     if constexpr (FUSED) {
       lds_barrier();
       constexpr int QSTEP = NW / NBF;
+      // blocks wave / NBF, + QSTEP, ...: a constant trip count with a uniform
+      // guard, so the loop unrolls
 #pragma unroll
-      for (int qb = wave / NBF; qb < NQB; qb += QSTEP) {
+      for (int i = 0; i < (NQB + QSTEP - 1) / QSTEP; ++i) {
+        const int qb = wave / NBF + i * QSTEP;
         const int qb0 = q0 + 32 * qb;
-        if (qb0 >= a.n_q) continue;
+        if (qb >= NQB || qb0 >= a.n_q) continue;
         f32x16 dqa = zero16();
 #pragma unroll
         for (int h = 0; h < HK; ++h) dqa = MF::run(fragcol_nat<T, BQ>(sdS, 0, 32 * qb, h, lane), kcf[h], dqa);
