@@ -82,6 +82,12 @@ SMALL = [
     # at 256 heads (24 tiles, causal)
     ("bf16-dec-h32-q16-k5000", "bf16", 128, 128, False, 1, 32, 16, 5000),
     ("bf16-dec-b4h64-q7-k3000-c", "bf16", 128, 128, True, 4, 64, 7, 3000),
+    # medium sizes, every row: several 256-key dK workgroups and 256-row dQ
+    # workgroups, many query and key tiles (an odd count, a ragged last one)
+    # and the causal frontier crossing workgroups, square and rectangular
+    ("bf16-d128-c-1500", "bf16", 128, 128, True, 1, 2, 1500, 1500),
+    ("bf16-d128x64-nc-1100x1700", "bf16", 128, 64, False, 1, 1, 1100, 1700),
+    ("bf16-d64-c-700x2100", "bf16", 64, 64, True, 1, 2, 700, 2100),
 ]
 
 
