@@ -203,3 +203,22 @@ def test_kl_loss_reduction(cuda_device):
     # one row: the value itself
     one = torch.tensor([0.25], device=cuda_device)
     assert sk.kl_loss(one).item() == 0.25
+
+
+@pytest.mark.parametrize("shape", ["prefill", "decode"])
+def test_repeated_fused_runs_agree(shape, cuda_device):
+    """The fused modes add dQ with fp32 atomics in no fixed order: repeated
+    runs may differ in dQ by fp32 reassociation only, and dK, summed in
+    registers by one wave per key block, repeats bit for bit."""
+    n_q, n_k = (700, 700) if shape == "prefill" else (16, 4000)
+    w = W("repeat", causal=shape == "prefill", H=4, n_q=n_q, n_k=n_k)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal)
+    for s in (1, 2):
+        runs = [sk.streamkl_bwd(s, q1, k1, q2, k2, w.causal, kl, l1, l2, g, bwd_mode=sk.BWD_FUSED) for _ in range(5)]
+        dq0, dk0 = runs[0]
+        for r, (dq, dk) in enumerate(runs[1:], 1):
+            assert torch.equal(dk, dk0), f"{shape} setting {s}: dK of run {r} differs"
+            # ~n_k / 128 fp32 terms per element, added in any order
+            check_grad(f"{shape} setting {s} run {r} dQ", to_np(dq), to_np(dq0), tol=1e-5)
