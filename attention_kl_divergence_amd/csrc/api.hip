@@ -310,6 +310,46 @@ FwdPlan make_fwd_plan(const streamkl_shape* s, int splits) {
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
+// The cost model of one problem's backward: FLOPs of each separate-mode
+// kernel and of the fused kernel, the fused kernel's atomic bytes, and the
+// workgroups of each launch against what the chip holds at once (the
+// separate dK and dQ kernels run one 8-wave workgroup, 256 rows, per CU; the
+// fused key-outer kernel one 4-wave workgroup, 128 keys, per CU).
+struct BwdWork {
+  double f_sep = 0, f_fused = 0, atomic = 0;
+  double wg_dk = 0, wg_dq = 0, wg_fk = 0;
+};
+constexpr double kBwdRate = 1.0e15;     // sustained MFMA FLOP/s assumed for these kernels
+constexpr double kAtomicRate = 1.2e12;  // device-scope fp32 atomic bytes/s
+
+// query-key pairs of one head (bottom-right causal alignment)
+double head_pairs(const streamkl_shape* s, int causal) {
+  return causal ? (double)s->n_q * (s->n_q + 1) / 2 + (double)s->n_q * (s->n_k - s->n_q) : (double)s->n_q * s->n_k;
+}
+
+BwdWork bwd_work(const streamkl_shape* s, int causal, int setting) {
+  const double ds = setting == 1 ? s->d2 : s->d1;
+  const double pairs = head_pairs(s, causal);
+  const double heads = (double)(s->B * s->H);
+  const double f_qk = 2.0 * (s->d1 + s->d2), f_grad = 2.0 * ds;
+  BwdWork w;
+  w.f_sep = heads * pairs * (f_qk + f_grad);
+  w.f_fused = heads * pairs * (f_qk + 2 * f_grad);
+  w.atomic = heads * pairs * 4.0 * ds / kBwdKRows;
+  w.wg_dk = heads * cdiv(s->n_k, kBwdKRowsSep);
+  w.wg_dq = heads * cdiv(s->n_q, kBwdQRows);
+  w.wg_fk = heads * cdiv(s->n_k, kBwdKRows);
+  return w;
+}
+
+double chip_use(double wg, int cus) { return wg < cus ? wg / cus : 1.0; }
+double t_separate(const BwdWork& w, int cus) {
+  return w.f_sep / (kBwdRate * chip_use(w.wg_dk, cus)) + w.f_sep / (kBwdRate * chip_use(w.wg_dq, cus));
+}
+double t_fused(const BwdWork& w, int cus) {
+  return std::max(w.f_fused / (kBwdRate * chip_use(w.wg_fk, cus)), w.atomic / kAtomicRate);
+}
+
 // Backward mode plan.  The fused kernel (Method 2: each query-key tile pair
 // visited once, dQ by atomics) moves 4*d_s bytes of fp32 atomics per query
 // row and 128-key block; on gfx950 device-scope fp32 atomics sustain about
@@ -320,26 +360,8 @@ int plan_bwd(const streamkl_shape* s, int causal, int setting, const streamkl_la
   // decode shapes: the fused decode kernel reads each key tile once and adds
   // to dQ once per wave; the separate dQ kernel would get one workgroup per head
   if (decode_shape(s)) return STREAMKL_BWD_FUSED;
-  const double ds = setting == 1 ? s->d2 : s->d1;
-  const double pairs = causal ? (double)s->n_q * (s->n_q + 1) / 2 + (double)s->n_q * (s->n_k - s->n_q)
-                              : (double)s->n_q * s->n_k;
-  const double heads = (double)(s->B * s->H);
-  const double rate = 1.0e15;  // sustained MFMA FLOP/s assumed for these kernels
-  const double f_qk = 2.0 * (s->d1 + s->d2), f_grad = 2.0 * ds;
-  // workgroups of each kernel against what the chip holds at once: the
-  // separate dK and dQ kernels run one 8-wave workgroup (256 rows) per CU,
-  // the fused key-outer kernel one 4-wave workgroup (128 keys) per CU
-  const double wg_dk = heads * cdiv(s->n_k, kBwdKRowsSep), wg_dq = heads * cdiv(s->n_q, kBwdQRows);
-  const double wg_fk = heads * cdiv(s->n_k, kBwdKRows);
-  const double full = cus;
-  auto use = [&](double wg) { return wg < full ? wg / full : 1.0; };
-  const double t_sep = heads * pairs * (f_qk + f_grad) / (rate * use(wg_dk)) +
-                       heads * pairs * (f_qk + f_grad) / (rate * use(wg_dq));
-  const double atomic_bytes = heads * pairs * 4.0 * ds / kBwdKRows;
-  double t_fused = heads * pairs * (f_qk + 2 * f_grad) / (rate * use(wg_fk));
-  const double t_atomic = atomic_bytes / 1.2e12;
-  if (t_atomic > t_fused) t_fused = t_atomic;
-  return t_fused < t_sep ? STREAMKL_BWD_FUSED : STREAMKL_BWD_SEPARATE;
+  const BwdWork w = bwd_work(s, causal, setting);
+  return t_fused(w, cus) < t_separate(w, cus) ? STREAMKL_BWD_FUSED : STREAMKL_BWD_SEPARATE;
 }
 
 streamkl_status hip_status(hipError_t e) {
@@ -396,6 +418,56 @@ P elem(P p, int64_t b, int64_t rows_per_elem, int64_t bytes_per_row) {
   return reinterpret_cast<P>(reinterpret_cast<C>(p) + b * rows_per_elem * bytes_per_row);
 }
 
+// Elements of a ragged batch that run one kernel go to that kernel in few
+// launches, each with a table of at most kRaggedMax elements (RaggedTable):
+// one launch fills the chip where launches of each element alone would run
+// one after another, each short of filling it.  Element ranges are rounded
+// up to a multiple of 8 workgroups (the XCD count); the elements with the
+// most query-key pairs come first, so the longest workgroups start first.
+struct RaggedLaunch {
+  RaggedTable t = {};
+  int64_t grid = 0;
+};
+
+// Grouping needs every workgroup index of a launch to fit an int; beyond
+// that (far past any batch that fits in memory) elements run on their own.
+bool groupable(const streamkl_shape* s) {
+  constexpr int64_t kMaxWg = int64_t(1) << 30;
+  return ragged(s) && s->B * s->H * (cdiv(std::max(s->n_q, s->n_k), 128) + 1) <= kMaxWg;
+}
+
+// The launches of one kernel over elements `els`; blocks(e): the kernel's
+// workgroups per head for element shape e.
+template <typename F>
+std::vector<RaggedLaunch> ragged_launches(const streamkl_shape* s, int causal, const std::vector<int64_t>& els,
+                                          F blocks) {
+  std::vector<std::pair<double, int64_t>> order;
+  for (int64_t b : els) {
+    const streamkl_shape e = element_shape(s, b);
+    order.push_back({head_pairs(&e, causal), b});
+  }
+  std::stable_sort(order.begin(), order.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+  std::vector<RaggedLaunch> out;
+  for (const auto& o : order) {
+    const streamkl_shape e = element_shape(s, o.second);
+    const int64_t nblk = blocks(e);
+    if (out.empty() || out.back().t.n == kRaggedMax) {
+      out.emplace_back();
+      out.back().t.H = (int)s->H;
+    }
+    RaggedLaunch& L = out.back();
+    const int i = L.t.n++;
+    L.t.start[i] = (int)L.grid;
+    L.t.b[i] = (int)o.second;
+    L.t.n_q[i] = (int)e.n_q;
+    L.t.n_k[i] = (int)e.n_k;
+    L.t.nblk[i] = (int)nblk;
+    L.grid += (s->H * nblk + 7) / 8 * 8;
+    L.t.start[i + 1] = (int)L.grid;
+  }
+  return out;
+}
+
 // ---- the problems of one forward call and their workspace ----
 
 constexpr size_t kInvalidBytes = ~(size_t)0;  // workspace queries with invalid arguments
@@ -406,32 +478,60 @@ streamkl_shape problem(const streamkl_shape* s, int64_t b) { return ragged(s) ? 
 
 struct FwdCall {
   size_t split_region = 0;  // bytes of split partials: the largest of any problem (they run one after another)
-  int64_t loss_slots = 0;   // fused-loss partials of all problems (consecutive, after the split region)
+  int64_t loss_slots = 0;   // fused-loss partials of all launches (consecutive, after the split region)
   double rows = 0;          // query rows the call finalizes (the mean's divisor)
+  std::vector<int64_t> single;          // problems launched on their own, in this order
+  std::vector<RaggedLaunch> pp, plain;  // then the unsplit elements of a ragged batch, grouped by forward kernel
 };
 
-FwdCall summarize(const streamkl_shape* s, const std::vector<int>& splits) {
+// The launches of a forward call with the given split counts and the
+// workspace they need.  Loss slots are numbered in launch order: the single
+// problems, then the grouped ping-pong launches, then the grouped 4-wave ones.
+FwdCall summarize(const streamkl_shape* s, int causal, const std::vector<int>& splits) {
   FwdCall c;
+  const bool group = groupable(s);
+  std::vector<int64_t> pp, plain;
   for (int64_t b = 0; b < problems(s); ++b) {
     const streamkl_shape e = problem(s, b);
     if (e.n_q == 0) continue;
+    c.rows += (double)(e.B * e.H * e.n_q);
+    if (group && splits[b] == 1) {
+      (e.n_q > kFwdRows ? pp : plain).push_back(b);
+      continue;
+    }
     const FwdPlan p = make_fwd_plan(&e, splits[b]);
     c.split_region = std::max(c.split_region, p.split_bytes);
     c.loss_slots += p.loss_slots;
-    c.rows += (double)(e.B * e.H * e.n_q);
+    c.single.push_back(b);
   }
+  c.pp = ragged_launches(s, causal, pp, [](const streamkl_shape& e) { return cdiv(e.n_q, kFwdPPRows); });
+  c.plain = ragged_launches(s, causal, plain, [](const streamkl_shape& e) { return cdiv(e.n_q, kFwdRows); });
+  for (const auto* v : {&c.pp, &c.plain})
+    for (const RaggedLaunch& L : *v) c.loss_slots += L.grid;
   return c;
 }
 
 size_t loss_base(const FwdCall& c) { return round256(c.split_region); }
 size_t loss_call_bytes(const FwdCall& c) { return loss_base(c) + 8 * (size_t)c.loss_slots; }
 
-// The split count of every problem (0 for empty ones) as the plan asks, or one split.
+// The split count of every problem (0 for empty ones) as the plan asks, or
+// one split.  A ragged batch whose elements (decode-shaped ones aside) fill
+// the chip without splits in one grouped launch runs them unsplit; the plan
+// of an element alone would split a short one.
 std::vector<int> planned_splits(const streamkl_shape* s, int causal, const streamkl_launch* l, int cus, bool one) {
   std::vector<int> sp((size_t)problems(s), 0);
+  bool fills = false;
+  if (groupable(s) && !(l && l->num_splits > 0)) {
+    int64_t wg = 0;  // unsplit workgroups of the 4-wave kernel, the measure plan_splits uses
+    for (int64_t b = 0; b < s->B; ++b) {
+      const streamkl_shape e = element_shape(s, b);
+      if (e.n_q > 0 && !decode_shape(&e)) wg += e.H * cdiv(e.n_q, kFwdRows);
+    }
+    fills = wg >= 2 * (int64_t)cus;
+  }
   for (int64_t b = 0; b < problems(s); ++b) {
     const streamkl_shape e = problem(s, b);
-    if (e.n_q > 0) sp[b] = one ? 1 : plan_splits(&e, causal, l, cus);
+    if (e.n_q > 0) sp[b] = one || (fills && !decode_shape(&e)) ? 1 : plan_splits(&e, causal, l, cus);
   }
   return sp;
 }
@@ -439,7 +539,7 @@ std::vector<int> planned_splits(const streamkl_shape* s, int causal, const strea
 // Workspace a call needs with the planned split counts (or one split each):
 // the split partials alone, or (loss) the split region then the loss partials.
 size_t call_bytes(const streamkl_shape* s, int causal, const streamkl_launch* l, int cus, bool loss, bool one) {
-  const FwdCall c = summarize(s, planned_splits(s, causal, l, cus, one));
+  const FwdCall c = summarize(s, causal, planned_splits(s, causal, l, cus, one));
   return loss ? loss_call_bytes(c) : c.split_region;
 }
 
@@ -462,15 +562,15 @@ streamkl_status plan_call(const streamkl_shape* s, int causal, const streamkl_la
       if (expl) return STREAMKL_ERR_WORKSPACE;
       splits[b] = 1;
     }
-    c = summarize(s, splits);
+    c = summarize(s, causal, splits);
     return STREAMKL_OK;
   }
   if (!ws || !aligned(ws, 16)) return STREAMKL_ERR_WORKSPACE;
-  c = summarize(s, splits);
+  c = summarize(s, causal, splits);
   if (loss_call_bytes(c) <= avail) return STREAMKL_OK;
   if (expl) return STREAMKL_ERR_WORKSPACE;
   splits = planned_splits(s, causal, l, cus, true);
-  c = summarize(s, splits);
+  c = summarize(s, causal, splits);
   return loss_call_bytes(c) <= avail ? STREAMKL_OK : STREAMKL_ERR_WORKSPACE;
 }
 
@@ -539,6 +639,29 @@ size_t streamkl_bwd_workspace_bytes(const streamkl_shape* shape, int causal, int
 namespace streamkl {
 namespace {
 
+// Arguments every forward launch shares: the problem's tensors, qs and ks
+// rows per head in memory (the padded lengths), shape->n_q and shape->n_k the
+// rows used.
+FwdArgs fwd_args(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal, float scale1,
+                 float scale2, float* out_kl, float* out_lse1, float* out_lse2, const streamkl_shape* shape,
+                 int64_t qs, int64_t ks, const float* lw) {
+  FwdArgs a = {};
+  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
+  a.kl = out_kl; a.lse1 = out_lse1; a.lse2 = out_lse2;
+  a.lw = lw;
+  a.BH = shape->B * shape->H;
+  a.n_q = (int)shape->n_q;
+  a.n_k = (int)shape->n_k;
+  a.qs = (int)qs;
+  a.ks = (int)ks;
+  a.causal = causal ? 1 : 0;
+  a.c1 = log2e_scale(scale1, shape->d1);
+  a.c2 = log2e_scale(scale2, shape->d2);
+  a.g1 = group1(shape);
+  a.g2 = group2(shape);
+  return a;
+}
+
 // The forward of one problem, validated and planned: qs, ks are the rows per
 // head in memory (the padded lengths), sh->n_q, sh->n_k the rows used; split
 // partials go to `ws`, fused-loss partials (when lpart is set) to lpart.
@@ -553,32 +676,35 @@ streamkl_status fwd_launch(const void* Q1, const void* K1, const void* Q2, const
                         : pick_fwd(shape->dtype, shape->d1, shape->d2);
   if (!fn) return STREAMKL_ERR_UNSUPPORTED;
 
-  FwdArgs a = {};
-  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
-  a.kl = out_kl; a.lse1 = out_lse1; a.lse2 = out_lse2;
+  FwdArgs a = fwd_args(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, qs, ks, lw);
   a.ws = p.splits > 1 ? ws : nullptr;
-  a.lw = lw;
   a.lpart = p.splits > 1 ? nullptr : lpart;  // split: the merge kernel finalizes the rows
-  a.BH = shape->B * shape->H;
-  a.n_q = (int)shape->n_q;
-  a.n_k = (int)shape->n_k;
-  a.qs = (int)qs;
-  a.ks = (int)ks;
   a.nsplit = p.splits;
   const int unit = p.dec ? kDecBlock : kFwdTile;
   a.keys_per_split = (int)(cdiv(cdiv(shape->n_k, unit), p.splits) * unit);
   a.nqb = (int)p.nqb;
-  a.causal = causal ? 1 : 0;
-  a.c1 = log2e_scale(scale1, shape->d1);
-  a.c2 = log2e_scale(scale2, shape->d2);
-  a.g1 = group1(shape);
-  a.g2 = group2(shape);
-  streamkl_status st = hip_status(fn(a, p.grid, s));
+  streamkl_status st = hip_status(fn(a, p.grid, s, nullptr));
   if (st != STREAMKL_OK || p.splits == 1) return st;
   const int64_t rows = a.BH * a.n_q;
   hipLaunchKernelGGL(splitk_merge_kernel, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, s, (const float*)a.ws,
                      out_kl, out_lse1, out_lse2, a.BH, a.n_q, p.splits, a.qs, lw, lpart);
   return hip_status(hipGetLastError());
+}
+
+// One grouped launch of the unsplit forward over elements of a ragged batch
+// (padded tensors `shape`, whole-batch pointers; pp: the ping-pong kernel).
+streamkl_status fwd_group_launch(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                                 float scale1, float scale2, float* out_kl, float* out_lse1, float* out_lse2,
+                                 const streamkl_shape* shape, bool pp, const RaggedLaunch& L, const float* lw,
+                                 double* lpart, hipStream_t s) {
+  FwdLaunch fn = pp ? pick_fwd_pp(shape->dtype, shape->d1, shape->d2) : pick_fwd(shape->dtype, shape->d1, shape->d2);
+  if (!fn) return STREAMKL_ERR_UNSUPPORTED;
+  FwdArgs a = fwd_args(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, shape->n_q,
+                       shape->n_k, lw);
+  a.lpart = lpart;
+  a.nsplit = 1;
+  a.keys_per_split = (int)(cdiv(shape->n_k, kFwdTile) * kFwdTile);  // covers every element's keys
+  return hip_status(fn(a, L.grid, s, &L.t));
 }
 
 // A whole forward call: every argument and the workspace are checked, and
@@ -612,8 +738,8 @@ streamkl_status fwd_call(const void* Q1, const void* K1, const void* Q2, const v
     st = fwd_launch(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, shape->n_q,
                     shape->n_k, make_fwd_plan(shape, splits[0]), split_ws, weights, lpart, s);
   } else {
-    // ragged batch: rows past an element's query length read 0; each element
-    // runs as a problem of its own in the padded tensors
+    // ragged batch: rows past an element's query length read 0; elements
+    // with a key split run on their own, the others in grouped launches
     const int64_t rows = shape->B * shape->H * shape->n_q;
     for (float* o : {out_kl, out_lse1, out_lse2}) {
       st = fill_zero(o, rows, s);
@@ -623,21 +749,51 @@ streamkl_status fwd_call(const void* Q1, const void* K1, const void* Q2, const v
     const int64_t qr = shape->H * shape->n_q, k1r = kv_heads(shape, 1) * shape->n_k,
                   k2r = kv_heads(shape, 2) * shape->n_k;
     int64_t slot = 0;
-    for (int64_t b = 0; b < shape->B && st == STREAMKL_OK; ++b) {
+    for (const int64_t b : c.single) {
       const streamkl_shape e = element_shape(shape, b);
-      if (e.n_q == 0) continue;
       const FwdPlan p = make_fwd_plan(&e, splits[b]);
       st = fwd_launch(elem(Q1, b, qr, es * e.d1), elem(K1, b, k1r, es * e.d1), elem(Q2, b, qr, es * e.d2),
                       elem(K2, b, k2r, es * e.d2), causal, scale1, scale2, elem(out_kl, b, qr, 4),
                       elem(out_lse1, b, qr, 4), elem(out_lse2, b, qr, 4), &e, shape->n_q, shape->n_k, p, split_ws,
                       elem(weights, b, qr, 4), lpart ? lpart + slot : nullptr, s);
+      if (st != STREAMKL_OK) return st;
       slot += p.loss_slots;
+    }
+    for (const bool pp : {true, false}) {
+      for (const RaggedLaunch& L : pp ? c.pp : c.plain) {
+        st = fwd_group_launch(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, pp, L,
+                              weights, lpart ? lpart + slot : nullptr, s);
+        if (st != STREAMKL_OK) return st;
+        slot += L.grid;
+      }
     }
   }
   if (st != STREAMKL_OK || !loss) return st;
   hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, s, (const double*)lpart, c.loss_slots,
                      weights ? 0.0 : c.rows, out_loss);
   return hip_status(hipGetLastError());
+}
+
+// Arguments every backward launch shares (the gradient outputs, the scale of
+// the model that receives them and the blocks per head aside): rows per head
+// in memory qs, ks; shape->n_q and shape->n_k the rows used.
+BwdArgs bwd_args(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal, float scale1,
+                 float scale2, const float* kl, const float* lse1, const float* lse2, const float* d_kl,
+                 const streamkl_shape* shape, int64_t qs, int64_t ks) {
+  BwdArgs a = {};
+  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
+  a.kl = kl; a.lse1 = lse1; a.lse2 = lse2; a.g = d_kl;
+  a.BH = shape->B * shape->H;
+  a.n_q = (int)shape->n_q;
+  a.n_k = (int)shape->n_k;
+  a.qs = (int)qs;
+  a.ks = (int)ks;
+  a.causal = causal ? 1 : 0;
+  a.c1 = log2e_scale(scale1, shape->d1);
+  a.c2 = log2e_scale(scale2, shape->d2);
+  a.g1 = group1(shape);
+  a.g2 = group2(shape);
+  return a;
 }
 
 // One backward setting of one problem (validated), rows per head qs, ks.
@@ -650,21 +806,9 @@ streamkl_status bwd_launch(int setting, const void* Q1, const void* K1, const vo
   if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
   const int mode = plan_bwd(shape, causal, setting, launch, dev.cus);
 
-  BwdArgs a = {};
-  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
-  a.kl = kl; a.lse1 = lse1; a.lse2 = lse2; a.g = d_kl;
+  BwdArgs a = bwd_args(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, shape, qs, ks);
   a.dq = dQ; a.dk = dK;
-  a.BH = shape->B * shape->H;
-  a.n_q = (int)shape->n_q;
-  a.n_k = (int)shape->n_k;
-  a.qs = (int)qs;
-  a.ks = (int)ks;
-  a.causal = causal ? 1 : 0;
-  a.c1 = log2e_scale(scale1, shape->d1);
-  a.c2 = log2e_scale(scale2, shape->d2);
   a.scale_s = setting == 1 ? plain_scale(scale2, shape->d2) : plain_scale(scale1, shape->d1);
-  a.g1 = group1(shape);
-  a.g2 = group2(shape);
   const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
   const int ds = setting == 1 ? shape->d2 : shape->d1;
   streamkl_status st;
@@ -681,17 +825,17 @@ streamkl_status bwd_launch(int setting, const void* Q1, const void* K1, const vo
       return hip_status(fd(a, setting, a.BH * a.nblk, s));
     }
     a.nblk = (int)nkb;
-    return hip_status(fk(a, setting, true, a.BH * nkb, s));
+    return hip_status(fk(a, setting, true, a.BH * nkb, s, nullptr));
   }
   if (mode != STREAMKL_BWD_DQ_ONLY) {
     const int64_t nkb8 = cdiv(a.n_k, kBwdKRowsSep);  // the separate dK kernel's 8-wave key blocks
     a.nblk = (int)nkb8;
-    st = hip_status(fk(a, setting, false, a.BH * nkb8, s));
+    st = hip_status(fk(a, setting, false, a.BH * nkb8, s, nullptr));
     if (st != STREAMKL_OK) return st;
   }
   if (mode == STREAMKL_BWD_DK_ONLY) return STREAMKL_OK;
   a.nblk = (int)nqb;
-  return hip_status(fq(a, setting, a.BH * nqb, s));
+  return hip_status(fq(a, setting, a.BH * nqb, s, nullptr));
 }
 
 // The joint kernels for one problem (validated, bf16), rows per head qs, ks.
@@ -702,22 +846,10 @@ streamkl_status joint_launch(const void* Q1, const void* K1, const void* Q2, con
   DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
   DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
   if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
-  BwdArgs a = {};
-  a.q1 = Q1; a.k1 = K1; a.q2 = Q2; a.k2 = K2;
-  a.kl = kl; a.lse1 = lse1; a.lse2 = lse2; a.g = d_kl;
+  BwdArgs a = bwd_args(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, shape, qs, ks);
   a.dk = dK1; a.dk2 = dK2;
-  a.BH = shape->B * shape->H;
-  a.n_q = (int)shape->n_q;
-  a.n_k = (int)shape->n_k;
-  a.qs = (int)qs;
-  a.ks = (int)ks;
-  a.causal = causal ? 1 : 0;
-  a.c1 = log2e_scale(scale1, shape->d1);
-  a.c2 = log2e_scale(scale2, shape->d2);
   a.scale_s = plain_scale(scale1, shape->d1);
   a.scale_s2 = plain_scale(scale2, shape->d2);
-  a.g1 = group1(shape);
-  a.g2 = group2(shape);
   const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
   streamkl_status st;
   if (mode != STREAMKL_BWD_DQ_ONLY) {
@@ -725,7 +857,7 @@ streamkl_status joint_launch(const void* Q1, const void* K1, const void* Q2, con
     if (st == STREAMKL_OK) st = clear_shared_dk(dK2, shape, shape->d2, a.g2, ks, s);
     if (st != STREAMKL_OK) return st;
     a.nblk = (int)nkb;
-    st = hip_status(fk(a, 3, false, a.BH * nkb, s));
+    st = hip_status(fk(a, 3, false, a.BH * nkb, s, nullptr));
     if (st != STREAMKL_OK || mode == STREAMKL_BWD_DK_ONLY) return st;
   }
   // dQ1 and dQ2: the query-outer kernel once per setting (one kernel holding
@@ -733,11 +865,102 @@ streamkl_status joint_launch(const void* Q1, const void* K1, const void* Q2, con
   // measured slower than these two)
   a.nblk = (int)nqb;
   a.dq = dQ1;
-  st = hip_status(fq(a, 2, a.BH * nqb, s));
+  st = hip_status(fq(a, 2, a.BH * nqb, s, nullptr));
   if (st != STREAMKL_OK) return st;
   a.dq = dQ2;
   a.scale_s = a.scale_s2;
-  return hip_status(fq(a, 1, a.BH * nqb, s));
+  return hip_status(fq(a, 1, a.BH * nqb, s, nullptr));
+}
+
+// Whether the separate-mode backward of a ragged batch runs its elements in
+// grouped launches: always for an explicit separate, dK-only or dQ-only
+// mode; in the automatic mode when the cost model puts the grouped separate
+// kernels (the workgroups of all elements together against the chip) at or
+// below each element on its own in its own best mode.  Decode-shaped
+// elements keep their decode backward and are left out of the comparison.
+bool group_bwd(const streamkl_shape* s, int causal, int setting, const streamkl_launch* l, int cus) {
+  if (!groupable(s)) return false;
+  const int req = l ? l->bwd_mode : STREAMKL_BWD_AUTO;
+  if (req != STREAMKL_BWD_AUTO) return req != STREAMKL_BWD_FUSED;
+  BwdWork all;
+  double each = 0;
+  for (int64_t b = 0; b < s->B; ++b) {
+    const streamkl_shape e = element_shape(s, b);
+    if (e.n_q == 0 || decode_shape(&e)) continue;
+    const BwdWork w = bwd_work(&e, causal, setting);
+    all.f_sep += w.f_sep;
+    all.wg_dk += w.wg_dk;
+    all.wg_dq += w.wg_dq;
+    each += std::min(t_separate(w, cus), t_fused(w, cus));
+  }
+  return all.f_sep > 0 && t_separate(all, cus) <= each;
+}
+
+// The separate-mode kernels of one backward setting over elements `els` of a
+// ragged batch, in grouped launches on the whole-batch tensors (validated;
+// mode: separate, dK only or dQ only; dQ and dK already cleared).
+streamkl_status bwd_group(int setting, const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                          float scale1, float scale2, const float* kl, const float* lse1, const float* lse2,
+                          const float* d_kl, float* dQ, float* dK, const streamkl_shape* shape,
+                          const std::vector<int64_t>& els, int mode, hipStream_t s) {
+  DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
+  DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
+  if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
+  BwdArgs a = bwd_args(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, shape, shape->n_q, shape->n_k);
+  a.dq = dQ; a.dk = dK;
+  a.scale_s = setting == 1 ? plain_scale(scale2, shape->d2) : plain_scale(scale1, shape->d1);
+  if (mode != STREAMKL_BWD_DQ_ONLY) {
+    for (const RaggedLaunch& L :
+         ragged_launches(shape, causal, els, [](const streamkl_shape& e) { return cdiv(e.n_k, kBwdKRowsSep); })) {
+      const streamkl_status st = hip_status(fk(a, setting, false, L.grid, s, &L.t));
+      if (st != STREAMKL_OK) return st;
+    }
+  }
+  if (mode == STREAMKL_BWD_DK_ONLY) return STREAMKL_OK;
+  for (const RaggedLaunch& L :
+       ragged_launches(shape, causal, els, [](const streamkl_shape& e) { return cdiv(e.n_q, kBwdQRows); })) {
+    const streamkl_status st = hip_status(fq(a, setting, L.grid, s, &L.t));
+    if (st != STREAMKL_OK) return st;
+  }
+  return STREAMKL_OK;
+}
+
+// The joint kernels over elements `els` of a ragged batch in grouped
+// launches (validated, bf16; outputs already cleared).
+streamkl_status joint_group(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal, float scale1,
+                            float scale2, const float* kl, const float* lse1, const float* lse2, const float* d_kl,
+                            float* dQ1, float* dK1, float* dQ2, float* dK2, const streamkl_shape* shape,
+                            const std::vector<int64_t>& els, int mode, hipStream_t s) {
+  DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
+  DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
+  if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
+  BwdArgs a = bwd_args(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, shape, shape->n_q, shape->n_k);
+  a.dk = dK1; a.dk2 = dK2;
+  a.scale_s = plain_scale(scale1, shape->d1);
+  a.scale_s2 = plain_scale(scale2, shape->d2);
+  streamkl_status st;
+  if (mode != STREAMKL_BWD_DQ_ONLY) {
+    for (const RaggedLaunch& L :
+         ragged_launches(shape, causal, els, [](const streamkl_shape& e) { return cdiv(e.n_k, kBwdKRows); })) {
+      st = hip_status(fk(a, 3, false, L.grid, s, &L.t));
+      if (st != STREAMKL_OK) return st;
+    }
+    if (mode == STREAMKL_BWD_DK_ONLY) return STREAMKL_OK;
+  }
+  const std::vector<RaggedLaunch> qls =
+      ragged_launches(shape, causal, els, [](const streamkl_shape& e) { return cdiv(e.n_q, kBwdQRows); });
+  a.dq = dQ1;
+  for (const RaggedLaunch& L : qls) {
+    st = hip_status(fq(a, 2, L.grid, s, &L.t));
+    if (st != STREAMKL_OK) return st;
+  }
+  a.dq = dQ2;
+  a.scale_s = a.scale_s2;
+  for (const RaggedLaunch& L : qls) {
+    st = hip_status(fq(a, 1, L.grid, s, &L.t));
+    if (st != STREAMKL_OK) return st;
+  }
+  return STREAMKL_OK;
 }
 
 }  // namespace
@@ -816,25 +1039,33 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
   if (!ragged(shape))
     return bwd_launch(setting, Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ, dK, shape,
                       shape->n_q, shape->n_k, launch, dev, s);
-  // ragged batch: padded rows of dQ and dK are zero; each element runs as a
-  // problem of its own in the padded tensors
+  // ragged batch: padded rows of dQ and dK are zero; elements run in grouped
+  // launches of the separate-mode kernels or each as a problem of its own
   const int ds = setting == 1 ? shape->d2 : shape->d1;
   const int64_t kvs = kv_heads(shape, setting == 1 ? 2 : 1);
   if (need_dq) st = fill_zero(dQ, shape->B * shape->H * shape->n_q * (int64_t)ds, s);
   if (st == STREAMKL_OK && need_dk) st = fill_zero(dK, shape->B * kvs * shape->n_k * (int64_t)ds, s);
   if (st != STREAMKL_OK) return st;
+  const bool group = group_bwd(shape, causal, setting, launch, dev.cus);
   const int64_t es = shape->dtype == STREAMKL_BF16 ? 2 : 4;
   const int64_t qr = shape->H * shape->n_q, k1r = kv_heads(shape, 1) * shape->n_k, k2r = kv_heads(shape, 2) * shape->n_k;
+  std::vector<int64_t> together;
   for (int64_t b = 0; b < shape->B; ++b) {
     const streamkl_shape e = element_shape(shape, b);
     if (e.n_q == 0) continue;
+    if (group && (req != STREAMKL_BWD_AUTO || !decode_shape(&e))) {
+      together.push_back(b);
+      continue;
+    }
     st = bwd_launch(setting, elem(Q1, b, qr, es * e.d1), elem(K1, b, k1r, es * e.d1), elem(Q2, b, qr, es * e.d2),
                     elem(K2, b, k2r, es * e.d2), causal, scale1, scale2, elem(kl, b, qr, 4), elem(lse1, b, qr, 4),
                     elem(lse2, b, qr, 4), elem(d_kl, b, qr, 4), elem(dQ, b, qr, 4 * ds),
                     elem(dK, b, kvs * shape->n_k, 4 * ds), &e, shape->n_q, shape->n_k, launch, dev, s);
     if (st != STREAMKL_OK) return st;
   }
-  return STREAMKL_OK;
+  if (together.empty()) return STREAMKL_OK;
+  return bwd_group(setting, Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ, dK, shape, together,
+                   req == STREAMKL_BWD_AUTO ? STREAMKL_BWD_SEPARATE : req, s);
 }
 
 streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
@@ -880,6 +1111,14 @@ streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q
     if (st == STREAMKL_OK) st = fill_zero(dK2, shape->B * kv2 * shape->n_k * shape->d2, s);
   }
   if (st != STREAMKL_OK) return st;
+  if (groupable(shape)) {  // every non-empty element in grouped launches
+    std::vector<int64_t> els;
+    for (int64_t b = 0; b < shape->B; ++b)
+      if (element_shape(shape, b).n_q > 0) els.push_back(b);
+    return els.empty() ? STREAMKL_OK
+                       : joint_group(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ1, dK1, dQ2, dK2,
+                                     shape, els, mode, s);
+  }
   const int64_t es = 2;
   const int64_t qr = shape->H * shape->n_q, k1r = kv1 * shape->n_k, k2r = kv2 * shape->n_k;
   const int d1 = shape->d1, d2 = shape->d2;

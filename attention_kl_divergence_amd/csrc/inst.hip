@@ -10,44 +10,95 @@
 
 namespace streamkl {
 
-// The joint dK kernel (setting 3) exists for bf16 only and has no fused
-// form; a template, so the fp32 kernel is never instantiated.  Internal
-// linkage and the head dims as parameters: every translation unit defines its
-// own.
+// Each kernel is instantiated for a plain launch (NoTable) and for a grouped
+// launch over elements of a ragged batch (RaggedTable); these helpers launch
+// one with the table type RT.  Internal linkage and the head dims as
+// template parameters: every translation unit defines its own.
 namespace {
-template <typename T, int D1, int D2>
-hipError_t launch_joint_dk(const BwdArgs& a, dim3 g, dim3 b, hipStream_t st, bool fused) {
-  if constexpr (sizeof(T) != 2) {
+template <typename RT>
+hipError_t fwd_go(const FwdArgs& a, int64_t nblocks, hipStream_t st, const RT& rt) {
+  const dim3 g((unsigned)nblocks), b(256);
+  // a.lpart set: the fused-loss instantiation (only unsplit launches finalize rows here)
+  if (a.lpart && a.nsplit == 1)
+    hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile, true, RT>), g, b, 0, st, a, rt);
+  else
+    hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile, false, RT>), g, b, 0, st, a, rt);
+  return hipGetLastError();
+}
+
+template <typename RT>
+hipError_t fwd_pp_go(const FwdArgs& a, int64_t nblocks, hipStream_t st, const RT& rt) {
+  constexpr int BK = kFwdPPTile<SKL_T>;
+  const dim3 g((unsigned)nblocks), b(512);
+  if (a.lpart)
+    hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, BK, true, RT>), g, b, 0, st, a, rt);
+  else
+    hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, BK, false, RT>), g, b, 0, st, a, rt);
+  return hipGetLastError();
+}
+
+template <typename RT>
+hipError_t dq_go(const BwdArgs& a, int setting, int64_t nblocks, hipStream_t st, const RT& rt) {
+  constexpr int W = kBwdQWaves;
+  const dim3 g((unsigned)nblocks), b(64 * W);
+  if (setting == 1)
+    hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 1, kBwdKeyTile, W, RT>), g, b, 0, st, a, rt);
+  else if (setting == 2)
+    hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 2, kBwdKeyTile, W, RT>), g, b, 0, st, a, rt);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// The joint dK kernel (setting 3) exists for bf16 only and has no fused form.
+template <typename RT>
+hipError_t joint_dk_go(const BwdArgs& a, dim3 g, hipStream_t st, const RT& rt) {
+  if constexpr (sizeof(SKL_T) != 2) {
     return hipErrorInvalidValue;
   } else {
-    if (fused) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dk_kernel<T, D1, D2, 3, false, kBwdQTile<T>>), g, b, 0, st, a);
+    hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 3, false, kBwdQTile<SKL_T>, 4, RT>), g, dim3(256), 0, st,
+                       a, rt);
     return hipGetLastError();
   }
 }
+
+// The separate (8-wave) and joint dK kernels; the fused (4-wave) form runs
+// plain launches only.
+template <typename RT>
+hipError_t dk_go(const BwdArgs& a, int setting, bool fused, int64_t nblocks, hipStream_t st, const RT& rt) {
+  constexpr int W = kBwdKWaves;
+  constexpr int BQ = kBwdQTile<SKL_T>;
+  const dim3 g((unsigned)nblocks), b(256), b8(64 * W);
+  if (setting == 3) return fused ? hipErrorInvalidValue : joint_dk_go(a, g, st, rt);
+  if (setting != 1 && setting != 2) return hipErrorInvalidValue;
+  if (fused) {
+    if constexpr (kRagged<RT>) {
+      return hipErrorInvalidValue;
+    } else {
+      if (setting == 1) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, true, BQ>), g, b, 0, st, a, rt);
+      else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, true, BQ>), g, b, 0, st, a, rt);
+    }
+  } else if (setting == 1) {
+    hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, false, BQ, W, RT>), g, b8, 0, st, a, rt);
+  } else {
+    hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, false, BQ, W, RT>), g, b8, 0, st, a, rt);
+  }
+  return hipGetLastError();
+}
 }  // namespace
 
-// a.lpart set: the fused-loss instantiation (only unsplit launches finalize rows here)
-hipError_t SKL_CAT(launch_fwd, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
-  if (a.lpart && a.nsplit == 1)
-    hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile, true>), dim3((unsigned)nblocks), dim3(256), 0, st,
-                       a);
-  else
-    hipLaunchKernelGGL((fwd_kernel<SKL_T, SKL_D1, SKL_D2, kFwdTile>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
-  return hipGetLastError();
+hipError_t SKL_CAT(launch_fwd, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st,
+                                                        const RaggedTable* rt) {
+  return rt ? fwd_go(a, nblocks, st, *rt) : fwd_go(a, nblocks, st, NoTable{});
 }
 
-hipError_t SKL_CAT(launch_fwd_pp, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
-  if (a.lpart)
-    hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, kFwdPPTile<SKL_T>, true>), dim3((unsigned)nblocks),
-                       dim3(512), 0, st, a);
-  else
-    hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, kFwdPPTile<SKL_T>>), dim3((unsigned)nblocks), dim3(512),
-                       0, st, a);
-  return hipGetLastError();
+hipError_t SKL_CAT(launch_fwd_pp, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st,
+                                                           const RaggedTable* rt) {
+  return rt ? fwd_pp_go(a, nblocks, st, *rt) : fwd_pp_go(a, nblocks, st, NoTable{});
 }
 
-hipError_t SKL_CAT(launch_fwd_dec, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st) {
+hipError_t SKL_CAT(launch_fwd_dec, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st,
+                                                            const RaggedTable* rt) {
+  if (rt) return hipErrorInvalidValue;  // the decode forward runs each element on its own
   if constexpr (sizeof(SKL_T) != 2) {
     return hipErrorInvalidValue;  // bf16 only
   } else {
@@ -57,29 +108,13 @@ hipError_t SKL_CAT(launch_fwd_dec, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int
 }
 
 hipError_t SKL_CAT(launch_bwd_dq, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, int64_t nblocks,
-                                                           hipStream_t st) {
-  const dim3 g((unsigned)nblocks), b(64 * kBwdQWaves);
-  constexpr int W = kBwdQWaves;
-  if (setting == 1) hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 1, kBwdKeyTile, W>), g, b, 0, st, a);
-  else if (setting == 2) hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 2, kBwdKeyTile, W>), g, b, 0, st, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+                                                           hipStream_t st, const RaggedTable* rt) {
+  return rt ? dq_go(a, setting, nblocks, st, *rt) : dq_go(a, setting, nblocks, st, NoTable{});
 }
 
 hipError_t SKL_CAT(launch_bwd_dk, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, bool fused, int64_t nblocks,
-                                                           hipStream_t st) {
-  const dim3 g((unsigned)nblocks), b(256), b8(64 * kBwdKWaves);
-  constexpr int W = kBwdKWaves;
-  if (setting == 1) {
-    if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, true, kBwdQTile<SKL_T>>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 1, false, kBwdQTile<SKL_T>, W>), g, b8, 0, st, a);
-  } else if (setting == 2) {
-    if (fused) hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, true, kBwdQTile<SKL_T>>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((bwd_dk_kernel<SKL_T, SKL_D1, SKL_D2, 2, false, kBwdQTile<SKL_T>, W>), g, b8, 0, st, a);
-  } else {
-    return launch_joint_dk<SKL_T, SKL_D1, SKL_D2>(a, g, b, st, fused);
-  }
-  return hipGetLastError();
+                                                           hipStream_t st, const RaggedTable* rt) {
+  return rt ? dk_go(a, setting, fused, nblocks, st, *rt) : dk_go(a, setting, fused, nblocks, st, NoTable{});
 }
 
 hipError_t SKL_CAT(launch_bwd_dec, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, int64_t nblocks,

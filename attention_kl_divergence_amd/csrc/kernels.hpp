@@ -168,6 +168,53 @@ __device__ __forceinline__ WorkItem work_item(int64_t lin, int64_t BH, int nblk)
   return {lin % BH, (int)(lin / BH)};
 }
 
+// Ragged batches in one launch.  The elements of a batch that run the same
+// kernel go in one table, passed as a kernel argument beside the problem's.
+// Element i owns workgroups [start[i], start[i+1]), a range whose length is
+// a multiple of 8, so each workgroup sits on the XCD it would have in a
+// launch of that element alone.  Within its range a workgroup serves
+// element b[i] (query heads b[i] H .. b[i] H + H - 1 of the padded tensors)
+// exactly as in such a launch, with that element's lengths and blocks per
+// head.  The workgroups past an element's H * nblk are padding and leave at
+// once.
+constexpr int kRaggedMax = 64;
+struct RaggedTable {
+  int n;                     // elements in the table (0: not ragged)
+  int H;                     // query heads per element
+  int start[kRaggedMax + 1];
+  int b[kRaggedMax];         // batch index of each element
+  int n_q[kRaggedMax], n_k[kRaggedMax];
+  int nblk[kRaggedMax];      // the kernel's blocks per head for the element
+};
+
+// The table type of a plain launch: no table.  Kernels take the table type
+// as a template parameter, so a plain launch compiles without the ragged
+// prologue and its code is unchanged by it.
+struct NoTable {};
+template <typename RT>
+constexpr bool kRagged = std::is_same<RT, RaggedTable>::value;
+
+struct RaggedItem {
+  int64_t lin;    // workgroup index within the element's range
+  int64_t head0;  // the element's first query head, b H
+  int n_q, n_k, nblk;
+  bool pad;       // a padding workgroup
+};
+
+__device__ __forceinline__ RaggedItem ragged_item(const RaggedTable& rt, int64_t lin) {
+  int e = 0;
+#pragma unroll 1
+  for (int i = 1; i < rt.n; ++i) e = lin >= rt.start[i] ? i : e;
+  RaggedItem r;
+  r.lin = lin - rt.start[e];
+  r.head0 = (int64_t)rt.b[e] * rt.H;
+  r.n_q = rt.n_q[e];
+  r.n_k = rt.n_k[e];
+  r.nblk = rt.nblk[e];
+  r.pad = r.lin >= (int64_t)rt.H * r.nblk;
+  return r;
+}
+
 // Fused loss (the distillation objective sum_i w_i KL_i): each workgroup that
 // finalizes rows writes the sum of w_i KL_i over its rows to its own slot, in
 // a fixed order (a butterfly over the wave's lanes, which leaves the same bits
@@ -572,8 +619,8 @@ __device__ __forceinline__ void fwd_tile(RowState& st, const T* sK1, const T* sK
 // LOSS: the fused-loss form (a.lpart set); a separate instantiation so the
 // plain forward's code is untouched by it.  Two workgroups per CU, except
 // fp32 with d1 = d2 = 128, whose operand fragments leave room for one.
-template <typename T, int D1, int D2, int BK, bool LOSS = false>
-__global__ __launch_bounds__(256, (sizeof(T) == 2 || D1 + D2 < 256) ? 2 : 1) void fwd_kernel(FwdArgs a) {
+template <typename T, int D1, int D2, int BK, bool LOSS = false, typename RT = NoTable>
+__global__ __launch_bounds__(256, (sizeof(T) == 2 || D1 + D2 < 256) ? 2 : 1) void fwd_kernel(FwdArgs a, const RT rt) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr int NW = 4;
@@ -584,11 +631,26 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 || D1 + D2 < 256) ? 2 : 1) voi
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
-  int64_t lin = blockIdx.x;
+  int64_t lin = blockIdx.x, head0 = 0, heads = a.BH;
+  if constexpr (kRagged<RT>) {  // one element of a ragged batch (unsplit)
+    const RaggedItem r = ragged_item(rt, lin);
+    if (r.pad) {
+      if constexpr (LOSS) {
+        if (tid == 0) a.lpart[blockIdx.x] = 0.0;
+      }
+      return;
+    }
+    lin = r.lin;
+    head0 = r.head0;
+    heads = rt.H;
+    a.n_q = r.n_q;
+    a.n_k = r.n_k;
+    a.nqb = r.nblk;
+  }
   const int z = (int)(lin % a.nsplit);
   lin /= a.nsplit;
-  const int64_t bh = lin % a.BH;
-  const int qb = a.nqb - 1 - (int)(lin / a.BH);  // longest causal rows first
+  const int64_t bh = head0 + lin % heads;
+  const int qb = a.nqb - 1 - (int)(lin / heads);  // longest causal rows first
   const int qwg0 = qb * 32 * NW;
   const int q0 = qwg0 + 32 * wave;
   const int qrow = q0 + col;
@@ -832,8 +894,8 @@ __device__ __forceinline__ void fwd_logits(f32x16 (&s1)[NKB], f32x16 (&s2)[NKB],
 // (waves 4-7, the other wave on each SIMD) runs the online update of tile
 // t-1; after a barrier the roles swap.  Each SIMD thus keeps one wave on the
 // matrix cores and one on the VALU.
-template <typename T, int D1, int D2, int BK, bool LOSS = false>
-__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
+template <typename T, int D1, int D2, int BK, bool LOSS = false, typename RT = NoTable>
+__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a, const RT rt) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr int NW = 8;
@@ -845,8 +907,24 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
   const int group = wave >> 2;
-  const WorkItem wi = work_item(blockIdx.x, a.BH, a.nqb);
-  const int64_t bh = wi.bh;
+  int64_t lin = blockIdx.x, head0 = 0, heads = a.BH;
+  if constexpr (kRagged<RT>) {  // one element of a ragged batch
+    const RaggedItem r = ragged_item(rt, lin);
+    if (r.pad) {
+      if constexpr (LOSS) {
+        if (tid == 0) a.lpart[blockIdx.x] = 0.0;
+      }
+      return;
+    }
+    lin = r.lin;
+    head0 = r.head0;
+    heads = rt.H;
+    a.n_q = r.n_q;
+    a.n_k = r.n_k;
+    a.nqb = r.nblk;
+  }
+  const WorkItem wi = work_item(lin, heads, a.nqb);
+  const int64_t bh = head0 + wi.bh;
   const int qb = a.nqb - 1 - wi.blk;  // longest causal rows first
   const int qwg0 = qb * 32 * NW;
   const int q0 = qwg0 + 32 * wave;
@@ -1108,8 +1186,8 @@ __device__ __forceinline__ void dS_rows_keyouter_joint(f32x16& s1, f32x16& s2, c
 // one query row, so dS from the accumulators is directly the A operand of
 // dQ = dS K_s; K_s's B operand is read down the key rows of its tile.
 // Deterministic; no atomics.
-template <typename T, int D1, int D2, int SETTING, int BK, int NW = 4>
-__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
+template <typename T, int D1, int D2, int SETTING, int BK, int NW = 4, typename RT = NoTable>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a, const RT rt) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr int DS = SETTING == 1 ? D2 : D1;
@@ -1125,8 +1203,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   // become scalar branches instead of exec-mask branches
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
-  const WorkItem wi = work_item(blockIdx.x, a.BH, a.nblk);
-  const int64_t bh = wi.bh;
+  int64_t lin = blockIdx.x, head0 = 0, heads = a.BH;
+  if constexpr (kRagged<RT>) {  // one element of a ragged batch
+    const RaggedItem r = ragged_item(rt, lin);
+    if (r.pad) return;
+    lin = r.lin;
+    head0 = r.head0;
+    heads = rt.H;
+    a.n_q = r.n_q;
+    a.n_k = r.n_k;
+    a.nblk = r.nblk;
+  }
+  const WorkItem wi = work_item(lin, heads, a.nblk);
+  const int64_t bh = head0 + wi.bh;
   const int qb = a.nblk - 1 - wi.blk;  // longest causal rows first
   const int q0 = qb * 32 * NW + 32 * wave;
   const int qrow = q0 + col;
@@ -1282,8 +1371,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 // to global dQ_s with fp32 atomics, so each query-key pair is visited once.
 // SETTING 3 (joint, not fused) forms dS1 and dS2 from the same logits and
 // accumulates dK1 (dk) and dK2 (dk2).
-template <typename T, int D1, int D2, int SETTING, bool FUSED, int BQ, int NW = 4>
-__global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a) {
+template <typename T, int D1, int D2, int SETTING, bool FUSED, int BQ, int NW = 4, typename RT = NoTable>
+__global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a, const RT rt) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr bool JOINT = SETTING == 3;
@@ -1312,8 +1401,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a) {
   // become scalar branches instead of exec-mask branches
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
-  const WorkItem wi = work_item(blockIdx.x, a.BH, a.nblk);
-  const int64_t bh = wi.bh;
+  int64_t lin = blockIdx.x, head0 = 0, heads = a.BH;
+  if constexpr (kRagged<RT>) {  // one element of a ragged batch
+    const RaggedItem r = ragged_item(rt, lin);
+    if (r.pad) return;
+    lin = r.lin;
+    head0 = r.head0;
+    heads = rt.H;
+    a.n_q = r.n_q;
+    a.n_k = r.n_k;
+    a.nblk = r.nblk;
+  }
+  const WorkItem wi = work_item(lin, heads, a.nblk);
+  const int64_t bh = head0 + wi.bh;
   const int kb = wi.blk;  // low key blocks see the most queries under causal masks: first
   const int kw0 = kb * BKW;
   const int kwave = kw0 + 32 * wave;

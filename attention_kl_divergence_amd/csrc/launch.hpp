@@ -9,6 +9,7 @@ namespace streamkl {
 
 struct FwdArgs;
 struct BwdArgs;
+struct RaggedTable;
 
 constexpr int kFwdRows = 128;     // query rows per forward workgroup (4 waves x 32)
 constexpr int kFwdPPRows = 256;   // query rows per ping-pong forward workgroup (8 waves x 32)
@@ -29,17 +30,20 @@ constexpr int kDecBwdTile = 128;  // key rows per tile of the decode backward (4
 // query rows per LDS tile of the dK kernel (fp32 tiles are twice as large)
 template <typename T> constexpr int kBwdQTile = sizeof(T) == 2 ? 64 : 32;
 
-using FwdLaunch = hipError_t (*)(const FwdArgs&, int64_t, hipStream_t);
-using DqLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t);
-using DkLaunch = hipError_t (*)(const BwdArgs&, int, bool, int64_t, hipStream_t);
+// The forward and the single-setting backward launchers take an optional
+// ragged-batch table (NULL: a plain launch); the decode kernels do not.
+using FwdLaunch = hipError_t (*)(const FwdArgs&, int64_t, hipStream_t, const RaggedTable*);
+using DqLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t, const RaggedTable*);
+using DkLaunch = hipError_t (*)(const BwdArgs&, int, bool, int64_t, hipStream_t, const RaggedTable*);
 using DecBwdLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t);
 
-#define SKL_DECL(tn, d1, d2)                                                                   \
-  hipError_t launch_fwd_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);              \
-  hipError_t launch_fwd_pp_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);           \
-  hipError_t launch_fwd_dec_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t);          \
-  hipError_t launch_bwd_dq_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t);      \
-  hipError_t launch_bwd_dk_##tn##_##d1##_##d2(const BwdArgs&, int, bool, int64_t, hipStream_t);     \
+#define SKL_DECL(tn, d1, d2)                                                                                  \
+  hipError_t launch_fwd_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t, const RaggedTable*);         \
+  hipError_t launch_fwd_pp_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t, const RaggedTable*);      \
+  hipError_t launch_fwd_dec_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t, const RaggedTable*);     \
+  hipError_t launch_bwd_dq_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t, const RaggedTable*); \
+  hipError_t launch_bwd_dk_##tn##_##d1##_##d2(const BwdArgs&, int, bool, int64_t, hipStream_t,                \
+                                             const RaggedTable*);                                             \
   hipError_t launch_bwd_dec_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t);
 SKL_DECL(f32, 64, 64)
 SKL_DECL(f32, 64, 128)

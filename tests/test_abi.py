@@ -209,18 +209,24 @@ def test_loss_workspace_query():
     split = sk.fwd_workspace_bytes(dec, False)
     assert split > 0
     assert sk.fwd_loss_workspace_bytes(dec, False) == (split + 255) // 256 * 256 + 8 * 2
-    # ragged: consecutive partials of every non-empty element after the
-    # largest split region; each element is planned as a problem of its own
-    lens = [600, 0, 100, 9000]
-    rag = shape(B=4, H=8, n_q=9000, n_k=9000).set_lengths(lens, lens)
-    slots = 0
-    for n in lens:
-        if n == 0:
-            continue
-        sp = sk.fwd_plan(shape(H=8, n_q=n, n_k=n), True)
-        slots += -(-8 * n // 256) if sp > 1 else 8 * -(-n // (256 if n > 128 else 128))
-    split = sk.fwd_workspace_bytes(rag, True)
-    assert sk.fwd_loss_workspace_bytes(rag, True) == (split + 255) // 256 * 256 + 8 * slots
+    # ragged: the largest split region of any element on its own, then
+    # consecutive partials.  An element with a key split: one partial per
+    # 256 merged rows; an unsplit one runs in a grouped launch whose range
+    # for it is its workgroups rounded up to a multiple of 8.  When the
+    # unsplit 128-row workgroups of the elements (decode-shaped ones aside)
+    # reach 2 per CU, those elements run unsplit; else each takes its own plan.
+    cus = 256  # no device here: the library assumes the MI355X's count
+    for lens, fills in (([600, 0, 100, 9000, 20], True), ([600, 0, 100, 1000], False)):
+        rag = shape(B=len(lens), H=8, n_q=max(lens), n_k=max(lens)).set_lengths(lens, lens)
+        assert (sum(8 * -(-n // 128) for n in lens if n > 32) >= 2 * cus) == fills
+        slots = 0
+        for n in lens:
+            if n == 0:
+                continue
+            sp = 1 if fills and n > 32 else sk.fwd_plan(shape(H=8, n_q=n, n_k=n), True)
+            slots += -(-8 * n // 256) if sp > 1 else -(-8 * -(-n // (256 if n > 128 else 128)) // 8) * 8
+        split = sk.fwd_workspace_bytes(rag, True)
+        assert sk.fwd_loss_workspace_bytes(rag, True) == (split + 255) // 256 * 256 + 8 * slots
     with pytest.raises(ValueError):
         sk.fwd_loss_workspace_bytes(shape(n_q=0), False)
 
