@@ -82,6 +82,33 @@ __global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* __restrict__ 
   for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
+// Spans of an fp32 tensor to clear, for up to kRaggedMax batch elements:
+// element i owns `count` spans of len[i] floats, span j at base[i] +
+// j * stride.  Each span is cleared in chunks of `chunk` floats, one
+// workgroup per chunk (grid: count * chunks per span, elements).
+struct SpanTable {
+  int n;
+  int count;
+  int64_t stride;
+  int64_t chunk;
+  int64_t nchunk;  // chunks per span of the longest len
+  int64_t base[kRaggedMax];
+  int64_t len[kRaggedMax];
+};
+
+__global__ __launch_bounds__(256) void fill_spans_kernel(float* __restrict__ p, const SpanTable t, int vec) {
+  const int e = blockIdx.y;
+  const int64_t span = blockIdx.x / t.nchunk, c = blockIdx.x % t.nchunk;
+  const int64_t lo = c * t.chunk, hi = min(t.len[e], lo + t.chunk);
+  float* s = p + t.base[e] + span * t.stride;
+  if (vec) {  // lo, hi and the span's start are multiples of 4 floats, p 16-byte aligned
+    float4* s4 = reinterpret_cast<float4*>(s);
+    for (int64_t i = lo / 4 + threadIdx.x; i < hi / 4; i += 256) s4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) s[i] = 0.f;
+  }
+}
+
 // Partials of the forward for callers that cannot allocate device memory
 // (streamkl_fwd_loss_noalloc): split-K states and fused-loss sums live in
 // this array, one copy per device, held until the process ends.  Host code
@@ -382,6 +409,42 @@ streamkl_status fill_zero(float* p, int64_t n, hipStream_t s) {
   return hip_status(hipGetLastError());
 }
 
+// Clears rows [row0[b], rows) of every head of each batch element b of an
+// fp32 tensor laid out [B][heads][rows][d] (row0[b] = rows: nothing to clear).
+// The kernels of a grouped ragged launch write every row below an element's
+// length, so only the rows past it need clearing.
+streamkl_status clear_rows(float* p, int64_t heads, int64_t rows, int d, const std::vector<int64_t>& row0,
+                           hipStream_t s) {
+  const bool vec = aligned(p, 16) && d % 4 == 0;
+  SpanTable t = {};
+  t.count = (int)heads;
+  t.stride = rows * d;
+  auto flush = [&]() -> streamkl_status {
+    if (t.n == 0) return STREAMKL_OK;
+    int64_t longest = 0;
+    for (int i = 0; i < t.n; ++i) longest = std::max(longest, t.len[i]);
+    // 8192 floats per workgroup, more where the grid would pass 2^23
+    // workgroups (a launch holds fewer than 2^32 threads per dimension)
+    t.chunk = std::max<int64_t>(8192, (cdiv(longest * heads, int64_t(1) << 23) + 3) / 4 * 4);
+    t.nchunk = cdiv(longest, t.chunk);
+    hipLaunchKernelGGL(fill_spans_kernel, dim3((unsigned)(heads * t.nchunk), (unsigned)t.n), dim3(256), 0, s, p, t,
+                       vec ? 1 : 0);
+    t.n = 0;
+    return hip_status(hipGetLastError());
+  };
+  for (size_t b = 0; b < row0.size(); ++b) {
+    if (row0[b] >= rows) continue;
+    const int i = t.n++;
+    t.base[i] = ((int64_t)b * heads * rows + row0[b]) * d;
+    t.len[i] = (rows - row0[b]) * d;
+    if (t.n == kRaggedMax) {
+      const streamkl_status st = flush();
+      if (st != STREAMKL_OK) return st;
+    }
+  }
+  return flush();
+}
+
 // dK of a model whose key heads are shared is summed with atomics: clear it
 // first.  ds: its head dim, g: query heads per key head, ks: key rows per
 // head in memory.
@@ -429,10 +492,11 @@ struct RaggedLaunch {
   int64_t grid = 0;
 };
 
-// Grouping needs every workgroup index of a launch to fit an int; beyond
-// that (far past any batch that fits in memory) elements run on their own.
+// A grouped launch holds at most the padded batch's workgroups plus 7 per
+// element; kept below 2^22 so that its threads (at most 512 per workgroup)
+// stay below the 2^32 a launch allows.  Beyond that elements run on their own.
 bool groupable(const streamkl_shape* s) {
-  constexpr int64_t kMaxWg = int64_t(1) << 30;
+  constexpr int64_t kMaxWg = int64_t(1) << 22;
   return ragged(s) && s->B * s->H * (cdiv(std::max(s->n_q, s->n_k), 128) + 1) <= kMaxWg;
 }
 
@@ -1043,18 +1107,31 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
   // launches of the separate-mode kernels or each as a problem of its own
   const int ds = setting == 1 ? shape->d2 : shape->d1;
   const int64_t kvs = kv_heads(shape, setting == 1 ? 2 : 1);
-  if (need_dq) st = fill_zero(dQ, shape->B * shape->H * shape->n_q * (int64_t)ds, s);
-  if (st == STREAMKL_OK && need_dk) st = fill_zero(dK, shape->B * kvs * shape->n_k * (int64_t)ds, s);
-  if (st != STREAMKL_OK) return st;
+  const bool shared = (setting == 1 ? group2(shape) : group1(shape)) > 1;
   const bool group = group_bwd(shape, causal, setting, launch, dev.cus);
+  // grouped elements: the kernels write every row below the element's
+  // lengths (dK of shared key heads aside, summed by atomics), so only the
+  // rows past them are cleared; other elements are cleared whole
+  std::vector<int64_t> together, q0((size_t)shape->B, 0), k0((size_t)shape->B, 0);
+  for (int64_t b = 0; b < shape->B; ++b) {
+    const streamkl_shape e = element_shape(shape, b);
+    if (e.n_q > 0 && group && (req != STREAMKL_BWD_AUTO || !decode_shape(&e))) {
+      together.push_back(b);
+      q0[b] = e.n_q;
+      k0[b] = shared ? 0 : e.n_k;
+    }
+  }
+  if (need_dq) st = clear_rows(dQ, shape->H, shape->n_q, ds, q0, s);
+  if (st == STREAMKL_OK && need_dk) st = clear_rows(dK, kvs, shape->n_k, ds, k0, s);
+  if (st != STREAMKL_OK) return st;
   const int64_t es = shape->dtype == STREAMKL_BF16 ? 2 : 4;
   const int64_t qr = shape->H * shape->n_q, k1r = kv_heads(shape, 1) * shape->n_k, k2r = kv_heads(shape, 2) * shape->n_k;
-  std::vector<int64_t> together;
+  size_t next = 0;  // the next grouped element
   for (int64_t b = 0; b < shape->B; ++b) {
     const streamkl_shape e = element_shape(shape, b);
     if (e.n_q == 0) continue;
-    if (group && (req != STREAMKL_BWD_AUTO || !decode_shape(&e))) {
-      together.push_back(b);
+    if (next < together.size() && together[next] == b) {
+      ++next;
       continue;
     }
     st = bwd_launch(setting, elem(Q1, b, qr, es * e.d1), elem(K1, b, k1r, es * e.d1), elem(Q2, b, qr, es * e.d2),
@@ -1101,6 +1178,30 @@ streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q
     return joint_launch(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ1, dK1, dQ2, dK2, shape,
                         shape->n_q, shape->n_k, mode, s);
   const int64_t kv1 = kv_heads(shape, 1), kv2 = kv_heads(shape, 2);
+  if (groupable(shape)) {
+    // every non-empty element in grouped launches: only the rows past its
+    // lengths are cleared (dK of shared key heads whole: summed by atomics)
+    std::vector<int64_t> els, q0((size_t)shape->B, 0), k01((size_t)shape->B, 0), k02((size_t)shape->B, 0);
+    for (int64_t b = 0; b < shape->B; ++b) {
+      const streamkl_shape e = element_shape(shape, b);
+      if (e.n_q == 0) continue;
+      els.push_back(b);
+      q0[b] = e.n_q;
+      k01[b] = group1(shape) > 1 ? 0 : e.n_k;
+      k02[b] = group2(shape) > 1 ? 0 : e.n_k;
+    }
+    if (need_dq) {
+      st = clear_rows(dQ1, shape->H, shape->n_q, shape->d1, q0, s);
+      if (st == STREAMKL_OK) st = clear_rows(dQ2, shape->H, shape->n_q, shape->d2, q0, s);
+    }
+    if (st == STREAMKL_OK && need_dk) {
+      st = clear_rows(dK1, kv1, shape->n_k, shape->d1, k01, s);
+      if (st == STREAMKL_OK) st = clear_rows(dK2, kv2, shape->n_k, shape->d2, k02, s);
+    }
+    if (st != STREAMKL_OK || els.empty()) return st;
+    return joint_group(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ1, dK1, dQ2, dK2, shape, els,
+                       mode, s);
+  }
   const int64_t BHQ = shape->B * shape->H * shape->n_q;
   if (need_dq) {
     st = fill_zero(dQ1, BHQ * shape->d1, s);
@@ -1111,14 +1212,6 @@ streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q
     if (st == STREAMKL_OK) st = fill_zero(dK2, shape->B * kv2 * shape->n_k * shape->d2, s);
   }
   if (st != STREAMKL_OK) return st;
-  if (groupable(shape)) {  // every non-empty element in grouped launches
-    std::vector<int64_t> els;
-    for (int64_t b = 0; b < shape->B; ++b)
-      if (element_shape(shape, b).n_q > 0) els.push_back(b);
-    return els.empty() ? STREAMKL_OK
-                       : joint_group(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ1, dK1, dQ2, dK2,
-                                     shape, els, mode, s);
-  }
   const int64_t es = 2;
   const int64_t qr = shape->H * shape->n_q, k1r = kv1 * shape->n_k, k2r = kv2 * shape->n_k;
   const int d1 = shape->d1, d2 = shape->d2;
