@@ -107,3 +107,27 @@ def test_captured_grouped_heads_backward(cuda_device):
         return kl, dq, dk
 
     _replays(w, step, (q1, k1, q2, k2, g), exact=(True, True, False), rtol=1e-5)
+
+
+def test_captured_ragged_grouped_step(cuda_device):
+    # 70 short sequences: the forward and both backward settings run as
+    # grouped launches over tables of up to 64 elements, and the padded rows
+    # are cleared by the span-fill kernel
+    import numpy as np
+    r = np.random.default_rng(12)
+    lens = [0 if i % 9 == 8 else int(r.integers(40, 600)) for i in range(70)]
+    n = max(lens)
+    w = workloads.Workload("graph-ragged", len(lens), 8, n, n, 128, 128, "bf16", True, 0.5, False, 6)
+    print(w.name, flush=True)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    weights = torch.rand((w.B, w.H, w.n_q), device=cuda_device)
+    lk = dict(q_len=lens, k_len=lens)
+
+    def step():
+        kl, l1, l2, loss = sk.streamkl_fwd_loss(q1, k1, q2, k2, True, weights, **lk)
+        dq, dk = sk.streamkl_bwd(1, q1, k1, q2, k2, True, kl, l1, l2, g, bwd_mode=sk.BWD_SEPARATE, **lk)
+        dq1, dk1, dq2, dk2 = sk.streamkl_bwd_joint(q1, k1, q2, k2, True, kl, l1, l2, g, **lk)
+        return kl, l1, l2, loss, dq, dk, dq1, dk1, dq2, dk2
+
+    _replays(w, step, (q1, k1, q2, k2, g), exact=(True,) * 10)
