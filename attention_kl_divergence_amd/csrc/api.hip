@@ -886,7 +886,7 @@ streamkl_status bwd_launch(int setting, const void* Q1, const void* K1, const vo
     if (st != STREAMKL_OK) return st;
     if (fd) {
       a.nblk = plan_dec_bwd_splits(shape, dev.cus);
-      return hip_status(fd(a, setting, a.BH * a.nblk, s));
+      return hip_status(fd(a, setting, a.BH * a.nblk, s, nullptr));
     }
     a.nblk = (int)nkb;
     return hip_status(fk(a, setting, true, a.BH * nkb, s, nullptr));
@@ -984,6 +984,35 @@ streamkl_status bwd_group(int setting, const void* Q1, const void* K1, const voi
   for (const RaggedLaunch& L :
        ragged_launches(shape, causal, els, [](const streamkl_shape& e) { return cdiv(e.n_q, kBwdQRows); })) {
     const streamkl_status st = hip_status(fq(a, setting, L.grid, s, &L.t));
+    if (st != STREAMKL_OK) return st;
+  }
+  return STREAMKL_OK;
+}
+
+// The decode backward over decode-shaped elements `els` of a ragged batch in
+// grouped launches (validated, bf16; dQ rows of these elements cleared whole,
+// since the kernel adds to them, dK past each element's key length, or whole
+// where key heads are shared).  One workgroup per CU in all, as for a single
+// problem: an element gets workgroups per head in proportion to its key
+// tiles, at least one and at most one per tile.
+streamkl_status dec_bwd_group(int setting, const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                              float scale1, float scale2, const float* kl, const float* lse1, const float* lse2,
+                              const float* d_kl, float* dQ, float* dK, const streamkl_shape* shape,
+                              const std::vector<int64_t>& els, int cus, hipStream_t s) {
+  const DecBwdLaunch fd = pick_dec_bwd(shape->dtype, shape->d1, shape->d2);
+  if (!fd) return STREAMKL_ERR_UNSUPPORTED;
+  BwdArgs a = bwd_args(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, shape, shape->n_q, shape->n_k);
+  a.dq = dQ; a.dk = dK;
+  a.scale_s = setting == 1 ? plain_scale(scale2, shape->d2) : plain_scale(scale1, shape->d1);
+  double tiles = 0;  // key tiles of all heads of these elements
+  for (int64_t b : els) tiles += (double)shape->H * cdiv(element_shape(shape, b).n_k, kDecBwdTile);
+  auto blocks = [&](const streamkl_shape& e) {
+    const int64_t t = cdiv(e.n_k, kDecBwdTile);
+    const int64_t sp = (int64_t)((double)cus * t / tiles);
+    return std::max<int64_t>(1, std::min(sp, t));
+  };
+  for (const RaggedLaunch& L : ragged_launches(shape, causal, els, blocks)) {
+    const streamkl_status st = hip_status(fd(a, setting, L.grid, s, &L.t));
     if (st != STREAMKL_OK) return st;
   }
   return STREAMKL_OK;
@@ -1109,16 +1138,26 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
   const int64_t kvs = kv_heads(shape, setting == 1 ? 2 : 1);
   const bool shared = (setting == 1 ? group2(shape) : group1(shape)) > 1;
   const bool group = group_bwd(shape, causal, setting, launch, dev.cus);
-  // grouped elements: the kernels write every row below the element's
-  // lengths (dK of shared key heads aside, summed by atomics), so only the
-  // rows past them are cleared; other elements are cleared whole
-  std::vector<int64_t> together, q0((size_t)shape->B, 0), k0((size_t)shape->B, 0);
+  // Grouped elements: the separate-mode kernels write every row below the
+  // element's lengths (dK of shared key heads aside, summed by atomics), so
+  // only the rows past them are cleared.  Decode-shaped elements in the
+  // fused (or automatic) mode run the decode backward grouped: it adds to
+  // dQ, whose rows are cleared whole, and writes dK.  Other elements run on
+  // their own and are cleared whole.
+  const bool group_dec = groupable(shape) && (req == STREAMKL_BWD_AUTO || req == STREAMKL_BWD_FUSED);
+  std::vector<int64_t> together, dec, single, q0((size_t)shape->B, 0), k0((size_t)shape->B, 0);
   for (int64_t b = 0; b < shape->B; ++b) {
     const streamkl_shape e = element_shape(shape, b);
-    if (e.n_q > 0 && group && (req != STREAMKL_BWD_AUTO || !decode_shape(&e))) {
+    if (e.n_q == 0) continue;
+    if (group && (req != STREAMKL_BWD_AUTO || !decode_shape(&e))) {
       together.push_back(b);
       q0[b] = e.n_q;
       k0[b] = shared ? 0 : e.n_k;
+    } else if (group_dec && decode_shape(&e)) {
+      dec.push_back(b);
+      k0[b] = shared ? 0 : e.n_k;
+    } else {
+      single.push_back(b);
     }
   }
   if (need_dq) st = clear_rows(dQ, shape->H, shape->n_q, ds, q0, s);
@@ -1126,18 +1165,17 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
   if (st != STREAMKL_OK) return st;
   const int64_t es = shape->dtype == STREAMKL_BF16 ? 2 : 4;
   const int64_t qr = shape->H * shape->n_q, k1r = kv_heads(shape, 1) * shape->n_k, k2r = kv_heads(shape, 2) * shape->n_k;
-  size_t next = 0;  // the next grouped element
-  for (int64_t b = 0; b < shape->B; ++b) {
+  for (const int64_t b : single) {
     const streamkl_shape e = element_shape(shape, b);
-    if (e.n_q == 0) continue;
-    if (next < together.size() && together[next] == b) {
-      ++next;
-      continue;
-    }
     st = bwd_launch(setting, elem(Q1, b, qr, es * e.d1), elem(K1, b, k1r, es * e.d1), elem(Q2, b, qr, es * e.d2),
                     elem(K2, b, k2r, es * e.d2), causal, scale1, scale2, elem(kl, b, qr, 4), elem(lse1, b, qr, 4),
                     elem(lse2, b, qr, 4), elem(d_kl, b, qr, 4), elem(dQ, b, qr, 4 * ds),
                     elem(dK, b, kvs * shape->n_k, 4 * ds), &e, shape->n_q, shape->n_k, launch, dev, s);
+    if (st != STREAMKL_OK) return st;
+  }
+  if (!dec.empty()) {
+    st = dec_bwd_group(setting, Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ, dK, shape, dec,
+                       dev.cus, s);
     if (st != STREAMKL_OK) return st;
   }
   if (together.empty()) return STREAMKL_OK;

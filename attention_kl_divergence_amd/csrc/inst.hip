@@ -118,15 +118,18 @@ hipError_t SKL_CAT(launch_bwd_dk, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int 
 }
 
 hipError_t SKL_CAT(launch_bwd_dec, SKL_TN, SKL_D1, SKL_D2)(const BwdArgs& a, int setting, int64_t nblocks,
-                                                            hipStream_t st) {
+                                                            hipStream_t st, const RaggedTable* rt) {
   if constexpr (sizeof(SKL_T) != 2) {
     return hipErrorInvalidValue;  // bf16 only
   } else {
-    if (setting == 1)
-      hipLaunchKernelGGL((bwd_decode_kernel<SKL_D1, SKL_D2, 1>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((bwd_decode_kernel<SKL_D1, SKL_D2, 2>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
-    return hipGetLastError();
+    auto go = [&](const auto& t) {
+      using RT = std::decay_t<decltype(t)>;
+      const dim3 g((unsigned)nblocks), b(256);
+      if (setting == 1) hipLaunchKernelGGL((bwd_decode_kernel<SKL_D1, SKL_D2, 1, RT>), g, b, 0, st, a, t);
+      else hipLaunchKernelGGL((bwd_decode_kernel<SKL_D1, SKL_D2, 2, RT>), g, b, 0, st, a, t);
+      return hipGetLastError();
+    };
+    return rt ? go(*rt) : go(NoTable{});
   }
 }
 

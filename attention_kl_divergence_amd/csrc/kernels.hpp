@@ -1724,8 +1724,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a, const RT rt)
 //                          [query][key] with the transpose read, B = Q_s
 //                          columns, held in registers for the whole kernel
 // K1 and K2 tiles (32 keys per wave) are double-buffered in LDS.
-template <int D1, int D2, int SETTING>
-__global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
+template <int D1, int D2, int SETTING, typename RT = NoTable>
+__global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a, const RT rt) {
   using MF = Mfma<bf16>;
   constexpr int NW = 4, BK = 32 * NW;
   constexpr int DS = SETTING == 1 ? D2 : D1;
@@ -1743,8 +1743,20 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a) {
   const int col = lane & 31, grp = lane >> 5;
   bf16* sdS = lds + 2 * TS + QE + wave * DSE;
   float* kbar = reinterpret_cast<float*>(lds + 2 * TS + QE + NW * DSE);
-  const int64_t bh = blockIdx.x / a.nblk;
-  const int z = (int)(blockIdx.x % a.nblk);
+  int64_t lin = blockIdx.x, head0 = 0;
+  if constexpr (kRagged<RT>) {  // one element of a ragged batch
+    const RaggedItem r = ragged_item(rt, lin);
+    if (r.pad) return;
+    lin = r.lin;
+    head0 = r.head0;
+    a.n_q = r.n_q;
+    a.n_k = r.n_k;
+    a.nblk = r.nblk;
+  }
+  // 32-bit division: the grid and every element's range hold fewer than 2^31 workgroups
+  const unsigned lw = (unsigned)lin, nb = (unsigned)a.nblk;
+  const int64_t bh = head0 + lw / nb;
+  const int z = (int)(lw % nb);
   const int off = a.n_k - a.n_q;
 
   const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.qs * D1;

@@ -31,11 +31,12 @@ constexpr int kDecBwdTile = 128;  // key rows per tile of the decode backward (4
 template <typename T> constexpr int kBwdQTile = sizeof(T) == 2 ? 64 : 32;
 
 // The forward and the single-setting backward launchers take an optional
-// ragged-batch table (NULL: a plain launch); the decode kernels do not.
+// ragged-batch table (NULL: a plain launch), as does the decode backward;
+// the decode forward does not.
 using FwdLaunch = hipError_t (*)(const FwdArgs&, int64_t, hipStream_t, const RaggedTable*);
 using DqLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t, const RaggedTable*);
 using DkLaunch = hipError_t (*)(const BwdArgs&, int, bool, int64_t, hipStream_t, const RaggedTable*);
-using DecBwdLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t);
+using DecBwdLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t, const RaggedTable*);
 
 #define SKL_DECL(tn, d1, d2)                                                                                  \
   hipError_t launch_fwd_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t, const RaggedTable*);         \
@@ -44,7 +45,7 @@ using DecBwdLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t);
   hipError_t launch_bwd_dq_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t, const RaggedTable*); \
   hipError_t launch_bwd_dk_##tn##_##d1##_##d2(const BwdArgs&, int, bool, int64_t, hipStream_t,                \
                                              const RaggedTable*);                                             \
-  hipError_t launch_bwd_dec_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t);
+  hipError_t launch_bwd_dec_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t, const RaggedTable*);
 SKL_DECL(f32, 64, 64)
 SKL_DECL(f32, 64, 128)
 SKL_DECL(f32, 128, 64)

@@ -140,3 +140,89 @@ def test_many_short_sequences(case, cuda_device):
                 check_grad(f"{w.name} b{b} s{s} auto h{h} dQ", dq[b, h, :nq], ref_dq[(s, h)])
             for kh in range(ref_dk[s].shape[0]):
                 check_grad(f"{w.name} b{b} s{s} auto kh{kh} dK", dk[b, kh, :nk], ref_dk[s][kh])
+
+
+DEC_CASES = [
+    # name, d1, d2, causal, H, kv1, kv2, B, seed
+    ("dec-bf16-nc-d128-b70", 128, 128, False, 8, 8, 8, 70, 4),
+    ("dec-bf16-c-d128x64-gqa-b66", 128, 64, True, 8, 4, 2, 66, 5),
+]
+
+
+@pytest.mark.parametrize("case", DEC_CASES, ids=[c[0] for c in DEC_CASES])
+def test_many_decode_sequences(case, cuda_device):
+    """Batches of decode-shaped sequences (at most 32 query rows against key
+    ranges of up to 3000 rows): the automatic backward runs the decode
+    backward over all of them in grouped launches.  Per sequence, dK equals
+    the sequence's own call on its trimmed tensors bitwise (a key tile's dK is
+    formed by one workgroup whatever the split count), except for shared key
+    heads (atomics); dQ, added by atomics over a different split, agrees to
+    fp32 rounding.  Sampled sequences are checked against the oracle."""
+    name, d1, d2, causal, H, kv1, kv2, B, seed = case
+    r = np.random.default_rng(900 + seed)
+    q_len, k_len = [], []
+    for i in range(B):
+        k = int(r.integers(33, 3000))
+        q = 0 if i % 11 == 10 else int(r.integers(1, 33))
+        q_len.append(q)
+        k_len.append(k)
+    n_q, n_k = max(q_len), max(k_len)
+    w = workloads.Workload(name, B, H, n_q, n_k, d1, d2, "bf16", causal, 0.0, True, 60 + seed)
+    q1, _, q2, _ = workloads.generate(w, cuda_device)
+    gen = torch.Generator(device=cuda_device).manual_seed(177 + seed)
+    k1 = torch.randn((B, kv1, n_k, d1), generator=gen, device=cuda_device).to(torch.bfloat16)
+    k2 = torch.randn((B, kv2, n_k, d2), generator=gen, device=cuda_device).to(torch.bfloat16)
+    g1, g2 = H // kv1, H // kv2
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    lens = dict(q_len=q_len, k_len=k_len)
+    print(f"ragged decode {name}", flush=True)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, causal, **lens)
+    grads = {s: sk.streamkl_bwd(s, q1, k1, q2, k2, causal, kl, l1, l2, g, **lens) for s in (1, 2)}
+    torch.cuda.synchronize()
+    for b in range(B):
+        nq, nk = q_len[b], k_len[b]
+        for s in (1, 2):
+            dq, dk = grads[s]
+            assert (dq[b, :, nq:] == 0).all() and (dk[b, :, nk:] == 0).all()
+            if nq == 0:
+                assert (dq[b] == 0).all() and (dk[b] == 0).all()
+        if nq == 0:
+            continue
+        t = [x[b:b + 1, :, :n].contiguous() for x, n in ((q1, nq), (k1, nk), (q2, nq), (k2, nk))]
+        gt = g[b:b + 1, :, :nq].contiguous()
+        rkl, rl1, rl2 = sk.streamkl_fwd(*t, causal)
+        assert torch.equal(kl[b:b + 1, :, :nq], rkl), f"{name} b{b}: KL differs from the element alone"
+        for s in (1, 2):
+            rdq, rdk = sk.streamkl_bwd(s, *t, causal, rkl, rl1, rl2, gt)
+            dq, dk = grads[s]
+            edq = dq[b:b + 1, :, :nq]
+            err = ((edq - rdq).norm() / rdq.norm().clamp_min(1e-30)).item()
+            assert err <= 1e-5, f"{name} b{b} s{s}: dQ relative L2 {err:.3e} against the element alone"
+            if (g2 if s == 1 else g1) == 1:
+                assert torch.equal(dk[b:b + 1, :, :nk], rdk), f"{name} b{b} s{s}: dK differs from the element alone"
+            else:
+                torch.testing.assert_close(dk[b:b + 1, :, :nk], rdk, rtol=1e-5, atol=1e-6 * rdk.abs().max().item())
+    torch.cuda.synchronize()
+    kl_n, l1n, l2n, gn = to_np(kl), to_np(l1), to_np(l2), to_np(g)
+    auto = {s: [to_np(t) for t in grads[s]] for s in (1, 2)}
+    for b in (0, int(np.argmax(k_len))):
+        nq, nk = q_len[b], k_len[b]
+        if nq == 0:
+            continue
+        ref_dk = {1: np.zeros((kv2, nk, d2)), 2: np.zeros((kv1, nk, d1))}
+        ref_dq = {}
+        for h in range(H):
+            hi = [to_np(q1[b, h, :nq]), to_np(k1[b, h // g1, :nk]), to_np(q2[b, h, :nq]), to_np(k2[b, h // g2, :nk])]
+            ref = oracle.head_forward(*hi, causal)
+            check_forward_rows(f"{name} b{b}h{h}", kl_n[b, h, :nq], l1n[b, h, :nq], l2n[b, h, :nq], ref,
+                               torch.bfloat16)
+            for s in (1, 2):
+                rdq, rdk = oracle.head_backward(s, *hi, causal, gn[b, h, :nq])
+                ref_dq[(s, h)] = rdq
+                ref_dk[s][h // (g2 if s == 1 else g1)] += rdk
+        for s in (1, 2):
+            dq, dk = auto[s]
+            for h in range(H):
+                check_grad(f"{name} b{b} s{s} h{h} dQ", dq[b, h, :nq], ref_dq[(s, h)])
+            for kh in range(ref_dk[s].shape[0]):
+                check_grad(f"{name} b{b} s{s} kh{kh} dK", dk[b, kh, :nk], ref_dk[s][kh])
