@@ -15,20 +15,33 @@ namespace streamkl {
 
 // Merge of the split partial states, then the epilogue (one thread per row);
 // with the fused loss each workgroup also writes its rows' sum of w_i KL_i.
+// With a DecTable, the rows of the table's elements: 256 of one element per
+// workgroup.
+template <typename RT = NoTable>
 __global__ __launch_bounds__(256) void splitk_merge_kernel(const float* __restrict__ ws, float* kl, float* lse1,
                                                            float* lse2, int64_t BH, int n_q, int nsplit, int qs,
-                                                           const float* __restrict__ lw, double* lpart) {
+                                                           const float* __restrict__ lw, double* lpart, const RT rt) {
   __shared__ double red[4];
-  const int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x;
+  int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x;
+  int64_t rows = BH * n_q, head0 = 0, base = 0, fs = BH * (int64_t)nsplit * n_q;
+  if constexpr (kDecTable<RT>) {
+    const int e = table_elem(rt.mstart, rt.n, blockIdx.x);
+    i = (blockIdx.x - rt.mstart[e]) * (int64_t)256 + threadIdx.x;
+    n_q = rt.n_q[e];
+    nsplit = rt.nsplit[e];
+    rows = (int64_t)rt.H * n_q;
+    head0 = (int64_t)rt.b[e] * rt.H;
+    base = rt.wsb[e];
+    fs = rt.fs;
+  }
   double lv = 0.0;
-  if (i < BH * n_q) {
-    const int64_t bh = i / n_q;
+  if (i < rows) {
+    const int64_t loc = i / n_q;  // the head within the problem (or the element)
     const int q = (int)(i % n_q);
-    const int64_t r = bh * qs + q;  // output row (qs rows per head in memory)
-    const int64_t fs = BH * (int64_t)nsplit * n_q;
+    const int64_t r = (head0 + loc) * qs + q;  // output row (qs rows per head in memory)
     RowState st = empty_state();
     for (int z = 0; z < nsplit; ++z) {
-      const int64_t o = (bh * nsplit + z) * (int64_t)n_q + q;
+      const int64_t o = base + (loc * nsplit + z) * (int64_t)n_q + q;
       RowState p = {ws[o], ws[o + fs], ws[o + 2 * fs], ws[o + 3 * fs], ws[o + 4 * fs]};
       st = merge_state(st, p);
     }
@@ -235,7 +248,7 @@ FwdLaunch pick_fwd_pp(int dtype, int d1, int d2) {
 #undef SKL_PICK
   return nullptr;
 }
-FwdLaunch pick_fwd_dec(int dtype, int d1, int d2) {
+DecFwdLaunch pick_fwd_dec(int dtype, int d1, int d2) {
 #define SKL_PICK(tn, a, b) if (d1 == a && d2 == b) return launch_fwd_dec_##tn##_##a##_##b;
   if (dtype == STREAMKL_BF16) { SKL_PICK(bf16, 64, 64) SKL_PICK(bf16, 64, 128) SKL_PICK(bf16, 128, 64) SKL_PICK(bf16, 128, 128) }
 #undef SKL_PICK
@@ -540,27 +553,77 @@ constexpr size_t kInvalidBytes = ~(size_t)0;  // workspace queries with invalid 
 int64_t problems(const streamkl_shape* s) { return ragged(s) ? s->B : 1; }
 streamkl_shape problem(const streamkl_shape* s, int64_t b) { return ragged(s) ? element_shape(s, b) : *s; }
 
+// A grouped split-K forward of decode-shaped ragged elements: the table, the
+// decode kernel's and the merge kernel's workgroups.
+struct DecLaunch {
+  DecTable t = {};
+  int64_t grid = 0, mgrid = 0;
+};
+
+// The grouped split-K launches over decode-shaped elements `els` with their
+// split counts, at most kRaggedMax elements each, the most pairs first.
+std::vector<DecLaunch> dec_launches(const streamkl_shape* s, int causal, const std::vector<int64_t>& els,
+                                    const std::vector<int>& splits) {
+  std::vector<std::pair<double, int64_t>> order;
+  for (int64_t b : els) {
+    const streamkl_shape e = element_shape(s, b);
+    order.push_back({head_pairs(&e, causal), b});
+  }
+  std::stable_sort(order.begin(), order.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+  std::vector<DecLaunch> out;
+  for (const auto& o : order) {
+    const streamkl_shape e = element_shape(s, o.second);
+    const int ns = splits[(size_t)o.second];
+    if (out.empty() || out.back().t.n == kRaggedMax) {
+      out.emplace_back();
+      out.back().t.H = (int)s->H;
+    }
+    DecLaunch& L = out.back();
+    const int i = L.t.n++;
+    L.t.start[i] = (int)L.grid;
+    L.t.mstart[i] = (int)L.mgrid;
+    L.t.b[i] = (int)o.second;
+    L.t.n_q[i] = (int)e.n_q;
+    L.t.n_k[i] = (int)e.n_k;
+    L.t.nsplit[i] = ns;
+    L.t.wsb[i] = L.t.fs;
+    L.t.fs += s->H * (int64_t)ns * e.n_q;
+    L.grid += (s->H * cdiv(ns, 4) + 7) / 8 * 8;
+    L.mgrid += cdiv(s->H * e.n_q, 256);
+    L.t.start[i + 1] = (int)L.grid;
+    L.t.mstart[i + 1] = (int)L.mgrid;
+  }
+  return out;
+}
+
 struct FwdCall {
-  size_t split_region = 0;  // bytes of split partials: the largest of any problem (they run one after another)
+  size_t split_region = 0;  // bytes of split partials: the largest of any launch (they run one after another)
   int64_t loss_slots = 0;   // fused-loss partials of all launches (consecutive, after the split region)
   double rows = 0;          // query rows the call finalizes (the mean's divisor)
   std::vector<int64_t> single;          // problems launched on their own, in this order
   std::vector<RaggedLaunch> pp, plain;  // then the unsplit elements of a ragged batch, grouped by forward kernel
+  std::vector<DecLaunch> dec;           // then its split decode-shaped elements, grouped
 };
 
 // The launches of a forward call with the given split counts and the
 // workspace they need.  Loss slots are numbered in launch order: the single
-// problems, then the grouped ping-pong launches, then the grouped 4-wave ones.
-FwdCall summarize(const streamkl_shape* s, int causal, const std::vector<int>& splits) {
+// problems, the grouped ping-pong launches, the grouped 4-wave ones, then
+// the merges of the grouped decode launches.  group_dec = false: split
+// decode-shaped elements run on their own.
+FwdCall summarize(const streamkl_shape* s, int causal, const std::vector<int>& splits, bool group_dec = true) {
   FwdCall c;
   const bool group = groupable(s);
-  std::vector<int64_t> pp, plain;
+  std::vector<int64_t> pp, plain, dec;
   for (int64_t b = 0; b < problems(s); ++b) {
     const streamkl_shape e = problem(s, b);
     if (e.n_q == 0) continue;
     c.rows += (double)(e.B * e.H * e.n_q);
     if (group && splits[b] == 1) {
       (e.n_q > kFwdRows ? pp : plain).push_back(b);
+      continue;
+    }
+    if (group && group_dec && decode_shape(&e)) {
+      dec.push_back(b);
       continue;
     }
     const FwdPlan p = make_fwd_plan(&e, splits[b]);
@@ -570,8 +633,13 @@ FwdCall summarize(const streamkl_shape* s, int causal, const std::vector<int>& s
   }
   c.pp = ragged_launches(s, causal, pp, [](const streamkl_shape& e) { return cdiv(e.n_q, kFwdPPRows); });
   c.plain = ragged_launches(s, causal, plain, [](const streamkl_shape& e) { return cdiv(e.n_q, kFwdRows); });
+  c.dec = dec_launches(s, causal, dec, splits);
   for (const auto* v : {&c.pp, &c.plain})
     for (const RaggedLaunch& L : *v) c.loss_slots += L.grid;
+  for (const DecLaunch& L : c.dec) {
+    c.split_region = std::max(c.split_region, (size_t)20 * (size_t)L.t.fs);
+    c.loss_slots += L.mgrid;
+  }
   return c;
 }
 
@@ -579,23 +647,43 @@ size_t loss_base(const FwdCall& c) { return round256(c.split_region); }
 size_t loss_call_bytes(const FwdCall& c) { return loss_base(c) + 8 * (size_t)c.loss_slots; }
 
 // The split count of every problem (0 for empty ones) as the plan asks, or
-// one split.  A ragged batch whose elements (decode-shaped ones aside) fill
-// the chip without splits in one grouped launch runs them unsplit; the plan
-// of an element alone would split a short one.
-std::vector<int> planned_splits(const streamkl_shape* s, int causal, const streamkl_launch* l, int cus, bool one) {
+// one split.  In a ragged batch that can be grouped (automatic split counts):
+// - when the elements other than decode-shaped ones fill the chip without
+//   splits in grouped launches, they run unsplit (the plan of an element
+//   alone would split a short one);
+// - with group_dec, the decode-shaped elements share one split-K launch, with
+//   about 64 key blocks (2048 keys) per split, in whole workgroups of 4
+//   splits, and at least 8 key blocks per split.  Many short splits, longest
+//   elements first, measured faster than a plan that shares out about 4 waves
+//   per CU (all resident, one sweep) as for a single problem: the waves of the
+//   long elements then outlast the rest.
+std::vector<int> planned_splits(const streamkl_shape* s, int causal, const streamkl_launch* l, int cus, bool one,
+                                bool group_dec = true) {
   std::vector<int> sp((size_t)problems(s), 0);
   bool fills = false;
+  bool dec = false;  // decode-shaped elements to group
   if (groupable(s) && !(l && l->num_splits > 0)) {
     int64_t wg = 0;  // unsplit workgroups of the 4-wave kernel, the measure plan_splits uses
     for (int64_t b = 0; b < s->B; ++b) {
       const streamkl_shape e = element_shape(s, b);
-      if (e.n_q > 0 && !decode_shape(&e)) wg += e.H * cdiv(e.n_q, kFwdRows);
+      if (e.n_q == 0) continue;
+      if (!decode_shape(&e)) wg += e.H * cdiv(e.n_q, kFwdRows);
+      else dec = group_dec;
     }
     fills = wg >= 2 * (int64_t)cus;
   }
+  auto dec_splits = [&](const streamkl_shape& e) {
+    const int64_t blocks = cdiv(e.n_k, kDecBlock);
+    const int64_t n = (cdiv(blocks, 64) + 3) / 4 * 4;
+    return (int)std::min<int64_t>(std::min<int64_t>(n, std::max<int64_t>(1, blocks / 8)), 4096);
+  };
   for (int64_t b = 0; b < problems(s); ++b) {
     const streamkl_shape e = problem(s, b);
-    if (e.n_q > 0) sp[b] = one || (fills && !decode_shape(&e)) ? 1 : plan_splits(&e, causal, l, cus);
+    if (e.n_q == 0) continue;
+    if (one) sp[b] = 1;
+    else if (dec && decode_shape(&e)) sp[b] = dec_splits(e);
+    else if (fills && !decode_shape(&e)) sp[b] = 1;
+    else sp[b] = plan_splits(&e, causal, l, cus);
   }
   return sp;
 }
@@ -608,17 +696,24 @@ size_t call_bytes(const streamkl_shape* s, int causal, const streamkl_launch* l,
 }
 
 // The split count of every problem given the workspace the caller offers
-// (`avail` bytes at `ws`), decided before anything is enqueued.  Without
-// the loss, a problem whose split partials do not fit falls back to one
-// split (auto) or fails (explicit split count); with the loss, the whole
-// call falls back to one split when both kinds of partials do not fit, and
-// fails if the loss partials alone do not fit.
+// (`avail` bytes at `ws`), decided before anything is enqueued.  Split
+// decode-shaped elements of a ragged batch run grouped when all their
+// partials fit, else each on its own plan, one after another.  Without the
+// loss, a problem whose split partials do not fit falls back to one split
+// (auto) or fails (explicit split count); with the loss, the whole call falls
+// back to one split when both kinds of partials do not fit, and fails if the
+// loss partials alone do not fit.
 streamkl_status plan_call(const streamkl_shape* s, int causal, const streamkl_launch* l, int cus, bool loss,
                           const void* ws, size_t avail, std::vector<int>& splits, FwdCall& c) {
   const bool expl = l && l->num_splits > 1;
   splits = planned_splits(s, causal, l, cus, false);
+  c = summarize(s, causal, splits);
   if (!loss) {
     const bool usable = ws && aligned(ws, 4);
+    if (!c.dec.empty()) {
+      if (usable && c.split_region <= avail) return STREAMKL_OK;
+      splits = planned_splits(s, causal, l, cus, false, false);
+    }
     for (int64_t b = 0; b < problems(s); ++b) {
       if (splits[b] <= 1) continue;
       const streamkl_shape e = problem(s, b);
@@ -626,12 +721,16 @@ streamkl_status plan_call(const streamkl_shape* s, int causal, const streamkl_la
       if (expl) return STREAMKL_ERR_WORKSPACE;
       splits[b] = 1;
     }
-    c = summarize(s, causal, splits);
+    c = summarize(s, causal, splits, false);
     return STREAMKL_OK;
   }
   if (!ws || !aligned(ws, 16)) return STREAMKL_ERR_WORKSPACE;
-  c = summarize(s, causal, splits);
   if (loss_call_bytes(c) <= avail) return STREAMKL_OK;
+  if (!c.dec.empty()) {
+    splits = planned_splits(s, causal, l, cus, false, false);
+    c = summarize(s, causal, splits, false);
+    if (loss_call_bytes(c) <= avail) return STREAMKL_OK;
+  }
   if (expl) return STREAMKL_ERR_WORKSPACE;
   splits = planned_splits(s, causal, l, cus, true);
   c = summarize(s, causal, splits);
@@ -735,10 +834,11 @@ streamkl_status fwd_launch(const void* Q1, const void* K1, const void* Q2, const
                            hipStream_t s) {
   // Without a key split, long query ranges use the 8-wave ping-pong kernel;
   // split short bf16 query ranges use the decode kernel.
-  FwdLaunch fn = p.dec  ? pick_fwd_dec(shape->dtype, shape->d1, shape->d2)
-                 : p.pp ? pick_fwd_pp(shape->dtype, shape->d1, shape->d2)
-                        : pick_fwd(shape->dtype, shape->d1, shape->d2);
-  if (!fn) return STREAMKL_ERR_UNSUPPORTED;
+  const DecFwdLaunch fd = p.dec ? pick_fwd_dec(shape->dtype, shape->d1, shape->d2) : nullptr;
+  const FwdLaunch fn = p.dec ? nullptr
+                       : p.pp ? pick_fwd_pp(shape->dtype, shape->d1, shape->d2)
+                              : pick_fwd(shape->dtype, shape->d1, shape->d2);
+  if (!fn && !fd) return STREAMKL_ERR_UNSUPPORTED;
 
   FwdArgs a = fwd_args(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, qs, ks, lw);
   a.ws = p.splits > 1 ? ws : nullptr;
@@ -747,11 +847,32 @@ streamkl_status fwd_launch(const void* Q1, const void* K1, const void* Q2, const
   const int unit = p.dec ? kDecBlock : kFwdTile;
   a.keys_per_split = (int)(cdiv(cdiv(shape->n_k, unit), p.splits) * unit);
   a.nqb = (int)p.nqb;
-  streamkl_status st = hip_status(fn(a, p.grid, s, nullptr));
+  streamkl_status st = hip_status(fd ? fd(a, p.grid, s, nullptr) : fn(a, p.grid, s, nullptr));
   if (st != STREAMKL_OK || p.splits == 1) return st;
   const int64_t rows = a.BH * a.n_q;
-  hipLaunchKernelGGL(splitk_merge_kernel, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, s, (const float*)a.ws,
-                     out_kl, out_lse1, out_lse2, a.BH, a.n_q, p.splits, a.qs, lw, lpart);
+  hipLaunchKernelGGL(splitk_merge_kernel<NoTable>, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, s,
+                     (const float*)a.ws, out_kl, out_lse1, out_lse2, a.BH, a.n_q, p.splits, a.qs, lw, lpart,
+                     NoTable{});
+  return hip_status(hipGetLastError());
+}
+
+// One grouped split-K forward of decode-shaped elements of a ragged batch
+// (padded tensors `shape`, whole-batch pointers): the decode kernel writes
+// the elements' split partials to `ws` as the table lays them out, then the
+// merge kernel finalizes their rows (and writes its loss partials).
+streamkl_status dec_group_launch(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
+                                 float scale1, float scale2, float* out_kl, float* out_lse1, float* out_lse2,
+                                 const streamkl_shape* shape, const DecLaunch& L, float* ws, const float* lw,
+                                 double* lpart, hipStream_t s) {
+  const DecFwdLaunch fd = pick_fwd_dec(shape->dtype, shape->d1, shape->d2);
+  if (!fd) return STREAMKL_ERR_UNSUPPORTED;
+  FwdArgs a = fwd_args(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, shape->n_q,
+                       shape->n_k, lw);
+  a.ws = ws;
+  streamkl_status st = hip_status(fd(a, L.grid, s, &L.t));
+  if (st != STREAMKL_OK) return st;
+  hipLaunchKernelGGL(splitk_merge_kernel<DecTable>, dim3((unsigned)L.mgrid), dim3(256), 0, s, (const float*)ws,
+                     out_kl, out_lse1, out_lse2, a.BH, a.n_q, 1, a.qs, lw, lpart, L.t);
   return hip_status(hipGetLastError());
 }
 
@@ -803,7 +924,9 @@ streamkl_status fwd_call(const void* Q1, const void* K1, const void* Q2, const v
                     shape->n_k, make_fwd_plan(shape, splits[0]), split_ws, weights, lpart, s);
   } else {
     // ragged batch: rows past an element's query length read 0; elements
-    // with a key split run on their own, the others in grouped launches
+    // run in grouped launches (unsplit ones by kernel, split decode-shaped
+    // ones in split-K launches) or, where a plan or the workspace asks, on
+    // their own
     const int64_t rows = shape->B * shape->H * shape->n_q;
     for (float* o : {out_kl, out_lse1, out_lse2}) {
       st = fill_zero(o, rows, s);
@@ -830,6 +953,12 @@ streamkl_status fwd_call(const void* Q1, const void* K1, const void* Q2, const v
         if (st != STREAMKL_OK) return st;
         slot += L.grid;
       }
+    }
+    for (const DecLaunch& L : c.dec) {
+      st = dec_group_launch(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, L, split_ws,
+                            weights, lpart ? lpart + slot : nullptr, s);
+      if (st != STREAMKL_OK) return st;
+      slot += L.mgrid;
     }
   }
   if (st != STREAMKL_OK || !loss) return st;

@@ -97,12 +97,13 @@ hipError_t SKL_CAT(launch_fwd_pp, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int6
 }
 
 hipError_t SKL_CAT(launch_fwd_dec, SKL_TN, SKL_D1, SKL_D2)(const FwdArgs& a, int64_t nblocks, hipStream_t st,
-                                                            const RaggedTable* rt) {
-  if (rt) return hipErrorInvalidValue;  // the decode forward runs each element on its own
+                                                            const DecTable* rt) {
   if constexpr (sizeof(SKL_T) != 2) {
     return hipErrorInvalidValue;  // bf16 only
   } else {
-    hipLaunchKernelGGL((fwd_decode_kernel<SKL_D1, SKL_D2>), dim3((unsigned)nblocks), dim3(256), 0, st, a);
+    const dim3 g((unsigned)nblocks), b(256);
+    if (rt) hipLaunchKernelGGL((fwd_decode_kernel<SKL_D1, SKL_D2, DecTable>), g, b, 0, st, a, *rt);
+    else hipLaunchKernelGGL((fwd_decode_kernel<SKL_D1, SKL_D2>), g, b, 0, st, a, NoTable{});
     return hipGetLastError();
   }
 }

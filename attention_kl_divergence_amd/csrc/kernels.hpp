@@ -201,10 +201,16 @@ struct RaggedItem {
   bool pad;       // a padding workgroup
 };
 
-__device__ __forceinline__ RaggedItem ragged_item(const RaggedTable& rt, int64_t lin) {
+// the element of a table whose range [start[e], start[e+1]) holds lin
+__device__ __forceinline__ int table_elem(const int* start, int n, int64_t lin) {
   int e = 0;
 #pragma unroll 1
-  for (int i = 1; i < rt.n; ++i) e = lin >= rt.start[i] ? i : e;
+  for (int i = 1; i < n; ++i) e = lin >= start[i] ? i : e;
+  return e;
+}
+
+__device__ __forceinline__ RaggedItem ragged_item(const RaggedTable& rt, int64_t lin) {
+  const int e = table_elem(rt.start, rt.n, lin);
   RaggedItem r;
   r.lin = lin - rt.start[e];
   r.head0 = (int64_t)rt.b[e] * rt.H;
@@ -214,6 +220,27 @@ __device__ __forceinline__ RaggedItem ragged_item(const RaggedTable& rt, int64_t
   r.pad = r.lin >= (int64_t)rt.H * r.nblk;
   return r;
 }
+
+// Decode-shaped elements of a ragged batch in one split-K forward launch and
+// one merge launch.  Element i has nsplit[i] key splits per head, 4 per
+// decode workgroup: it owns decode workgroups [start[i], start[i+1]) (its H
+// heads' workgroups, the range rounded up to a multiple of 8) and merge
+// workgroups [mstart[i], mstart[i+1]) (256 of its H n_q[i] rows each).  Its
+// split partials are rows [wsb[i], wsb[i] + H nsplit[i] n_q[i]) of each of
+// the five fields, laid out as a single problem's, fields fs rows apart.
+struct DecTable {
+  int n;
+  int H;
+  int64_t fs;
+  int start[kRaggedMax + 1];
+  int mstart[kRaggedMax + 1];
+  int b[kRaggedMax];
+  int n_q[kRaggedMax], n_k[kRaggedMax];
+  int nsplit[kRaggedMax];
+  int64_t wsb[kRaggedMax];
+};
+template <typename RT>
+constexpr bool kDecTable = std::is_same<RT, DecTable>::value;
 
 // Fused loss (the distillation objective sum_i w_i KL_i): each workgroup that
 // finalizes rows writes the sum of w_i KL_i over its rows to its own slot, in
@@ -768,8 +795,8 @@ __device__ __forceinline__ void dec_stage_q(bf16* tile, const bf16* q, int n_q, 
   }
 }
 
-template <int D1, int D2>
-__global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
+template <int D1, int D2, typename RT = NoTable>
+__global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a, const RT rt) {
   constexpr int NB = 2;  // blocks in flight per wave
   using MF = Mfma<bf16>;
   constexpr int S1 = D1 / 16, S2 = D2 / 16;
@@ -778,9 +805,27 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
   bf16* sQ2 = sq + 32 * D1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
-  const int64_t nwg = (a.nsplit + 3) / 4;
-  const int64_t bh = blockIdx.x / nwg;
-  const int z = (int)(blockIdx.x % nwg) * 4 + wave;
+  int64_t bh, loc;  // the head, and its index within the problem (or the element)
+  int z;
+  int64_t wsb = 0;  // the problem's (the element's) first partial
+  if constexpr (kDecTable<RT>) {
+    const int e = table_elem(rt.start, rt.n, blockIdx.x);
+    const int64_t lin = blockIdx.x - rt.start[e];
+    a.n_q = rt.n_q[e];
+    a.n_k = rt.n_k[e];
+    a.nsplit = rt.nsplit[e];
+    const int64_t nwg = (a.nsplit + 3) / 4;
+    if (lin >= (int64_t)rt.H * nwg) return;  // padding of the element's range
+    loc = lin / nwg;
+    bh = (int64_t)rt.b[e] * rt.H + loc;
+    z = (int)(lin % nwg) * 4 + wave;
+    wsb = rt.wsb[e];
+  } else {
+    const int64_t nwg = (a.nsplit + 3) / 4;
+    bh = blockIdx.x / nwg;
+    loc = bh;
+    z = (int)(blockIdx.x % nwg) * 4 + wave;
+  }
   const int off = a.n_k - a.n_q;
 
   const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.qs * D1;
@@ -853,8 +898,10 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a) {
 
   st = merge_state(st, shfl_xor_state(st, 32));
   if (grp == 0 && qrow < a.n_q) {
-    const int64_t fs = a.BH * (int64_t)a.nsplit * a.n_q;
-    const int64_t o = (bh * a.nsplit + z) * (int64_t)a.n_q + qrow;
+    int64_t fs;
+    if constexpr (kDecTable<RT>) fs = rt.fs;
+    else fs = a.BH * (int64_t)a.nsplit * a.n_q;
+    const int64_t o = wsb + (loc * a.nsplit + z) * (int64_t)a.n_q + qrow;
     a.ws[o] = st.M1;
     a.ws[o + fs] = st.l1;
     a.ws[o + 2 * fs] = st.A;

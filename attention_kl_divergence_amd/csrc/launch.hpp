@@ -10,6 +10,7 @@ namespace streamkl {
 struct FwdArgs;
 struct BwdArgs;
 struct RaggedTable;
+struct DecTable;
 
 constexpr int kFwdRows = 128;     // query rows per forward workgroup (4 waves x 32)
 constexpr int kFwdPPRows = 256;   // query rows per ping-pong forward workgroup (8 waves x 32)
@@ -32,8 +33,9 @@ template <typename T> constexpr int kBwdQTile = sizeof(T) == 2 ? 64 : 32;
 
 // The forward and the single-setting backward launchers take an optional
 // ragged-batch table (NULL: a plain launch), as does the decode backward;
-// the decode forward does not.
+// the decode forward takes a table with its split partials' layout.
 using FwdLaunch = hipError_t (*)(const FwdArgs&, int64_t, hipStream_t, const RaggedTable*);
+using DecFwdLaunch = hipError_t (*)(const FwdArgs&, int64_t, hipStream_t, const DecTable*);
 using DqLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t, const RaggedTable*);
 using DkLaunch = hipError_t (*)(const BwdArgs&, int, bool, int64_t, hipStream_t, const RaggedTable*);
 using DecBwdLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t, const RaggedTable*);
@@ -41,7 +43,7 @@ using DecBwdLaunch = hipError_t (*)(const BwdArgs&, int, int64_t, hipStream_t, c
 #define SKL_DECL(tn, d1, d2)                                                                                  \
   hipError_t launch_fwd_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t, const RaggedTable*);         \
   hipError_t launch_fwd_pp_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t, const RaggedTable*);      \
-  hipError_t launch_fwd_dec_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t, const RaggedTable*);     \
+  hipError_t launch_fwd_dec_##tn##_##d1##_##d2(const FwdArgs&, int64_t, hipStream_t, const DecTable*);        \
   hipError_t launch_bwd_dq_##tn##_##d1##_##d2(const BwdArgs&, int, int64_t, hipStream_t, const RaggedTable*); \
   hipError_t launch_bwd_dk_##tn##_##d1##_##d2(const BwdArgs&, int, bool, int64_t, hipStream_t,                \
                                              const RaggedTable*);                                             \

@@ -227,6 +227,27 @@ def test_loss_workspace_query():
             slots += -(-8 * n // 256) if sp > 1 else -(-8 * -(-n // (256 if n > 128 else 128)) // 8) * 8
         split = sk.fwd_workspace_bytes(rag, True)
         assert sk.fwd_loss_workspace_bytes(rag, True) == (split + 255) // 256 * 256 + 8 * slots
+    # ragged decode-shaped (bf16, at most 32 query rows) elements share one
+    # split-K launch: about 64 blocks of 32 keys per split, in multiples of 4,
+    # at least 8 blocks per split.  Their partials (20 bytes per head, split
+    # and query row) sit side by side; the merge writes one loss partial per
+    # 256 rows of each element.
+    H = 8
+    q_len, k_len = [16, 1, 0, 32, 9], [5000, 70000, 300, 12000, 200]
+    rag = shape(B=5, H=H, n_q=32, n_k=70000).set_lengths(q_len, k_len)
+    blocks = [-(-k // 32) for k in k_len]
+    part = slots = 0
+    for q, b in zip(q_len, blocks):
+        if q == 0:
+            continue
+        n = min((-(-b // 64) + 3) // 4 * 4, max(1, b // 8), 4096)
+        if n > 1:
+            part += H * n * q
+            slots += -(-H * q // 256)
+        else:  # unsplit: a grouped launch of the 4-wave forward
+            slots += -(-H * -(-q // 128) // 8) * 8
+    assert sk.fwd_workspace_bytes(rag, False) == 20 * part
+    assert sk.fwd_loss_workspace_bytes(rag, False) == (20 * part + 255) // 256 * 256 + 8 * slots
     with pytest.raises(ValueError):
         sk.fwd_loss_workspace_bytes(shape(n_q=0), False)
 

@@ -47,6 +47,20 @@ def _lengths(B, causal, seed):
     return q_len, k_len
 
 
+def _decode_splits(q_len, k_len, dtype):
+    """The key splits the library plans for the decode-shaped (bf16, at most
+    32 query rows) sequences of a ragged batch that it groups: about 64
+    blocks of 32 keys per split, in multiples of 4, at least 8 blocks per
+    split (1: unsplit).  An element's own call with this split count runs the
+    same arithmetic."""
+    out = []
+    for q, k in zip(q_len, k_len):
+        b = -(-k // 32)
+        dec = dtype == "bf16" and 0 < q <= 32
+        out.append(min((-(-b // 64) + 3) // 4 * 4, max(1, b // 8), 4096) if dec else None)
+    return out
+
+
 def _inputs(case, dev):
     name, dt, d1, d2, causal, H, kv1, kv2, B, seed = case
     ql, kln = _lengths(B, causal, seed)
@@ -81,6 +95,7 @@ def test_many_short_sequences(case, cuda_device):
     ref_loss = sum((weights[b, :, :n].double() * kl[b, :, :n].double()).sum() for b, n in enumerate(ql))
     assert abs(loss.item() - ref_loss.item()) <= 1e-5 * abs(ref_loss.item()) + 1e-6
 
+    dsplits = _decode_splits(ql, kln, w.dtype)
     for b in range(B):
         nq, nk = ql[b], kln[b]
         assert (kl[b, :, nq:] == 0).all() and (l1[b, :, nq:] == 0).all() and (l2[b, :, nq:] == 0).all()
@@ -92,9 +107,8 @@ def test_many_short_sequences(case, cuda_device):
             continue
         t = [x[b:b + 1, :, :n].contiguous() for x, n in ((q1, nq), (k1, nk), (q2, nq), (k2, nk))]
         gt = g[b:b + 1, :, :nq].contiguous()
-        # decode-shaped bf16 sequences keep their own key-split plan; the rest run unsplit
-        decode = w.dtype == "bf16" and nq <= 32
-        rkl, rl1, rl2 = sk.streamkl_fwd(*t, w.causal, num_splits=0 if decode else 1)
+        # decode-shaped bf16 sequences take the batch's split plan; the rest run unsplit
+        rkl, rl1, rl2 = sk.streamkl_fwd(*t, w.causal, num_splits=dsplits[b] or 1)
         assert torch.equal(kl[b:b + 1, :, :nq], rkl), f"{w.name} b{b}: KL differs from the element alone"
         assert torch.equal(l1[b:b + 1, :, :nq], rl1) and torch.equal(l2[b:b + 1, :, :nq], rl2)
         rj = sk.streamkl_bwd_joint(*t, w.causal, rkl, rl1, rl2, gt, bwd_mode=sk.BWD_SEPARATE)
@@ -152,8 +166,11 @@ DEC_CASES = [
 @pytest.mark.parametrize("case", DEC_CASES, ids=[c[0] for c in DEC_CASES])
 def test_many_decode_sequences(case, cuda_device):
     """Batches of decode-shaped sequences (at most 32 query rows against key
-    ranges of up to 3000 rows): the automatic backward runs the decode
-    backward over all of them in grouped launches.  Per sequence, dK equals
+    ranges of up to 3000 rows): the forward runs them in grouped split-K
+    launches (the split partials of up to 64 sequences side by side, one
+    merge launch), bitwise equal per sequence to its own call with the same
+    split count; the automatic backward runs the decode backward over all of
+    them in grouped launches.  Per sequence, dK equals
     the sequence's own call on its trimmed tensors bitwise (a key tile's dK is
     formed by one workgroup whatever the split count), except for shared key
     heads (atomics); dQ, added by atomics over a different split, agrees to
@@ -177,8 +194,14 @@ def test_many_decode_sequences(case, cuda_device):
     lens = dict(q_len=q_len, k_len=k_len)
     print(f"ragged decode {name}", flush=True)
     kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, causal, **lens)
+    weights = torch.rand((B, H, n_q), device=cuda_device)
+    lkl, _, _, loss = sk.streamkl_fwd_loss(q1, k1, q2, k2, causal, weights, **lens)
     grads = {s: sk.streamkl_bwd(s, q1, k1, q2, k2, causal, kl, l1, l2, g, **lens) for s in (1, 2)}
     torch.cuda.synchronize()
+    assert torch.equal(lkl, kl)
+    ref_loss = sum((weights[b, :, :n].double() * kl[b, :, :n].double()).sum() for b, n in enumerate(q_len))
+    assert abs(loss.item() - ref_loss.item()) <= 1e-5 * abs(ref_loss.item()) + 1e-6
+    dsplits = _decode_splits(q_len, k_len, "bf16")
     for b in range(B):
         nq, nk = q_len[b], k_len[b]
         for s in (1, 2):
@@ -190,8 +213,9 @@ def test_many_decode_sequences(case, cuda_device):
             continue
         t = [x[b:b + 1, :, :n].contiguous() for x, n in ((q1, nq), (k1, nk), (q2, nq), (k2, nk))]
         gt = g[b:b + 1, :, :nq].contiguous()
-        rkl, rl1, rl2 = sk.streamkl_fwd(*t, causal)
+        rkl, rl1, rl2 = sk.streamkl_fwd(*t, causal, num_splits=dsplits[b])
         assert torch.equal(kl[b:b + 1, :, :nq], rkl), f"{name} b{b}: KL differs from the element alone"
+        assert torch.equal(l1[b:b + 1, :, :nq], rl1) and torch.equal(l2[b:b + 1, :, :nq], rl2)
         for s in (1, 2):
             rdq, rdk = sk.streamkl_bwd(s, *t, causal, rkl, rl1, rl2, gt)
             dq, dk = grads[s]
