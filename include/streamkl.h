@@ -88,7 +88,9 @@ typedef struct {
    * 0 <= q_len[b] <= n_q, 0 <= k_len[b] <= n_k, k_len[b] >= 1 when
    * q_len[b] >= 1, and q_len[b] <= k_len[b] under a causal mask (aligned
    * bottom-right within the element).  Outputs of padded rows (KL, LSE, dQ,
-   * dK) are 0.  Read during the call only. */
+   * dK) are 0.  Read during the call only.  Elements that run the same
+   * kernel share a launch (up to 64 per launch); a grouped element computes
+   * what a call on its trimmed tensors with the same split count computes. */
   const int64_t* q_len;
   const int64_t* k_len;
 } streamkl_shape;
@@ -112,7 +114,11 @@ typedef struct {
  * summary, Method 3 (GPU kernel optimisations), partitions the key
  * dimension across thread blocks for small N_Q; each split leaves five fp32
  * partial scalars per row, so the workspace is 20 * B * H * n_q * splits
- * bytes (ragged batches: the largest of any element; they reuse it).
+ * bytes.  Ragged batches: the largest of what any launch needs, launches
+ * reusing it one after another; the split decode-shaped elements (bf16,
+ * at most 32 query rows) of one grouped launch hold their partials side by
+ * side.  A smaller workspace that still holds each element's own partials
+ * runs those elements one after another instead.
  */
 size_t streamkl_fwd_workspace_bytes(const streamkl_shape* shape, int causal,
                                     const streamkl_launch* launch);
