@@ -131,3 +131,26 @@ def test_captured_ragged_grouped_step(cuda_device):
         return kl, l1, l2, loss, dq, dk, dq1, dk1, dq2, dk2
 
     _replays(w, step, (q1, k1, q2, k2, g), exact=(True,) * 10)
+
+
+def test_captured_ragged_decode_step(cuda_device):
+    # 40 decode-shaped requests (1-32 query rows, 300-5000 keys): grouped
+    # split-K forward with its merge and the grouped decode backward
+    import numpy as np
+    r = np.random.default_rng(13)
+    q_len = [int(r.integers(1, 33)) for _ in range(40)]
+    k_len = [int(r.integers(300, 5000)) for _ in range(40)]
+    w = workloads.Workload("graph-ragged-decode", 40, 8, max(q_len), max(k_len), 128, 128, "bf16", False, 0.5,
+                           False, 7)
+    print(w.name, flush=True)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    lk = dict(q_len=q_len, k_len=k_len)
+
+    def step():
+        kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, False, **lk)
+        dq, dk = sk.streamkl_bwd(1, q1, k1, q2, k2, False, kl, l1, l2, g, **lk)
+        return kl, l1, l2, dq, dk
+
+    # the decode backward adds its dQ partials with atomics
+    _replays(w, step, (q1, k1, q2, k2, g), exact=(True, True, True, False, True), rtol=1e-5)
