@@ -513,20 +513,28 @@ bool groupable(const streamkl_shape* s) {
   return ragged(s) && s->B * s->H * (cdiv(std::max(s->n_q, s->n_k), 128) + 1) <= kMaxWg;
 }
 
-// The launches of one kernel over elements `els`; blocks(e): the kernel's
-// workgroups per head for element shape e.
-template <typename F>
-std::vector<RaggedLaunch> ragged_launches(const streamkl_shape* s, int causal, const std::vector<int64_t>& els,
-                                          F blocks) {
+// Elements `els` by query-key pairs per head, the most first, so that the
+// longest workgroups of a grouped launch start first.
+std::vector<int64_t> by_pairs(const streamkl_shape* s, int causal, const std::vector<int64_t>& els) {
   std::vector<std::pair<double, int64_t>> order;
   for (int64_t b : els) {
     const streamkl_shape e = element_shape(s, b);
     order.push_back({head_pairs(&e, causal), b});
   }
   std::stable_sort(order.begin(), order.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+  std::vector<int64_t> out;
+  for (const auto& o : order) out.push_back(o.second);
+  return out;
+}
+
+// The launches of one kernel over elements `els`; blocks(e): the kernel's
+// workgroups per head for element shape e.
+template <typename F>
+std::vector<RaggedLaunch> ragged_launches(const streamkl_shape* s, int causal, const std::vector<int64_t>& els,
+                                          F blocks) {
   std::vector<RaggedLaunch> out;
-  for (const auto& o : order) {
-    const streamkl_shape e = element_shape(s, o.second);
+  for (const int64_t b : by_pairs(s, causal, els)) {
+    const streamkl_shape e = element_shape(s, b);
     const int64_t nblk = blocks(e);
     if (out.empty() || out.back().t.n == kRaggedMax) {
       out.emplace_back();
@@ -535,7 +543,7 @@ std::vector<RaggedLaunch> ragged_launches(const streamkl_shape* s, int causal, c
     RaggedLaunch& L = out.back();
     const int i = L.t.n++;
     L.t.start[i] = (int)L.grid;
-    L.t.b[i] = (int)o.second;
+    L.t.b[i] = (int)b;
     L.t.n_q[i] = (int)e.n_q;
     L.t.n_k[i] = (int)e.n_k;
     L.t.nblk[i] = (int)nblk;
@@ -564,16 +572,10 @@ struct DecLaunch {
 // split counts, at most kRaggedMax elements each, the most pairs first.
 std::vector<DecLaunch> dec_launches(const streamkl_shape* s, int causal, const std::vector<int64_t>& els,
                                     const std::vector<int>& splits) {
-  std::vector<std::pair<double, int64_t>> order;
-  for (int64_t b : els) {
-    const streamkl_shape e = element_shape(s, b);
-    order.push_back({head_pairs(&e, causal), b});
-  }
-  std::stable_sort(order.begin(), order.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
   std::vector<DecLaunch> out;
-  for (const auto& o : order) {
-    const streamkl_shape e = element_shape(s, o.second);
-    const int ns = splits[(size_t)o.second];
+  for (const int64_t b : by_pairs(s, causal, els)) {
+    const streamkl_shape e = element_shape(s, b);
+    const int ns = splits[(size_t)b];
     if (out.empty() || out.back().t.n == kRaggedMax) {
       out.emplace_back();
       out.back().t.H = (int)s->H;
@@ -582,7 +584,7 @@ std::vector<DecLaunch> dec_launches(const streamkl_shape* s, int causal, const s
     const int i = L.t.n++;
     L.t.start[i] = (int)L.grid;
     L.t.mstart[i] = (int)L.mgrid;
-    L.t.b[i] = (int)o.second;
+    L.t.b[i] = (int)b;
     L.t.n_q[i] = (int)e.n_q;
     L.t.n_k[i] = (int)e.n_k;
     L.t.nsplit[i] = ns;
@@ -1262,7 +1264,8 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
     return bwd_launch(setting, Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ, dK, shape,
                       shape->n_q, shape->n_k, launch, dev, s);
   // ragged batch: padded rows of dQ and dK are zero; elements run in grouped
-  // launches of the separate-mode kernels or each as a problem of its own
+  // launches (separate-mode kernels, or the decode backward) or each as a
+  // problem of its own
   const int ds = setting == 1 ? shape->d2 : shape->d1;
   const int64_t kvs = kv_heads(shape, setting == 1 ? 2 : 1);
   const bool shared = (setting == 1 ? group2(shape) : group1(shape)) > 1;
