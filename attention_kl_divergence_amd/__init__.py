@@ -11,6 +11,7 @@ from .streamkl import (  # noqa: F401
     BWD_SEPARATE,
     StreamKLError,
     attention_kl,
+    attention_kl_loss,
     bwd_plan,
     bwd_workspace_bytes,
     fwd_plan,

@@ -377,6 +377,30 @@ def kl_loss(kl, weights=None, out=None):
     return out
 
 
+def _kl_input_grads(ctx, g):
+    """Gradients of sum_i g_i KL_i to Q1, K1, Q2, K2 (those that need them):
+    setting 1 for the student side, setting 2 for the teacher side, the
+    joint backward for both."""
+    q1, k1, q2, k2, kl, lse1, lse2 = ctx.saved_tensors[:7]
+    g = g.contiguous().to(torch.float32)
+    grads = [None, None, None, None]
+    teacher = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
+    student = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
+    if teacher and student:
+        dq1, dk1, dq2, dk2 = streamkl_bwd_joint(q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1,
+                                                ctx.scale2, ctx.bwd_mode, **ctx.lens)
+        return [dq1.to(q1.dtype), dk1.to(k1.dtype), dq2.to(q2.dtype), dk2.to(k2.dtype)]
+    if student:
+        dq2, dk2 = streamkl_bwd(1, q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1, ctx.scale2,
+                                ctx.bwd_mode, **ctx.lens)
+        grads[2], grads[3] = dq2.to(q2.dtype), dk2.to(k2.dtype)
+    if teacher:
+        dq1, dk1 = streamkl_bwd(2, q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1, ctx.scale2,
+                                ctx.bwd_mode, **ctx.lens)
+        grads[0], grads[1] = dq1.to(q1.dtype), dk1.to(k1.dtype)
+    return grads
+
+
 class _KLFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q1, k1, q2, k2, causal, scale1, scale2, bwd_mode, q_len, k_len):
@@ -388,25 +412,32 @@ class _KLFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, g):
-        q1, k1, q2, k2, kl, lse1, lse2 = ctx.saved_tensors
-        g = g.contiguous().to(torch.float32)
-        grads = [None, None, None, None]
-        teacher = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
-        student = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
-        if teacher and student:
-            dq1, dk1, dq2, dk2 = streamkl_bwd_joint(q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1,
-                                                    ctx.scale2, ctx.bwd_mode, **ctx.lens)
-            return (dq1.to(q1.dtype), dk1.to(k1.dtype), dq2.to(q2.dtype), dk2.to(k2.dtype),
-                    None, None, None, None, None, None)
-        if student:
-            dq2, dk2 = streamkl_bwd(1, q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1, ctx.scale2,
-                                    ctx.bwd_mode, **ctx.lens)
-            grads[2], grads[3] = dq2.to(q2.dtype), dk2.to(k2.dtype)
-        if teacher:
-            dq1, dk1 = streamkl_bwd(2, q1, k1, q2, k2, ctx.causal, kl, lse1, lse2, g, ctx.scale1, ctx.scale2,
-                                    ctx.bwd_mode, **ctx.lens)
-            grads[0], grads[1] = dq1.to(q1.dtype), dk1.to(k1.dtype)
-        return (*grads, None, None, None, None, None, None)
+        return (*_kl_input_grads(ctx, g), None, None, None, None, None, None)
+
+
+class _KLLossFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q1, k1, q2, k2, weights, causal, scale1, scale2, bwd_mode, q_len, k_len):
+        kl, lse1, lse2, loss = streamkl_fwd_loss(q1, k1, q2, k2, causal, weights, scale1, scale2,
+                                                 q_len=q_len, k_len=k_len)
+        ctx.save_for_backward(q1, k1, q2, k2, kl, lse1, lse2, weights)
+        ctx.causal, ctx.scale1, ctx.scale2, ctx.bwd_mode = causal, scale1, scale2, bwd_mode
+        ctx.lens = dict(q_len=q_len, k_len=k_len)
+        B, H, n_q = kl.shape
+        ctx.rows = H * (sum(int(x) for x in q_len) if q_len is not None else B * n_q)
+        return loss
+
+    @staticmethod
+    def backward(ctx, gl):
+        kl, weights = ctx.saved_tensors[4], ctx.saved_tensors[7]
+        gl = gl.to(torch.float32)
+        # d loss / d KL_i: w_i, or 1 / rows for the mean over the rows counted
+        if weights is not None:
+            g = weights * gl
+        else:
+            g = torch.empty_like(kl).fill_(1.0 / max(ctx.rows, 1)).mul_(gl)
+        grad_w = kl * gl if ctx.needs_input_grad[4] else None
+        return (*_kl_input_grads(ctx, g), grad_w, None, None, None, None, None, None)
 
 
 def attention_kl(q1, k1, q2, k2, causal: bool = False, scale1: float = 0.0, scale2: float = 0.0,
@@ -420,3 +451,15 @@ def attention_kl(q1, k1, q2, k2, causal: bool = False, scale1: float = 0.0, scal
     lengths of a ragged batch in padded tensors (padded rows give 0).
     """
     return _KLFunction.apply(q1, k1, q2, k2, causal, scale1, scale2, bwd_mode, q_len, k_len)
+
+
+def attention_kl_loss(q1, k1, q2, k2, causal: bool = False, weights=None, scale1: float = 0.0,
+                      scale2: float = 0.0, bwd_mode: int = BWD_AUTO, q_len=None, k_len=None):
+    """The distillation loss sum_i w_i KL_i (weights: fp32 [B, H, N_Q]), or the
+    mean KL over the query rows (ragged batches: each element's rows), as a
+    0-dim autograd tensor.  The forward forms it in its epilogue
+    (streamkl_fwd_loss: no second pass over the KL, bitwise repeatable); the
+    backward feeds d loss / d KL_i = w_i (or 1 / rows) to the kernels as
+    attention_kl does, and gives weights the gradient KL_i when they
+    require one."""
+    return _KLLossFunction.apply(q1, k1, q2, k2, weights, causal, scale1, scale2, bwd_mode, q_len, k_len)

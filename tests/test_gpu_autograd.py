@@ -77,3 +77,40 @@ def test_student_only_mean_loss(cuda_device):
         dq2, dk2 = oracle.head_backward(1, *hi, w.causal, g)
         check_grad(f"{w.name} h{h} dQ2", to_np(q2l.grad[0, h]), dq2)
         check_grad(f"{w.name} h{h} dK2", to_np(k2l.grad[0, h]), dk2)
+
+
+@pytest.mark.parametrize("ragged", [False, True], ids=["dense", "ragged"])
+def test_fused_loss_autograd_matches_unfused(ragged, cuda_device):
+    """attention_kl_loss (the loss formed in the forward's epilogue) against
+    attention_kl followed by the same reduction in PyTorch: the loss agrees
+    to fp32 rounding, and the input gradients are bitwise equal (both feed
+    the same d loss / d KL_i to the same deterministic kernels).  Weighted
+    with a gradient to the weights, and the mean over the rows (ragged:
+    each element's rows only)."""
+    B, H, n_q, n_k = 3, 2, 200, 260
+    w = workloads.Workload("loss-autograd", B, H, n_q, n_k, 128, 128, "bf16", True, 0.5, False, 21)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    lens = dict(q_len=[200, 0, 77], k_len=[260, 5, 100]) if ragged else {}
+    valid = torch.zeros((B, H, n_q), device=cuda_device)
+    for b, n in enumerate(lens.get("q_len", [n_q] * B)):
+        valid[b, :, :n] = 1.0
+    rows = valid.sum().item()
+    print(f"fused loss autograd ragged={ragged}", flush=True)
+    for weighted in (True, False):
+        wt = torch.rand((B, H, n_q), device=cuda_device) if weighted else None
+        fused = [t.clone().requires_grad_(True) for t in (q1, k1, q2, k2)]
+        plain = [t.clone().requires_grad_(True) for t in (q1, k1, q2, k2)]
+        wf = wt.clone().requires_grad_(True) if weighted else None
+        wp = wt.clone().requires_grad_(True) if weighted else None
+        loss = sk.attention_kl_loss(*fused, causal=True, weights=wf, bwd_mode=sk.BWD_SEPARATE, **lens)
+        kl = sk.attention_kl(*plain, causal=True, bwd_mode=sk.BWD_SEPARATE, **lens)
+        ref = (kl * wp).sum() if weighted else (kl * valid).sum() / rows
+        loss.backward()
+        ref.backward()
+        torch.cuda.synchronize()
+        assert loss.dim() == 0
+        assert abs(loss.item() - ref.item()) <= 1e-5 * abs(ref.item()) + 1e-7, (loss.item(), ref.item())
+        for i, (a, b) in enumerate(zip(fused, plain)):
+            assert torch.equal(a.grad, b.grad), f"weighted={weighted} input {i}: gradients differ"
+        if weighted:
+            assert torch.equal(wf.grad, wp.grad)
