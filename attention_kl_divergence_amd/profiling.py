@@ -471,6 +471,82 @@ def mode_sweep(shapes=MODE_SWEEP) -> str:
         f"{100 * max(regrets):.1f}%.", ""])
 
 
+# ragged batches for the backward plan: (label, B, H, causal, q range, k range
+# or None for k = q, seed); lengths uniform in each range
+RAGGED_SWEEP = [
+    ("short prefill", 64, 32, True, (256, 2048), None, 1),
+    ("medium prefill", 16, 32, True, (1024, 8192), None, 2),
+    ("long prefill", 4, 32, True, (8192, 32768), None, 3),
+    ("chunks vs long keys", 32, 32, False, (64, 512), (8192, 65536), 4),
+    ("few rows vs long keys", 8, 32, False, (64, 192), (32768, 65536), 5),
+    ("decode", 64, 32, False, (1, 32), (2048, 32768), 6),
+]
+
+
+def ragged_mode_sweep(batches=RAGGED_SWEEP) -> str:
+    """Markdown table: the setting-1 backward of ragged batches in the
+    automatic mode against the separate mode (grouped launches) and the
+    fused mode (decode-shaped elements grouped, the others one launch each),
+    best of 3 launches each on cuda:0."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import workloads
+    from . import streamkl as sk
+    dev = torch.device("cuda:0")
+
+    def best_ms(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    rows, regrets = [], []
+    for label, B, H, causal, qr, kr, seed in batches:
+        r = np.random.default_rng(seed)
+        q_len = [int(x) for x in r.integers(qr[0], qr[1] + 1, size=B)]
+        k_len = list(q_len) if kr is None else [int(x) for x in r.integers(kr[0], kr[1] + 1, size=B)]
+        w = workloads.Workload("ragged-modes", B, H, max(q_len), max(k_len), 128, 128, "bf16", causal, 0.5, False,
+                               7)
+        q1, k1, q2, k2 = workloads.generate(w, dev)
+        g = workloads.upstream_grad(w, dev, "mean")
+        lens = dict(q_len=q_len, k_len=k_len)
+        kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, causal, **lens)
+        t = {m: best_ms(lambda m=m: sk.streamkl_bwd(1, q1, k1, q2, k2, causal, kl, l1, l2, g, bwd_mode=m, **lens))
+             for m in (sk.BWD_AUTO, sk.BWD_SEPARATE, sk.BWD_FUSED)}
+        fast = min(t[sk.BWD_SEPARATE], t[sk.BWD_FUSED])
+        regret = t[sk.BWD_AUTO] / fast - 1.0
+        regrets.append(regret)
+        kdesc = "= N_Q" if kr is None else f"{kr[0]}-{kr[1]}"
+        rows.append(f"| {label} | {B} | {qr[0]}-{qr[1]} | {kdesc} | {'yes' if causal else 'no'} | "
+                    f"{t[sk.BWD_AUTO]:.3f} | {t[sk.BWD_SEPARATE]:.3f} | {t[sk.BWD_FUSED]:.3f} | "
+                    f"{100 * regret:+.1f}% |")
+        del q1, k1, q2, k2, g, kl, l1, l2
+        torch.cuda.empty_cache()
+    return "\n".join([
+        "# Backward mode plan on ragged batches, one MI355X", "",
+        "Command: `python -m attention_kl_divergence_amd.profiling modes --ragged "
+        "--out profiles/bwd_mode_plan_ragged.md`", "",
+        "H = 32, d1 = d2 = 128, bf16, setting 1, inputs from `workloads.generate` (seed 7), upstream",
+        "gradient 1/N_Q per row; each batch draws its lengths uniformly from the ranges shown (fixed seeds).",
+        "Automatic: the separate-mode kernels grouped over the batch when the cost model puts that at or",
+        "below each element in its own best mode, else each element on its own plan; decode-shaped elements",
+        "(at most 32 query rows) run the grouped decode backward.  Separate: every element in grouped",
+        "launches.  Fused: decode-shaped elements grouped, the others one fused launch each.  Best of 3",
+        "launches each (HIP events on the launch stream).", "",
+        "| batch | B | N_Q | N_K | causal | automatic ms | separate ms | fused ms | automatic against the faster |",
+        "|---|---|---|---|---|---|---|---|---|", *rows, "",
+        f"The largest cost of the automatic choice against the faster forced mode is {100 * max(regrets):+.1f}%.",
+        ""])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -500,9 +576,10 @@ def main(argv=None):
     pb.add_argument("--out", default=None)
     md = sub.add_parser("modes", help="fused vs separate backward over a sweep of shapes, against the plan (needs a GPU)")
     md.add_argument("--out", default=None)
+    md.add_argument("--ragged", action="store_true", help="ragged batches instead of single problems")
     args = ap.parse_args(argv)
     if args.cmd == "modes":
-        text = mode_sweep()
+        text = ragged_mode_sweep() if args.ragged else mode_sweep()
         if args.out:
             with open(args.out, "w") as fo:
                 fo.write(text)
