@@ -726,6 +726,8 @@ streamkl_status plan_call(const streamkl_shape* s, int causal, const streamkl_la
     c = summarize(s, causal, splits, false);
     return STREAMKL_OK;
   }
+  // a ragged batch of empty elements needs no workspace (its loss is 0)
+  if (loss_call_bytes(c) == 0) return STREAMKL_OK;
   if (!ws || !aligned(ws, 16)) return STREAMKL_ERR_WORKSPACE;
   if (loss_call_bytes(c) <= avail) return STREAMKL_OK;
   if (!c.dec.empty()) {
@@ -920,7 +922,7 @@ streamkl_status fwd_call(const void* Q1, const void* K1, const void* Q2, const v
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* split_ws = static_cast<float*>(ws);
-  double* lpart = loss ? reinterpret_cast<double*>(static_cast<char*>(ws) + loss_base(c)) : nullptr;
+  double* lpart = loss && ws ? reinterpret_cast<double*>(static_cast<char*>(ws) + loss_base(c)) : nullptr;
   if (!ragged(shape)) {
     st = fwd_launch(Q1, K1, Q2, K2, causal, scale1, scale2, out_kl, out_lse1, out_lse2, shape, shape->n_q,
                     shape->n_k, make_fwd_plan(shape, splits[0]), split_ws, weights, lpart, s);

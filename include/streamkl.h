@@ -167,7 +167,8 @@ streamkl_status streamkl_fwd(const void* Q1, const void* K1, const void* Q2, con
  * Significance; the preprint's abstract).  Everything streamkl_fwd does,
  * plus, when out_loss is not NULL, *out_loss = sum_i w_i KL_i over every
  * query row (weights: device fp32 [B,H,n_q], or NULL for the mean KL over
- * the rows; ragged batches count only each element's rows).  Each
+ * the rows; ragged batches count only each element's rows, and a batch of
+ * empty elements has the loss 0 and needs no workspace).  Each
  * workgroup that finalizes rows writes the sum of its rows' w_i KL_i to the
  * workspace and one small kernel adds those partials in a fixed order, so
  * the loss is bitwise repeatable and no second pass reads the KL.  The

@@ -248,6 +248,10 @@ def test_loss_workspace_query():
             slots += -(-H * -(-q // 128) // 8) * 8
     assert sk.fwd_workspace_bytes(rag, False) == 20 * part
     assert sk.fwd_loss_workspace_bytes(rag, False) == (20 * part + 255) // 256 * 256 + 8 * slots
+    # a ragged batch of empty elements needs no workspace at all
+    empty = shape(B=3, H=8, n_q=64, n_k=64).set_lengths([0, 0, 0], [5, 0, 64])
+    assert sk.fwd_workspace_bytes(empty, True) == 0
+    assert sk.fwd_loss_workspace_bytes(empty, True) == 0
     with pytest.raises(ValueError):
         sk.fwd_loss_workspace_bytes(shape(n_q=0), False)
 

@@ -130,3 +130,30 @@ def test_ragged_workload_full_size(cuda_device):
                                to_np(l2[b, h])[rows], ref, w.torch_dtype)
             rdq, _ = oracle.head_backward(1, *hi, True, gn[b, h, :n], rows=rows, block=64)
             check_grad(f"ragged b{b}h{h} dQ rows", to_np(dq[b, h])[rows], rdq)
+
+
+def test_ragged_batch_of_empty_elements(cuda_device):
+    """Every element empty: every entry point succeeds without a workspace,
+    writes zeros to every output (over earlier contents), and the fused loss
+    is 0."""
+    w = workloads.Workload("ragged-empty", 3, 2, 40, 60, 128, 128, "bf16", False, 0.0, False, 8)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    lens = dict(q_len=[0, 0, 0], k_len=[5, 0, 60])
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    print("ragged empty", flush=True)
+    f32 = dict(device=cuda_device, dtype=torch.float32)
+    out = tuple(torch.full((3, 2, 40), 7.0, **f32) for _ in range(3))
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, False, out=out, **lens)
+    for t in (kl, l1, l2):
+        assert (t == 0).all()
+    kl2, _, _, loss = sk.streamkl_fwd_loss(q1, k1, q2, k2, False, **lens)
+    wt = torch.rand((3, 2, 40), **f32)
+    _, _, _, loss_w = sk.streamkl_fwd_loss(q1, k1, q2, k2, False, wt, **lens)
+    torch.cuda.synchronize()
+    assert (kl2 == 0).all() and loss.item() == 0.0 and loss_w.item() == 0.0
+    for s in (1, 2):
+        for m in (sk.BWD_AUTO, sk.BWD_FUSED, sk.BWD_SEPARATE):
+            dq, dk = sk.streamkl_bwd(s, q1, k1, q2, k2, False, kl, l1, l2, g, bwd_mode=m, **lens)
+            assert (dq == 0).all() and (dk == 0).all()
+    for t in sk.streamkl_bwd_joint(q1, k1, q2, k2, False, kl, l1, l2, g, **lens):
+        assert (t == 0).all()
