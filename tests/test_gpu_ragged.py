@@ -8,6 +8,8 @@ a shared key head, summed by atomics in no fixed order); padded rows
 of every output are exactly 0.  The elements mix long ranges, decode-shaped
 ones (at most 32 query rows, which take the decode kernels) and empty ones.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -157,3 +159,55 @@ def test_ragged_batch_of_empty_elements(cuda_device):
             assert (dq == 0).all() and (dk == 0).all()
     for t in sk.streamkl_bwd_joint(q1, k1, q2, k2, False, kl, l1, l2, g, **lens):
         assert (t == 0).all()
+
+
+def test_ragged_split_elements_and_workspace_fallback(cuda_device):
+    """Elements that take a key split of their own: short query ranges
+    (40-100 rows) against 2000-4000 keys in a batch too small to fill the
+    chip unsplit (bf16: the 4-wave split-K kernel and its merge, one element
+    after another), beside decode-shaped ones (grouped split-K).  Each
+    element equals its own call bitwise.  Then a batch of decode-shaped
+    requests given a workspace too small for their grouped partials but
+    large enough for each request's own: each request then runs on its own
+    plan and equals its own call bitwise."""
+    q_len, k_len = [64, 16, 100, 0, 9, 40], [2000, 3000, 4000, 10, 2500, 2100]
+    B, H = len(q_len), 2
+    w = workloads.Workload("ragged-split", B, H, max(q_len), max(k_len), 128, 128, "bf16", False, 0.0, False, 12)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    print("ragged split elements", flush=True)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, False, q_len=q_len, k_len=k_len)
+    for b, (nq, nk) in enumerate(zip(q_len, k_len)):
+        if nq == 0:
+            continue
+        t = [x[b:b + 1, :, :n].contiguous() for x, n in ((q1, nq), (k1, nk), (q2, nq), (k2, nk))]
+        if nq > 32:  # its own plan, as in the batch
+            assert sk.fwd_plan(sk.shape_of(*t), False) > 1, "the case should split"
+            rkl, rl1, rl2 = sk.streamkl_fwd(*t, False)
+        else:  # the grouped decode plan: about 64 blocks of 32 keys per split, whole groups of 4
+            blocks = -(-nk // 32)
+            ns = min((-(-blocks // 64) + 3) // 4 * 4, max(1, blocks // 8), 4096)
+            rkl, rl1, rl2 = sk.streamkl_fwd(*t, False, num_splits=ns)
+        assert torch.equal(kl[b:b + 1, :, :nq], rkl), f"b{b}: KL differs from the element alone"
+        assert torch.equal(l1[b:b + 1, :, :nq], rl1) and torch.equal(l2[b:b + 1, :, :nq], rl2)
+
+    k_len = [2500, 2700, 3000, 2600, 2900, 2800]
+    q_len = [16] * 6
+    w = workloads.Workload("ragged-fallback", 6, H, 16, max(k_len), 128, 128, "bf16", False, 0.0, False, 13)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    shp = sk.shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
+    own = [sk.fwd_workspace_bytes(sk.make_shape(1, H, 16, nk, 128, 128, sk.BF16), False) for nk in k_len]
+    need = sk.fwd_workspace_bytes(shp, False)
+    assert need > max(own) + 256, (need, own)
+    # through the C ABI: the binding would replace a workspace that is too small
+    ws = torch.empty(need - 256, dtype=torch.uint8, device=cuda_device)
+    ln = sk.Launch(0, 0, ws.data_ptr(), need - 256)
+    kl, l1, l2 = (torch.full((6, H, 16), 7.0, device=cuda_device, dtype=torch.float32) for _ in range(3))
+    st = sk.library().streamkl_fwd(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), 0, 0.0, 0.0,
+                                   kl.data_ptr(), l1.data_ptr(), l2.data_ptr(), ctypes.byref(shp), ctypes.byref(ln),
+                                   sk._stream(cuda_device))
+    assert st == 0, st
+    for b, nk in enumerate(k_len):
+        t = [x[b:b + 1, :, :n].contiguous() for x, n in ((q1, 16), (k1, nk), (q2, 16), (k2, nk))]
+        rkl, rl1, rl2 = sk.streamkl_fwd(*t, False)
+        assert torch.equal(kl[b:b + 1], rkl), f"fallback b{b}: KL differs from the request alone"
+        assert torch.equal(l1[b:b + 1], rl1) and torch.equal(l2[b:b + 1], rl2)
