@@ -19,6 +19,7 @@ from .streamkl import (  # noqa: F401
     fwd_workspace_bytes,
     library,
     make_shape,
+    packed_shape_of,
     shape_of,
     streamkl_bwd,
     streamkl_bwd_joint,

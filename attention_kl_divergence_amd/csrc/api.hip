@@ -24,8 +24,10 @@ __global__ __launch_bounds__(256) void splitk_merge_kernel(const float* __restri
   __shared__ double red[4];
   int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x;
   int64_t rows = BH * n_q, head0 = 0, base = 0, fs = BH * (int64_t)nsplit * n_q;
+  int qo = 0;  // the element's first row within a head (packed batches)
   if constexpr (kDecTable<RT>) {
     const int e = table_elem(rt.mstart, rt.n, blockIdx.x);
+    qo = rt.qoff[e];
     i = (blockIdx.x - rt.mstart[e]) * (int64_t)256 + threadIdx.x;
     n_q = rt.n_q[e];
     nsplit = rt.nsplit[e];
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(256) void splitk_merge_kernel(const float* __restri
   if (i < rows) {
     const int64_t loc = i / n_q;  // the head within the problem (or the element)
     const int q = (int)(i % n_q);
-    const int64_t r = (head0 + loc) * qs + q;  // output row (qs rows per head in memory)
+    const int64_t r = (head0 + loc) * qs + qo + q;  // output row (qs rows per head in memory)
     RowState st = empty_state();
     for (int z = 0; z < nsplit; ++z) {
       const int64_t o = base + (loc * nsplit + z) * (int64_t)n_q + q;
@@ -196,6 +198,8 @@ bool finite_bits(float f) {
 }
 
 bool ragged(const streamkl_shape* s);
+bool packed(const streamkl_shape* s);
+streamkl_shape element_shape(const streamkl_shape* s, int64_t b);
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -210,11 +214,22 @@ streamkl_status check_shape(const streamkl_shape* s, int causal) {
   if (s->B > (int64_t(1) << 20) || s->H > (int64_t(1) << 20) || s->B * s->H > (int64_t(1) << 20))
     return STREAMKL_ERR_UNSUPPORTED;
   if (causal && s->n_q > s->n_k) return STREAMKL_ERR_INVALID;
+  if ((s->q_off == nullptr) != (s->k_off == nullptr)) return STREAMKL_ERR_INVALID;
+  if (packed(s)) {
+    // offsets from 0 to the total rows, nondecreasing; the lengths they give
+    // follow the rules of ragged batches below
+    if (s->q_len || s->k_len) return STREAMKL_ERR_INVALID;
+    if (s->q_off[0] != 0 || s->k_off[0] != 0 || s->q_off[s->B] != s->n_q || s->k_off[s->B] != s->n_k)
+      return STREAMKL_ERR_INVALID;
+    for (int64_t b = 0; b < s->B; ++b)
+      if (s->q_off[b + 1] < s->q_off[b] || s->k_off[b + 1] < s->k_off[b]) return STREAMKL_ERR_INVALID;
+  }
   if (ragged(s)) {
     // every batch element: lengths within the padded sizes, some key for
     // every query row, bottom-right causal alignment needs q <= k
     for (int64_t b = 0; b < s->B; ++b) {
-      const int64_t q = s->q_len ? s->q_len[b] : s->n_q, k = s->k_len ? s->k_len[b] : s->n_k;
+      const streamkl_shape e = element_shape(s, b);
+      const int64_t q = e.n_q, k = e.n_k;
       if (q < 0 || q > s->n_q || k < 0 || k > s->n_k) return STREAMKL_ERR_INVALID;
       if (q > 0 && k == 0) return STREAMKL_ERR_INVALID;
       if (causal && q > k) return STREAMKL_ERR_INVALID;
@@ -397,6 +412,18 @@ double t_fused(const BwdWork& w, int cus) {
 // mode cannot fill the chip (few query rows, long key ranges).
 int plan_bwd(const streamkl_shape* s, int causal, int setting, const streamkl_launch* l, int cus) {
   if (l && l->bwd_mode != STREAMKL_BWD_AUTO) return l->bwd_mode;
+  if (ragged(s)) {
+    // a ragged batch (whole-batch plans only: its elements plan on their
+    // own) as the padded batch of its longest lengths, the same in either layout
+    streamkl_shape v = element_shape(s, 0);
+    v.B = s->B;
+    for (int64_t b = 1; b < s->B; ++b) {
+      const streamkl_shape e = element_shape(s, b);
+      v.n_q = std::max(v.n_q, e.n_q);
+      v.n_k = std::max(v.n_k, e.n_k);
+    }
+    return plan_bwd(&v, causal, setting, nullptr, cus);
+  }
   // decode shapes: the fused decode kernel reads each key tile once and adds
   // to dQ once per wave; the separate dQ kernel would get one workgroup per head
   if (decode_shape(s)) return STREAMKL_BWD_FUSED;
@@ -422,16 +449,15 @@ streamkl_status fill_zero(float* p, int64_t n, hipStream_t s) {
   return hip_status(hipGetLastError());
 }
 
-// Clears rows [row0[b], rows) of every head of each batch element b of an
-// fp32 tensor laid out [B][heads][rows][d] (row0[b] = rows: nothing to clear).
-// The kernels of a grouped ragged launch write every row below an element's
-// length, so only the rows past it need clearing.
-streamkl_status clear_rows(float* p, int64_t heads, int64_t rows, int d, const std::vector<int64_t>& row0,
-                           hipStream_t s) {
+// Clears, in every head of an fp32 tensor (heads head_rows rows apart, d
+// floats per row), the rows [first, first + n) of each span (first counted
+// in head 0; spans with n <= 0 are skipped).
+streamkl_status clear_rows(float* p, int64_t heads, int64_t head_rows, int d,
+                           const std::vector<std::pair<int64_t, int64_t>>& spans, hipStream_t s) {
   const bool vec = aligned(p, 16) && d % 4 == 0;
   SpanTable t = {};
   t.count = (int)heads;
-  t.stride = rows * d;
+  t.stride = head_rows * d;
   auto flush = [&]() -> streamkl_status {
     if (t.n == 0) return STREAMKL_OK;
     int64_t longest = 0;
@@ -445,17 +471,36 @@ streamkl_status clear_rows(float* p, int64_t heads, int64_t rows, int d, const s
     t.n = 0;
     return hip_status(hipGetLastError());
   };
-  for (size_t b = 0; b < row0.size(); ++b) {
-    if (row0[b] >= rows) continue;
+  for (const auto& sp : spans) {
+    if (sp.second <= 0) continue;
     const int i = t.n++;
-    t.base[i] = ((int64_t)b * heads * rows + row0[b]) * d;
-    t.len[i] = (rows - row0[b]) * d;
+    t.base[i] = sp.first * d;
+    t.len[i] = sp.second * d;
     if (t.n == kRaggedMax) {
       const streamkl_status st = flush();
       if (st != STREAMKL_OK) return st;
     }
   }
   return flush();
+}
+
+// The rows of each batch element b from row0[b] on (the rows its kernels do
+// not write), as spans for clear_rows in a query-side (H heads) or
+// key-side tensor: padded batches to the padded length, packed batches to
+// the element's own length (a packed element has no padding).
+std::vector<std::pair<int64_t, int64_t>> rows_past(const streamkl_shape* s, int64_t heads, bool key,
+                                                   const std::vector<int64_t>& row0) {
+  std::vector<std::pair<int64_t, int64_t>> out;
+  for (int64_t b = 0; b < s->B; ++b) {
+    if (packed(s)) {
+      const int64_t* off = key ? s->k_off : s->q_off;
+      out.push_back({off[b] + row0[b], off[b + 1] - off[b] - row0[b]});
+    } else {
+      const int64_t rows = key ? s->n_k : s->n_q;
+      out.push_back({b * heads * rows + row0[b], rows - row0[b]});
+    }
+  }
+  return out;
 }
 
 // dK of a model whose key heads are shared is summed with atomics: clear it
@@ -468,16 +513,24 @@ streamkl_status clear_shared_dk(float* dK, const streamkl_shape* sh, int ds, int
 
 // ---- ragged batches: per batch element lengths inside padded tensors ----
 
-bool ragged(const streamkl_shape* s) { return s->q_len || s->k_len; }
+bool ragged(const streamkl_shape* s) { return s->q_len || s->k_len || s->q_off; }
+bool packed(const streamkl_shape* s) { return s->q_off != nullptr; }
 
 // Batch element b as a problem of its own: B = 1, its lengths, no length arrays.
 streamkl_shape element_shape(const streamkl_shape* s, int64_t b) {
   streamkl_shape e = *s;
   e.B = 1;
-  e.n_q = s->q_len ? s->q_len[b] : s->n_q;
-  e.n_k = s->k_len ? s->k_len[b] : s->n_k;
+  if (packed(s)) {
+    e.n_q = s->q_off[b + 1] - s->q_off[b];
+    e.n_k = s->k_off[b + 1] - s->k_off[b];
+  } else {
+    e.n_q = s->q_len ? s->q_len[b] : s->n_q;
+    e.n_k = s->k_len ? s->k_len[b] : s->n_k;
+  }
   e.q_len = nullptr;
   e.k_len = nullptr;
+  e.q_off = nullptr;
+  e.k_off = nullptr;
   return e;
 }
 
@@ -486,12 +539,20 @@ int64_t kv_heads(const streamkl_shape* s, int model) {
   return kv > 0 ? kv : s->H;
 }
 
-// Element b's part of a tensor: rows_per_elem = heads * rows per head.
+// The first row of batch element b in a query-side tensor (Q, the per-row
+// vectors, dQ: H heads) or a key-side tensor (K, dK: kv heads).  Padded
+// batches: element b's heads follow element b-1's, n rows each; packed
+// batches: the element's first row within head 0 (heads n_q or n_k rows
+// apart, the total).  A pointer at that row, with the tensor's head stride
+// as the rows per head, addresses the element as a problem of its own.
+int64_t qrow(const streamkl_shape* s, int64_t b) { return packed(s) ? s->q_off[b] : b * s->H * s->n_q; }
+int64_t krow(const streamkl_shape* s, int64_t b, int64_t kv) { return packed(s) ? s->k_off[b] : b * kv * s->n_k; }
+
 template <typename P>
-P elem(P p, int64_t b, int64_t rows_per_elem, int64_t bytes_per_row) {
+P at_row(P p, int64_t row, int64_t bytes_per_row) {
   if (!p) return p;
   using C = std::conditional_t<std::is_const_v<std::remove_pointer_t<P>>, const char*, char*>;
-  return reinterpret_cast<P>(reinterpret_cast<C>(p) + b * rows_per_elem * bytes_per_row);
+  return reinterpret_cast<P>(reinterpret_cast<C>(p) + row * bytes_per_row);
 }
 
 // Elements of a ragged batch that run one kernel go to that kernel in few
@@ -510,7 +571,11 @@ struct RaggedLaunch {
 // stay below the 2^32 a launch allows.  Beyond that elements run on their own.
 bool groupable(const streamkl_shape* s) {
   constexpr int64_t kMaxWg = int64_t(1) << 22;
-  return ragged(s) && s->B * s->H * (cdiv(std::max(s->n_q, s->n_k), 128) + 1) <= kMaxWg;
+  if (!ragged(s)) return false;
+  // packed: n_q and n_k are the totals over the elements
+  const int64_t wg = packed(s) ? s->H * (cdiv(std::max(s->n_q, s->n_k), 128) + 2 * s->B)
+                               : s->B * s->H * (cdiv(std::max(s->n_q, s->n_k), 128) + 1);
+  return wg <= kMaxWg;
 }
 
 // Elements `els` by query-key pairs per head, the most first, so that the
@@ -543,10 +608,12 @@ std::vector<RaggedLaunch> ragged_launches(const streamkl_shape* s, int causal, c
     RaggedLaunch& L = out.back();
     const int i = L.t.n++;
     L.t.start[i] = (int)L.grid;
-    L.t.b[i] = (int)b;
+    L.t.b[i] = packed(s) ? 0 : (int)b;  // packed: every element's heads are heads 0 .. H-1
     L.t.n_q[i] = (int)e.n_q;
     L.t.n_k[i] = (int)e.n_k;
     L.t.nblk[i] = (int)nblk;
+    L.t.qoff[i] = packed(s) ? (int)s->q_off[b] : 0;
+    L.t.koff[i] = packed(s) ? (int)s->k_off[b] : 0;
     L.grid += (s->H * nblk + 7) / 8 * 8;
     L.t.start[i + 1] = (int)L.grid;
   }
@@ -584,7 +651,9 @@ std::vector<DecLaunch> dec_launches(const streamkl_shape* s, int causal, const s
     const int i = L.t.n++;
     L.t.start[i] = (int)L.grid;
     L.t.mstart[i] = (int)L.mgrid;
-    L.t.b[i] = (int)b;
+    L.t.b[i] = packed(s) ? 0 : (int)b;
+    L.t.qoff[i] = packed(s) ? (int)s->q_off[b] : 0;
+    L.t.koff[i] = packed(s) ? (int)s->k_off[b] : 0;
     L.t.n_q[i] = (int)e.n_q;
     L.t.n_k[i] = (int)e.n_k;
     L.t.nsplit[i] = ns;
@@ -748,7 +817,7 @@ using namespace streamkl;
 
 extern "C" {
 
-int streamkl_version(void) { return 4; }
+int streamkl_version(void) { return 5; }
 
 const char* streamkl_status_string(int status) {
   switch (status) {
@@ -931,22 +1000,24 @@ streamkl_status fwd_call(const void* Q1, const void* K1, const void* Q2, const v
     // run in grouped launches (unsplit ones by kernel, split decode-shaped
     // ones in split-K launches) or, where a plan or the workspace asks, on
     // their own
+    // (packed batches have no padded rows: every row is some element's)
     const int64_t rows = shape->B * shape->H * shape->n_q;
     for (float* o : {out_kl, out_lse1, out_lse2}) {
+      if (packed(shape)) break;
       st = fill_zero(o, rows, s);
       if (st != STREAMKL_OK) return st;
     }
     const int64_t es = shape->dtype == STREAMKL_BF16 ? 2 : 4;
-    const int64_t qr = shape->H * shape->n_q, k1r = kv_heads(shape, 1) * shape->n_k,
-                  k2r = kv_heads(shape, 2) * shape->n_k;
+    const int64_t kv1 = kv_heads(shape, 1), kv2 = kv_heads(shape, 2);
     int64_t slot = 0;
     for (const int64_t b : c.single) {
       const streamkl_shape e = element_shape(shape, b);
       const FwdPlan p = make_fwd_plan(&e, splits[b]);
-      st = fwd_launch(elem(Q1, b, qr, es * e.d1), elem(K1, b, k1r, es * e.d1), elem(Q2, b, qr, es * e.d2),
-                      elem(K2, b, k2r, es * e.d2), causal, scale1, scale2, elem(out_kl, b, qr, 4),
-                      elem(out_lse1, b, qr, 4), elem(out_lse2, b, qr, 4), &e, shape->n_q, shape->n_k, p, split_ws,
-                      elem(weights, b, qr, 4), lpart ? lpart + slot : nullptr, s);
+      const int64_t qr = qrow(shape, b), k1r = krow(shape, b, kv1), k2r = krow(shape, b, kv2);
+      st = fwd_launch(at_row(Q1, qr, es * e.d1), at_row(K1, k1r, es * e.d1), at_row(Q2, qr, es * e.d2),
+                      at_row(K2, k2r, es * e.d2), causal, scale1, scale2, at_row(out_kl, qr, 4),
+                      at_row(out_lse1, qr, 4), at_row(out_lse2, qr, 4), &e, shape->n_q, shape->n_k, p, split_ws,
+                      at_row(weights, qr, 4), lpart ? lpart + slot : nullptr, s);
       if (st != STREAMKL_OK) return st;
       slot += p.loss_slots;
     }
@@ -994,10 +1065,13 @@ BwdArgs bwd_args(const void* Q1, const void* K1, const void* Q2, const void* K2,
 }
 
 // One backward setting of one problem (validated), rows per head qs, ks.
+// cleared: the caller has cleared the problem's dQ and dK rows (the rows of
+// a ragged batch's element need not be one block of memory).
 streamkl_status bwd_launch(int setting, const void* Q1, const void* K1, const void* Q2, const void* K2, int causal,
                            float scale1, float scale2, const float* kl, const float* lse1, const float* lse2,
                            const float* d_kl, float* dQ, float* dK, const streamkl_shape* shape, int64_t qs,
-                           int64_t ks, const streamkl_launch* launch, const DeviceInfo& dev, hipStream_t s) {
+                           int64_t ks, const streamkl_launch* launch, const DeviceInfo& dev, hipStream_t s,
+                           bool cleared = false) {
   DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
   DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
   if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
@@ -1009,14 +1083,16 @@ streamkl_status bwd_launch(int setting, const void* Q1, const void* K1, const vo
   const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
   const int ds = setting == 1 ? shape->d2 : shape->d1;
   streamkl_status st;
-  if (mode != STREAMKL_BWD_DQ_ONLY) {
+  if (mode != STREAMKL_BWD_DQ_ONLY && !cleared) {
     st = clear_shared_dk(dK, shape, ds, setting == 1 ? a.g2 : a.g1, ks, s);
     if (st != STREAMKL_OK) return st;
   }
   if (mode == STREAMKL_BWD_FUSED) {
     const DecBwdLaunch fd = decode_shape(shape) ? pick_dec_bwd(shape->dtype, shape->d1, shape->d2) : nullptr;
-    st = fill_zero(dQ, a.BH * qs * (int64_t)ds, s);
-    if (st != STREAMKL_OK) return st;
+    if (!cleared) {
+      st = fill_zero(dQ, a.BH * qs * (int64_t)ds, s);
+      if (st != STREAMKL_OK) return st;
+    }
     if (fd) {
       a.nblk = plan_dec_bwd_splits(shape, dev.cus);
       return hip_status(fd(a, setting, a.BH * a.nblk, s, nullptr));
@@ -1039,7 +1115,7 @@ streamkl_status bwd_launch(int setting, const void* Q1, const void* K1, const vo
 streamkl_status joint_launch(const void* Q1, const void* K1, const void* Q2, const void* K2, int causal, float scale1,
                              float scale2, const float* kl, const float* lse1, const float* lse2, const float* d_kl,
                              float* dQ1, float* dK1, float* dQ2, float* dK2, const streamkl_shape* shape, int64_t qs,
-                             int64_t ks, int mode, hipStream_t s) {
+                             int64_t ks, int mode, hipStream_t s, bool cleared = false) {
   DqLaunch fq = pick_dq(shape->dtype, shape->d1, shape->d2);
   DkLaunch fk = pick_dk(shape->dtype, shape->d1, shape->d2);
   if (!fq || !fk) return STREAMKL_ERR_UNSUPPORTED;
@@ -1050,8 +1126,8 @@ streamkl_status joint_launch(const void* Q1, const void* K1, const void* Q2, con
   const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
   streamkl_status st;
   if (mode != STREAMKL_BWD_DQ_ONLY) {
-    st = clear_shared_dk(dK1, shape, shape->d1, a.g1, ks, s);
-    if (st == STREAMKL_OK) st = clear_shared_dk(dK2, shape, shape->d2, a.g2, ks, s);
+    st = cleared ? STREAMKL_OK : clear_shared_dk(dK1, shape, shape->d1, a.g1, ks, s);
+    if (st == STREAMKL_OK && !cleared) st = clear_shared_dk(dK2, shape, shape->d2, a.g2, ks, s);
     if (st != STREAMKL_OK) return st;
     a.nblk = (int)nkb;
     st = hip_status(fk(a, 3, false, a.BH * nkb, s, nullptr));
@@ -1294,17 +1370,18 @@ streamkl_status streamkl_bwd(int setting, const void* Q1, const void* K1, const 
       single.push_back(b);
     }
   }
-  if (need_dq) st = clear_rows(dQ, shape->H, shape->n_q, ds, q0, s);
-  if (st == STREAMKL_OK && need_dk) st = clear_rows(dK, kvs, shape->n_k, ds, k0, s);
+  if (need_dq) st = clear_rows(dQ, shape->H, shape->n_q, ds, rows_past(shape, shape->H, false, q0), s);
+  if (st == STREAMKL_OK && need_dk) st = clear_rows(dK, kvs, shape->n_k, ds, rows_past(shape, kvs, true, k0), s);
   if (st != STREAMKL_OK) return st;
   const int64_t es = shape->dtype == STREAMKL_BF16 ? 2 : 4;
-  const int64_t qr = shape->H * shape->n_q, k1r = kv_heads(shape, 1) * shape->n_k, k2r = kv_heads(shape, 2) * shape->n_k;
+  const int64_t kv1 = kv_heads(shape, 1), kv2 = kv_heads(shape, 2);
   for (const int64_t b : single) {
     const streamkl_shape e = element_shape(shape, b);
-    st = bwd_launch(setting, elem(Q1, b, qr, es * e.d1), elem(K1, b, k1r, es * e.d1), elem(Q2, b, qr, es * e.d2),
-                    elem(K2, b, k2r, es * e.d2), causal, scale1, scale2, elem(kl, b, qr, 4), elem(lse1, b, qr, 4),
-                    elem(lse2, b, qr, 4), elem(d_kl, b, qr, 4), elem(dQ, b, qr, 4 * ds),
-                    elem(dK, b, kvs * shape->n_k, 4 * ds), &e, shape->n_q, shape->n_k, launch, dev, s);
+    const int64_t qr = qrow(shape, b), k1r = krow(shape, b, kv1), k2r = krow(shape, b, kv2), ksr = krow(shape, b, kvs);
+    st = bwd_launch(setting, at_row(Q1, qr, es * e.d1), at_row(K1, k1r, es * e.d1), at_row(Q2, qr, es * e.d2),
+                    at_row(K2, k2r, es * e.d2), causal, scale1, scale2, at_row(kl, qr, 4), at_row(lse1, qr, 4),
+                    at_row(lse2, qr, 4), at_row(d_kl, qr, 4), at_row(dQ, qr, 4 * ds), at_row(dK, ksr, 4 * ds), &e,
+                    shape->n_q, shape->n_k, launch, dev, s, true);
     if (st != STREAMKL_OK) return st;
   }
   if (!dec.empty()) {
@@ -1363,37 +1440,39 @@ streamkl_status streamkl_bwd_joint(const void* Q1, const void* K1, const void* Q
       k02[b] = group2(shape) > 1 ? 0 : e.n_k;
     }
     if (need_dq) {
-      st = clear_rows(dQ1, shape->H, shape->n_q, shape->d1, q0, s);
-      if (st == STREAMKL_OK) st = clear_rows(dQ2, shape->H, shape->n_q, shape->d2, q0, s);
+      st = clear_rows(dQ1, shape->H, shape->n_q, shape->d1, rows_past(shape, shape->H, false, q0), s);
+      if (st == STREAMKL_OK)
+        st = clear_rows(dQ2, shape->H, shape->n_q, shape->d2, rows_past(shape, shape->H, false, q0), s);
     }
     if (st == STREAMKL_OK && need_dk) {
-      st = clear_rows(dK1, kv1, shape->n_k, shape->d1, k01, s);
-      if (st == STREAMKL_OK) st = clear_rows(dK2, kv2, shape->n_k, shape->d2, k02, s);
+      st = clear_rows(dK1, kv1, shape->n_k, shape->d1, rows_past(shape, kv1, true, k01), s);
+      if (st == STREAMKL_OK) st = clear_rows(dK2, kv2, shape->n_k, shape->d2, rows_past(shape, kv2, true, k02), s);
     }
     if (st != STREAMKL_OK || els.empty()) return st;
     return joint_group(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, dQ1, dK1, dQ2, dK2, shape, els,
                        mode, s);
   }
-  const int64_t BHQ = shape->B * shape->H * shape->n_q;
+  const int64_t nb = packed(shape) ? 1 : shape->B;  // a packed tensor has no batch dimension
+  const int64_t BHQ = nb * shape->H * shape->n_q;
   if (need_dq) {
     st = fill_zero(dQ1, BHQ * shape->d1, s);
     if (st == STREAMKL_OK) st = fill_zero(dQ2, BHQ * shape->d2, s);
   }
   if (st == STREAMKL_OK && need_dk) {
-    st = fill_zero(dK1, shape->B * kv1 * shape->n_k * shape->d1, s);
-    if (st == STREAMKL_OK) st = fill_zero(dK2, shape->B * kv2 * shape->n_k * shape->d2, s);
+    st = fill_zero(dK1, nb * kv1 * shape->n_k * shape->d1, s);
+    if (st == STREAMKL_OK) st = fill_zero(dK2, nb * kv2 * shape->n_k * shape->d2, s);
   }
   if (st != STREAMKL_OK) return st;
   const int64_t es = 2;
-  const int64_t qr = shape->H * shape->n_q, k1r = kv1 * shape->n_k, k2r = kv2 * shape->n_k;
   const int d1 = shape->d1, d2 = shape->d2;
   for (int64_t b = 0; b < shape->B; ++b) {
     const streamkl_shape e = element_shape(shape, b);
     if (e.n_q == 0) continue;
-    st = joint_launch(elem(Q1, b, qr, es * d1), elem(K1, b, k1r, es * d1), elem(Q2, b, qr, es * d2),
-                      elem(K2, b, k2r, es * d2), causal, scale1, scale2, elem(kl, b, qr, 4), elem(lse1, b, qr, 4),
-                      elem(lse2, b, qr, 4), elem(d_kl, b, qr, 4), elem(dQ1, b, qr, 4 * d1), elem(dK1, b, k1r, 4 * d1),
-                      elem(dQ2, b, qr, 4 * d2), elem(dK2, b, k2r, 4 * d2), &e, shape->n_q, shape->n_k, mode, s);
+    const int64_t qr = qrow(shape, b), k1r = krow(shape, b, kv1), k2r = krow(shape, b, kv2);
+    st = joint_launch(at_row(Q1, qr, es * d1), at_row(K1, k1r, es * d1), at_row(Q2, qr, es * d2),
+                      at_row(K2, k2r, es * d2), causal, scale1, scale2, at_row(kl, qr, 4), at_row(lse1, qr, 4),
+                      at_row(lse2, qr, 4), at_row(d_kl, qr, 4), at_row(dQ1, qr, 4 * d1), at_row(dK1, k1r, 4 * d1),
+                      at_row(dQ2, qr, 4 * d2), at_row(dK2, k2r, 4 * d2), &e, shape->n_q, shape->n_k, mode, s, true);
     if (st != STREAMKL_OK) return st;
   }
   return STREAMKL_OK;

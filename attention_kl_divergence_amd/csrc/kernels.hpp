@@ -176,7 +176,9 @@ __device__ __forceinline__ WorkItem work_item(int64_t lin, int64_t BH, int nblk)
 // element b[i] (query heads b[i] H .. b[i] H + H - 1 of the padded tensors)
 // exactly as in such a launch, with that element's lengths and blocks per
 // head.  The workgroups past an element's H * nblk are padding and leave at
-// once.
+// once.  In a packed batch the elements' rows lie one after another in each
+// head (heads qs and ks rows apart): b[i] is 0 and qoff[i], koff[i] are the
+// element's first rows, added to every row index.
 constexpr int kRaggedMax = 64;
 struct RaggedTable {
   int n;                     // elements in the table (0: not ragged)
@@ -185,6 +187,8 @@ struct RaggedTable {
   int b[kRaggedMax];         // batch index of each element
   int n_q[kRaggedMax], n_k[kRaggedMax];
   int nblk[kRaggedMax];      // the kernel's blocks per head for the element
+  int qoff[kRaggedMax];      // packed batches: the element's first query row within a head (else 0)
+  int koff[kRaggedMax];      // and its first key row
 };
 
 // The table type of a plain launch: no table.  Kernels take the table type
@@ -196,8 +200,9 @@ constexpr bool kRagged = std::is_same<RT, RaggedTable>::value;
 
 struct RaggedItem {
   int64_t lin;    // workgroup index within the element's range
-  int64_t head0;  // the element's first query head, b H
+  int64_t head0;  // the element's first query head, b H (0 in a packed batch)
   int n_q, n_k, nblk;
+  int qoff, koff;  // the element's first query and key rows within a head
   bool pad;       // a padding workgroup
 };
 
@@ -217,6 +222,8 @@ __device__ __forceinline__ RaggedItem ragged_item(const RaggedTable& rt, int64_t
   r.n_q = rt.n_q[e];
   r.n_k = rt.n_k[e];
   r.nblk = rt.nblk[e];
+  r.qoff = rt.qoff[e];
+  r.koff = rt.koff[e];
   r.pad = r.lin >= (int64_t)rt.H * r.nblk;
   return r;
 }
@@ -238,6 +245,7 @@ struct DecTable {
   int n_q[kRaggedMax], n_k[kRaggedMax];
   int nsplit[kRaggedMax];
   int64_t wsb[kRaggedMax];
+  int qoff[kRaggedMax], koff[kRaggedMax];  // as in RaggedTable
 };
 template <typename RT>
 constexpr bool kDecTable = std::is_same<RT, DecTable>::value;
@@ -659,8 +667,11 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 || D1 + D2 < 256) ? 2 : 1) voi
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
   int64_t lin = blockIdx.x, head0 = 0, heads = a.BH;
+  int qo = 0, ko = 0;  // the element's first query and key rows within a head (packed batches)
   if constexpr (kRagged<RT>) {  // one element of a ragged batch (unsplit)
     const RaggedItem r = ragged_item(rt, lin);
+    qo = r.qoff;
+    ko = r.koff;
     if (r.pad) {
       if constexpr (LOSS) {
         if (tid == 0) a.lpart[blockIdx.x] = 0.0;
@@ -683,10 +694,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 || D1 + D2 < 256) ? 2 : 1) voi
   const int qrow = q0 + col;
   const int off = a.n_k - a.n_q;
 
-  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.qs * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
-  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.qs * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
+  const T* Q1 = reinterpret_cast<const T*>(a.q1) + (bh * (int64_t)a.qs + qo) * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + (key_head(bh, a.g1) * (int64_t)a.ks + ko) * D1;
+  const T* Q2 = reinterpret_cast<const T*>(a.q2) + (bh * (int64_t)a.qs + qo) * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + (key_head(bh, a.g2) * (int64_t)a.ks + ko) * D2;
 
   const int kbeg = z * a.keys_per_split;
   int kend = min(a.n_k, kbeg + a.keys_per_split);
@@ -737,7 +748,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 || D1 + D2 < 256) ? 2 : 1) voi
   st = merge_state(st, shfl_xor_state(st, 32));
   double lv = 0.0;
   if (grp == 0 && qrow < a.n_q) {
-    const int64_t r = bh * a.qs + qrow;
+    const int64_t r = bh * a.qs + qo + qrow;
     if (a.nsplit == 1) {
       const float klv = finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
       if constexpr (LOSS) lv = loss_term(a, r, klv);
@@ -808,8 +819,11 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a, const RT 
   int64_t bh, loc;  // the head, and its index within the problem (or the element)
   int z;
   int64_t wsb = 0;  // the problem's (the element's) first partial
+  int qo = 0, ko = 0;  // the element's first query and key rows within a head (packed batches)
   if constexpr (kDecTable<RT>) {
     const int e = table_elem(rt.start, rt.n, blockIdx.x);
+    qo = rt.qoff[e];
+    ko = rt.koff[e];
     const int64_t lin = blockIdx.x - rt.start[e];
     a.n_q = rt.n_q[e];
     a.n_k = rt.n_k[e];
@@ -828,10 +842,10 @@ __global__ __launch_bounds__(256, 2) void fwd_decode_kernel(FwdArgs a, const RT 
   }
   const int off = a.n_k - a.n_q;
 
-  const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.qs * D1;
-  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
-  const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.qs * D2;
-  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
+  const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + (bh * (int64_t)a.qs + qo) * D1;
+  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + (key_head(bh, a.g1) * (int64_t)a.ks + ko) * D1;
+  const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + (bh * (int64_t)a.qs + qo) * D2;
+  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + (key_head(bh, a.g2) * (int64_t)a.ks + ko) * D2;
   dec_stage_q<D1>(sQ1, Q1, a.n_q, tid);
   dec_stage_q<D2>(sQ2, Q2, a.n_q, tid);
   __syncthreads();
@@ -955,8 +969,11 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a, const RT rt) 
   const int col = lane & 31, grp = lane >> 5;
   const int group = wave >> 2;
   int64_t lin = blockIdx.x, head0 = 0, heads = a.BH;
+  int qo = 0, ko = 0;  // the element's first query and key rows within a head (packed batches)
   if constexpr (kRagged<RT>) {  // one element of a ragged batch
     const RaggedItem r = ragged_item(rt, lin);
+    qo = r.qoff;
+    ko = r.koff;
     if (r.pad) {
       if constexpr (LOSS) {
         if (tid == 0) a.lpart[blockIdx.x] = 0.0;
@@ -978,10 +995,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a, const RT rt) 
   const int qrow = q0 + col;
   const int off = a.n_k - a.n_q;
 
-  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.qs * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
-  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.qs * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
+  const T* Q1 = reinterpret_cast<const T*>(a.q1) + (bh * (int64_t)a.qs + qo) * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + (key_head(bh, a.g1) * (int64_t)a.ks + ko) * D1;
+  const T* Q2 = reinterpret_cast<const T*>(a.q2) + (bh * (int64_t)a.qs + qo) * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + (key_head(bh, a.g2) * (int64_t)a.ks + ko) * D2;
 
   int kend = a.n_k;
   if (a.causal) kend = min(kend, min(a.n_q, qwg0 + 32 * NW) - 1 + off + 1);
@@ -1052,7 +1069,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a, const RT rt) 
   st = merge_state(st, shfl_xor_state(st, 32));
   double lv = 0.0;
   if (grp == 0 && qrow < a.n_q) {
-    const int64_t r = bh * a.qs + qrow;
+    const int64_t r = bh * a.qs + qo + qrow;
     const float klv = finish_state(st, a.kl + r, a.lse1 + r, a.lse2 + r);
     if constexpr (LOSS) lv = loss_term(a, r, klv);
   }
@@ -1251,8 +1268,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a, const RT rt)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
   int64_t lin = blockIdx.x, head0 = 0, heads = a.BH;
+  int qo = 0, ko = 0;  // the element's first query and key rows within a head (packed batches)
   if constexpr (kRagged<RT>) {  // one element of a ragged batch
     const RaggedItem r = ragged_item(rt, lin);
+    qo = r.qoff;
+    ko = r.koff;
     if (r.pad) return;
     lin = r.lin;
     head0 = r.head0;
@@ -1268,10 +1288,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a, const RT rt)
   const int qrow = q0 + col;
   const int off = a.n_k - a.n_q;
 
-  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.qs * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
-  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.qs * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
+  const T* Q1 = reinterpret_cast<const T*>(a.q1) + (bh * (int64_t)a.qs + qo) * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + (key_head(bh, a.g1) * (int64_t)a.ks + ko) * D1;
+  const T* Q2 = reinterpret_cast<const T*>(a.q2) + (bh * (int64_t)a.qs + qo) * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + (key_head(bh, a.g2) * (int64_t)a.ks + ko) * D2;
 
   int kend = a.n_k;
   if (a.causal) kend = min(kend, min(a.n_q, qb * 32 * NW + 32 * NW) - 1 + off + 1);
@@ -1292,7 +1312,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a, const RT rt)
   for (int s = 0; s < S1; ++s) qf1[s] = frag_global<T, D1>(Q1, qrow, a.n_q - 1, qv, s, grp);
 #pragma unroll
   for (int s = 0; s < S2; ++s) qf2[s] = frag_global<T, D2>(Q2, qrow, a.n_q - 1, qv, s, grp);
-  const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.qs + qrow, qv);
+  const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.qs + qo + qrow, qv);
   const float row_sign = SETTING == 1 ? rg.gs : 1.f;
 
   f32x16 dqa[NB];
@@ -1402,7 +1422,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a, const RT rt)
       const int r = acc_row(e, grp);
       const int q = q0 + r;
       const float v = ((neg >> r) & 1) ? -dqa[nb][e] : dqa[nb][e];
-      if (q < a.n_q) a.dq[(bh * a.qs + q) * DS + nb * 32 + col] = v;
+      if (q < a.n_q) a.dq[(bh * a.qs + qo + q) * DS + nb * 32 + col] = v;
     }
 }
 
@@ -1449,8 +1469,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a, const RT rt)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
   int64_t lin = blockIdx.x, head0 = 0, heads = a.BH;
+  int qo = 0, ko = 0;  // the element's first query and key rows within a head (packed batches)
   if constexpr (kRagged<RT>) {  // one element of a ragged batch
     const RaggedItem r = ragged_item(rt, lin);
+    qo = r.qoff;
+    ko = r.koff;
     if (r.pad) return;
     lin = r.lin;
     head0 = r.head0;
@@ -1467,10 +1490,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a, const RT rt)
   const int krow = kwave + col;
   const int off = a.n_k - a.n_q;
 
-  const T* Q1 = reinterpret_cast<const T*>(a.q1) + bh * (int64_t)a.qs * D1;
-  const T* K1 = reinterpret_cast<const T*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
-  const T* Q2 = reinterpret_cast<const T*>(a.q2) + bh * (int64_t)a.qs * D2;
-  const T* K2 = reinterpret_cast<const T*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
+  const T* Q1 = reinterpret_cast<const T*>(a.q1) + (bh * (int64_t)a.qs + qo) * D1;
+  const T* K1 = reinterpret_cast<const T*>(a.k1) + (key_head(bh, a.g1) * (int64_t)a.ks + ko) * D1;
+  const T* Q2 = reinterpret_cast<const T*>(a.q2) + (bh * (int64_t)a.qs + qo) * D2;
+  const T* K2 = reinterpret_cast<const T*>(a.k2) + (key_head(bh, a.g2) * (int64_t)a.ks + ko) * D2;
   const T* KS = SETTING == 1 ? K2 : K1;
 
   // Query tiles are visited from the last one down: under a causal mask every
@@ -1486,7 +1509,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a, const RT rt)
   // they are scaled and stored to LDS after the tile's compute, behind a
   // scheduling barrier, so their load latency overlaps the whole tile
   auto load_stats = [&](int q0, RawRowGrad& r) {
-    r = load_rowgrad_raw<SETTING>(a, bh * a.qs + q0 + tid, tid < BQ && q0 + tid < a.n_q);
+    r = load_rowgrad_raw<SETTING>(a, bh * a.qs + qo + q0 + tid, tid < BQ && q0 + tid < a.n_q);
   };
   auto store_stats = [&](int buf, const RawRowGrad& raw) {
     const RowGrad rg = scale_rowgrad<SETTING>(a, raw);
@@ -1705,7 +1728,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a, const RT rt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int q = qb0 + acc_row(e, grp);
-          if (q < a.n_q) atomicAdd(a.dq + (bh * a.qs + q) * DS + dcol, dqa[e]);
+          if (q < a.n_q) atomicAdd(a.dq + (bh * a.qs + qo + q) * DS + dcol, dqa[e]);
         }
       }
     }
@@ -1726,7 +1749,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dk_kernel(BwdArgs a, const RT rt)
   // query head); without sharing each element is stored once
   auto put = [&](float* dk, int g, const f32x16* acc, auto D_) {
     constexpr int D = decltype(D_)::value;
-    float* base = dk + key_head(bh, g) * a.ks * D + col;
+    float* base = dk + (key_head(bh, g) * a.ks + ko) * D + col;
     if (g > 1) {
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb)
@@ -1791,8 +1814,11 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a, const RT 
   bf16* sdS = lds + 2 * TS + QE + wave * DSE;
   float* kbar = reinterpret_cast<float*>(lds + 2 * TS + QE + NW * DSE);
   int64_t lin = blockIdx.x, head0 = 0;
+  int qo = 0, ko = 0;  // the element's first query and key rows within a head (packed batches)
   if constexpr (kRagged<RT>) {  // one element of a ragged batch
     const RaggedItem r = ragged_item(rt, lin);
+    qo = r.qoff;
+    ko = r.koff;
     if (r.pad) return;
     lin = r.lin;
     head0 = r.head0;
@@ -1806,10 +1832,10 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a, const RT 
   const int z = (int)(lw % nb);
   const int off = a.n_k - a.n_q;
 
-  const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + bh * (int64_t)a.qs * D1;
-  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + key_head(bh, a.g1) * (int64_t)a.ks * D1;
-  const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + bh * (int64_t)a.qs * D2;
-  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + key_head(bh, a.g2) * (int64_t)a.ks * D2;
+  const bf16* Q1 = reinterpret_cast<const bf16*>(a.q1) + (bh * (int64_t)a.qs + qo) * D1;
+  const bf16* K1 = reinterpret_cast<const bf16*>(a.k1) + (key_head(bh, a.g1) * (int64_t)a.ks + ko) * D1;
+  const bf16* Q2 = reinterpret_cast<const bf16*>(a.q2) + (bh * (int64_t)a.qs + qo) * D2;
+  const bf16* K2 = reinterpret_cast<const bf16*>(a.k2) + (key_head(bh, a.g2) * (int64_t)a.ks + ko) * D2;
 
   const int ntile = (a.n_k + BK - 1) / BK;
   const int count = z < ntile ? (ntile - z + a.nblk - 1) / a.nblk : 0;
@@ -1827,7 +1853,7 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a, const RT 
   ref_key<DS>(kbar, SETTING == 1 ? K2 : K1, a.n_k, tid, 256);
   // lane column col is query row col: its statistics are fixed for the kernel
   const bool qv = col < a.n_q;
-  const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.qs + col, qv);
+  const RowGrad rg = load_rowgrad<SETTING>(a, bh * a.qs + qo + col, qv);
   const float c1 = a.c1, c2 = a.c2;
   // last key this lane's query sees, and the last key of which every query
   // of a wave block is visible (beyond it blocks take the element mask)
@@ -1897,7 +1923,7 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a, const RT 
       for (int nb = 0; nb < NB; ++nb) dka[nb] = MF::run(af, qcol[h][nb], dka[nb]);
     }
     const int gs = SETTING == 1 ? a.g2 : a.g1;
-    float* dk = a.dk + (key_head(bh, gs) * a.ks + kw) * (int64_t)DS + col;
+    float* dk = a.dk + (key_head(bh, gs) * a.ks + ko + kw) * (int64_t)DS + col;
     const int kleft = a.n_k - kw;
     if (gs > 1) {
       // query heads sharing a key head add their parts into the cleared dK
@@ -1934,7 +1960,7 @@ __global__ __launch_bounds__(256, 1) void bwd_decode_kernel(BwdArgs a, const RT 
   // same kbar: the sum over them is the row's r kbar
   rsum += __shfl_xor(rsum, 32);
   if (qv) {
-    float* dq = a.dq + (bh * a.qs + col) * (int64_t)DS;
+    float* dq = a.dq + (bh * a.qs + qo + col) * (int64_t)DS;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll

@@ -471,6 +471,23 @@ def mode_sweep(shapes=MODE_SWEEP) -> str:
         f"{100 * max(regrets):.1f}%.", ""])
 
 
+def _best_ms(fn, n=3):
+    """Best of n timed calls of fn (after one untimed), HIP events on torch's
+    current stream, where the binding launches."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    return best
+
+
 # ragged batches for the backward plan: (label, B, H, causal, q range, k range
 # or None for k = q, seed); lengths uniform in each range
 RAGGED_SWEEP = [
@@ -494,20 +511,7 @@ def ragged_mode_sweep(batches=RAGGED_SWEEP) -> str:
     import workloads
     from . import streamkl as sk
     dev = torch.device("cuda:0")
-
-    def best_ms(fn, n=3):
-        fn()
-        torch.cuda.synchronize()
-        best = float("inf")
-        for _ in range(n):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            best = min(best, e0.elapsed_time(e1))
-        return best
-
+    best_ms = _best_ms
     rows, regrets = [], []
     for label, B, H, causal, qr, kr, seed in batches:
         r = np.random.default_rng(seed)
@@ -547,6 +551,70 @@ def ragged_mode_sweep(batches=RAGGED_SWEEP) -> str:
         ""])
 
 
+# ragged batches for the layout comparison: (label, B, causal, q range, k range
+# or None for k = q, seed); H = 32, d = 128, bf16
+LAYOUT_SWEEP = [
+    ("short prefill", 64, True, (256, 2048), None, 3),
+    ("medium prefill", 32, True, (1024, 4096), None, 4),
+    ("tiny prefill", 16, True, (64, 512), None, 5),
+    ("decode", 64, False, (1, 16), (512, 8192), 6),
+]
+
+
+def layout_sweep(batches=LAYOUT_SWEEP) -> str:
+    """Markdown table: one forward plus setting-1 backward (automatic mode)
+    of ragged batches in padded tensors against the same sequences packed,
+    best of 5 each on cuda:0."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import workloads
+    from . import streamkl as sk
+    dev = torch.device("cuda:0")
+
+    def pack(x, lens):
+        return torch.cat([x[b, :, :n] for b, n in enumerate(lens)], dim=1).contiguous()
+
+    rows = []
+    for label, B, causal, qr, kr, seed in batches:
+        r = np.random.default_rng(seed)
+        q_len = [int(x) for x in r.integers(qr[0], qr[1] + 1, size=B)]
+        k_len = list(q_len) if kr is None else [int(x) for x in r.integers(kr[0], kr[1] + 1, size=B)]
+        w = workloads.Workload("ragged-layout", B, 32, max(q_len), max(k_len), 128, 128, "bf16", causal, 0.5,
+                               False, 9)
+        q1, k1, q2, k2 = workloads.generate(w, dev)
+        g = workloads.upstream_grad(w, dev, "mean")
+        lens = (q_len, k_len, q_len, k_len)
+        P = [pack(x, n) for x, n in zip((q1, k1, q2, k2), lens)]
+        gp = pack(g, q_len)
+        pad = dict(q_len=q_len, k_len=k_len)
+        pk = dict(q_off=[0, *np.cumsum(q_len).tolist()], k_off=[0, *np.cumsum(k_len).tolist()])
+
+        def step(t, gg, kw):
+            kl, l1, l2 = sk.streamkl_fwd(*t, causal, **kw)
+            sk.streamkl_bwd(1, *t, causal, kl, l1, l2, gg, **kw)
+
+        t_pad = _best_ms(lambda: step((q1, k1, q2, k2), g, pad), 5)
+        t_pk = _best_ms(lambda: step(P, gp, pk), 5)
+        mib = [sum(x.numel() * x.element_size() for x in ts) / 2 ** 20 for ts in ((q1, k1, q2, k2), P)]
+        kdesc = "= N_Q" if kr is None else f"{kr[0]}-{kr[1]}"
+        rows.append(f"| {label} | {B} | {qr[0]}-{qr[1]} | {kdesc} | {'yes' if causal else 'no'} | {t_pad:.3f} | "
+                    f"{t_pk:.3f} | {t_pad / t_pk:.2f} | {mib[0]:.0f} | {mib[1]:.0f} |")
+        del q1, k1, q2, k2, g, P, gp
+        torch.cuda.empty_cache()
+    return "\n".join([
+        "# Ragged batches padded and packed, one MI355X", "",
+        "Command: `python -m attention_kl_divergence_amd.profiling packed --out profiles/ragged_packed_layout.md`",
+        "",
+        "H = 32, d1 = d2 = 128, bf16, inputs from `workloads.generate` (seed 9), upstream gradient 1/N_Q per",
+        "row; each batch draws its lengths uniformly from the ranges shown (fixed seeds).  One step is",
+        "`streamkl_fwd` plus the setting-1 `streamkl_bwd` in the automatic mode, on the padded tensors with",
+        "per-sequence lengths and on the same sequences packed with row offsets.  Best of 5 steps each",
+        "(HIP events on the launch stream).  Memory: Q1, K1, Q2, K2 in each layout.", "",
+        "| batch | B | N_Q | N_K | causal | padded ms | packed ms | speed-up | padded MiB | packed MiB |",
+        "|---|---|---|---|---|---|---|---|---|---|", *rows, ""])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -577,7 +645,16 @@ def main(argv=None):
     md = sub.add_parser("modes", help="fused vs separate backward over a sweep of shapes, against the plan (needs a GPU)")
     md.add_argument("--out", default=None)
     md.add_argument("--ragged", action="store_true", help="ragged batches instead of single problems")
+    pl = sub.add_parser("packed", help="ragged batches padded against packed (needs a GPU)")
+    pl.add_argument("--out", default=None)
     args = ap.parse_args(argv)
+    if args.cmd == "packed":
+        text = layout_sweep()
+        if args.out:
+            with open(args.out, "w") as fo:
+                fo.write(text)
+        print(text)
+        return 0
     if args.cmd == "modes":
         text = ragged_mode_sweep() if args.ragged else mode_sweep()
         if args.out:

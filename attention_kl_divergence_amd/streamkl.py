@@ -36,7 +36,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("n_q", ctypes.c_int64), ("n_k", ctypes.c_int64),
                 ("d1", ctypes.c_int32), ("d2", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("kv_heads1", ctypes.c_int32), ("kv_heads2", ctypes.c_int32),
-                ("q_len", ctypes.POINTER(ctypes.c_int64)), ("k_len", ctypes.POINTER(ctypes.c_int64))]
+                ("q_len", ctypes.POINTER(ctypes.c_int64)), ("k_len", ctypes.POINTER(ctypes.c_int64)),
+                ("q_off", ctypes.POINTER(ctypes.c_int64)), ("k_off", ctypes.POINTER(ctypes.c_int64))]
 
     def set_lengths(self, q_len=None, k_len=None):
         """Ragged batch: per batch element query and key lengths (sequences of
@@ -53,8 +54,20 @@ class Shape(ctypes.Structure):
             setattr(self, name, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
         return self
 
+    def set_offsets(self, q_off, k_off):
+        """Packed batch: B + 1 query and key row offsets (sequences one after
+        another in every head).  The arrays live on this object."""
+        for name, v in (("q_off", q_off), ("k_off", k_off)):
+            v = [int(x) for x in v]
+            if len(v) != self.B + 1:
+                raise ValueError(f"{name} needs {self.B + 1} offsets")
+            arr = (ctypes.c_int64 * len(v))(*v)
+            setattr(self, "_" + name, arr)
+            setattr(self, name, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+        return self
 
-ABI_VERSION = 4
+
+ABI_VERSION = 5
 INVALID_BYTES = (1 << 64) - 1  # STREAMKL_INVALID_BYTES
 
 
@@ -146,6 +159,55 @@ def shape_of(q1, k1, q2, k2) -> Shape:
     return make_shape(B, H, n_q, n_k, d1, d2, q1.dtype, 0 if kv1 == H else kv1, 0 if kv2 == H else kv2)
 
 
+def packed_shape_of(q1, k1, q2, k2, q_off, k_off) -> Shape:
+    """The shape of a packed batch: Q_t [H, total_q, d_t], K_t [kv_t, total_k,
+    d_t], sequence b at rows [q_off[b], q_off[b+1]) and [k_off[b],
+    k_off[b+1]) of every head."""
+    for t in (q1, k1, q2, k2):
+        if t.dim() != 3:
+            raise ValueError("packed Q and K tensors must be [H, N, d]")
+        if not t.is_contiguous():
+            raise ValueError("Q and K tensors must be contiguous")
+        if t.dtype != q1.dtype:
+            raise ValueError("Q1, K1, Q2, K2 must share one dtype")
+        if t.device != q1.device:
+            raise ValueError("Q1, K1, Q2, K2 must be on one device")
+    if k_off is None or len(q_off) != len(k_off) or len(q_off) < 2:
+        raise ValueError("q_off and k_off need B + 1 offsets each")
+    H, n_q, d1 = q1.shape
+    kv1, n_k, _ = k1.shape
+    kv2, _, d2 = k2.shape
+    if (tuple(k1.shape) != (kv1, n_k, d1) or tuple(q2.shape) != (H, n_q, d2) or tuple(k2.shape) != (kv2, n_k, d2)
+            or H % kv1 or H % kv2):
+        raise ValueError("inconsistent Q/K shapes")
+    shp = make_shape(len(q_off) - 1, H, n_q, n_k, d1, d2, q1.dtype, 0 if kv1 == H else kv1, 0 if kv2 == H else kv2)
+    return shp.set_offsets(q_off, k_off)
+
+
+class _Layout:
+    """The shapes of a call's tensors: [B, H, n_q] per-row vectors and
+    [B, heads, n, d] gradients, or, for a packed batch, the same without the
+    batch dimension."""
+
+    def __init__(self, q1, k1, q2, k2, q_len=None, k_len=None, q_off=None, k_off=None):
+        self.packed = q_off is not None or k_off is not None
+        if self.packed:
+            if q_len is not None or k_len is not None:
+                raise ValueError("give lengths (padded batch) or offsets (packed batch), not both")
+            self.shp = packed_shape_of(q1, k1, q2, k2, q_off, k_off)
+        else:
+            self.shp = shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
+        s = self.shp
+        self.lead = () if self.packed else (s.B,)
+        self.rows = self.lead + (s.H, s.n_q)
+
+    def dq(self, d):
+        return self.lead + (self.shp.H, self.shp.n_q, d)
+
+    def dk(self, model, d):
+        return self.lead + (_kv(self.shp, model), self.shp.n_k, d)
+
+
 def _kv(shp: Shape, model: int) -> int:
     """Key heads of model 1 or 2."""
     kv = shp.kv_heads1 if model == 1 else shp.kv_heads2
@@ -173,10 +235,12 @@ def _check_out(t, shape, device, what):
 
 
 def _check_rows(t, shp: Shape, device, what):
-    """A per-row input vector: contiguous fp32 [B, H, n_q] on the device."""
-    if (t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != shp.B * shp.H * shp.n_q
-            or t.device != device):
-        raise ValueError(f"{what} must be contiguous fp32 [B, H, n_q] on {device}")
+    """A per-row input vector: contiguous fp32 [B, H, n_q] ([H, n_q] for a
+    packed batch) on the device."""
+    rows = shp.H * shp.n_q * (1 if shp.q_off else shp.B)
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != rows or t.device != device:
+        raise ValueError(f"{what} must be contiguous fp32 with one value per query row ([B, H, n_q], or [H, n_q] "
+                         f"packed) on {device}")
 
 
 def _bytes(n: int, what: str) -> int:
@@ -229,16 +293,20 @@ def bwd_plan(shape: Shape, causal: bool, setting: int, bwd_mode: int = BWD_AUTO)
 
 
 def streamkl_fwd(q1, k1, q2, k2, causal: bool, scale1: float = 0.0, scale2: float = 0.0,
-                 num_splits: int = 0, out=None, workspace=None, q_len=None, k_len=None):
+                 num_splits: int = 0, out=None, workspace=None, q_len=None, k_len=None, q_off=None, k_off=None):
     """Forward: returns (kl, lse1, lse2), fp32 [B, H, n_q].
 
     num_splits: 0 = library's choice, 1 = no key split, k = k key splits.
     out: optional preallocated (kl, lse1, lse2).  workspace: optional uint8
     device tensor (allocated here when a split needs one and none is given).
+    q_len, k_len: ragged batch in padded [B, H, N, d] tensors.  q_off, k_off:
+    packed batch (B + 1 row offsets each) in [H, N, d] tensors; the outputs
+    are then [H, n_q].
     """
-    shp = shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
+    lay = _Layout(q1, k1, q2, k2, q_len, k_len, q_off, k_off)
+    shp = lay.shp
     dev = q1.device
-    rows = (shp.B, shp.H, shp.n_q)
+    rows = lay.rows
     if out is None:
         kw = dict(device=dev, dtype=torch.float32)
         out = tuple(torch.empty(rows, **kw) for _ in range(3))
@@ -260,16 +328,18 @@ def streamkl_fwd(q1, k1, q2, k2, causal: bool, scale1: float = 0.0, scale2: floa
 
 
 def streamkl_fwd_loss(q1, k1, q2, k2, causal: bool, weights=None, scale1: float = 0.0, scale2: float = 0.0,
-                      num_splits: int = 0, out=None, workspace=None, q_len=None, k_len=None):
+                      num_splits: int = 0, out=None, workspace=None, q_len=None, k_len=None, q_off=None,
+                      k_off=None):
     """Forward with the loss fused into its epilogue: returns (kl, lse1, lse2, loss).
 
     loss is a 0-dim fp32 tensor: sum_i weights_i KL_i over every query row, or
     the mean KL over the rows when weights is None (bitwise repeatable).
-    out: optional preallocated (kl, lse1, lse2, loss).
+    out: optional preallocated (kl, lse1, lse2, loss).  Batches as streamkl_fwd.
     """
-    shp = shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
+    lay = _Layout(q1, k1, q2, k2, q_len, k_len, q_off, k_off)
+    shp = lay.shp
     dev = q1.device
-    rows = (shp.B, shp.H, shp.n_q)
+    rows = lay.rows
     if out is None:
         kw = dict(device=dev, dtype=torch.float32)
         out = tuple(torch.empty(rows, **kw) for _ in range(3)) + (torch.empty((), **kw),)
@@ -295,25 +365,26 @@ def streamkl_fwd_loss(q1, k1, q2, k2, causal: bool, weights=None, scale1: float 
 
 def streamkl_bwd(setting: int, q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
                  scale1: float = 0.0, scale2: float = 0.0, bwd_mode: int = BWD_AUTO, out=None,
-                 q_len=None, k_len=None):
+                 q_len=None, k_len=None, q_off=None, k_off=None):
     """Backward: returns (dQ, dK) in fp32 for the trained model.
 
     setting 1 -> (dQ2, dK2) with P1 fixed; setting 2 -> (dQ1, dK1) with P2 fixed.
-    q_len, k_len: ragged-batch lengths, as given to the forward.
+    q_len, k_len or q_off, k_off: the batch as given to the forward.
     """
-    shp = shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
+    lay = _Layout(q1, k1, q2, k2, q_len, k_len, q_off, k_off)
+    shp = lay.shp
     dev = q1.device
     ds = shp.d2 if setting == 1 else shp.d1
+    model = 2 if setting == 1 else 1
     if out is None:
         kw = dict(device=dev, dtype=torch.float32)
-        out = (None if bwd_mode == BWD_DK_ONLY else torch.empty((shp.B, shp.H, shp.n_q, ds), **kw),
-               None if bwd_mode == BWD_DQ_ONLY else torch.empty((shp.B, _kv(shp, 2 if setting == 1 else 1), shp.n_k, ds),
-                                                                **kw))
+        out = (None if bwd_mode == BWD_DK_ONLY else torch.empty(lay.dq(ds), **kw),
+               None if bwd_mode == BWD_DQ_ONLY else torch.empty(lay.dk(model, ds), **kw))
     dq, dk = out
     if bwd_mode != BWD_DK_ONLY:
-        _check_out(dq, (shp.B, shp.H, shp.n_q, ds), dev, "out dQ")
+        _check_out(dq, lay.dq(ds), dev, "out dQ")
     if bwd_mode != BWD_DQ_ONLY:
-        _check_out(dk, (shp.B, _kv(shp, 2 if setting == 1 else 1), shp.n_k, ds), dev, "out dK")
+        _check_out(dk, lay.dk(model, ds), dev, "out dK")
     for t, n in zip((lse1, lse2, d_kl, kl), ("lse1", "lse2", "d_kl", "kl")):
         if t is not None:
             _check_rows(t, shp, dev, n)
@@ -329,21 +400,19 @@ def streamkl_bwd(setting: int, q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_k
 
 def streamkl_bwd_joint(q1, k1, q2, k2, causal: bool, kl, lse1, lse2, d_kl,
                        scale1: float = 0.0, scale2: float = 0.0, bwd_mode: int = BWD_AUTO, out=None,
-                       q_len=None, k_len=None):
+                       q_len=None, k_len=None, q_off=None, k_off=None):
     """Joint backward: returns (dQ1, dK1, dQ2, dK2) in fp32, the gradients to
     both models in one pass (equal to setting 2 and setting 1 of streamkl_bwd)."""
-    shp = shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len)
+    lay = _Layout(q1, k1, q2, k2, q_len, k_len, q_off, k_off)
+    shp = lay.shp
     dev = q1.device
+    shapes = (lay.dq(shp.d1), lay.dk(1, shp.d1), lay.dq(shp.d2), lay.dk(2, shp.d2))
     if out is None:
         kw = dict(device=dev, dtype=torch.float32)
         nq = bwd_mode == BWD_DK_ONLY
         nk = bwd_mode == BWD_DQ_ONLY
-        out = (None if nq else torch.empty((shp.B, shp.H, shp.n_q, shp.d1), **kw),
-               None if nk else torch.empty((shp.B, _kv(shp, 1), shp.n_k, shp.d1), **kw),
-               None if nq else torch.empty((shp.B, shp.H, shp.n_q, shp.d2), **kw),
-               None if nk else torch.empty((shp.B, _kv(shp, 2), shp.n_k, shp.d2), **kw))
-    shapes = ((shp.B, shp.H, shp.n_q, shp.d1), (shp.B, _kv(shp, 1), shp.n_k, shp.d1),
-              (shp.B, shp.H, shp.n_q, shp.d2), (shp.B, _kv(shp, 2), shp.n_k, shp.d2))
+        out = tuple(None if (nq and i % 2 == 0) or (nk and i % 2 == 1) else torch.empty(sh, **kw)
+                    for i, sh in enumerate(shapes))
     for i, (t, want, n) in enumerate(zip(out, shapes, ("dQ1", "dK1", "dQ2", "dK2"))):
         if (bwd_mode == BWD_DK_ONLY and i % 2 == 0) or (bwd_mode == BWD_DQ_ONLY and i % 2 == 1):
             continue
@@ -403,28 +472,28 @@ def _kl_input_grads(ctx, g):
 
 class _KLFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q1, k1, q2, k2, causal, scale1, scale2, bwd_mode, q_len, k_len):
-        kl, lse1, lse2 = streamkl_fwd(q1, k1, q2, k2, causal, scale1, scale2, q_len=q_len, k_len=k_len)
+    def forward(ctx, q1, k1, q2, k2, causal, scale1, scale2, bwd_mode, q_len, k_len, q_off, k_off):
+        ctx.lens = dict(q_len=q_len, k_len=k_len, q_off=q_off, k_off=k_off)
+        kl, lse1, lse2 = streamkl_fwd(q1, k1, q2, k2, causal, scale1, scale2, **ctx.lens)
         ctx.save_for_backward(q1, k1, q2, k2, kl, lse1, lse2)
         ctx.causal, ctx.scale1, ctx.scale2, ctx.bwd_mode = causal, scale1, scale2, bwd_mode
-        ctx.lens = dict(q_len=q_len, k_len=k_len)
         return kl
 
     @staticmethod
     def backward(ctx, g):
-        return (*_kl_input_grads(ctx, g), None, None, None, None, None, None)
+        return (*_kl_input_grads(ctx, g), None, None, None, None, None, None, None, None)
 
 
 class _KLLossFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q1, k1, q2, k2, weights, causal, scale1, scale2, bwd_mode, q_len, k_len):
-        kl, lse1, lse2, loss = streamkl_fwd_loss(q1, k1, q2, k2, causal, weights, scale1, scale2,
-                                                 q_len=q_len, k_len=k_len)
+    def forward(ctx, q1, k1, q2, k2, weights, causal, scale1, scale2, bwd_mode, q_len, k_len, q_off, k_off):
+        ctx.lens = dict(q_len=q_len, k_len=k_len, q_off=q_off, k_off=k_off)
+        kl, lse1, lse2, loss = streamkl_fwd_loss(q1, k1, q2, k2, causal, weights, scale1, scale2, **ctx.lens)
         ctx.save_for_backward(q1, k1, q2, k2, kl, lse1, lse2, weights)
         ctx.causal, ctx.scale1, ctx.scale2, ctx.bwd_mode = causal, scale1, scale2, bwd_mode
-        ctx.lens = dict(q_len=q_len, k_len=k_len)
-        B, H, n_q = kl.shape
-        ctx.rows = H * (sum(int(x) for x in q_len) if q_len is not None else B * n_q)
+        # the rows the mean counts: a packed batch has no padding
+        H = kl.shape[-2]
+        ctx.rows = kl.numel() if q_len is None else H * sum(int(x) for x in q_len)
         return loss
 
     @staticmethod
@@ -437,24 +506,26 @@ class _KLLossFunction(torch.autograd.Function):
         else:
             g = torch.empty_like(kl).fill_(1.0 / max(ctx.rows, 1)).mul_(gl)
         grad_w = kl * gl if ctx.needs_input_grad[4] else None
-        return (*_kl_input_grads(ctx, g), grad_w, None, None, None, None, None, None)
+        return (*_kl_input_grads(ctx, g), grad_w, None, None, None, None, None, None, None, None)
 
 
 def attention_kl(q1, k1, q2, k2, causal: bool = False, scale1: float = 0.0, scale2: float = 0.0,
-                 bwd_mode: int = BWD_AUTO, q_len=None, k_len=None):
+                 bwd_mode: int = BWD_AUTO, q_len=None, k_len=None, q_off=None, k_off=None):
     """Per-row KL(P1 || P2) as an autograd function (gradients by streamkl_bwd).
 
     Gradients flow to whichever of (Q1, K1) / (Q2, K2) require grad: the
     student side uses setting 1 (teacher distribution held fixed), the
     teacher side setting 2 (student distribution held fixed), and both
     sides together the joint backward.  q_len, k_len: per batch element
-    lengths of a ragged batch in padded tensors (padded rows give 0).
+    lengths of a ragged batch in padded tensors (padded rows give 0);
+    q_off, k_off: row offsets of a packed batch in [H, N, d] tensors.
     """
-    return _KLFunction.apply(q1, k1, q2, k2, causal, scale1, scale2, bwd_mode, q_len, k_len)
+    return _KLFunction.apply(q1, k1, q2, k2, causal, scale1, scale2, bwd_mode, q_len, k_len, q_off, k_off)
 
 
 def attention_kl_loss(q1, k1, q2, k2, causal: bool = False, weights=None, scale1: float = 0.0,
-                      scale2: float = 0.0, bwd_mode: int = BWD_AUTO, q_len=None, k_len=None):
+                      scale2: float = 0.0, bwd_mode: int = BWD_AUTO, q_len=None, k_len=None, q_off=None,
+                      k_off=None):
     """The distillation loss sum_i w_i KL_i (weights: fp32 [B, H, N_Q]), or the
     mean KL over the query rows (ragged batches: each element's rows), as a
     0-dim autograd tensor.  The forward forms it in its epilogue
@@ -462,4 +533,5 @@ def attention_kl_loss(q1, k1, q2, k2, causal: bool = False, weights=None, scale1
     backward feeds d loss / d KL_i = w_i (or 1 / rows) to the kernels as
     attention_kl does, and gives weights the gradient KL_i when they
     require one."""
-    return _KLLossFunction.apply(q1, k1, q2, k2, weights, causal, scale1, scale2, bwd_mode, q_len, k_len)
+    return _KLLossFunction.apply(q1, k1, q2, k2, weights, causal, scale1, scale2, bwd_mode, q_len, k_len, q_off,
+                                 k_off)

@@ -93,6 +93,20 @@ typedef struct {
    * what a call on its trimmed tensors with the same split count computes. */
   const int64_t* q_len;
   const int64_t* k_len;
+  /* Packed batches (HOST arrays of B + 1 row offsets, or NULL; set both or
+   * neither, and then leave q_len and k_len NULL): the sequences lie one
+   * after another in every head, with no padding.  Batch element b owns
+   * query rows [q_off[b], q_off[b+1]) and key rows [k_off[b], k_off[b+1])
+   * of every head.  The tensors have no batch dimension: Q_t [H, n_q, d_t],
+   * K_t [kv_heads_t, n_k, d_t], KL, LSE1, LSE2, weights and d_kl [H, n_q],
+   * dQ_s [H, n_q, d_s], dK_s [kv_heads_s, n_k, d_s], where n_q = q_off[B]
+   * and n_k = k_off[B] are the total rows.  Offsets start at 0 and never
+   * decrease, and each element's lengths follow the rules of ragged batches
+   * above.  The same per-sequence kernels serve both layouts (the pages'
+   * next step for ragged batches: per-sequence offsets); a packed batch has
+   * no padded rows to clear.  Read during the call only. */
+  const int64_t* q_off;
+  const int64_t* k_off;
 } streamkl_shape;
 
 /* Launch options (host struct; a NULL pointer means all defaults). */
@@ -214,7 +228,10 @@ streamkl_status streamkl_fwd_loss_noalloc(const void* Q1, const void* K1, const 
                                           void* stream);
 
 /* The backward mode streamkl_bwd will use (1 fused, 2 separate, or the
- * requested 3/4), 0 if invalid. */
+ * requested 3/4), 0 if invalid.  For a ragged batch, padded or packed, it is
+ * the mode of the padded batch of the longest query and key lengths: the
+ * plan streamkl_bwd_joint takes for the whole batch (in the automatic mode,
+ * streamkl_bwd plans each element, or each group of elements, on its own). */
 int streamkl_bwd_plan(const streamkl_shape* shape, int causal, int setting,
                       const streamkl_launch* launch);
 
@@ -286,7 +303,8 @@ int streamkl_last_hip_error(void);
 
 /* Library version, for the Python binding's load check (3: streamkl_shape
  * carries kv_heads1, kv_heads2 and the ragged-batch lengths; 4: the fused
- * loss, the backward workspace query, STREAMKL_INVALID_BYTES). */
+ * loss, the backward workspace query, STREAMKL_INVALID_BYTES; 5:
+ * streamkl_shape carries the packed-batch offsets q_off, k_off). */
 int streamkl_version(void);
 
 #ifdef __cplusplus

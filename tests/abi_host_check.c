@@ -96,6 +96,31 @@ int main(void) {
   EXPECT(streamkl_fwd(p, p, p, p, 1, 0.f, 0.f, fp, fp, fp, &r, NULL, NULL) == STREAMKL_ERR_INVALID);
   EXPECT(streamkl_fwd_loss_workspace_bytes(&r, 1, NULL) == STREAMKL_INVALID_BYTES);
 
+  /* packed batches: offsets from 0 to the totals, nondecreasing, both or neither, no lengths beside them */
+  int64_t qo[4] = {0, 600, 600, 697}, ko[4] = {0, 600, 605, 702};
+  streamkl_shape pk = shape(3, 8, 697, 702, 128, 128, STREAMKL_BF16);
+  pk.q_off = qo; pk.k_off = ko;
+  EXPECT(streamkl_fwd_workspace_bytes(&pk, 1, NULL) != STREAMKL_INVALID_BYTES);
+  EXPECT(streamkl_fwd_loss_workspace_bytes(&pk, 1, NULL) != STREAMKL_INVALID_BYTES);
+  EXPECT(streamkl_fwd_plan(&pk, 1, NULL) >= 1);
+  pk.n_q = 700;  /* the total rows disagree with the offsets */
+  EXPECT(streamkl_fwd(p, p, p, p, 1, 0.f, 0.f, fp, fp, fp, &pk, NULL, NULL) == STREAMKL_ERR_INVALID);
+  pk.n_q = 697;
+  int64_t qdown[4] = {0, 600, 500, 697};  /* decreasing */
+  pk.q_off = qdown;
+  EXPECT(streamkl_fwd(p, p, p, p, 1, 0.f, 0.f, fp, fp, fp, &pk, NULL, NULL) == STREAMKL_ERR_INVALID);
+  pk.q_off = qo;
+  pk.k_off = NULL;  /* one without the other */
+  EXPECT(streamkl_fwd_workspace_bytes(&pk, 1, NULL) == STREAMKL_INVALID_BYTES);
+  pk.k_off = ko;
+  pk.q_len = ql;  /* lengths beside offsets */
+  EXPECT(streamkl_fwd_workspace_bytes(&pk, 1, NULL) == STREAMKL_INVALID_BYTES);
+  pk.q_len = NULL;
+  int64_t kshort[4] = {0, 600, 605, 605};  /* element 2: 97 query rows, no key */
+  pk.k_off = kshort;
+  pk.n_k = 605;
+  EXPECT(streamkl_fwd_workspace_bytes(&pk, 0, NULL) == STREAMKL_INVALID_BYTES);
+
   /* planning and sizing of valid shapes (no device: the planner assumes 256 compute units) */
   streamkl_shape dec = shape(1, 32, 16, 131072, 128, 128, STREAMKL_BF16);
   size_t ws = streamkl_fwd_workspace_bytes(&dec, 0, NULL);
@@ -110,7 +135,7 @@ int main(void) {
   EXPECT(streamkl_bwd_plan(&big, 1, 1, NULL) == STREAMKL_BWD_SEPARATE);
   EXPECT(streamkl_bwd_plan(&dec, 0, 1, NULL) == STREAMKL_BWD_FUSED);
   for (int st = 0; st < 6; ++st) EXPECT(streamkl_status_string(st) != NULL);
-  EXPECT(streamkl_version() == 4);
+  EXPECT(streamkl_version() == 5);
 
   if (failures) {
     fprintf(stderr, "%d check(s) failed\n", failures);

@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from attention_kl_divergence_amd import streamkl as sk
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = sk.library()
-    assert lib.streamkl_version() == sk.ABI_VERSION == 4
+    assert lib.streamkl_version() == sk.ABI_VERSION == 5
     assert lib.streamkl_status_string(0) == b"ok"
     assert lib.streamkl_status_string(4) == b"HIP runtime error"
     assert lib.streamkl_status_string(99) == b"unknown status"
@@ -308,3 +309,27 @@ def test_bwd_mode_plan():
     assert sk.bwd_plan(small_q, False, 1) == sk.BWD_FUSED
     assert sk.bwd_plan(big, True, 1, sk.BWD_FUSED) == sk.BWD_FUSED
     assert sk.bwd_plan(small_q, False, 2, sk.BWD_SEPARATE) == sk.BWD_SEPARATE
+
+
+@pytest.mark.parametrize("q_len,k_len,causal", [
+    ([16, 1, 0, 32], [131072, 4000, 9, 600], False),     # decode-shaped elements
+    ([4096, 300, 0, 8192], [4096, 300, 5, 8192], True),  # prefill elements
+    ([64, 16, 100, 0, 9, 40], [2000, 3000, 4000, 10, 2500, 2100], False),
+])
+def test_ragged_plans_match_in_both_layouts(q_len, k_len, causal):
+    """A ragged batch plans and sizes the same padded or packed; its whole-batch
+    backward plan is that of the padded batch of its longest lengths."""
+    B = len(q_len)
+    pad = shape(B=B, H=8, n_q=max(q_len), n_k=max(k_len)).set_lengths(q_len, k_len)
+    off = lambda v: [0] + list(np.cumsum(v))
+    pk = shape(B=B, H=8, n_q=sum(q_len), n_k=sum(k_len)).set_offsets(off(q_len), off(k_len))
+    dense = shape(B=B, H=8, n_q=max(q_len), n_k=max(k_len))
+    lib = sk.library()
+    for setting in (1, 2):
+        assert sk.bwd_plan(pad, causal, setting) == sk.bwd_plan(pk, causal, setting) == \
+            sk.bwd_plan(dense, causal, setting)
+        for mode in (sk.BWD_AUTO, sk.BWD_FUSED, sk.BWD_SEPARATE):
+            assert sk.bwd_workspace_bytes(pad, causal, setting, mode) == sk.bwd_workspace_bytes(pk, causal, setting, mode)
+    for ws in (lib.streamkl_fwd_workspace_bytes, lib.streamkl_fwd_loss_workspace_bytes):
+        assert ws(ctypes.byref(pad), int(causal), None) == ws(ctypes.byref(pk), int(causal), None)
+    assert sk.fwd_plan(pad, causal) == sk.fwd_plan(pk, causal)
