@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--compare-modes", action="store_true",
                     help="after the timed steps, time each backward setting once in the mode the plan "
                          "did not pick (fused vs separate) and report it as alt_bwd_ms")
+    ap.add_argument("--packed", action="store_true",
+                    help="ragged workloads: the sequences one after another in every head, with row offsets, "
+                         "instead of padded tensors with lengths")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="launch one plain device copy of this size first (the counter reference "
                          "for the HBM traffic summary)")
@@ -63,9 +66,9 @@ def cpu_baseline(w, rows_wanted, head_bytes=None, gpu=None):
     head_bytes (the algorithmic HBM bytes of one head's step, for the
     bandwidth-bound decode shapes) the sample must be whole heads and the rate
     is in GB/s.  gpu: head 0's inputs as the GPU received them and its outputs
-    ({"inputs": [q1, k1, q2, k2], "kl", "lse1", "lse2", "dq": {setting: array}},
-    host arrays); the oracle runs on those inputs and the errors of the GPU's
-    rows against it are returned too."""
+    ({"inputs": [q1, k1, q2, k2], "g", "kl", "lse1", "lse2", "dq": {setting:
+    array}}, host arrays, g the step's upstream gradient); the oracle runs on
+    those inputs and the errors of the GPU's rows against it are returned too."""
     import numpy as np
     import oracle
     try:
@@ -75,7 +78,7 @@ def cpu_baseline(w, rows_wanted, head_bytes=None, gpu=None):
         threads = os.cpu_count() or 1
     hi = gpu["inputs"]
     n_q, n_k = hi[0].shape[0], hi[1].shape[0]
-    g = np.full(n_q, 1.0 / n_q)  # the step's upstream gradient (mean KL)
+    g = gpu["g"]
     rows = np.arange(max(0, n_q - rows_wanted), n_q)
     block = max(1, min(64, (1 << 22) // n_k))
     t0 = time.perf_counter()
@@ -135,13 +138,30 @@ def main():
     g = workloads.upstream_grad(w, dev, "mean")
     # ragged workloads: the same lengths for queries and keys of each element
     lens = dict(q_len=list(w.lengths), k_len=list(w.lengths)) if w.lengths else {}
-    shp = sk.shape_of(q1, k1, q2, k2).set_lengths(**lens)
     kv = k1.shape[1]
+    packed = args.packed
+    if packed:
+        if not w.lengths:
+            print(json.dumps({"error": f"--packed needs a ragged workload; {w.name} has none"}))
+            return 2
+        # element b's rows [0, n_b) of every head, one element after another
+        pack = lambda t: torch.cat([t[b, :, :n] for b, n in enumerate(w.lengths)], dim=1).contiguous()  # noqa: E731
+        q1, k1, q2, k2, g = (pack(t) for t in (q1, k1, q2, k2, g))
+        torch.cuda.empty_cache()
+        off = [0]
+        for n in w.lengths:
+            off.append(off[-1] + n)
+        lens = dict(q_off=off, k_off=off)
+        shp = sk.packed_shape_of(q1, k1, q2, k2, off, off)
+        rows_q, rows_k = (w.H, off[-1]), (kv, off[-1])  # per-row outputs, dK leading dims
+    else:
+        shp = sk.shape_of(q1, k1, q2, k2).set_lengths(**lens)
+        rows_q, rows_k = (w.B, w.H, w.n_q), (w.B, kv, w.n_k)
     mode = {"auto": sk.BWD_AUTO, "fused": sk.BWD_FUSED, "separate": sk.BWD_SEPARATE}[args.bwd_mode]
     splits = sk.fwd_plan(shp, w.causal)
 
     f32 = dict(device=dev, dtype=torch.float32)
-    kl, l1, l2 = (torch.empty((w.B, w.H, w.n_q), **f32) for _ in range(3))
+    kl, l1, l2 = (torch.empty(rows_q, **f32) for _ in range(3))
     ws_bytes = sk.fwd_workspace_bytes(shp, w.causal)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
@@ -151,8 +171,8 @@ def main():
     modes = {}
     joint = args.joint and tuple(sorted(w.settings)) == (1, 2)
     if joint:
-        jo = (torch.empty((w.B, w.H, w.n_q, w.d1), **f32), torch.empty((w.B, kv, w.n_k, w.d1), **f32),
-              torch.empty((w.B, w.H, w.n_q, w.d2), **f32), torch.empty((w.B, kv, w.n_k, w.d2), **f32))
+        jo = (torch.empty((*rows_q, w.d1), **f32), torch.empty((*rows_k, w.d1), **f32),
+              torch.empty((*rows_q, w.d2), **f32), torch.empty((*rows_k, w.d2), **f32))
         calls.append(("bwdj_dk", lambda: sk.streamkl_bwd_joint(q1, k1, q2, k2, w.causal, kl, l1, l2, g,
                                                                 bwd_mode=sk.BWD_DK_ONLY, out=(None, jo[1], None, jo[3]),
                                                                 **lens)))
@@ -164,8 +184,8 @@ def main():
         grads = {2: (jo[0], jo[1]), 1: (jo[2], jo[3])}
     for setting in (() if joint else w.settings):
         ds = w.d2 if setting == 1 else w.d1
-        dq = torch.empty((w.B, w.H, w.n_q, ds), **f32)
-        dk = torch.empty((w.B, kv, w.n_k, ds), **f32)
+        dq = torch.empty((*rows_q, ds), **f32)
+        dk = torch.empty((*rows_k, ds), **f32)
         grads[setting] = (dq, dk)
         plan = sk.bwd_plan(shp, w.causal, setting, mode)
         modes[setting] = plan
@@ -288,7 +308,9 @@ def main():
         roof["traffic"] = int(t.get("fetch_bytes", 0) + t.get("write_bytes", 0))
         roof["traffic_unit"] = "bytes per launch: FETCH_SIZE + WRITE_SIZE, copy-calibrated"
 
-    extra_hbm = 3 * 4 * w.B * w.H * w.n_q + ws_bytes
+    extra_hbm = 3 * 4 * kl.numel() + ws_bytes
+    # the two bf16 probability matrices a materialising implementation would hold
+    qk_cells = sum(n * n for n in w.lengths) if w.lengths else w.B * w.n_q * w.n_k
     names = {sk.BWD_FUSED: "fused", sk.BWD_SEPARATE: "separate"}
     headline = w.name == "h32-n64k-d128-bf16-causal"
     out = {
@@ -311,12 +333,13 @@ def main():
                    "bwd_modes": {str(k): names[v] for k, v in modes.items()} if not joint else {"1+2": "joint"},
                    "fwd_splits": splits, "parallelism": "single GPU",
                    **({"kv_heads": kv} if kv != w.H else {}),
-                   **({"lengths": list(w.lengths)} if w.lengths else {})},
+                   **({"lengths": list(w.lengths), "layout": "packed" if packed else "padded"}
+                      if w.lengths else {})},
         "pct_of_mfma_peak": round(100 * value / peak, 2),
         "per_kernel_ms": {k: round(v, 4) for k, v in per_call.items()},
         "algorithmic_tflop_per_step": round(flops_step / 1e12, 4),
         "extra_hbm_bytes": extra_hbm,
-        "materialised_bytes_avoided": 2 * w.B * w.H * w.n_q * w.n_k * 2,
+        "materialised_bytes_avoided": 2 * 2 * w.H * qk_cells,
         "roofline": roof,
         "device_probe": probe,
     }
@@ -370,8 +393,8 @@ def main():
         for setting in (() if joint else w.settings):
             ds = w.d2 if setting == 1 else w.d1
             other = sk.BWD_SEPARATE if modes[setting] == sk.BWD_FUSED else sk.BWD_FUSED
-            dq = torch.empty((w.B, w.H, w.n_q, ds), **f32)
-            dk = torch.empty((w.B, kv, w.n_k, ds), **f32)
+            dq = torch.empty((*rows_q, ds), **f32)
+            dk = torch.empty((*rows_k, ds), **f32)
             run = lambda: sk.streamkl_bwd(setting, q1, k1, q2, k2, w.causal, kl, l1, l2, g,  # noqa: E731
                                           bwd_mode=other, out=(dq, dk), **lens)
             run()
@@ -387,10 +410,11 @@ def main():
         hb = sum(nbytes[n] for n, _ in calls) / (w.B * w.H) if decode else None
         n0 = w.lengths[0] if w.lengths else w.n_q  # rows (= keys of a ragged element) of batch element 0
         nk0 = w.lengths[0] if w.lengths else w.n_k
-        host = lambda t, n: t.float().cpu().numpy().astype("float64")[:n]  # noqa: E731
-        gpu = {"inputs": [host(q1[0, 0], n0), host(k1[0, 0], nk0), host(q2[0, 0], n0), host(k2[0, 0], nk0)],
-               "kl": host(kl[0, 0], n0), "lse1": host(l1[0, 0], n0), "lse2": host(l2[0, 0], n0),
-               "dq": {st: host(grads[st][0][0, 0], n0) for st in w.settings if st in grads}}
+        # head 0 of element 0 (a packed element 0 starts at row 0 of every head)
+        host = lambda t, n: (t[0] if packed else t[0, 0]).float().cpu().numpy().astype("float64")[:n]  # noqa: E731
+        gpu = {"inputs": [host(q1, n0), host(k1, nk0), host(q2, n0), host(k2, nk0)], "g": host(g, n0),
+               "kl": host(kl, n0), "lse1": host(l1, n0), "lse2": host(l2, n0),
+               "dq": {st: host(grads[st][0], n0) for st in w.settings if st in grads}}
         out["cpu_baseline"], out["oracle_errors"] = cpu_baseline(w, min(args.cpu_rows, max(1, int(4e8 // nk0))),
                                                                  hb, gpu)
     print(json.dumps(out))
