@@ -102,9 +102,9 @@ typedef struct {
    * dQ_s [H, n_q, d_s], dK_s [kv_heads_s, n_k, d_s], where n_q = q_off[B]
    * and n_k = k_off[B] are the total rows.  Offsets start at 0 and never
    * decrease, and each element's lengths follow the rules of ragged batches
-   * above.  The same per-sequence kernels serve both layouts (the pages'
-   * next step for ragged batches: per-sequence offsets); a packed batch has
-   * no padded rows to clear.  Read during the call only. */
+   * above, and the batch holds at least one query and one key row.  The
+   * same per-sequence kernels serve both layouts; a packed batch has no
+   * padded rows to clear.  Read during the call only. */
   const int64_t* q_off;
   const int64_t* k_off;
 } streamkl_shape;
