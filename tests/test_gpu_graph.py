@@ -154,3 +154,35 @@ def test_captured_ragged_decode_step(cuda_device):
 
     # the decode backward adds its dQ partials with atomics
     _replays(w, step, (q1, k1, q2, k2, g), exact=(True, True, True, False, True), rtol=1e-5)
+
+
+def test_captured_packed_step(cuda_device):
+    # a packed batch (sequences one after another, row offsets): 50 causal
+    # sequences of 30-500 rows and, in a second batch, 30 decode-shaped
+    # requests; forward with the loss, the separate and the automatic backward
+    import numpy as np
+    r = np.random.default_rng(14)
+    for causal, q_len, k_len in (
+            (True, *(2 * [[int(r.integers(30, 500)) for _ in range(50)]])),
+            (False, [int(r.integers(1, 33)) for _ in range(30)], [int(r.integers(300, 4000)) for _ in range(30)])):
+        qo, ko = [0, *np.cumsum(q_len).tolist()], [0, *np.cumsum(k_len).tolist()]
+        H, nq, nk = 8, qo[-1], ko[-1]
+        name = f"graph-packed-{'causal' if causal else 'decode'}"
+        print(name, flush=True)
+        gen = torch.Generator(device=cuda_device).manual_seed(15)
+        q1, q2 = (torch.randn((H, nq, 128), generator=gen, device=cuda_device).to(torch.bfloat16) for _ in range(2))
+        k1, k2 = (torch.randn((H, nk, 128), generator=gen, device=cuda_device).to(torch.bfloat16) for _ in range(2))
+        g = torch.randn((H, nq), generator=gen, device=cuda_device) / 100
+        weights = torch.rand((H, nq), device=cuda_device)
+        lk = dict(q_off=qo, k_off=ko)
+
+        def step():
+            kl, l1, l2, loss = sk.streamkl_fwd_loss(q1, k1, q2, k2, causal, weights, **lk)
+            dq, dk = sk.streamkl_bwd(1, q1, k1, q2, k2, causal, kl, l1, l2, g, bwd_mode=sk.BWD_SEPARATE, **lk)
+            dqa, dka = sk.streamkl_bwd(2, q1, k1, q2, k2, causal, kl, l1, l2, g, **lk)
+            return kl, l1, l2, loss, dq, dk, dqa, dka
+
+        # the automatic backward may add dQ with atomics (decode-shaped or
+        # fused elements)
+        w = workloads.Workload(name, len(q_len), H, nq, nk, 128, 128, "bf16", causal, 0.5, False, 8)
+        _replays(w, step, (q1, k1, q2, k2, g), exact=(True,) * 6 + (False, True), rtol=1e-5)

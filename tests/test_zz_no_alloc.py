@@ -4,6 +4,7 @@ through the C ABI: two calls in a row, the second with a smaller input,
 then the plain forward through it, then a request too large for its scratch."""
 import ctypes
 
+import numpy as np
 import pytest
 import torch
 
@@ -35,8 +36,8 @@ def _outs(w, dev, fill=7.0):
     return tuple(torch.full((w.B, w.H, w.n_q), fill, **f32) for _ in range(3)) + (torch.full((), fill, **f32),)
 
 
-def _noalloc(lib, q1, k1, q2, k2, causal, weights, out, num_splits=0, with_loss=True):
-    shp = sk.shape_of(q1, k1, q2, k2)
+def _noalloc(lib, q1, k1, q2, k2, causal, weights, out, num_splits=0, with_loss=True, shp=None):
+    shp = sk.shape_of(q1, k1, q2, k2) if shp is None else shp
     ln = sk.Launch(num_splits, 0, None, 0)
     return lib.streamkl_fwd_loss_noalloc(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), int(causal), 0.0, 0.0,
                                          _ptr(weights), *(_ptr(t) for t in out[:3]),
@@ -95,3 +96,34 @@ def test_noalloc_rejects_requests_beyond_its_scratch(cuda_device):
     torch.cuda.synchronize()
     for a, b in zip(out, ref):
         assert torch.equal(a, b)
+
+
+def test_noalloc_ragged_batches(cuda_device):
+    """A ragged batch of decode-shaped requests (grouped split-K partials in
+    the scratch), longer query ranges and an empty element, padded and
+    packed: every output equal to streamkl_fwd_loss with a workspace, padded
+    rows cleared over earlier contents."""
+    lib = _lib()
+    q_len = [16, 1, 0, 200, 9, 32, 64, 5]
+    k_len = [3000, 700, 40, 900, 5000, 2048, 2500, 64]
+    B, H = len(q_len), 8
+    w = workloads.Workload("na-ragged", B, H, max(q_len), max(k_len), 128, 128, "bf16", False, 0.5, False, 25)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    wt = torch.rand((B, H, w.n_q), device=cuda_device)
+
+    def pack(t, lens):
+        return torch.cat([t[b, :, :n] for b, n in enumerate(lens)], dim=1).contiguous()
+
+    qo, ko = [0, *np.cumsum(q_len).tolist()], [0, *np.cumsum(k_len).tolist()]
+    P = [pack(t, n) for t, n in zip((q1, k1, q2, k2), (q_len, k_len, q_len, k_len))]
+    layouts = [("padded", (q1, k1, q2, k2), wt, sk.shape_of(q1, k1, q2, k2).set_lengths(q_len, k_len),
+                dict(q_len=q_len, k_len=k_len)),
+               ("packed", P, pack(wt, q_len), sk.packed_shape_of(*P, qo, ko), dict(q_off=qo, k_off=ko))]
+    for name, t, wts, shp, kw in layouts:
+        _say(f"ragged {name}: fwd plan {sk.fwd_plan(shp, False)}")
+        ref = sk.streamkl_fwd_loss(*t, False, wts, **kw)
+        out = tuple(torch.full_like(r, 7.0) for r in ref)
+        assert _noalloc(lib, *t, False, wts, out, shp=shp) == sk.OK
+        torch.cuda.synchronize()
+        for a, b, n in zip(out, ref, ("kl", "lse1", "lse2", "loss")):
+            assert torch.equal(a, b), f"{name}: {n} differs from streamkl_fwd_loss"
