@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import test_gpu_random_ragged as random_ragged
 import workloads
 from attention_kl_divergence_amd import streamkl as sk
 from parity import check_forward_rows, check_grad, to_np
@@ -74,9 +75,10 @@ def _same(a, b, exact, what):
         torch.testing.assert_close(a, b, rtol=1e-5, atol=1e-6 * b.abs().max().item(), msg=what)
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_packed_matches_padded(case, cuda_device):
-    w, (q1, k1, q2, k2, g), q_len, k_len = _inputs(case, cuda_device)
+def _check_layouts(w, q1, k1, q2, k2, g, q_len, k_len, dev, oracle_rows=True):
+    """Every entry point on the padded batch and on the same sequences packed:
+    each sequence's outputs equal across the layouts (bitwise except sums
+    formed by atomics); the longest sequence against the oracle."""
     H, causal = w.H, w.causal
     g1, g2 = H // k1.shape[1], H // k2.shape[1]
     pad = dict(q_len=q_len, k_len=k_len)
@@ -87,7 +89,7 @@ def test_packed_matches_padded(case, cuda_device):
 
     fwd_a = sk.streamkl_fwd(q1, k1, q2, k2, causal, **pad)
     fwd_b = sk.streamkl_fwd(*P, causal, **pk)
-    weights = torch.rand((w.B, H, w.n_q), device=cuda_device)
+    weights = torch.rand((w.B, H, w.n_q), device=dev)
     loss_a = sk.streamkl_fwd_loss(q1, k1, q2, k2, causal, weights, **pad)[3]
     loss_b = sk.streamkl_fwd_loss(*P, causal, _pack(weights, q_len), **pk)[3]
     modes = (sk.BWD_AUTO, sk.BWD_SEPARATE, sk.BWD_FUSED)
@@ -116,6 +118,8 @@ def test_packed_matches_padded(case, cuda_device):
         lens = q_len if i % 2 == 0 else k_len
         exact = (i % 2 == 0 and joint_sep) or (i % 2 == 1 and (g1 if i == 1 else g2) == 1)
         _same(b, _pack(a, lens), exact, f"{w.name} joint output {i}")
+    if not oracle_rows:
+        return
 
     # one sequence straight against the oracle, from the packed outputs
     b = int(np.argmax(q_len))
@@ -135,6 +139,30 @@ def test_packed_matches_padded(case, cuda_device):
         ref_dk[h // g2] += rdk
     for kh in range(ref_dk.shape[0]):
         check_grad(f"{w.name} packed b{b} kh{kh} dK", dk[kh, ko:ko + nk], ref_dk[kh])
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_packed_matches_padded(case, cuda_device):
+    w, (q1, k1, q2, k2, g), q_len, k_len = _inputs(case, cuda_device)
+    _check_layouts(w, q1, k1, q2, k2, g, q_len, k_len, cuda_device)
+
+
+RANDOM = [c for c in random_ragged.CASES if sum(c[10]) > 0]
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_batches_packed(case, cuda_device):
+    """The seeded random ragged batches (dtypes, head dims, masks, grouped
+    keys, empty and decode-shaped sequences) packed against padded."""
+    name, dt, d1, d2, causal, H, kv1, kv2, n_q, n_k, q_len, k_len = case
+    B = len(q_len)
+    w = workloads.Workload(name, B, H, n_q, n_k, d1, d2, dt, causal, 0.0, True, 31)
+    q1, _, q2, _ = workloads.generate(w, cuda_device)
+    gen = torch.Generator(device=cuda_device).manual_seed(91)
+    k1 = torch.randn((B, kv1, n_k, d1), generator=gen, device=cuda_device).to(w.torch_dtype)
+    k2 = torch.randn((B, kv2, n_k, d2), generator=gen, device=cuda_device).to(w.torch_dtype)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    _check_layouts(w, q1, k1, q2, k2, g, q_len, k_len, cuda_device, oracle_rows=False)
 
 
 def test_packed_autograd_loss(cuda_device):
