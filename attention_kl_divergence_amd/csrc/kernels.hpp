@@ -527,6 +527,7 @@ __device__ __forceinline__ void fwd_tile_max(const f32x16 (&s1)[NKB], const f32x
 // into the state.  Together they equal fwd_update<false>.
 struct FwdPre {
   float M1n, M2n, al1, al2;
+  bool fresh;  // held offsets: the state had no offset yet (first unmasked tile)
 };
 template <int NKB>
 __device__ __forceinline__ FwdPre fwd_pre(const RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], float c1, float c2) {
@@ -567,6 +568,90 @@ __device__ __forceinline__ void fwd_post(RowState& st, const f32x16 (&t1)[NKB], 
   st.A = fmaf(p.al1, st.A, fmaf(p.M1n - p.M2n, sl1, sA));
   st.M1 = p.M1n;
   st.M2 = p.M2n;
+}
+
+// An unmasked tile's update with the state's offsets held.  The offsets M_t
+// need not be the running maxima: any M_t give the same KL and LSE as long as
+// no term 2^(y_t - M_t) overflows and the largest terms stay normal floats.
+// fwd_pre_held turns the logits in place into t_t = y_t - M_t with the
+// state's offsets (0 for an offset still at -inf, whose sums are 0), so the
+// logits phase takes no tile maxima.  fwd_post_held sums 2^t.  A lane whose
+// state had no offset yet (its first unmasked tile), or whose tile sums pass
+// 2^64 or overflow, raises its offsets to the tile maxima of y instead (never
+// lowering them) and sums again.  So every offset is a maximum of y over keys
+// already seen, every term stays below 2^64 and the largest ones near 1.
+template <int NKB>
+__device__ __forceinline__ FwdPre fwd_pre_held(const RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], float c1,
+                                               float c2) {
+  FwdPre p;
+  p.fresh = st.M1 == kNegInf || st.M2 == kNegInf;
+  p.M1n = finite_or_zero(st.M1);
+  p.M2n = finite_or_zero(st.M2);
+  p.al1 = 1.f;
+  p.al2 = 1.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s1[kb][e] = fmaf(s1[kb][e], c1, -p.M1n);
+      s2[kb][e] = fmaf(s2[kb][e], c2, -p.M2n);
+    }
+  return p;
+}
+template <int NKB>
+__device__ __forceinline__ void fwd_post_held(RowState& st, const f32x16 (&t1)[NKB], const f32x16 (&t2)[NKB],
+                                              const FwdPre& p) {
+  constexpr float kCap = 18446744073709551616.f;  // 2^64
+  float sl1 = 0.f, sl2 = 0.f, sA = 0.f;
+  bool again = p.fresh;
+  if (!again) {
+    float tl1[4] = {0.f, 0.f, 0.f, 0.f}, tl2[4] = {0.f, 0.f, 0.f, 0.f}, tA[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p1 = exp2_fast(t1[kb][e]);
+        const float p2 = exp2_fast(t2[kb][e]);
+        tl1[e & 3] += p1;
+        tl2[e & 3] += p2;
+        tA[e & 3] = fmaf(p1, t1[kb][e] - t2[kb][e], tA[e & 3]);
+      }
+    sl1 = (tl1[0] + tl1[1]) + (tl1[2] + tl1[3]);
+    sl2 = (tl2[0] + tl2[1]) + (tl2[2] + tl2[3]);
+    sA = (tA[0] + tA[1]) + (tA[2] + tA[3]);
+    again = !(sl1 <= kCap && sl2 <= kCap);
+  }
+  float m1 = p.M1n, m2 = p.M2n, al1 = 1.f, al2 = 1.f;
+  if (__builtin_expect(again, 0)) {
+    // offsets raised to the tile maxima (a fresh state takes them whole; the
+    // old sums of a fresh state are 0) and the tile summed again
+    float mx1, mx2;
+    fwd_tile_max<NKB>(t1, t2, mx1, mx2);
+    const float h1 = p.fresh ? mx1 : fmaxf(mx1, 0.f), h2 = p.fresh ? mx2 : fmaxf(mx2, 0.f);
+    m1 += h1;
+    m2 += h2;
+    al1 = p.fresh ? 0.f : exp2_fast(-h1);
+    al2 = p.fresh ? 0.f : exp2_fast(-h2);
+    float u1[4] = {0.f, 0.f, 0.f, 0.f}, u2[4] = {0.f, 0.f, 0.f, 0.f}, uA[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float v1 = t1[kb][e] - h1, v2 = t2[kb][e] - h2;
+        const float p1 = exp2_fast(v1);
+        u1[e & 3] += p1;
+        u2[e & 3] += exp2_fast(v2);
+        uA[e & 3] = fmaf(p1, v1 - v2, uA[e & 3]);
+      }
+    sl1 = (u1[0] + u1[1]) + (u1[2] + u1[3]);
+    sl2 = (u2[0] + u2[1]) + (u2[2] + u2[3]);
+    sA = (uA[0] + uA[1]) + (uA[2] + uA[3]);
+  }
+  st.l1 = fmaf(al1, st.l1, sl1);
+  st.l2 = fmaf(al2, st.l2, sl2);
+  st.A = fmaf(al1, st.A, fmaf(m1 - m2, sl1, sA));
+  st.M1 = m1;
+  st.M2 = m2;
 }
 
 // Forward online update of one lane's running state with NKB 32-key blocks of
@@ -1029,15 +1114,18 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a, const RT rt) 
   // update phase, the longer one, keeps the exponentials and sums (fwd_post).
   // Forward 37.1 -> 35.2 ms at 64K causal against the whole update in the
   // update phase (36.2 ms with only the maxima moved).
+  // Unmasked tiles hold the state's offsets (fwd_pre_held), so their logits
+  // phase takes no maxima; masked tiles take them.
   auto masked = [&](int k0) { return (k0 + BK > kend) || (a.causal && k0 + BK - 1 > q0 + off); };
   auto logits = [&](const T* sK1, const T* sK2, int k0) {
     fwd_logits<T, D1, D2, NKB>(s1, s2, sK1, sK2, qf1, qf2, col, grp);
-    if (!masked(k0)) pre = fwd_pre<NKB>(st, s1, s2, c1, c2);
+    if (masked(k0)) return;
+    pre = fwd_pre_held<NKB>(st, s1, s2, c1, c2);
   };
   auto update = [&](int k0) {
     if (!wave_rows || k0 > wave_kmax) return;
     if (masked(k0)) fwd_update<true, NKB>(st, s1, s2, c1, c2, k0, lim_row, grp);
-    else fwd_post<NKB>(st, s1, s2, pre);
+    else fwd_post_held<NKB>(st, s1, s2, pre);
   };
 
   for (int t = 0; t < ntiles; ++t) {

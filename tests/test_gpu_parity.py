@@ -173,6 +173,50 @@ def run_sampled(w, dev, settings, heads=None, mode=sk.BWD_AUTO, dk_tail=2048, nr
     return kl, grads
 
 
+def _tile_scaled_inputs(kind, n_q, n_k, d, seed):
+    """Q near a common direction and K scaled per 128-key tile: "rising"
+    moves the row maxima of the logits up by about 80 (base-2 units) per
+    tile; "sinking" puts every logit near -270, where terms taken against an
+    offset of 0 would all underflow."""
+    r = np.random.default_rng(seed)
+    q = 1.0 + 0.3 * r.standard_normal((n_q, d))
+    k = 1.0 + 0.3 * r.standard_normal((n_k, d))
+    tile = np.arange(n_k) // 128
+    if kind == "rising":
+        scale = 5.0 * tile + 0.05
+    else:
+        scale = -18.0 + 0.05 * tile
+    return q, k * scale[:, None]
+
+
+@pytest.mark.parametrize("kind", ["rising", "sinking"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_row_maxima_far_from_the_first_tile(kind, causal, cuda_device):
+    """Logit maxima that move by hundreds (base 2) from one key tile to the
+    next, or all far below 0: the forward kernels hold the offsets over
+    later tiles and must raise them when a tile's terms pass their bound, and
+    take the first tile's own maxima.  Every row against the oracle, the
+    unsplit long-range form and the split form."""
+    n_q, n_k, d, H = 512, 1024, 128, 2
+    ins = []
+    for h in range(H):
+        q1, k1 = _tile_scaled_inputs(kind, n_q, n_k, d, 40 + h)
+        q2, k2 = _tile_scaled_inputs(kind, n_q, n_k, d, 50 + h)
+        ins.append((q1, 0.9 * k1, q2, k2))
+    to = lambda i: torch.tensor(np.stack([x[i] for x in ins])[None], dtype=torch.bfloat16,  # noqa: E731
+                                device=cuda_device).contiguous()
+    q1, k1, q2, k2 = (to(i) for i in range(4))
+    for sp in (1, 0):
+        _say(f"  fwd {kind} causal={causal} splits={sp}")
+        kl, l1, l2 = (to_np(t) for t in sk.streamkl_fwd(q1, k1, q2, k2, causal, num_splits=sp))
+        for h in range(H):
+            hi = head_inputs(q1, k1, q2, k2, 0, h)
+            ref = oracle.head_forward(*hi, causal)
+            assert np.isfinite(ref[0]).all()
+            check_forward_rows(f"{kind} c{int(causal)} sp{sp} h{h}", kl[0, h], l1[0, h], l2[0, h], ref,
+                               torch.bfloat16)
+
+
 def test_workload_8k_causal_both_settings(cuda_device):
     w = workloads.WORKLOADS["h32-n8k-d128-bf16-causal"]
     run_sampled(w, cuda_device, settings=(1, 2), heads=[0, 13, 31], nrows=256)
