@@ -258,7 +258,7 @@ FwdLaunch pick_fwd(int dtype, int d1, int d2) {
 }
 FwdLaunch pick_fwd_pp(int dtype, int d1, int d2) {
 #define SKL_PICK(tn, a, b) if (d1 == a && d2 == b) return launch_fwd_pp_##tn##_##a##_##b;
-  if (dtype == STREAMKL_F32) { SKL_PICK(f32, 64, 64) SKL_PICK(f32, 64, 128) SKL_PICK(f32, 128, 64) SKL_PICK(f32, 128, 128) }
+  if (dtype == STREAMKL_F32) { SKL_PICK(f32, 64, 64) }  // see use_pp
   else { SKL_PICK(bf16, 64, 64) SKL_PICK(bf16, 64, 128) SKL_PICK(bf16, 128, 64) SKL_PICK(bf16, 128, 128) }
 #undef SKL_PICK
   return nullptr;
@@ -349,11 +349,19 @@ struct FwdPlan {
   int64_t loss_slots;   // workgroups that finalize rows: one fused-loss partial each
 };
 
+// The ping-pong forward for an unsplit query range longer than one 4-wave
+// workgroup's rows, except fp32 with head dims past 64 + 64, whose operand
+// fragments do not fit two waves per SIMD without spilling: those keep the
+// 4-wave form at one wave per SIMD.
+bool use_pp(const streamkl_shape* s) {
+  return s->n_q > kFwdRows && !(s->dtype == STREAMKL_F32 && s->d1 + s->d2 > 128);
+}
+
 FwdPlan make_fwd_plan(const streamkl_shape* s, int splits) {
   FwdPlan p;
   const int64_t BH = s->B * s->H;
   p.splits = splits;
-  p.pp = splits == 1 && s->n_q > kFwdRows;
+  p.pp = splits == 1 && use_pp(s);
   p.dec = splits > 1 && decode_shape(s);
   p.nqb = cdiv(s->n_q, p.pp ? kFwdPPRows : kFwdRows);
   p.grid = p.dec ? BH * cdiv(splits, 4) : BH * p.nqb * splits;
@@ -690,7 +698,7 @@ FwdCall summarize(const streamkl_shape* s, int causal, const std::vector<int>& s
     if (e.n_q == 0) continue;
     c.rows += (double)(e.B * e.H * e.n_q);
     if (group && splits[b] == 1) {
-      (e.n_q > kFwdRows ? pp : plain).push_back(b);
+      (use_pp(&e) ? pp : plain).push_back(b);
       continue;
     }
     if (group && group_dec && decode_shape(&e)) {

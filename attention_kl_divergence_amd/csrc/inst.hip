@@ -26,15 +26,21 @@ hipError_t fwd_go(const FwdArgs& a, int64_t nblocks, hipStream_t st, const RT& r
   return hipGetLastError();
 }
 
+// fp32 with head dims past 64 + 64 has no ping-pong form (its fragments
+// spill at two waves per SIMD; the planner keeps those on the 4-wave kernel)
 template <typename RT>
 hipError_t fwd_pp_go(const FwdArgs& a, int64_t nblocks, hipStream_t st, const RT& rt) {
-  constexpr int BK = kFwdPPTile<SKL_T>;
-  const dim3 g((unsigned)nblocks), b(512);
-  if (a.lpart)
-    hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, BK, true, RT>), g, b, 0, st, a, rt);
-  else
-    hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, BK, false, RT>), g, b, 0, st, a, rt);
-  return hipGetLastError();
+  if constexpr (sizeof(SKL_T) == 4 && SKL_D1 + SKL_D2 > 128) {
+    return hipErrorInvalidValue;
+  } else {
+    constexpr int BK = kFwdPPTile<SKL_T>;
+    const dim3 g((unsigned)nblocks), b(512);
+    if (a.lpart)
+      hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, BK, true, RT>), g, b, 0, st, a, rt);
+    else
+      hipLaunchKernelGGL((fwd_pp_kernel<SKL_T, SKL_D1, SKL_D2, BK, false, RT>), g, b, 0, st, a, rt);
+    return hipGetLastError();
+  }
 }
 
 template <typename RT>

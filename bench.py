@@ -264,7 +264,7 @@ def main():
     # bf16 query ranges, the 8-wave ping-pong form for long unsplit ones
     if splits > 1 and w.dtype == "bf16" and w.n_q <= 32:
         fwd_kernel = "fwd_decode_kernel"
-    elif splits == 1 and w.n_q > 128:
+    elif splits == 1 and w.n_q > 128 and not (w.dtype == "f32" and w.d1 + w.d2 > 128):
         fwd_kernel = "fwd_pp_kernel"
     else:
         fwd_kernel = "fwd_kernel"
