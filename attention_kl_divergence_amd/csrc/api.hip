@@ -399,8 +399,8 @@ BwdWork bwd_work(const streamkl_shape* s, int causal, int setting) {
   w.f_sep = heads * pairs * (f_qk + f_grad);
   w.f_fused = heads * pairs * (f_qk + 2 * f_grad);
   w.atomic = heads * pairs * 4.0 * ds / kBwdKRows;
-  w.wg_dk = heads * cdiv(s->n_k, kBwdKRowsSep);
-  w.wg_dq = heads * cdiv(s->n_q, kBwdQRows);
+  w.wg_dk = heads * cdiv(s->n_k, bwd_rows(s->dtype == STREAMKL_F32));
+  w.wg_dq = heads * cdiv(s->n_q, bwd_rows(s->dtype == STREAMKL_F32));
   w.wg_fk = heads * cdiv(s->n_k, kBwdKRows);
   return w;
 }
@@ -1088,7 +1088,7 @@ streamkl_status bwd_launch(int setting, const void* Q1, const void* K1, const vo
   BwdArgs a = bwd_args(Q1, K1, Q2, K2, causal, scale1, scale2, kl, lse1, lse2, d_kl, shape, qs, ks);
   a.dq = dQ; a.dk = dK;
   a.scale_s = setting == 1 ? plain_scale(scale2, shape->d2) : plain_scale(scale1, shape->d1);
-  const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
+  const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, bwd_rows(shape->dtype == STREAMKL_F32));
   const int ds = setting == 1 ? shape->d2 : shape->d1;
   streamkl_status st;
   if (mode != STREAMKL_BWD_DQ_ONLY && !cleared) {
@@ -1109,7 +1109,7 @@ streamkl_status bwd_launch(int setting, const void* Q1, const void* K1, const vo
     return hip_status(fk(a, setting, true, a.BH * nkb, s, nullptr));
   }
   if (mode != STREAMKL_BWD_DQ_ONLY) {
-    const int64_t nkb8 = cdiv(a.n_k, kBwdKRowsSep);  // the separate dK kernel's 8-wave key blocks
+    const int64_t nkb8 = cdiv(a.n_k, bwd_rows(shape->dtype == STREAMKL_F32));  // the separate dK kernel's key blocks
     a.nblk = (int)nkb8;
     st = hip_status(fk(a, setting, false, a.BH * nkb8, s, nullptr));
     if (st != STREAMKL_OK) return st;
@@ -1131,7 +1131,7 @@ streamkl_status joint_launch(const void* Q1, const void* K1, const void* Q2, con
   a.dk = dK1; a.dk2 = dK2;
   a.scale_s = plain_scale(scale1, shape->d1);
   a.scale_s2 = plain_scale(scale2, shape->d2);
-  const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, kBwdQRows);
+  const int64_t nkb = cdiv(a.n_k, kBwdKRows), nqb = cdiv(a.n_q, bwd_rows(false));  // bf16 only
   streamkl_status st;
   if (mode != STREAMKL_BWD_DQ_ONLY) {
     st = cleared ? STREAMKL_OK : clear_shared_dk(dK1, shape, shape->d1, a.g1, ks, s);
@@ -1192,14 +1192,16 @@ streamkl_status bwd_group(int setting, const void* Q1, const void* K1, const voi
   a.scale_s = setting == 1 ? plain_scale(scale2, shape->d2) : plain_scale(scale1, shape->d1);
   if (mode != STREAMKL_BWD_DQ_ONLY) {
     for (const RaggedLaunch& L :
-         ragged_launches(shape, causal, els, [](const streamkl_shape& e) { return cdiv(e.n_k, kBwdKRowsSep); })) {
+         ragged_launches(shape, causal, els,
+                         [](const streamkl_shape& e) { return cdiv(e.n_k, bwd_rows(e.dtype == STREAMKL_F32)); })) {
       const streamkl_status st = hip_status(fk(a, setting, false, L.grid, s, &L.t));
       if (st != STREAMKL_OK) return st;
     }
   }
   if (mode == STREAMKL_BWD_DK_ONLY) return STREAMKL_OK;
   for (const RaggedLaunch& L :
-       ragged_launches(shape, causal, els, [](const streamkl_shape& e) { return cdiv(e.n_q, kBwdQRows); })) {
+       ragged_launches(shape, causal, els,
+                       [](const streamkl_shape& e) { return cdiv(e.n_q, bwd_rows(e.dtype == STREAMKL_F32)); })) {
     const streamkl_status st = hip_status(fq(a, setting, L.grid, s, &L.t));
     if (st != STREAMKL_OK) return st;
   }
@@ -1257,8 +1259,8 @@ streamkl_status joint_group(const void* Q1, const void* K1, const void* Q2, cons
     }
     if (mode == STREAMKL_BWD_DK_ONLY) return STREAMKL_OK;
   }
-  const std::vector<RaggedLaunch> qls =
-      ragged_launches(shape, causal, els, [](const streamkl_shape& e) { return cdiv(e.n_q, kBwdQRows); });
+  const std::vector<RaggedLaunch> qls =  // the joint backward is bf16 only
+      ragged_launches(shape, causal, els, [](const streamkl_shape& e) { return cdiv(e.n_q, bwd_rows(false)); });
   a.dq = dQ1;
   for (const RaggedLaunch& L : qls) {
     st = hip_status(fq(a, 2, L.grid, s, &L.t));

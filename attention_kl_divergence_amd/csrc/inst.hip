@@ -45,7 +45,7 @@ hipError_t fwd_pp_go(const FwdArgs& a, int64_t nblocks, hipStream_t st, const RT
 
 template <typename RT>
 hipError_t dq_go(const BwdArgs& a, int setting, int64_t nblocks, hipStream_t st, const RT& rt) {
-  constexpr int W = kBwdQWaves;
+  constexpr int W = kBwdWaves<SKL_T>;
   const dim3 g((unsigned)nblocks), b(64 * W);
   if (setting == 1)
     hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 1, kBwdKeyTile, W, RT>), g, b, 0, st, a, rt);
@@ -67,11 +67,11 @@ hipError_t joint_dk_go(const BwdArgs& a, dim3 g, hipStream_t st, const RT& rt) {
   }
 }
 
-// The separate (8-wave) and joint dK kernels; the fused (4-wave) form runs
-// plain launches only.
+// The separate (8-wave in bf16, 4-wave in fp32) and joint dK kernels; the
+// fused (4-wave) form runs plain launches only.
 template <typename RT>
 hipError_t dk_go(const BwdArgs& a, int setting, bool fused, int64_t nblocks, hipStream_t st, const RT& rt) {
-  constexpr int W = kBwdKWaves;
+  constexpr int W = kBwdWaves<SKL_T>;
   constexpr int BQ = kBwdQTile<SKL_T>;
   const dim3 g((unsigned)nblocks), b(256), b8(64 * W);
   if (setting == 3) return fused ? hipErrorInvalidValue : joint_dk_go(a, g, st, rt);

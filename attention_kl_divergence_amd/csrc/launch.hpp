@@ -21,12 +21,14 @@ constexpr int kFwdTile = 64;      // key rows per forward LDS tile
 template <typename T> constexpr int kFwdPPTile = sizeof(T) == 2 ? 128 : 64;
 constexpr int kDecRows = 32;      // longest query range of the decode forward (one wave's rows)
 constexpr int kDecBlock = 32;     // key rows per decode-forward block
-constexpr int kBwdQWaves = 8;     // waves per dQ workgroup
-constexpr int kBwdQRows = 32 * kBwdQWaves;  // query rows per dQ workgroup
+// waves per dQ workgroup and per separate single-setting dK workgroup: 8
+// (two per SIMD) in bf16; 4 in fp32, whose operand fragments would spill at
+// two waves per SIMD
+template <typename T> constexpr int kBwdWaves = sizeof(T) == 2 ? 8 : 4;
+// their query (dQ) or key (dK) rows per workgroup, 32 per wave
+constexpr int bwd_rows(bool f32) { return f32 ? 32 * 4 : 32 * 8; }
 constexpr int kBwdKeyTile = 64;   // key rows per dQ-kernel LDS tile
 constexpr int kBwdKRows = 128;    // key rows per dK workgroup (4 waves x 32): fused and joint forms
-constexpr int kBwdKWaves = 8;     // waves of the separate single-setting dK workgroup
-constexpr int kBwdKRowsSep = 32 * kBwdKWaves;  // its key rows
 constexpr int kDecBwdTile = 128;  // key rows per tile of the decode backward (4 waves x 32)
 // query rows per LDS tile of the dK kernel (fp32 tiles are twice as large)
 template <typename T> constexpr int kBwdQTile = sizeof(T) == 2 ? 64 : 32;
