@@ -48,9 +48,9 @@ hipError_t dq_go(const BwdArgs& a, int setting, int64_t nblocks, hipStream_t st,
   constexpr int W = kBwdWaves<SKL_T>;
   const dim3 g((unsigned)nblocks), b(64 * W);
   if (setting == 1)
-    hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 1, kBwdKeyTile, W, RT>), g, b, 0, st, a, rt);
+    hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 1, kBwdKeyTile<SKL_T>, W, RT>), g, b, 0, st, a, rt);
   else if (setting == 2)
-    hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 2, kBwdKeyTile, W, RT>), g, b, 0, st, a, rt);
+    hipLaunchKernelGGL((bwd_dq_kernel<SKL_T, SKL_D1, SKL_D2, 2, kBwdKeyTile<SKL_T>, W, RT>), g, b, 0, st, a, rt);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

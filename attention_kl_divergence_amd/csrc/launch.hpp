@@ -27,7 +27,8 @@ constexpr int kDecBlock = 32;     // key rows per decode-forward block
 template <typename T> constexpr int kBwdWaves = sizeof(T) == 2 ? 8 : 4;
 // their query (dQ) or key (dK) rows per workgroup, 32 per wave
 constexpr int bwd_rows(bool f32) { return f32 ? 32 * 4 : 32 * 8; }
-constexpr int kBwdKeyTile = 64;   // key rows per dQ-kernel LDS tile
+// key rows per dQ-kernel LDS tile (fp32: 32, whose 64-key tiles spill)
+template <typename T> constexpr int kBwdKeyTile = sizeof(T) == 2 ? 64 : 32;
 constexpr int kBwdKRows = 128;    // key rows per dK workgroup (4 waves x 32): fused and joint forms
 constexpr int kDecBwdTile = 128;  // key rows per tile of the decode backward (4 waves x 32)
 // query rows per LDS tile of the dK kernel (fp32 tiles are twice as large)
