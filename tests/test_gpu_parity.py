@@ -173,48 +173,54 @@ def run_sampled(w, dev, settings, heads=None, mode=sk.BWD_AUTO, dk_tail=2048, nr
     return kl, grads
 
 
-def _tile_scaled_inputs(kind, n_q, n_k, d, seed):
-    """Q near a common direction and K scaled per 128-key tile: "rising"
-    moves the row maxima of the logits up by about 80 (base-2 units) per
-    tile; "sinking" puts every logit near -270, where terms taken against an
-    offset of 0 would all underflow."""
+def _tile_scaled_inputs(kind, n_q, n_k, d, seed, tile_rows):
+    """Q near a common direction and K scaled per key tile of the forward
+    (tile_rows keys): "rising" moves the row maxima of the logits up by about
+    80 (base-2 units, default scale) per tile; "sinking" puts every logit near
+    -270, where terms taken against an offset of 0 would all underflow."""
     r = np.random.default_rng(seed)
     q = 1.0 + 0.3 * r.standard_normal((n_q, d))
     k = 1.0 + 0.3 * r.standard_normal((n_k, d))
-    tile = np.arange(n_k) // 128
+    tile = np.arange(n_k) // tile_rows
+    unit = np.log2(np.e) * np.sqrt(d)  # base-2 logit of q . k per unit of key scale (q, k near all-ones)
     if kind == "rising":
-        scale = 5.0 * tile + 0.05
+        scale = (80.0 * tile + 1.0) / unit
     else:
-        scale = -18.0 + 0.05 * tile
+        scale = (-290.0 + 1.0 * tile) / unit
     return q, k * scale[:, None]
 
 
+# (dtype, head dim, key rows per forward tile of the long-range kernel)
+FAR_CASES = [("bf16", 128, 128), ("f32", 64, 64)]
+
+
+@pytest.mark.parametrize("dtype,d,tile_rows", FAR_CASES, ids=[f"{c[0]}-d{c[1]}" for c in FAR_CASES])
 @pytest.mark.parametrize("kind", ["rising", "sinking"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_forward_row_maxima_far_from_the_first_tile(kind, causal, cuda_device):
+def test_forward_row_maxima_far_from_the_first_tile(kind, causal, dtype, d, tile_rows, cuda_device):
     """Logit maxima that move by hundreds (base 2) from one key tile to the
     next, or all far below 0: the forward kernels hold the offsets over
     later tiles and must raise them when a tile's terms pass their bound, and
     take the first tile's own maxima.  Every row against the oracle, the
     unsplit long-range form and the split form."""
-    n_q, n_k, d, H = 512, 1024, 128, 2
+    n_q, n_k, H = 512, 8 * tile_rows, 2  # eight key tiles
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     ins = []
     for h in range(H):
-        q1, k1 = _tile_scaled_inputs(kind, n_q, n_k, d, 40 + h)
-        q2, k2 = _tile_scaled_inputs(kind, n_q, n_k, d, 50 + h)
+        q1, k1 = _tile_scaled_inputs(kind, n_q, n_k, d, 40 + h, tile_rows)
+        q2, k2 = _tile_scaled_inputs(kind, n_q, n_k, d, 50 + h, tile_rows)
         ins.append((q1, 0.9 * k1, q2, k2))
-    to = lambda i: torch.tensor(np.stack([x[i] for x in ins])[None], dtype=torch.bfloat16,  # noqa: E731
+    to = lambda i: torch.tensor(np.stack([x[i] for x in ins])[None], dtype=tdt,  # noqa: E731
                                 device=cuda_device).contiguous()
     q1, k1, q2, k2 = (to(i) for i in range(4))
     for sp in (1, 0):
-        _say(f"  fwd {kind} causal={causal} splits={sp}")
+        _say(f"  fwd {kind} {dtype} d{d} causal={causal} splits={sp}")
         kl, l1, l2 = (to_np(t) for t in sk.streamkl_fwd(q1, k1, q2, k2, causal, num_splits=sp))
         for h in range(H):
             hi = head_inputs(q1, k1, q2, k2, 0, h)
             ref = oracle.head_forward(*hi, causal)
             assert np.isfinite(ref[0]).all()
-            check_forward_rows(f"{kind} c{int(causal)} sp{sp} h{h}", kl[0, h], l1[0, h], l2[0, h], ref,
-                               torch.bfloat16)
+            check_forward_rows(f"{kind} {dtype} c{int(causal)} sp{sp} h{h}", kl[0, h], l1[0, h], l2[0, h], ref, tdt)
 
 
 def test_workload_8k_causal_both_settings(cuda_device):
