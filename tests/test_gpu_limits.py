@@ -41,3 +41,28 @@ def test_longest_key_range(cuda_device):
                        w.torch_dtype)
     rdq, _ = oracle.head_backward(1, *hi, w.causal, to_np(g[0, 0]), rows=rows, block=4, want_dk=False)
     check_grad(f"{w.name} dQ", to_np(dq[0, 0])[rows], rdq)
+
+
+def test_longest_key_range_unsplit_long_query_form(cuda_device):
+    """2^24 keys streamed by the unsplit long-range forward (256 query rows,
+    one split): 131072 key tiles through the ping-pong kernel, whose unmasked
+    tiles hold the state's offsets. The first tile dominates row 0, a late
+    tile (keys 2^23 .. 2^23 + 31, 6x row 100's query, logits near 100 in
+    base 2) dominates row 100, so that row's offsets must rise far into the
+    range; compared with the fp64 oracle."""
+    w = workloads.Workload("nk-2^24-nq256-d128-bf16", 1, 1, 256, 1 << 24, 128, 128, "bf16", False, 0.5, False, 14)
+    print(f"generate {w.name}", flush=True)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    late = 1 << 23
+    for q, k in ((q1, k1), (q2, k2)):
+        k[0, 0, 0:32] = (3 * q[0, 0, 0].float()).to(k.dtype)
+        k[0, 0, late:late + 32] = (6 * q[0, 0, 100].float()).to(k.dtype)
+    print("forward, one split", flush=True)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal, num_splits=1)
+    torch.cuda.synchronize()
+    rows = np.array([0, 100, 255])
+    print("oracle", flush=True)
+    hi = [to_np(t[0, 0]) for t in (q1, k1, q2, k2)]
+    ref = oracle.head_forward(*hi, w.causal, rows=rows, block=4)
+    check_forward_rows(w.name, to_np(kl[0, 0])[rows], to_np(l1[0, 0])[rows], to_np(l2[0, 0])[rows], ref,
+                       w.torch_dtype)
