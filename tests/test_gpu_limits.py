@@ -1,4 +1,7 @@
-"""The largest key range the boundary accepts (2^24 keys), bf16, d = 128.
+"""The largest sizes the boundary accepts: 2^24 keys (bf16, d = 128) and
+2^20 query heads over the batch.
+
+2^24 keys:
 
 Each K row is 256 bytes, so the whole range is 2^32 bytes: the direct-to-LDS
 tile loaders must size their buffers by the tile, not by the rows left (a
@@ -66,3 +69,31 @@ def test_longest_key_range_unsplit_long_query_form(cuda_device):
     ref = oracle.head_forward(*hi, w.causal, rows=rows, block=4)
     check_forward_rows(w.name, to_np(kl[0, 0])[rows], to_np(l1[0, 0])[rows], to_np(l2[0, 0])[rows], ref,
                        w.torch_dtype)
+
+
+@pytest.mark.parametrize("dt,n", [("bf16", 8), ("f32", 40)])
+def test_most_heads(dt, n, cuda_device):
+    """B * H = 2^20, the most the boundary accepts (a grid of 2^20 or more
+    workgroups): forward and both backward settings, sampled heads against
+    the fp64 oracle. bf16 with 8 rows takes the decode kernels, fp32 with 40
+    rows the 4-wave forward and the separate backward."""
+    w = workloads.Workload(f"bh-2^20-n{n}-{dt}", 1024, 1024, n, n, 64, 64, dt, False, 0.5, False, 15)
+    print(f"generate {w.name}", flush=True)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    print("forward", flush=True)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal)
+    grads = {}
+    for s in (1, 2):
+        print(f"backward setting {s}", flush=True)
+        grads[s] = sk.streamkl_bwd(s, q1, k1, q2, k2, w.causal, kl, l1, l2, g)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (511, 777), (1023, 1023)):
+        hi = [to_np(t[b, h]) for t in (q1, k1, q2, k2)]
+        ref = oracle.head_forward(*hi, w.causal)
+        check_forward_rows(f"{w.name} b{b}h{h}", to_np(kl[b, h]), to_np(l1[b, h]), to_np(l2[b, h]), ref,
+                           w.torch_dtype)
+        for s in (1, 2):
+            rdq, rdk = oracle.head_backward(s, *hi, w.causal, to_np(g[b, h]))
+            check_grad(f"{w.name} b{b}h{h} s{s} dQ", to_np(grads[s][0][b, h]), rdq)
+            check_grad(f"{w.name} b{b}h{h} s{s} dK", to_np(grads[s][1][b, h]), rdk)
