@@ -1,9 +1,7 @@
 """The largest sizes the boundary accepts: 2^24 keys (bf16, d = 128) and
 2^20 query heads over the batch.
 
-2^24 keys:
-
-Each K row is 256 bytes, so the whole range is 2^32 bytes: the direct-to-LDS
+With 2^24 keys each K row is 256 bytes, so the whole range is 2^32 bytes: the direct-to-LDS
 tile loaders must size their buffers by the tile, not by the rows left (a
 size of 2^32 wraps to 0 and the tile reads as zeros).  The first key tile is
 made to dominate rows 0 and 17 (keys 0-31 and 32-63 are 3x those rows'
