@@ -1,5 +1,5 @@
-"""The largest sizes the boundary accepts: 2^24 keys (bf16, d = 128) and
-2^20 query heads over the batch.
+"""The largest sizes the boundary accepts: 2^24 keys or 2^24 query rows
+(bf16, d = 128) and 2^20 query heads over the batch.
 
 With 2^24 keys each K row is 256 bytes, so the whole range is 2^32 bytes: the direct-to-LDS
 tile loaders must size their buffers by the tile, not by the rows left (a
@@ -95,3 +95,35 @@ def test_most_heads(dt, n, cuda_device):
             rdq, rdk = oracle.head_backward(s, *hi, w.causal, to_np(g[b, h]))
             check_grad(f"{w.name} b{b}h{h} s{s} dQ", to_np(grads[s][0][b, h]), rdq)
             check_grad(f"{w.name} b{b}h{h} s{s} dK", to_np(grads[s][1][b, h]), rdk)
+
+
+def test_most_query_rows(cuda_device):
+    """2^24 query rows against 64 keys (bf16, d = 128, not causal): Q is 2^32
+    bytes per head, so row offsets need 64 bits in the forward, the
+    query-outer dQ kernel and the key-outer dK kernel's query tiles. The
+    upstream gradient is 0 except on 3072 rows at the start, the middle and
+    the end, so dK is those rows' contribution alone: with the forward and
+    dQ of those rows, it is checked against the fp64 oracle on just them."""
+    w = workloads.Workload("nq-2^24-nk64-d128-bf16", 1, 1, 1 << 24, 64, 128, 128, "bf16", False, 0.5, False, 16)
+    print(f"generate {w.name}", flush=True)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    n = 1 << 24
+    rows = np.concatenate([np.arange(0, 1024), np.arange(n // 2, n // 2 + 1024), np.arange(n - 1024, n)])
+    g = torch.zeros((1, 1, n), device=cuda_device)
+    gen = torch.Generator(device=cuda_device).manual_seed(17)
+    idx = torch.tensor(rows, device=cuda_device)
+    g[0, 0, idx] = torch.randn(len(rows), generator=gen, device=cuda_device) / len(rows)
+    print("forward", flush=True)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal)
+    print("backward", flush=True)
+    dq, dk = sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g, bwd_mode=sk.BWD_SEPARATE)
+    torch.cuda.synchronize()
+    print("oracle", flush=True)
+    sub = [to_np(q1[0, 0, idx]), to_np(k1[0, 0]), to_np(q2[0, 0, idx]), to_np(k2[0, 0])]
+    ref = oracle.head_forward(*sub, w.causal)
+    check_forward_rows(w.name, to_np(kl[0, 0, idx]), to_np(l1[0, 0, idx]), to_np(l2[0, 0, idx]), ref,
+                       w.torch_dtype)
+    rdq, rdk = oracle.head_backward(1, *sub, w.causal, to_np(g[0, 0, idx]))
+    check_grad(f"{w.name} dQ", to_np(dq[0, 0, idx]), rdq)
+    check_grad(f"{w.name} dK", to_np(dk[0, 0]), rdk)
+    assert (dq[0, 0, 1024:2048] == 0).all()  # rows with g = 0
