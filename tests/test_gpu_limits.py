@@ -115,15 +115,18 @@ def test_most_query_rows(cuda_device):
     g[0, 0, idx] = torch.randn(len(rows), generator=gen, device=cuda_device) / len(rows)
     print("forward", flush=True)
     kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal)
-    print("backward", flush=True)
-    dq, dk = sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g, bwd_mode=sk.BWD_SEPARATE)
-    torch.cuda.synchronize()
     print("oracle", flush=True)
     sub = [to_np(q1[0, 0, idx]), to_np(k1[0, 0]), to_np(q2[0, 0, idx]), to_np(k2[0, 0])]
     ref = oracle.head_forward(*sub, w.causal)
     check_forward_rows(w.name, to_np(kl[0, 0, idx]), to_np(l1[0, 0, idx]), to_np(l2[0, 0, idx]), ref,
                        w.torch_dtype)
     rdq, rdk = oracle.head_backward(1, *sub, w.causal, to_np(g[0, 0, idx]))
-    check_grad(f"{w.name} dQ", to_np(dq[0, 0, idx]), rdq)
-    check_grad(f"{w.name} dK", to_np(dk[0, 0]), rdk)
-    assert (dq[0, 0, 1024:2048] == 0).all()  # rows with g = 0
+    # the separate kernels, and the fused kernel whose dQ goes out by atomics
+    for mode in (sk.BWD_SEPARATE, sk.BWD_FUSED):
+        print(f"backward mode {mode}", flush=True)
+        dq, dk = sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g, bwd_mode=mode)
+        torch.cuda.synchronize()
+        check_grad(f"{w.name} m{mode} dQ", to_np(dq[0, 0, idx]), rdq)
+        check_grad(f"{w.name} m{mode} dK", to_np(dk[0, 0]), rdk)
+        assert (dq[0, 0, 1024:2048] == 0).all()  # rows with g = 0
+        del dq, dk
