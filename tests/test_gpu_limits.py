@@ -130,3 +130,36 @@ def test_most_query_rows(cuda_device):
         check_grad(f"{w.name} m{mode} dK", to_np(dk[0, 0]), rdk)
         assert (dq[0, 0, 1024:2048] == 0).all()  # rows with g = 0
         del dq, dk
+
+
+def test_longest_key_range_decode(cuda_device):
+    """16 query rows against 2^24 keys: the split-K decode forward and the
+    decode backward stream K1, K2 (2^32 bytes each) and write dK (2^33
+    bytes). Every row's forward and dQ, and dK of keys at the start, the
+    middle and the end, against the fp64 oracle."""
+    w = workloads.Workload("dec-nk-2^24-d128-bf16", 1, 1, 16, 1 << 24, 128, 128, "bf16", False, 0.5, False, 18)
+    print(f"generate {w.name}", flush=True)
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    # the first key tile dominates row 0 in the teacher only. With it in both
+    # models, row 0's P1 and P2 on those keys both sit near 1/32 and differ
+    # by about 1e-9, below what their fp32 exponentials resolve: that row's
+    # dS there is rounding noise as large as the other rows' whole dK on
+    # those keys (the separate and the decode backward both miss by 1.5e-2)
+    k1[0, 0, 0:32] = (3 * q1[0, 0, 0].float()).to(k1.dtype)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    print("forward", flush=True)
+    kl, l1, l2 = sk.streamkl_fwd(q1, k1, q2, k2, w.causal)
+    print("backward", flush=True)
+    dq, dk = sk.streamkl_bwd(1, q1, k1, q2, k2, w.causal, kl, l1, l2, g)
+    torch.cuda.synchronize()
+    print("oracle", flush=True)
+    hi = [to_np(t[0, 0]) for t in (q1, k1, q2, k2)]
+    ref = oracle.head_forward(*hi, w.causal, block=2)
+    check_forward_rows(w.name, to_np(kl[0, 0]), to_np(l1[0, 0]), to_np(l2[0, 0]), ref, w.torch_dtype)
+    gn = to_np(g[0, 0])
+    rdq, _ = oracle.head_backward(1, *hi, w.causal, gn, block=2, want_dk=False)
+    check_grad(f"{w.name} dQ", to_np(dq[0, 0]), rdq)
+    n = 1 << 24
+    keys = np.concatenate([np.arange(0, 64), np.arange(n // 2, n // 2 + 64), np.arange(n - 64, n)])
+    rdk = oracle.head_dk_keys(1, *hi, w.causal, gn, keys, ref)
+    check_grad(f"{w.name} dK", to_np(dk[0, 0])[keys], rdk)
