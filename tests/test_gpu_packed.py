@@ -182,3 +182,36 @@ def test_packed_autograd_loss(cuda_device):
     assert abs(loss_b.item() - loss_a.item()) <= 1e-5 * abs(loss_a.item())
     for a, b, n in zip(pad_leaves, pk_leaves, (q_len, k_len, q_len, k_len)):
         assert torch.equal(b.grad, _pack(a.grad, n))
+
+
+def test_packed_ragged_workload_full_size(cuda_device):
+    """The ragged benchmark workload (causal sequences of 8K, 16K, 4K and 32K
+    rows, 32 heads) packed, as the benchmark's packed line runs it: sampled
+    rows of every sequence on two heads, forward and dQ, against the oracle;
+    the packed outputs equal the padded call's on every sequence's rows."""
+    w = workloads.WORKLOADS["ragged-b4-h32-n32k-d128-bf16-causal"]
+    q1, k1, q2, k2 = workloads.generate(w, cuda_device)
+    L = list(w.lengths)
+    g = workloads.upstream_grad(w, cuda_device, "random")
+    off = _offsets(L)
+    P = [_pack(t, L) for t in (q1, k1, q2, k2)]
+    gp = _pack(g, L)
+    print("packed ragged workload", flush=True)
+    kl, l1, l2 = sk.streamkl_fwd(*P, True, q_off=off, k_off=off)
+    dq, _ = sk.streamkl_bwd(1, *P, True, kl, l1, l2, gp, bwd_mode=sk.BWD_DQ_ONLY, q_off=off, k_off=off)
+    kla, l1a, l2a = sk.streamkl_fwd(q1, k1, q2, k2, True, q_len=L, k_len=L)
+    torch.cuda.synchronize()
+    assert torch.equal(kl, _pack(kla, L)) and torch.equal(l1, _pack(l1a, L)) and torch.equal(l2, _pack(l2a, L))
+    rng = np.random.default_rng(8)
+    gn = to_np(gp)
+    for b, n in enumerate(L):
+        o = off[b]
+        rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 24, replace=False)]))
+        for h in (0, 31):
+            print(f"oracle sequence {b} head {h}", flush=True)
+            hi = [to_np(t[h, o:o + n]) for t in P]
+            ref = oracle.head_forward(*hi, True, rows=rows, block=64)
+            check_forward_rows(f"packed ragged b{b}h{h}", to_np(kl[h, o:o + n])[rows], to_np(l1[h, o:o + n])[rows],
+                               to_np(l2[h, o:o + n])[rows], ref, w.torch_dtype)
+            rdq, _ = oracle.head_backward(1, *hi, True, gn[h, o:o + n], rows=rows, block=64, want_dk=False)
+            check_grad(f"packed ragged b{b}h{h} dQ rows", to_np(dq[h, o:o + n])[rows], rdq)
