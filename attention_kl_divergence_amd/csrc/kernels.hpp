@@ -570,16 +570,19 @@ __device__ __forceinline__ void fwd_post(RowState& st, const f32x16 (&t1)[NKB], 
   st.M2 = p.M2n;
 }
 
-// An unmasked tile's update with the state's offsets held.  The offsets M_t
-// need not be the running maxima: any M_t give the same KL and LSE as long as
-// no term 2^(y_t - M_t) overflows and the largest terms stay normal floats.
+// An unmasked tile's update with the state's offsets held.  The online
+// formulation (technical summary, Method 1) rescales by the running maxima;
+// the offsets M_t need not be those maxima: any M_t give the same KL and LSE
+// as long as no term 2^(y_t - M_t) overflows and the largest terms stay
+// normal floats.
 // fwd_pre_held turns the logits in place into t_t = y_t - M_t with the
 // state's offsets (0 for an offset still at -inf, whose sums are 0), so the
 // logits phase takes no tile maxima.  fwd_post_held sums 2^t.  A lane whose
 // state had no offset yet (its first unmasked tile), or whose tile sums pass
 // 2^64 or overflow, raises its offsets to the tile maxima of y instead (never
 // lowering them) and sums again.  So every offset is a maximum of y over keys
-// already seen, every term stays below 2^64 and the largest ones near 1.
+// already seen, every term stays below 2^64 and the largest ones at or
+// above 1.
 template <int NKB>
 __device__ __forceinline__ FwdPre fwd_pre_held(const RowState& st, f32x16 (&s1)[NKB], f32x16 (&s2)[NKB], float c1,
                                                float c2) {
